@@ -1,0 +1,247 @@
+"""Benchmark: one sparse MoE layer forward on one MI355X.
+
+A step is one whole-layer forward (router -> softmax/top-k -> capacity-limited
+dispatch -> SwiGLU expert GEMMs (+ shared expert) -> weighted combine -> load
+statistics) over one batch of synthetic input already resident in HBM.
+
+Prints one JSON line: tokens/s of the Mixtral-shaped layer (T=4096, d=4096,
+m=14336, E=8, k=2, bf16 activations and weights, fp32 router and accumulation),
+a per-phase time split measured with HIP events on the launch stream, the
+roofline fraction of the dominant kernel (expert GEMM1: gate/up + SwiGLU), and
+the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from sparse_mixture_experts_23_amd import _lib as L  # noqa: E402
+from sparse_mixture_experts_23_amd import api  # noqa: E402
+from sparse_mixture_experts_23_amd.workloads import CONFIGS, make_inputs  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+METRIC = "MoE-layer tokens/sec on 1 MI355X (Mixtral shape); expert-GEMM % of MFMA peak"
+
+# HBM counter calibration: FETCH_SIZE / WRITE_SIZE of the expert GEMM1 kernel over
+# one launch (KiB per dispatch), scaled by the ratio measured on a plain copy
+# kernel of known size.  None until taken for the current kernel.
+GEMM1_TRAFFIC_BYTES = None
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Stages:
+    """Pre-allocated buffers so that each C-ABI stage can be timed on its own."""
+
+    def __init__(self, shape, inp):
+        dev = inp.x.device
+        T, k, E, d, m = shape.T, shape.k, shape.E, shape.d, shape.m
+        R = L.moe_max_rows(shape)
+        self.shape, self.inp, self.R = shape, inp, R
+        z = lambda *s, dt=torch.int32: torch.empty(s, dtype=dt, device=dev)  # noqa: E731
+        self.ids, self.w, self.status = z(T, k), z(T, k, dt=torch.float32), z(1)
+        self.load, self.offsets, self.slot, self.row_of = z(E), z(E + 1), z(T, k), z(T, k)
+        self.src, self.stats = z(max(R, 1)), z(L.MOE_STAT_COUNT)
+        self.x_perm = z(max(R, 1), d, dt=inp.x.dtype)
+        self.h = z(max(R, 1), m, dt=inp.x.dtype)
+        self.H = z(max(R, 1), d, dt=torch.float32)
+        self.y = z(T, d, dt=torch.float32)
+        self.s = z(T, d, dt=torch.float32) if shape.m_shared else None
+        self.ws_d = api.workspace(shape, L.MOE_WS_DISPATCH, dev)
+        self.ws_f = api.workspace(shape, L.MOE_WS_FFN, dev)
+        self.ws_s = api.workspace(shape, L.MOE_WS_SHARED, dev) if shape.m_shared else None
+
+    def run(self, phase, st):
+        s, i, p = self.shape, self.inp, lambda t: None if t is None else t.data_ptr()  # noqa: E731
+        if phase == "route":
+            rc = L.moe_route(s, p(i.x), p(i.w_r), p(i.b_r), p(self.ids), p(self.w), p(self.status), st)
+        elif phase == "dispatch":
+            rc = L.moe_dispatch(s, p(i.x), p(self.ids), p(self.load), p(self.offsets), p(self.slot), p(self.row_of),
+                                p(self.src), p(self.x_perm), p(self.stats), p(self.ws_d), self.ws_d.numel(), st)
+        elif phase == "gemm1":
+            rc = L.moe_expert_gemm1(s, p(self.x_perm), p(self.offsets), p(i.w_gate), p(i.w_up), p(self.h),
+                                    p(self.ws_f), self.ws_f.numel(), st)
+        elif phase == "gemm2":
+            rc = L.moe_expert_gemm2(s, p(self.h), p(self.offsets), p(i.w_down), p(self.H), p(self.ws_f),
+                                    self.ws_f.numel(), st)
+        elif phase == "shared":
+            rc = L.moe_shared_ffn(s, p(i.x), p(i.s_gate), p(i.s_up), p(i.s_down), p(self.s), p(self.ws_s),
+                                  self.ws_s.numel(), st)
+        elif phase == "combine":
+            rc = L.moe_combine(s, p(self.H), p(self.row_of), p(self.w), p(self.s), p(self.y), st)
+        else:
+            raise ValueError(phase)
+        L.check(rc, phase)
+
+
+def cpu_baseline(cfg, inp, budget_tokens):
+    """Time the oracle, as it stands, on a bounded sample of the same workload:
+    the first `budget_tokens` tokens form the routing group (same d, m, E, k)."""
+    import numpy as np
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+    except Exception:  # pragma: no cover
+        threadpool_info = None
+    Ts = budget_tokens
+    x = inp.x[:Ts].float().cpu().numpy().astype(np.float64)
+    wr = inp.w_r.cpu().numpy()
+    b = None if inp.b_r is None else inp.b_r.cpu().numpy()
+    experts = (inp.w_gate.float().cpu().numpy(), inp.w_up.float().cpu().numpy(), inp.w_down.float().cpu().numpy())
+    shared = None
+    if cfg.m_shared:
+        shared = (inp.s_gate.float().cpu().numpy(), inp.s_up.float().cpu().numpy(), inp.s_down.float().cpu().numpy())
+    C = None if cfg.cf is None else O.capacity(Ts, cfg.k, cfg.E, *cfg.cf)
+    t0 = time.perf_counter()
+    O.forward(x, wr, b, experts, cfg.k, cfg.gate_mode, C=C, shared=shared, round_h_bf16=cfg.dtype == "bf16",
+              renorm_form=cfg.renorm_form)
+    dt = time.perf_counter() - t0
+    threads = 1
+    if threadpool_info is not None:
+        info = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if info:
+            threads = max(p.get("num_threads", 1) for p in info)
+    return {"value": Ts / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{Ts}-token routing group of the {cfg.name} layer (d={cfg.d}, m={cfg.m}, E={cfg.E}, "
+                      f"k={cfg.k}), fp64 numpy oracle, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mixtral", choices=sorted(CONFIGS))
+    ap.add_argument("--cpu-sample-tokens", type=int, default=48)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--phases", default="1", help="0 disables the per-phase timing loop")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this layer forward is built and timed on a single MI355X; "
+              "runs on more than one GPU are not supported.", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs the MI355X"
+
+    cfg = CONFIGS[args.workload]
+    log(f"[bench] workload {cfg.name}: generating inputs on the GPU")
+    inp = make_inputs(cfg, seed=0, device="cuda")
+    C = 0 if cfg.cf is None else api.capacity(cfg.T, cfg.k, cfg.E, *cfg.cf)
+    shape = api.make_shape(cfg.T, cfg.d, cfg.m, cfg.E, cfg.k, C, cfg.gate_mode, cfg.torch_dtype, cfg.m_shared)
+    layer = api.MoELayer(shape, "cuda")
+    fwd = lambda: layer.forward(inp.x, inp.w_r, inp.b_r, inp.w_gate, inp.w_up, inp.w_down,  # noqa: E731
+                                inp.s_gate, inp.s_up, inp.s_down)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        fwd()
+    torch.cuda.synchronize()
+    layer.check_status()
+    log(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        fwd()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed * 1e3 / max(args.steps, 1)
+    tokens_per_s = cfg.T / (ms / 1e3)
+    stats = layer.stats.cpu().tolist()
+    load = layer.load.cpu().tolist()
+    A = stats[L.MOE_STAT_ACCEPTED]
+    log(f"[bench] {ms:.3f} ms/step, {tokens_per_s:,.0f} tokens/s, accepted paths {A}")
+
+    # per-phase split with HIP events on the launch stream
+    phases = {}
+    if args.phases != "0":
+        stg = Stages(shape, inp)
+        st = torch.cuda.current_stream()
+        names = ["route", "dispatch", "gemm1", "gemm2"] + (["shared"] if cfg.m_shared else []) + ["combine"]
+        for n in names:   # warm each stage once
+            stg.run(n, st.cuda_stream)
+        torch.cuda.synchronize()
+        reps = max(args.steps, 1)
+        ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+              for n in names}
+        for r in range(reps):
+            for n in names:
+                a, b = ev[n][r]
+                a.record(st)
+                stg.run(n, st.cuda_stream)
+                b.record(st)
+        torch.cuda.synchronize()
+        for n in names:
+            phases[n] = sum(a.elapsed_time(b) for a, b in ev[n]) / reps
+        log("[bench] phases (ms): " + ", ".join(f"{n}={v:.4f}" for n, v in phases.items()))
+
+    d, m, k, T = cfg.d, cfg.m, cfg.k, cfg.T
+    es = 2 if cfg.dtype == "bf16" else 4
+    gemm1_flop = 4.0 * A * d * m           # gate and up: 2 * A * d * m each
+    gemm2_flop = 2.0 * A * d * m
+    active = sum(1 for v in load if v > 0)
+    roofline = None
+    extra = {}
+    if phases:
+        t1 = phases["gemm1"] * 1e-3
+        t2 = phases["gemm2"] * 1e-3
+        ach = gemm1_flop / t1 / 1e12
+        roofline = {"bound": "mfma", "kernel": "expert GEMM1 (gate/up + SwiGLU, bf16 MFMA)",
+                    "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                    "traffic": GEMM1_TRAFFIC_BYTES}
+        # algorithmic bytes of the memory-bound phases
+        route_bytes = T * d * es + 4 * cfg.E * d + 8 * T * k
+        disp_bytes = T * d * es + A * d * es + 12 * T * k + 4 * A
+        comb_bytes = A * d * 4 + T * d * 4 + 8 * T * k + (T * d * 4 if cfg.m_shared else 0)
+        hbm = lambda b, ms_: round(b / (ms_ * 1e-3) / 1e9, 1)  # noqa: E731
+        extra = {
+            "phase_ms": {n: round(v, 4) for n, v in phases.items()},
+            "expert_gemm_tflops": round((gemm1_flop + gemm2_flop) / (t1 + t2) / 1e12, 2),
+            "expert_gemm_mfma_frac": round((gemm1_flop + gemm2_flop) / (t1 + t2) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "gemm2_tflops": round(gemm2_flop / t2 / 1e12, 2),
+            "hbm_gbs": {"route": hbm(route_bytes, phases["route"]), "dispatch": hbm(disp_bytes, phases["dispatch"]),
+                        "combine": hbm(comb_bytes, phases["combine"])},
+            "hbm_peak_gbs": PEAK_HBM_GBS,
+        }
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights)",
+        "config": {"workload": f"{cfg.name} MoE layer", "T": T, "d": d, "m": m, "E": cfg.E, "k": k,
+                   "capacity": C or "unlimited", "gate": "switch" if cfg.gate_mode else "renorm",
+                   "shared_expert_m": cfg.m_shared, "router": "fp32", "accumulate": "fp32"},
+        "stats": {"accepted_paths": A, "overflow": stats[L.MOE_STAT_OVERFLOW],
+                  "max_load": stats[L.MOE_STAT_MAX_LOAD], "rho_max": round(stats[L.MOE_STAT_MAX_LOAD] / (T * k / cfg.E), 4),
+                  "tokens_dropped": stats[L.MOE_STAT_TOKENS_DROPPED], "active_experts": active},
+        "roofline": roofline,
+        **extra,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] timing the CPU oracle on a {args.cpu_sample_tokens}-token sample")
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,205 @@
+/*
+ * moe.h -- C-ABI of the MI355X (gfx950) sparse Mixture-of-Experts layer forward.
+ *
+ * The layer (one routing group of T valid tokens):
+ *   router scores  g = x W_r^T + b_r, softmax over the experts
+ *       ("LLM from scratch" ch. 36 §36.1; "MoE token routing" §2)
+ *   top-k          k distinct experts by descending score, ties to the lower id
+ *       (ch. 36 §36.1 and Algorithm 36.1 in §36.4)
+ *   weights        renormalised within the selected set, or the Switch
+ *                  convention that keeps the full-softmax probability
+ *       (ch. 36 §36.2)
+ *   dispatch       capacity C per expert, slots first-come-first-served in
+ *                  token order, overflowing paths rejected (contribute 0,
+ *                  no second renormalisation)
+ *       (ch. 36 §36.3 and Algorithm 36.1; "The real cost of sparse expert
+ *        models" equation for C_e and O)
+ *   experts        SwiGLU  E_i(x) = [SiLU(x W_gate,i) (*) (x W_up,i)] W_down,i
+ *       ("MoE token routing" §3)
+ *   shared expert  optional, applied to every token, unweighted
+ *       (ch. 36 §36.6; "Sizzling MoE skewer analogy" DeepSeek-V3 formula)
+ *   combine        y_t = s_t + sum over accepted paths of a_te * H_e[slot]
+ *       (Algorithm 36.1; "MoE token routing" §3)
+ *   statistics     requested load L_e, accepted, overflow O, max load,
+ *                  tokens affected / fully dropped; rho_max = max L_e/(Tk/E)
+ *       (ch. 36 §36.4; "The real cost of sparse expert models" equations)
+ *
+ * Conventions common to every call:
+ *  - Pointers are DEVICE pointers unless a comment says "host".  The caller
+ *    owns every buffer; the library never allocates or frees memory and keeps
+ *    no per-call state.  Inputs and outputs must not alias.
+ *  - Every compute call is asynchronous on `stream` (a hipStream_t passed as
+ *    void*, NULL = the null stream).  Argument errors are detected on the host,
+ *    before anything is launched, and returned synchronously.
+ *  - Expert ids are 0-based.  Matrices are row-major.  Weights are stored
+ *    out-features x in-features (the transpose convention ch. 36 §36.8
+ *    mentions): router w_r [E,d], gate/up [E,m,d], down [E,d,m].
+ *  - dtype MOE_F32: x, expert weights, h are fp32.  MOE_BF16: x and expert
+ *    weights are bf16, h is bf16; all accumulation is fp32.  The router
+ *    weights, bias, routing weights, H, s and y are always fp32.
+ *  - y excludes the residual: a token whose every path is rejected gets
+ *    y_t = s_t (0 without a shared expert); the caller adds its residual.
+ *  - Calls are reentrant; concurrent calls must use disjoint buffers.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARGUMENT = 1,   /* bad shape, pointer, k or capacity      */
+    MOE_ERR_NONFINITE_LOGIT = 2,    /* written to the device status word only */
+    MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+    MOE_ERR_UNSUPPORTED = 4,        /* valid but outside the supported shapes */
+    MOE_ERR_HIP = 5                 /* a HIP runtime call or launch failed    */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+typedef enum { MOE_GATE_RENORM = 0, MOE_GATE_SWITCH = 1 } moe_gate_mode;
+
+/* Layer shape.  capacity: C >= 1, or 0 = unlimited (no path can be rejected).
+ * Supported: T >= 0; d, m >= 1; 1 <= k <= E <= 1024, k <= 32; for MOE_BF16 d
+ * and m must be multiples of 8 (16-byte rows).  m_shared: 0 = no shared
+ * expert, else its width (same alignment rule). */
+typedef struct {
+    int64_t T;
+    int32_t d, m, E, k;
+    int32_t capacity;
+    int32_t gate_mode;   /* moe_gate_mode */
+    int32_t dtype;       /* moe_dtype     */
+    int32_t m_shared;
+} moe_shape;
+
+/* Indices of the int32 statistics vector written by moe_dispatch. */
+enum {
+    MOE_STAT_OVERFLOW = 0,        /* O = sum_e max(0, L_e - C) = rejected paths   */
+    MOE_STAT_ACCEPTED = 1,        /* A = sum_e min(L_e, C): rows of x_perm / H    */
+    MOE_STAT_MAX_LOAD = 2,        /* max_e L_e (requested, before capacity)      */
+    MOE_STAT_TOKENS_DROPPED = 3,  /* tokens with every path rejected             */
+    MOE_STAT_TOKENS_AFFECTED = 4, /* tokens with at least one path rejected      */
+    MOE_STAT_COUNT = 8
+};
+
+/* Which call a workspace is sized for. */
+typedef enum { MOE_WS_DISPATCH = 0, MOE_WS_FFN = 1, MOE_WS_SHARED = 2, MOE_WS_FORWARD = 3 } moe_ws_kind;
+
+/* ---- host helpers ------------------------------------------------------ */
+
+/* Capacity C = ceil(cf * T * k / E) with cf = cf_num / cf_den, in exact
+ * integer arithmetic ("The real cost of sparse expert models", equation for
+ * C_e; ch. 36 §36.3; "MoE token routing" §6).  Returns -1 on invalid input
+ * (T < 0, k < 1, E < 1, cf_num < 1, cf_den < 1) or if C exceeds INT32_MAX. */
+int32_t moe_capacity(int64_t T, int32_t k, int32_t E, int32_t cf_num, int32_t cf_den);
+
+/* Upper bound on the accepted paths A = rows of x_perm / h / H:
+ * min(T*k, E*C) (C = T when unlimited).  0 for an invalid shape. */
+int64_t moe_max_rows(const moe_shape* shape);
+
+/* Bytes of device workspace the named call needs (256-byte aligned start
+ * required).  0 for an invalid shape. */
+size_t moe_workspace_bytes(const moe_shape* shape, int32_t kind);
+
+/* Checks a shape; returns MOE_OK, MOE_ERR_INVALID_ARGUMENT or MOE_ERR_UNSUPPORTED. */
+moe_status moe_check_shape(const moe_shape* shape);
+
+/* Static string for a status code (never NULL). */
+const char* moe_status_str(int32_t status);
+
+/* ---- hot-path calls ---------------------------------------------------- */
+
+/* Router scores, softmax, top-k and routing weights (ch. 36 §36.1-§36.2,
+ * Algorithm 36.1 selection step; "MoE token routing" §2).
+ *   x        [T,d]  dtype
+ *   w_r      [E,d]  fp32;  b_r [E] fp32 or NULL
+ *   topk_ids [T,k]  int32 out: rank order (descending fp32 score, lower id first on ties)
+ *   topk_w   [T,k]  fp32 out: RENORM a = p_e / sum_{j in S} p_j (sums to 1);
+ *                   SWITCH a = p_e (full softmax)
+ *   status   [1]    int32 out: set to MOE_OK, or MOE_ERR_NONFINITE_LOGIT if any
+ *                   score is NaN/Inf; such a token gets ids 0..k-1 and weights 0
+ *                   so that later calls stay in bounds.  Read it after the
+ *                   stream synchronises. */
+moe_status moe_route(const moe_shape* shape, const void* x, const float* w_r, const float* b_r,
+                     int32_t* topk_ids, float* topk_w, int32_t* status, void* stream);
+
+/* Capacity-limited dispatch and load statistics (ch. 36 §36.3, Algorithm
+ * 36.1 acceptance step and its invariants; "The real cost of sparse expert
+ * models" equations for C_e, O and rho_max).
+ *   x         [T,d]      dtype
+ *   topk_ids  [T,k]      int32 in (values must lie in [0,E); each row distinct)
+ *   load      [E]        int32 out: requested load L_e
+ *   offsets   [E+1]      int32 out: exclusive prefix sum of min(L_e, C)
+ *   slot      [T,k]      int32 out: slot c within the expert (number of earlier
+ *                        tokens that requested the same expert), or -1 if rejected
+ *   row_of    [T,k]      int32 out: offsets[e] + slot, or -1
+ *   src_token [max_rows] int32 out: token of each grouped row (rows >= A untouched)
+ *   x_perm    [max_rows,d] dtype out: x_perm[row] = x[src_token[row]]; rows are
+ *                        grouped by expert, token order inside each expert
+ *   stats     [MOE_STAT_COUNT] int32 out (see the MOE_STAT_* indices)
+ *   ws        >= moe_workspace_bytes(shape, MOE_WS_DISPATCH) bytes */
+moe_status moe_dispatch(const moe_shape* shape, const void* x, const int32_t* topk_ids,
+                        int32_t* load, int32_t* offsets, int32_t* slot, int32_t* row_of,
+                        int32_t* src_token, void* x_perm, int32_t* stats,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* Routed expert FFNs over the grouped rows ("MoE token routing" §3; ch. 36
+ * §36.1 gated expert and Algorithm 36.1 expert step):
+ *   h = SiLU(x_perm W_gate[e]^T) (*) (x_perm W_up[e]^T)   (rounded to dtype)
+ *   H = h W_down[e]^T                                     (fp32)
+ * for the rows [offsets[e], offsets[e+1]) of every expert e.
+ *   x_perm  [max_rows,d] dtype;  offsets [E+1] int32 (non-decreasing, offsets[0]=0,
+ *           offsets[E] <= moe_max_rows)
+ *   w_gate, w_up [E,m,d] dtype;  w_down [E,d,m] dtype
+ *   H       [max_rows,d] fp32 out (rows >= offsets[E] untouched)
+ *   ws      >= moe_workspace_bytes(shape, MOE_WS_FFN) (holds h) */
+moe_status moe_expert_ffn(const moe_shape* shape, const void* x_perm, const int32_t* offsets,
+                          const void* w_gate, const void* w_up, const void* w_down, float* H,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* The first half of moe_expert_ffn alone: h [max_rows,m] (dtype) out. */
+moe_status moe_expert_gemm1(const moe_shape* shape, const void* x_perm, const int32_t* offsets,
+                            const void* w_gate, const void* w_up, void* h,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* The second half of moe_expert_ffn alone: H [max_rows,d] fp32 out from h. */
+moe_status moe_expert_gemm2(const moe_shape* shape, const void* h, const int32_t* offsets,
+                            const void* w_down, float* H, void* ws, size_t ws_bytes, void* stream);
+
+/* Shared expert on every token, unweighted (ch. 36 §36.6; "Sizzling MoE
+ * skewer analogy" DeepSeek-V3 formula): s = SwiGLU(x) with
+ *   s_gate, s_up [m_shared,d] dtype;  s_down [d,m_shared] dtype;  s [T,d] fp32 out.
+ *   ws >= moe_workspace_bytes(shape, MOE_WS_SHARED).  Needs shape->m_shared > 0. */
+moe_status moe_shared_ffn(const moe_shape* shape, const void* x, const void* s_gate,
+                          const void* s_up, const void* s_down, float* s,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* Weighted combine back into token order (Algorithm 36.1 combine step;
+ * "MoE token routing" §3):
+ *   y[t] = shared_out[t] + sum_{r=0..k-1, row_of[t,r] >= 0} topk_w[t,r] * H[row_of[t,r]]
+ * summed in rank order r = 0..k-1, in fp32.
+ *   H [max_rows,d] fp32;  row_of, topk_w [T,k];  shared_out [T,d] fp32 or NULL;
+ *   y [T,d] fp32 out (fully overwritten). */
+moe_status moe_combine(const moe_shape* shape, const float* H, const int32_t* row_of,
+                       const float* topk_w, const float* shared_out, float* y, void* stream);
+
+/* The whole layer: route -> dispatch -> expert FFN (+ shared) -> combine,
+ * queued on `stream` with no host synchronisation.  s_gate/s_up/s_down may be
+ * NULL only when shape->m_shared == 0.  Outputs as in the calls above;
+ * every intermediate lives in ws (>= moe_workspace_bytes(shape, MOE_WS_FORWARD)). */
+moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_r, const float* b_r,
+                       const void* w_gate, const void* w_up, const void* w_down,
+                       const void* s_gate, const void* s_up, const void* s_down,
+                       float* y, int32_t* topk_ids, float* topk_w, int32_t* load,
+                       int32_t* slot, int32_t* stats, int32_t* status,
+                       void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,80 @@
+// Weighted combine back into token order.
+//
+//   y[t] = s[t] + sum_{r : row_of[t,r] >= 0} a[t,r] * H[row_of[t,r]]
+//
+// ("LLM from scratch" ch. 36 Algorithm 36.1 combine step: every accepted record
+// is added once, rejected records add nothing and the other weights are not
+// renormalised; "MoE token routing" §3 weighted sum; shared expert added
+// unweighted, ch. 36 §36.6.)  The scatter-add of the definition is computed as a
+// token-major gather: each token's row is written by exactly one wave, summing
+// its paths in rank order with fp32 fused multiply-adds, so the result is
+// deterministic without atomics.
+#include "common.h"
+
+namespace {
+
+template <bool VEC4>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ H, const int32_t* __restrict__ row_of,
+                                                      const float* __restrict__ w, const float* __restrict__ shared_out,
+                                                      float* __restrict__ y, int64_t T, int d, int k) {
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+    if (t >= T) return;
+    const int myrow = lane < k ? row_of[t * k + lane] : -1;
+    const float myw = lane < k ? w[t * k + lane] : 0.f;
+    if (VEC4) {
+        const int nv = d / 4;
+        const float4* H4 = reinterpret_cast<const float4*>(H);
+        const float4* S4 = reinterpret_cast<const float4*>(shared_out);
+        float4* Y4 = reinterpret_cast<float4*>(y);
+        // uniform trip count: every lane stays active around lane_value
+        for (int c0 = 0; c0 < nv; c0 += 64) {
+            const int c = c0 + lane;
+            const bool ok = c < nv;
+            float4 acc = (shared_out && ok) ? S4[t * nv + c] : float4{0.f, 0.f, 0.f, 0.f};
+            for (int r = 0; r < k; ++r) {
+                const int row = lane_value(myrow, r);
+                const float a = lane_value(myw, r);
+                if (row >= 0 && ok) {
+                    const float4 h = H4[(int64_t)row * nv + c];
+                    acc.x = fmaf(a, h.x, acc.x);
+                    acc.y = fmaf(a, h.y, acc.y);
+                    acc.z = fmaf(a, h.z, acc.z);
+                    acc.w = fmaf(a, h.w, acc.w);
+                }
+            }
+            if (ok) Y4[t * nv + c] = acc;
+        }
+    } else {
+        for (int c0 = 0; c0 < d; c0 += 64) {
+            const int c = c0 + lane;
+            const bool ok = c < d;
+            float acc = (shared_out && ok) ? shared_out[t * d + c] : 0.f;
+            for (int r = 0; r < k; ++r) {
+                const int row = lane_value(myrow, r);
+                const float a = lane_value(myw, r);
+                if (row >= 0 && ok) acc = fmaf(a, H[(int64_t)row * d + c], acc);
+            }
+            if (ok) y[t * d + c] = acc;
+        }
+    }
+}
+
+}  // namespace
+
+namespace moe_kernels {
+
+hipError_t launch_combine(const moe_dims& s, const float* H, const int32_t* row_of, const float* topk_w,
+                          const float* shared_out, float* y, hipStream_t st) {
+    if (s.T == 0) return hipSuccess;
+    const unsigned grid = (unsigned)((s.T + 3) / 4);
+    if (s.d % 4 == 0)
+        hipLaunchKernelGGL(combine_kernel<true>, dim3(grid), dim3(256), 0, st, H, row_of, topk_w, shared_out, y, s.T,
+                           s.d, s.k);
+    else
+        hipLaunchKernelGGL(combine_kernel<false>, dim3(grid), dim3(256), 0, st, H, row_of, topk_w, shared_out, y, s.T,
+                           s.d, s.k);
+    return hipGetLastError();
+}
+
+}  // namespace moe_kernels

@@ -1,0 +1,104 @@
+// Shared device helpers for the gfx950 (CDNA4) MoE kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;   // MFMA bf16 operand (8 x K)
+typedef __attribute__((ext_vector_type(4))) float floatx4_t;    // 16x16 MFMA accumulator
+typedef __attribute__((ext_vector_type(16))) float floatx16_t;  // 32x32 MFMA accumulator
+
+#define MOE_WAVE 64
+
+// bf16 is carried as its 16-bit pattern in memory.
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t v) { return __uint_as_float(v << 16); }
+
+// fp32 -> bf16 bit pattern, round to nearest, ties to even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// SiLU(z) = z * sigmoid(z) = z / (1 + e^-z); e^-z from the hardware exp2.
+__device__ __forceinline__ float silu_f32(float z) {
+    return z / (1.0f + __expf(-z));
+}
+
+// Total order on finite floats as unsigned keys (larger float -> larger key);
+// -0.0 is mapped to +0.0 first so that the two compare equal.
+__device__ __forceinline__ uint32_t float_order_key(float f) {
+    uint32_t u = __float_as_uint(f + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Value of `v` in lane `lane` (wave-uniform), read with v_readlane: unlike a
+// shuffle it does not depend on which lanes are active at the call site, so it
+// is safe inside lane-divergent loops as long as `v` was written before them.
+__device__ __forceinline__ int lane_value(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+__device__ __forceinline__ float lane_value(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, MOE_WAVE);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, MOE_WAVE));
+    return v;
+}
+
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        unsigned long long w = __shfl_xor(v, o, MOE_WAVE);
+        v = w > v ? w : v;
+    }
+    return v;
+}
+
+// ---- host-side launch helpers shared by the translation units ----------------
+
+struct moe_dims {
+    int64_t T;
+    int d, m, E, k;
+    int C;          // effective capacity (T when unlimited)
+    int gate_mode;
+    int dtype;
+    int m_shared;
+};
+
+namespace moe_kernels {
+
+// Router: scores, softmax, top-k, weights.
+hipError_t launch_route(const moe_dims& s, const void* x, const float* w_r, const float* b_r,
+                        int32_t* topk_ids, float* topk_w, int32_t* status, hipStream_t st);
+
+// Dispatch.
+size_t dispatch_ws_bytes(const moe_dims& s);
+hipError_t launch_dispatch(const moe_dims& s, const void* x, const int32_t* ids, int32_t* load,
+                           int32_t* offsets, int32_t* slot, int32_t* row_of, int32_t* src_token,
+                           void* x_perm, int32_t* stats, void* ws, hipStream_t st);
+
+// Grouped expert GEMMs.  offsets == nullptr means one group covering rows [0, nrows).
+size_t gemm_ws_bytes(int G);
+hipError_t launch_gemm1(int dtype, const void* A, const int32_t* offsets, int G, int64_t max_rows,
+                        const void* w_gate, const void* w_up, void* h, int N, int K,
+                        void* ws, hipStream_t st);
+hipError_t launch_gemm2(int dtype, const void* h, const int32_t* offsets, int G, int64_t max_rows,
+                        const void* w_down, float* H, int N, int K, void* ws, hipStream_t st);
+
+// Combine.
+hipError_t launch_combine(const moe_dims& s, const float* H, const int32_t* row_of,
+                          const float* topk_w, const float* shared_out, float* y, hipStream_t st);
+
+}  // namespace moe_kernels

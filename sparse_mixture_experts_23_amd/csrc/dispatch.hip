@@ -1,0 +1,220 @@
+// Capacity-limited dispatch: slots in token order, grouped row map, row gather,
+// load statistics.
+//
+// Definition ("LLM from scratch" ch. 36 Algorithm 36.1 acceptance step, §36.3):
+// per-expert counters start at 0; token by token, each selected path takes the
+// next slot of its expert if fewer than C slots are used, otherwise it is
+// rejected.  Because a token selects each expert at most once, the slot of path
+// (t, e) equals the number of earlier tokens that selected e -- an exclusive
+// prefix count in token order -- so the serial definition is computed here in
+// parallel, exactly:
+//   count : per 256-token block, the tokens selecting each expert
+//   scan  : per expert, exclusive prefix over blocks; L_e, min(L_e, C),
+//           grouped-row offsets, overflow O ("The real cost of sparse expert
+//           models", equations for C_e and O), max load
+//   place : rank inside the block = popcount of a per-expert bit mask of the
+//           earlier lanes (built with order-independent LDS atomic ORs), so
+//           the result never depends on thread timing
+//   gather: x_perm[row] = x[token], one wave per token, 16-byte vector copies.
+#include "common.h"
+
+namespace {
+
+constexpr int DB_TOK = 256;   // tokens per count/place workgroup (4 waves x 64)
+
+__device__ __forceinline__ void build_masks(unsigned long long* masks, const int32_t* __restrict__ ids, int64_t T,
+                                            int k, int E) {
+    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+    for (int i = tid; i < 4 * E; i += DB_TOK) masks[i] = 0ull;
+    __syncthreads();
+    const int64_t t = (int64_t)blockIdx.x * DB_TOK + tid;
+    if (t < T) {
+        for (int r = 0; r < k; ++r) {
+            const int e = ids[t * k + r];
+            if ((unsigned)e < (unsigned)E) atomicOr(&masks[wave * E + e], 1ull << lane);
+        }
+    }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(DB_TOK) void dispatch_count_kernel(const int32_t* __restrict__ ids, int64_t T, int k,
+                                                                int E, int32_t* __restrict__ hist) {
+    extern __shared__ unsigned long long masks[];
+    build_masks(masks, ids, T, k, E);
+    for (int e = threadIdx.x; e < E; e += DB_TOK) {
+        int c = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) c += __popcll(masks[w * E + e]);
+        hist[(int64_t)blockIdx.x * E + e] = c;
+    }
+}
+
+// One workgroup of 1024 threads (E <= 1024): thread e scans expert e over blocks.
+__global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict__ hist, int NB, int E, int C,
+                                                             int32_t* __restrict__ load, int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ stats) {
+    __shared__ int s_sum[16], s_over[16], s_max[16];
+    const int e = threadIdx.x, wave = e / 64, lane = e % 64;
+    int L = 0;
+    if (e < E) {
+        for (int b = 0; b < NB; ++b) {
+            const int h = hist[(int64_t)b * E + e];
+            hist[(int64_t)b * E + e] = L;   // becomes the block's base slot for expert e
+            L += h;
+        }
+        load[e] = L;
+    }
+    const int acc = e < E ? min(L, C) : 0;
+    const int over = e < E ? max(L - C, 0) : 0;
+    // inclusive wave scan of acc
+    int incl = acc;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o, MOE_WAVE);
+        if (lane >= o) incl += v;
+    }
+    int ov = over, mx = L;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        ov += __shfl_xor(ov, o, MOE_WAVE);
+        mx = max(mx, __shfl_xor(mx, o, MOE_WAVE));
+    }
+    if (lane == 63) s_sum[wave] = incl;
+    if (lane == 0) {
+        s_over[wave] = ov;
+        s_max[wave] = mx;
+    }
+    __syncthreads();
+    int before = 0, total = 0, otot = 0, mtot = 0;
+    for (int w = 0; w < 16; ++w) {
+        if (w < wave) before += s_sum[w];
+        total += s_sum[w];
+        otot += s_over[w];
+        mtot = max(mtot, s_max[w]);
+    }
+    if (e < E) offsets[e] = before + incl - acc;
+    if (e == 0) {
+        offsets[E] = total;
+        stats[MOE_STAT_OVERFLOW] = otot;
+        stats[MOE_STAT_ACCEPTED] = total;
+        stats[MOE_STAT_MAX_LOAD] = mtot;
+        for (int i = MOE_STAT_TOKENS_DROPPED; i < MOE_STAT_COUNT; ++i) stats[i] = 0;
+    }
+}
+
+__global__ __launch_bounds__(DB_TOK) void dispatch_place_kernel(const int32_t* __restrict__ ids, int64_t T, int k,
+                                                                int E, int C, const int32_t* __restrict__ base,
+                                                                const int32_t* __restrict__ offsets,
+                                                                int32_t* __restrict__ slot, int32_t* __restrict__ row_of,
+                                                                int32_t* __restrict__ src_token,
+                                                                int32_t* __restrict__ stats) {
+    extern __shared__ unsigned long long masks[];
+    __shared__ int s_drop[4], s_aff[4];
+    build_masks(masks, ids, T, k, E);
+    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+    const int64_t t = (int64_t)blockIdx.x * DB_TOK + tid;
+    int dropped = 0, affected = 0;
+    if (t < T) {
+        const unsigned long long below = (1ull << lane) - 1ull;
+        int nrej = 0;
+        for (int r = 0; r < k; ++r) {
+            const int e = ids[t * k + r];
+            int c = -1, row = -1;
+            if ((unsigned)e < (unsigned)E) {
+                int rank = __popcll(masks[wave * E + e] & below);
+                for (int w = 0; w < wave; ++w) rank += __popcll(masks[w * E + e]);
+                const int cand = base[(int64_t)blockIdx.x * E + e] + rank;
+                if (cand < C) {
+                    c = cand;
+                    row = offsets[e] + cand;
+                    src_token[row] = (int32_t)t;
+                }
+            }
+            slot[t * k + r] = c;
+            row_of[t * k + r] = row;
+            nrej += c < 0;
+        }
+        dropped = nrej == k;
+        affected = nrej > 0;
+    }
+    // workgroup sums, then one integer atomic add each (order-independent)
+    for (int o = 32; o >= 1; o >>= 1) {
+        dropped += __shfl_xor(dropped, o, MOE_WAVE);
+        affected += __shfl_xor(affected, o, MOE_WAVE);
+    }
+    if (lane == 0) {
+        s_drop[wave] = dropped;
+        s_aff[wave] = affected;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        const int dsum = s_drop[0] + s_drop[1] + s_drop[2] + s_drop[3];
+        const int asum = s_aff[0] + s_aff[1] + s_aff[2] + s_aff[3];
+        if (dsum) atomicAdd(&stats[MOE_STAT_TOKENS_DROPPED], dsum);
+        if (asum) atomicAdd(&stats[MOE_STAT_TOKENS_AFFECTED], asum);
+    }
+}
+
+// x_perm[row] = x[t] for every accepted path of token t; one wave per token.
+template <typename V>
+__global__ __launch_bounds__(256) void dispatch_gather_kernel(const V* __restrict__ x, int64_t T, int k,
+                                                              int64_t vec_per_row, const int32_t* __restrict__ row_of,
+                                                              V* __restrict__ x_perm) {
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+    if (t >= T) return;
+    const int myrow = lane < k ? row_of[t * k + lane] : -1;
+    const V* src = x + t * vec_per_row;
+    // uniform trip count: every lane stays active around lane_value
+    for (int64_t c0 = 0; c0 < vec_per_row; c0 += 64) {
+        const int64_t c = c0 + lane;
+        const bool ok = c < vec_per_row;
+        V v;
+        if (ok) v = src[c];
+        for (int r = 0; r < k; ++r) {
+            const int row = lane_value(myrow, r);
+            if (row >= 0 && ok) x_perm[(int64_t)row * vec_per_row + c] = v;
+        }
+    }
+}
+
+}  // namespace
+
+namespace moe_kernels {
+
+size_t dispatch_ws_bytes(const moe_dims& s) {
+    const int64_t NB = (s.T + DB_TOK - 1) / DB_TOK;
+    return (size_t)NB * (size_t)s.E * sizeof(int32_t);
+}
+
+hipError_t launch_dispatch(const moe_dims& s, const void* x, const int32_t* ids, int32_t* load, int32_t* offsets,
+                           int32_t* slot, int32_t* row_of, int32_t* src_token, void* x_perm, int32_t* stats, void* ws,
+                           hipStream_t st) {
+    const int NB = (int)((s.T + DB_TOK - 1) / DB_TOK);
+    int32_t* hist = static_cast<int32_t*>(ws);
+    const size_t mask_lds = sizeof(unsigned long long) * 4 * s.E;
+    if (NB > 0) {
+        hipLaunchKernelGGL(dispatch_count_kernel, dim3(NB), dim3(DB_TOK), mask_lds, st, ids, s.T, s.k, s.E, hist);
+    }
+    hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, st, hist, NB, s.E, s.C, load, offsets, stats);
+    if (NB == 0) return hipGetLastError();
+    hipLaunchKernelGGL(dispatch_place_kernel, dim3(NB), dim3(DB_TOK), mask_lds, st, ids, s.T, s.k, s.E, s.C, hist,
+                       offsets, slot, row_of, src_token, stats);
+    const int elem = s.dtype == MOE_BF16 ? 2 : 4;
+    const int64_t row_bytes = (int64_t)s.d * elem;
+    const unsigned grid = (unsigned)((s.T + 3) / 4);
+    if (row_bytes % 16 == 0)
+        hipLaunchKernelGGL(dispatch_gather_kernel<uint4>, dim3(grid), dim3(256), 0, st, static_cast<const uint4*>(x),
+                           s.T, s.k, row_bytes / 16, row_of, static_cast<uint4*>(x_perm));
+    else if (row_bytes % 4 == 0)
+        hipLaunchKernelGGL(dispatch_gather_kernel<uint32_t>, dim3(grid), dim3(256), 0, st,
+                           static_cast<const uint32_t*>(x), s.T, s.k, row_bytes / 4, row_of,
+                           static_cast<uint32_t*>(x_perm));
+    else
+        hipLaunchKernelGGL(dispatch_gather_kernel<uint16_t>, dim3(grid), dim3(256), 0, st,
+                           static_cast<const uint16_t*>(x), s.T, s.k, row_bytes / 2, row_of,
+                           static_cast<uint16_t*>(x_perm));
+    return hipGetLastError();
+}
+
+}  // namespace moe_kernels

@@ -1,0 +1,260 @@
+// C-ABI entry points: argument checks, workspace carve-up and launch sequencing.
+// Every call only queues kernels on the caller's stream; nothing here
+// allocates, frees or synchronises.
+#include <climits>
+
+#include "common.h"
+
+using namespace moe_kernels;
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+inline size_t align_up(size_t v) { return (v + ALIGN - 1) & ~(ALIGN - 1); }
+
+moe_status check_shape(const moe_shape* s, moe_dims* out) {
+    if (!s) return MOE_ERR_INVALID_ARGUMENT;
+    if (s->T < 0 || s->d < 1 || s->m < 1 || s->E < 1 || s->k < 1 || s->k > s->E) return MOE_ERR_INVALID_ARGUMENT;
+    if (s->capacity < 0 || s->m_shared < 0) return MOE_ERR_INVALID_ARGUMENT;
+    if (s->gate_mode != MOE_GATE_RENORM && s->gate_mode != MOE_GATE_SWITCH) return MOE_ERR_INVALID_ARGUMENT;
+    if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
+    if (s->E > 1024 || s->k > 32) return MOE_ERR_UNSUPPORTED;
+    if (s->T * (int64_t)s->k > (int64_t)INT_MAX) return MOE_ERR_UNSUPPORTED;
+    if (s->dtype == MOE_BF16 && (s->d % 8 || s->m % 8 || s->m_shared % 8)) return MOE_ERR_UNSUPPORTED;
+    if (out) {
+        out->T = s->T;
+        out->d = s->d;
+        out->m = s->m;
+        out->E = s->E;
+        out->k = s->k;
+        out->C = s->capacity > 0 ? s->capacity : (int)(s->T > 0 ? s->T : 1);
+        out->gate_mode = s->gate_mode;
+        out->dtype = s->dtype;
+        out->m_shared = s->m_shared;
+    }
+    return MOE_OK;
+}
+
+int64_t max_rows(const moe_dims& d) {
+    const int64_t a = d.T * d.k, b = (int64_t)d.E * d.C;
+    return a < b ? a : b;
+}
+
+size_t elem(const moe_dims& d) { return d.dtype == MOE_BF16 ? 2 : 4; }
+
+size_t ffn_ws(const moe_dims& d) { return align_up(gemm_ws_bytes(d.E)) + align_up((size_t)max_rows(d) * d.m * elem(d)); }
+size_t shared_ws(const moe_dims& d) {
+    return align_up(gemm_ws_bytes(1)) + align_up((size_t)d.T * d.m_shared * elem(d));
+}
+
+struct ForwardWs {
+    int32_t* offsets;
+    int32_t* row_of;
+    int32_t* src_token;
+    void* x_perm;
+    float* H;
+    float* s;
+    void* dispatch;
+    void* ffn;
+    void* shared;
+    size_t total;
+};
+
+ForwardWs carve_forward(const moe_dims& d, void* base) {
+    ForwardWs w{};
+    char* p = static_cast<char*>(base);
+    size_t off = 0;
+    auto take = [&](size_t bytes) -> void* {
+        void* r = p ? p + off : nullptr;
+        off += align_up(bytes);
+        return r;
+    };
+    const int64_t R = max_rows(d);
+    w.offsets = static_cast<int32_t*>(take(sizeof(int32_t) * (d.E + 1)));
+    w.row_of = static_cast<int32_t*>(take(sizeof(int32_t) * d.T * d.k));
+    w.src_token = static_cast<int32_t*>(take(sizeof(int32_t) * R));
+    w.x_perm = take((size_t)R * d.d * elem(d));
+    w.H = static_cast<float*>(take(sizeof(float) * R * d.d));
+    w.s = d.m_shared ? static_cast<float*>(take(sizeof(float) * d.T * d.d)) : nullptr;
+    w.dispatch = take(dispatch_ws_bytes(d));
+    w.ffn = take(ffn_ws(d));
+    w.shared = d.m_shared ? take(shared_ws(d)) : nullptr;
+    w.total = off;
+    return w;
+}
+
+inline moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+#define MOE_CHECK_HIP(expr)                        \
+    do {                                           \
+        hipError_t e_ = (expr);                    \
+        if (e_ != hipSuccess) return MOE_ERR_HIP;  \
+    } while (0)
+
+moe_status ffn_impl(const moe_dims& d, const void* x_perm, const int32_t* offsets, const void* w_gate,
+                    const void* w_up, const void* w_down, float* H, void* ws, hipStream_t st) {
+    void* tp = ws;
+    void* h = static_cast<char*>(ws) + align_up(gemm_ws_bytes(d.E));
+    const int64_t R = max_rows(d);
+    MOE_CHECK_HIP(launch_gemm1(d.dtype, x_perm, offsets, d.E, R, w_gate, w_up, h, d.m, d.d, tp, st));
+    MOE_CHECK_HIP(launch_gemm2(d.dtype, h, offsets, d.E, R, w_down, H, d.d, d.m, tp, st));
+    return MOE_OK;
+}
+
+moe_status shared_impl(const moe_dims& d, const void* x, const void* s_gate, const void* s_up, const void* s_down,
+                       float* s, void* ws, hipStream_t st) {
+    void* tp = ws;
+    void* h = static_cast<char*>(ws) + align_up(gemm_ws_bytes(1));
+    MOE_CHECK_HIP(launch_gemm1(d.dtype, x, nullptr, 1, d.T, s_gate, s_up, h, d.m_shared, d.d, tp, st));
+    MOE_CHECK_HIP(launch_gemm2(d.dtype, h, nullptr, 1, d.T, s_down, s, d.d, d.m_shared, tp, st));
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_capacity(int64_t T, int32_t k, int32_t E, int32_t cf_num, int32_t cf_den) {
+    if (T < 0 || k < 1 || E < 1 || cf_num < 1 || cf_den < 1) return -1;
+    // ceil(cf_num * T * k / (cf_den * E)) without overflow for T < 2^31
+    const __int128 num = (__int128)cf_num * T * k;
+    const __int128 den = (__int128)cf_den * E;
+    const __int128 c = (num + den - 1) / den;
+    if (c > INT_MAX) return -1;
+    return (int32_t)c;
+}
+
+moe_status moe_check_shape(const moe_shape* shape) { return check_shape(shape, nullptr); }
+
+int64_t moe_max_rows(const moe_shape* shape) {
+    moe_dims d;
+    if (check_shape(shape, &d) != MOE_OK) return 0;
+    return max_rows(d);
+}
+
+size_t moe_workspace_bytes(const moe_shape* shape, int32_t kind) {
+    moe_dims d;
+    if (check_shape(shape, &d) != MOE_OK) return 0;
+    switch (kind) {
+        case MOE_WS_DISPATCH: return align_up(dispatch_ws_bytes(d)) + ALIGN;
+        case MOE_WS_FFN: return ffn_ws(d);
+        case MOE_WS_SHARED: return d.m_shared ? shared_ws(d) : 0;
+        case MOE_WS_FORWARD: return carve_forward(d, nullptr).total;
+        default: return 0;
+    }
+}
+
+const char* moe_status_str(int32_t status) {
+    switch (status) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT: bad shape, pointer, k or capacity";
+        case MOE_ERR_NONFINITE_LOGIT: return "MOE_ERR_NONFINITE_LOGIT: a router score is NaN or infinite";
+        case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape outside the supported range";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP runtime call or kernel launch failed";
+        default: return "unknown moe_status";
+    }
+}
+
+moe_status moe_route(const moe_shape* shape, const void* x, const float* w_r, const float* b_r, int32_t* topk_ids,
+                     float* topk_w, int32_t* status, void* stream) {
+    moe_dims d;
+    moe_status rc = check_shape(shape, &d);
+    if (rc != MOE_OK) return rc;
+    if (!status || (d.T > 0 && (!x || !w_r || !topk_ids || !topk_w))) return MOE_ERR_INVALID_ARGUMENT;
+    return hip_status(launch_route(d, x, w_r, b_r, topk_ids, topk_w, status, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_dispatch(const moe_shape* shape, const void* x, const int32_t* topk_ids, int32_t* load,
+                        int32_t* offsets, int32_t* slot, int32_t* row_of, int32_t* src_token, void* x_perm,
+                        int32_t* stats, void* ws, size_t ws_bytes, void* stream) {
+    moe_dims d;
+    moe_status rc = check_shape(shape, &d);
+    if (rc != MOE_OK) return rc;
+    if (!load || !offsets || !stats || !ws) return MOE_ERR_INVALID_ARGUMENT;
+    if (d.T > 0 && (!x || !topk_ids || !slot || !row_of || !src_token || !x_perm)) return MOE_ERR_INVALID_ARGUMENT;
+    if (ws_bytes < moe_workspace_bytes(shape, MOE_WS_DISPATCH)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    return hip_status(launch_dispatch(d, x, topk_ids, load, offsets, slot, row_of, src_token, x_perm, stats, ws,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_expert_gemm1(const moe_shape* shape, const void* x_perm, const int32_t* offsets, const void* w_gate,
+                            const void* w_up, void* h, void* ws, size_t ws_bytes, void* stream) {
+    moe_dims d;
+    moe_status rc = check_shape(shape, &d);
+    if (rc != MOE_OK) return rc;
+    if (!offsets || !ws || !w_gate || !w_up || (max_rows(d) > 0 && (!x_perm || !h))) return MOE_ERR_INVALID_ARGUMENT;
+    if (ws_bytes < align_up(gemm_ws_bytes(d.E))) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    return hip_status(launch_gemm1(d.dtype, x_perm, offsets, d.E, max_rows(d), w_gate, w_up, h, d.m, d.d, ws,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_expert_gemm2(const moe_shape* shape, const void* h, const int32_t* offsets, const void* w_down,
+                            float* H, void* ws, size_t ws_bytes, void* stream) {
+    moe_dims d;
+    moe_status rc = check_shape(shape, &d);
+    if (rc != MOE_OK) return rc;
+    if (!offsets || !ws || !w_down || (max_rows(d) > 0 && (!h || !H))) return MOE_ERR_INVALID_ARGUMENT;
+    if (ws_bytes < align_up(gemm_ws_bytes(d.E))) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    return hip_status(launch_gemm2(d.dtype, h, offsets, d.E, max_rows(d), w_down, H, d.d, d.m, ws,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_expert_ffn(const moe_shape* shape, const void* x_perm, const int32_t* offsets, const void* w_gate,
+                          const void* w_up, const void* w_down, float* H, void* ws, size_t ws_bytes, void* stream) {
+    moe_dims d;
+    moe_status rc = check_shape(shape, &d);
+    if (rc != MOE_OK) return rc;
+    if (!offsets || !ws || !w_gate || !w_up || !w_down || (max_rows(d) > 0 && (!x_perm || !H)))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (ws_bytes < ffn_ws(d)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    return ffn_impl(d, x_perm, offsets, w_gate, w_up, w_down, H, ws, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_shared_ffn(const moe_shape* shape, const void* x, const void* s_gate, const void* s_up,
+                          const void* s_down, float* s, void* ws, size_t ws_bytes, void* stream) {
+    moe_dims d;
+    moe_status rc = check_shape(shape, &d);
+    if (rc != MOE_OK) return rc;
+    if (d.m_shared == 0 || !s_gate || !s_up || !s_down || !ws || (d.T > 0 && (!x || !s)))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (ws_bytes < shared_ws(d)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    return shared_impl(d, x, s_gate, s_up, s_down, s, ws, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_combine(const moe_shape* shape, const float* H, const int32_t* row_of, const float* topk_w,
+                       const float* shared_out, float* y, void* stream) {
+    moe_dims d;
+    moe_status rc = check_shape(shape, &d);
+    if (rc != MOE_OK) return rc;
+    if (d.T > 0 && (!row_of || !topk_w || !y || (!H && max_rows(d) > 0))) return MOE_ERR_INVALID_ARGUMENT;
+    return hip_status(launch_combine(d, H, row_of, topk_w, shared_out, y, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_r, const float* b_r,
+                       const void* w_gate, const void* w_up, const void* w_down, const void* s_gate,
+                       const void* s_up, const void* s_down, float* y, int32_t* topk_ids, float* topk_w,
+                       int32_t* load, int32_t* slot, int32_t* stats, int32_t* status, void* ws, size_t ws_bytes,
+                       void* stream) {
+    moe_dims d;
+    moe_status rc = check_shape(shape, &d);
+    if (rc != MOE_OK) return rc;
+    if (!status || !load || !stats || !ws || !w_gate || !w_up || !w_down) return MOE_ERR_INVALID_ARGUMENT;
+    if (d.T > 0 && (!x || !w_r || !y || !topk_ids || !topk_w || !slot)) return MOE_ERR_INVALID_ARGUMENT;
+    if (d.m_shared && (!s_gate || !s_up || !s_down)) return MOE_ERR_INVALID_ARGUMENT;
+    ForwardWs w = carve_forward(d, ws);
+    if (ws_bytes < w.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    MOE_CHECK_HIP(launch_route(d, x, w_r, b_r, topk_ids, topk_w, status, st));
+    MOE_CHECK_HIP(launch_dispatch(d, x, topk_ids, load, w.offsets, slot, w.row_of, w.src_token, w.x_perm, stats,
+                                  w.dispatch, st));
+    rc = ffn_impl(d, w.x_perm, w.offsets, w_gate, w_up, w_down, w.H, w.ffn, st);
+    if (rc != MOE_OK) return rc;
+    if (d.m_shared) {
+        rc = shared_impl(d, x, s_gate, s_up, s_down, w.s, w.shared, st);
+        if (rc != MOE_OK) return rc;
+    }
+    return hip_status(launch_combine(d, w.H, w.row_of, topk_w, w.s, y, st));
+}
+
+}  // extern "C"
