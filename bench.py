@@ -125,7 +125,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mixtral", choices=sorted(CONFIGS))
-    ap.add_argument("--cpu-sample-tokens", type=int, default=48)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--phases", default="1", help="0 disables the per-phase timing loop")
     args = ap.parse_args()
