@@ -13,9 +13,9 @@
 //     BN up rows of the weights into one B tile so that each lane owns the gate
 //     and the up value of the same output element and applies SiLU(g) * u in
 //     registers before a single bf16 store.
-//   * main kernel (K % 32 == 0): 8 waves (2 per SIMD), K tiles of 32 streamed
-//     into a 4-stage LDS ring by gfx950's direct global->LDS loads, so three
-//     tiles are in flight while one is multiplied; see gemm_bf16_pipe_kernel.
+//   * main kernel (K % 32 == 0): 8 waves (2 per SIMD), K tiles of 64 (or 32)
+//     streamed into an LDS ring by gfx950's direct global->LDS loads; see
+//     gemm_bf16_ring_kernel.
 //   * fallback kernel (any K % 8 == 0): 4 waves, register-staged loads, K tiles
 //     of 64 double-buffered in LDS, zero-filled K tail.
 //   * LDS rows are stored with their 16-byte chunks XOR-swizzled by row, so the
@@ -32,7 +32,7 @@
 namespace {
 
 constexpr int XCDS = 8;
-constexpr int NSUPER = 8;
+constexpr int NSUPER = 4;
 
 struct TileCoord {
     int g, nt;
@@ -48,12 +48,13 @@ __device__ __forceinline__ bool tile_coords(int b, const int32_t* __restrict__ o
     const int x = b % XCDS, j = b / XCDS;
     const int q = total / XCDS, rmd = total % XCDS;
     const int w = x * q + min(x, rmd) + j;
-    const int per_super = MT * NSUPER;
+    constexpr int nsup = NSUPER;
+    const int per_super = MT * nsup;
     const int ns = w / per_super;
     const int rem = w - ns * per_super;
-    const int width = min(NSUPER, NT - ns * NSUPER);
+    const int width = min(nsup, NT - ns * nsup);
     const int mtg = rem / width;
-    tc.nt = ns * NSUPER + rem % width;
+    tc.nt = ns * nsup + rem % width;
     if (offsets) {
         int lo = 0, hi = G - 1;
         while (lo < hi) {
@@ -278,87 +279,80 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const uint16_t* __res
 // consecutive rows 16 different groups of a 256-byte window.
 __device__ __forceinline__ int lds_swz4(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 
-__device__ __forceinline__ void dma16(const uint16_t* src, uint4* lds_wave_base) {
-    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
-                                     (void __attribute__((address_space(3)))*)lds_wave_base, 16, 0, 0);
+// The same global->LDS load issued from a tiny asm statement.  It has no
+// register outputs (the data goes to LDS), so it does not touch the rule that
+// asm loads must wait for their outputs; what it changes is that the compiler
+// no longer sees an LDS write it cannot place, and so it stops making every LDS
+// read wait for all of these loads.  Callers order them with explicit vmcnt
+// waits and barriers.  M0 (the LDS base of the load) is saved and restored.
+__device__ __forceinline__ void dma16_async(const uint16_t* src, uint32_t lds_wave_addr) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(lds_wave_addr)
+        : "memory");
 }
-
-// Workgroup barrier without the memory fence __syncthreads() adds: the fence
-// would make the compiler wait for every outstanding global->LDS load.  Callers
-// wait for the loads they need with an explicit vmcnt first; the empty asm
-// statements keep the compiler from moving memory accesses across the barrier.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// ---------------------------------------------------------------------------
-// bf16 MFMA grouped GEMM: 8 waves, 4-stage global->LDS pipeline
-// ---------------------------------------------------------------------------
-//
-// Fast path for K % 32 == 0.  Three K tiles stream into LDS by
-// global_load_lds_dwordx4 while a fourth is multiplied, so memory latency is
-// covered by three tiles of work and costs no staging registers.  The compiler
-// cannot tell which LDS stage a global->LDS load writes and would make every
-// LDS read wait for all loads in flight; the operand reads are therefore issued
-// from small asm blocks (each ends with its own lgkmcnt wait, so its outputs
-// are complete when it returns), and the loads are waited for explicitly with
-// vmcnt before the stage barrier.  With 2 waves per SIMD each wave keeps a
-// 64 x 128 accumulator tile, and the two waves cover each other's LDS waits.
-
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint32_t lds_byte_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// Six 16-byte LDS reads (2 A operands from one base, 4 B operands from another)
-// at immediate byte offsets; returns after all six have landed.
-template <int A0, int A1, int B0, int B1, int B2, int B3>
-__device__ __forceinline__ void lds_read6(uint32_t a_addr, uint32_t b_addr, u32x4_t& a0, u32x4_t& a1, u32x4_t& b0,
-                                          u32x4_t& b1, u32x4_t& b2, u32x4_t& b3) {
-    asm volatile(
-        "ds_read_b128 %0, %6 offset:%8\n\t"
-        "ds_read_b128 %1, %6 offset:%9\n\t"
-        "ds_read_b128 %2, %7 offset:%10\n\t"
-        "ds_read_b128 %3, %7 offset:%11\n\t"
-        "ds_read_b128 %4, %7 offset:%12\n\t"
-        "ds_read_b128 %5, %7 offset:%13\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a0), "=&v"(a1), "=&v"(b0), "=&v"(b1), "=&v"(b2), "=&v"(b3)
-        : "v"(a_addr), "v"(b_addr), "i"(A0), "i"(A1), "i"(B0), "i"(B1), "i"(B2), "i"(B3)
-        : "memory");
+// ---------------------------------------------------------------------------
+// bf16 MFMA grouped GEMM: 8 waves, global->LDS ring, barrier per K tile
+// ---------------------------------------------------------------------------
+//
+// Workgroup tile 256 rows x BN output columns (GEMM1: 128 gate + 128 up weight
+// rows in one B tile), 8 waves = 2 per SIMD, each owning a 64 x 128 tile of
+// 32x32x16 MFMA accumulators.  K tiles (BK = 64: 2 LDS stages; BK = 32: 4
+// stages; 128 KB either way) are written straight into LDS by dma16_async, one
+// full 128-byte line per row segment at BK = 64.  The compiler schedules the
+// ordinary LDS operand reads of the next K substep between the MFMAs of the
+// current one.  The barrier sits before the last substep of a tile: by then
+// every wave has read all of tile kt, so its stage is refilled with tile
+// kt + STAGES at once, and the next tile's first operands are read while the
+// last substep multiplies.
+// Wait until at most n K tiles of LOADS global->LDS loads each are still in flight.
+template <int LOADS>
+__device__ __forceinline__ void wait_tiles(int n) {
+    if (n >= 3) asm volatile("s_waitcnt vmcnt(%0)" ::"i"(3 * LOADS) : "memory");
+    else if (n == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"i"(2 * LOADS) : "memory");
+    else if (n == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"i"(LOADS) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <int N_OUTSTANDING_LOADS>
-__device__ __forceinline__ void wait_vmcnt_n() {
-    if constexpr (N_OUTSTANDING_LOADS == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    else if constexpr (N_OUTSTANDING_LOADS == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else if constexpr (N_OUTSTANDING_LOADS == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else static_assert(N_OUTSTANDING_LOADS == 0, "unsupported wait count");
+// Barrier after this wave's LDS reads have completed (no wave still reads a
+// stage when the next load into it is issued).
+__device__ __forceinline__ void lds_barrier_reads_done() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int BM, int BN, bool SWIGLU>
-__global__ __launch_bounds__(512, 1) void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A,
-                                                                const uint16_t* __restrict__ B0,
-                                                                const uint16_t* __restrict__ B1,
-                                                                void* __restrict__ Cout,
-                                                                const int32_t* __restrict__ offsets,
-                                                                const int32_t* __restrict__ tprefix, int G,
-                                                                int64_t nrows, int N, int K) {
-    constexpr int WGM = 4, WGN = 2;                   // 8 waves
-    constexpr int BK = 32, CPR = BK / 8, ROWB = BK * 2;   // 64-byte tile rows
-    constexpr int STAGES = 4;
+template <int BM, int BN, bool SWIGLU, int WGM, int WGN, int BK>
+__global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_bf16_ring_kernel(const uint16_t* __restrict__ A,
+                                                                         const uint16_t* __restrict__ B0,
+                                                                         const uint16_t* __restrict__ B1,
+                                                                         void* __restrict__ Cout,
+                                                                         const int32_t* __restrict__ offsets,
+                                                                         const int32_t* __restrict__ tprefix, int G,
+                                                                         int64_t nrows, int N, int K) {
+    constexpr int NTHR = WGM * WGN * 64;
+    constexpr int CPR = BK / 8;                     // 16-byte chunks per tile row (4 or 8)
+    constexpr int RPI = 64 / CPR;                   // tile rows per wave load instruction
+    constexpr int STAGES = BK == 32 ? 4 : 2;        // 128 KB of LDS either way
+    constexpr int SUB = BK / 16;                    // MFMA K substeps per tile
     constexpr int NOPS = SWIGLU ? 2 : 1;
     constexpr int BROWS = NOPS * BN;
     constexpr int WM = BM / WGM, WN = BN / WGN;
     constexpr int MT = WM / 32, NTW = WN / 32;
-    static_assert(MT == 2 && NOPS * NTW == 4, "operand reads are laid out for 2 A and 4 B operands");
-    constexpr int A_CH = BM * CPR, B_CH = BROWS * CPR;          // chunks per stage
-    constexpr int A_LD = A_CH / 512, B_LD = B_CH / 512;          // DMA per thread per tile
-    static_assert(A_LD + B_LD == 4, "wait counts assume 4 loads per thread per tile");
-    constexpr int A_STAGE_BYTES = A_CH * 16, B_STAGE_BYTES = B_CH * 16;
+    constexpr int A_CH = BM * CPR, B_CH = BROWS * CPR;
+    constexpr int A_LD = A_CH / NTHR, B_LD = B_CH / NTHR;    // DMA per thread per tile
+    constexpr int LOADS = A_LD + B_LD;
+    constexpr int WAVES = WGM * WGN;
+    static_assert(BK == 32 || BK == 64, "K tile");
+    static_assert(A_CH % NTHR == 0 && B_CH % NTHR == 0 && 3 * LOADS <= 63, "load plan");
 
     __shared__ uint4 sA[STAGES * A_CH];
     __shared__ uint4 sB[STAGES * B_CH];
@@ -374,34 +368,37 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pipe_kernel(const uint16_t* 
     const uint16_t* Bg = B0 + (int64_t)tc.g * wstride;
     const uint16_t* Bu = SWIGLU ? B1 + (int64_t)tc.g * wstride : Bg;
 
-    // DMA plan: instruction i of wave w fills chunks [(8 i + w) * 64, +64) = 16 tile
-    // rows; this lane fills row (8 i + w) * 16 + lane / 4 at physical chunk
-    // lane % 4, i.e. logical chunk (lane % 4) ^ swz(row).
-    const int lrow16 = lane / 4;
-    const int lchunk = (lane % 4) ^ lds_swz4(lrow16);
+    auto swz = [](int r) { return CPR == 4 ? lds_swz4(r) : lds_swz(r); };
+    // DMA plan: instruction i of wave w fills chunks [(WAVES i + w) * 64, +64) =
+    // RPI tile rows; this lane fills row (WAVES i + w) * RPI + lane / CPR at
+    // physical chunk lane % CPR, i.e. logical chunk (lane % CPR) ^ swz(row).
     const uint16_t* a_src[A_LD];
     const uint16_t* b_src[B_LD];
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
-        const int row = (8 * i + wave) * 16 + lrow16;
+        const int row = (WAVES * i + wave) * RPI + lane / CPR;
         int64_t gr = tc.row_start + row;
         if (gr >= tc.row_end) gr = tc.row_start;
-        a_src[i] = A + gr * K + lchunk * 8;
+        a_src[i] = A + gr * K + ((lane % CPR) ^ swz(row)) * 8;
     }
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
-        const int row = (8 * i + wave) * 16 + lrow16;
+        const int row = (WAVES * i + wave) * RPI + lane / CPR;
         const int op = row / BN;
         int n = n0 + row % BN;
         if (n >= N) n = n0;
-        b_src[i] = (op ? Bu : Bg) + (int64_t)n * K + lchunk * 8;
+        b_src[i] = (op ? Bu : Bg) + (int64_t)n * K + ((lane % CPR) ^ swz(row)) * 8;
     }
+    const uint32_t sA_addr = lds_byte_addr(sA), sB_addr = lds_byte_addr(sB);
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     auto issue = [&](int kt, int stage) {
         const int k0 = kt * BK;
 #pragma unroll
-        for (int i = 0; i < A_LD; ++i) dma16(a_src[i] + k0, sA + stage * A_CH + (8 * i + wave) * 64);
+        for (int i = 0; i < A_LD; ++i)
+            dma16_async(a_src[i] + k0, sA_addr + (uint32_t)((stage * A_CH + (WAVES * i + wave_u) * 64) * 16));
 #pragma unroll
-        for (int i = 0; i < B_LD; ++i) dma16(b_src[i] + k0, sB + stage * B_CH + (8 * i + wave) * 64);
+        for (int i = 0; i < B_LD; ++i)
+            dma16_async(b_src[i] + k0, sB_addr + (uint32_t)((stage * B_CH + (WAVES * i + wave_u) * 64) * 16));
     };
 
     floatx16_t acc[NOPS][MT][NTW];
@@ -415,58 +412,69 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pipe_kernel(const uint16_t* 
                 for (int v = 0; v < 16; ++v) acc[o][i][j][v] = 0.f;
 
     const int KT = K / BK;
-#pragma unroll
-    for (int t = 0; t < STAGES - 1; ++t)
-        if (t < KT) issue(t, t);
+    for (int t = 0; t < STAGES && t < KT; ++t) issue(t, t);
 
-    // Operand read addresses (stage 0, substep 0).  Substep 1 reads chunk cc ^ 2.
     const int lrow = lane % 32, lhalf = lane / 32;
-    const int cc0 = lhalf ^ lds_swz4(lrow);
-    const uint32_t a_base = lds_byte_addr(sA) + (wm * WM + lrow) * ROWB;
-    const uint32_t b_base = lds_byte_addr(sB) + (wn * WN + lrow) * ROWB;
-    const uint32_t a_s[2] = {a_base + cc0 * 16, a_base + (cc0 ^ 2) * 16};
-    const uint32_t b_s[2] = {b_base + cc0 * 16, b_base + (cc0 ^ 2) * 16};
-    // B operand (o, j) sits (o * BN + j * 32) rows further; A operand i, i * 32 rows.
-    constexpr int BO1 = (NOPS == 2 ? 0 * BN + 1 * 32 : 1 * 32) * ROWB;
-    constexpr int BO2 = (NOPS == 2 ? 1 * BN + 0 * 32 : 2 * 32) * ROWB;
-    constexpr int BO3 = (NOPS == 2 ? 1 * BN + 1 * 32 : 3 * 32) * ROWB;
-
-    auto mma = [&](const u32x4_t& a0, const u32x4_t& a1, const u32x4_t& b0, const u32x4_t& b1, const u32x4_t& b2,
-                   const u32x4_t& b3) {
-        const bf16x8_t av[2] = {__builtin_bit_cast(bf16x8_t, a0), __builtin_bit_cast(bf16x8_t, a1)};
-        const bf16x8_t bv[4] = {__builtin_bit_cast(bf16x8_t, b0), __builtin_bit_cast(bf16x8_t, b1),
-                                __builtin_bit_cast(bf16x8_t, b2), __builtin_bit_cast(bf16x8_t, b3)};
+    const int rswz = swz(lrow);    // operand rows are lrow + multiples of 32
+    auto read_ops = [&](int stage, int s, bf16x8_t (&a)[MT], bf16x8_t (&b)[NOPS][NTW]) {
+        const uint4* As = sA + stage * A_CH;
+        const uint4* Bs = sB + stage * B_CH;
+        const int cc = (2 * s + lhalf) ^ rswz;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int o = q / NTW, j = q % NTW;
+        for (int i = 0; i < MT; ++i) a[i] = as_bf16x8(As[(wm * WM + i * 32 + lrow) * CPR + cc]);
 #pragma unroll
-            for (int i = 0; i < MT; ++i)
-                acc[o][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[q], acc[o][i][j], 0, 0, 0);
-        }
+        for (int o = 0; o < NOPS; ++o)
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) b[o][j] = as_bf16x8(Bs[(o * BN + wn * WN + j * 32 + lrow) * CPR + cc]);
+    };
+    auto mma = [&](const bf16x8_t (&a)[MT], const bf16x8_t (&b)[NOPS][NTW]) {
+#pragma unroll
+        for (int o = 0; o < NOPS; ++o)
+#pragma unroll
+            for (int j = 0; j < NTW; ++j)
+#pragma unroll
+                for (int i = 0; i < MT; ++i)
+                    acc[o][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[o][j], acc[o][i][j], 0, 0, 0);
     };
 
-    auto step = [&](auto stage_c, int kt) {
-        constexpr int S = decltype(stage_c)::value;
-        const int later = min(STAGES - 2, KT - 1 - kt);
-        if (later >= 2) wait_vmcnt_n<8>();
-        else if (later == 1) wait_vmcnt_n<4>();
-        else wait_vmcnt_n<0>();
-        lds_barrier();
-        if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1, (S + STAGES - 1) % STAGES);
-        constexpr int AO = S * A_STAGE_BYTES, BOF = S * B_STAGE_BYTES;
+    wait_tiles<LOADS>(min(STAGES - 1, KT - 1));
+    lds_barrier_reads_done();
+    bf16x8_t xa[MT], xb[NOPS][NTW], ya[MT], yb[NOPS][NTW];
+    read_ops(0, 0, xa, xb);
+    for (int kt = 0; kt < KT; ++kt) {
+        const int stage = kt % STAGES;
+        // substeps 0 .. SUB-2: multiply x while reading the next substep into y, then swap
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            u32x4_t a0, a1, b0, b1, b2, b3;
-            lds_read6<AO, AO + 32 * ROWB, BOF, BOF + BO1, BOF + BO2, BOF + BO3>(a_s[s], b_s[s], a0, a1, b0, b1, b2,
-                                                                               b3);
-            mma(a0, a1, b0, b1, b2, b3);
+        for (int s = 0; s + 1 < SUB; ++s) {
+            if (s % 2 == 0) {
+                read_ops(stage, s + 1, ya, yb);
+                mma(xa, xb);
+            } else {
+                read_ops(stage, s + 1, xa, xb);
+                mma(ya, yb);
+            }
         }
-    };
-    for (int kt = 0; kt < KT; kt += STAGES) {
-        step(std::integral_constant<int, 0>{}, kt);
-        if (kt + 1 < KT) step(std::integral_constant<int, 1>{}, kt + 1);
-        if (kt + 2 < KT) step(std::integral_constant<int, 2>{}, kt + 2);
-        if (kt + 3 < KT) step(std::integral_constant<int, 3>{}, kt + 3);
+        // last substep: every wave has now read all of tile kt -> barrier, refill its
+        // stage, and read the next tile's first substep while multiplying
+        auto& la = (SUB % 2 == 0) ? ya : xa;
+        auto& lb = (SUB % 2 == 0) ? yb : xb;
+        auto& na = (SUB % 2 == 0) ? xa : ya;
+        auto& nb = (SUB % 2 == 0) ? xb : yb;
+        if (kt + 1 < KT) {
+            wait_tiles<LOADS>(min(STAGES - 2, KT - 2 - kt));
+            lds_barrier_reads_done();
+            if (kt + STAGES < KT) issue(kt + STAGES, stage);
+            read_ops((kt + 1) % STAGES, 0, na, nb);
+        }
+        mma(la, lb);
+        if (SUB % 2 == 1) {   // keep "x = operands of substep 0" for the next tile
+#pragma unroll
+            for (int i = 0; i < MT; ++i) xa[i] = ya[i];
+#pragma unroll
+            for (int o = 0; o < NOPS; ++o)
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) xb[o][j] = yb[o][j];
+        }
     }
 
 #pragma unroll
@@ -552,6 +560,17 @@ constexpr int BF16_BN1 = 128;   // GEMM1 output columns per tile (256 weight row
 constexpr int BF16_BN2 = 256;   // GEMM2 output columns per tile
 constexpr int F32_BM = 64, F32_BN = 64;
 
+template <int BM, int BN, bool SWIGLU>
+void launch_ring(unsigned grid, hipStream_t st, const uint16_t* A, const uint16_t* B0, const uint16_t* B1, void* C,
+                 const int32_t* offsets, const int32_t* tp, int G, int64_t nrows, int N, int K) {
+    if (K % 64 == 0)
+        hipLaunchKernelGGL((gemm_bf16_ring_kernel<BM, BN, SWIGLU, 4, 2, 64>), dim3(grid), dim3(512), 0, st, A, B0, B1,
+                           C, offsets, tp, G, nrows, N, K);
+    else
+        hipLaunchKernelGGL((gemm_bf16_ring_kernel<BM, BN, SWIGLU, 4, 2, 32>), dim3(grid), dim3(512), 0, st, A, B0, B1,
+                           C, offsets, tp, G, nrows, N, K);
+}
+
 hipError_t prep_tiles(const int32_t* offsets, int G, int BM, void* ws, hipStream_t st) {
     if (!offsets) return hipSuccess;
     hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, offsets, G, BM, static_cast<int32_t*>(ws));
@@ -580,7 +599,7 @@ hipError_t launch_gemm1(int dtype, const void* A, const int32_t* offsets, int G,
     if (grid == 0) return hipSuccess;
     const int32_t* tp = static_cast<const int32_t*>(ws);
     if (dtype == MOE_BF16 && K % 32 == 0)
-        hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BF16_BM, BF16_BN1, true>), dim3(grid), dim3(512), 0, st,
+        launch_ring<BF16_BM, BF16_BN1, true>(grid, st,
                            static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(w_gate),
                            static_cast<const uint16_t*>(w_up), h, offsets, tp, G, max_rows, N, K);
     else if (dtype == MOE_BF16)
@@ -604,7 +623,7 @@ hipError_t launch_gemm2(int dtype, const void* h, const int32_t* offsets, int G,
     if (grid == 0) return hipSuccess;
     const int32_t* tp = static_cast<const int32_t*>(ws);
     if (dtype == MOE_BF16 && K % 32 == 0)
-        hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BF16_BM, BF16_BN2, false>), dim3(grid), dim3(512), 0, st,
+        launch_ring<BF16_BM, BF16_BN2, false>(grid, st,
                            static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w_down), nullptr, H,
                            offsets, tp, G, max_rows, N, K);
     else if (dtype == MOE_BF16)
