@@ -60,6 +60,7 @@ class Stages:
         self.H = z(max(R, 1), d, dt=torch.float32)
         self.y = z(T, d, dt=torch.float32)
         self.s = z(T, d, dt=torch.float32) if shape.m_shared else None
+        self.ws_r = api.workspace(shape, L.MOE_WS_ROUTE, dev)
         self.ws_d = api.workspace(shape, L.MOE_WS_DISPATCH, dev)
         self.ws_f = api.workspace(shape, L.MOE_WS_FFN, dev)
         self.ws_s = api.workspace(shape, L.MOE_WS_SHARED, dev) if shape.m_shared else None
@@ -67,7 +68,8 @@ class Stages:
     def run(self, phase, st):
         s, i, p = self.shape, self.inp, lambda t: None if t is None else t.data_ptr()  # noqa: E731
         if phase == "route":
-            rc = L.moe_route(s, p(i.x), p(i.w_r), p(i.b_r), p(self.ids), p(self.w), p(self.status), st)
+            rc = L.moe_route(s, p(i.x), p(i.w_r), p(i.b_r), p(self.ids), p(self.w), p(self.status), p(self.ws_r),
+                             self.ws_r.numel(), st)
         elif phase == "dispatch":
             rc = L.moe_dispatch(s, p(i.x), p(self.ids), p(self.load), p(self.offsets), p(self.slot), p(self.row_of),
                                 p(self.src), p(self.x_perm), p(self.stats), p(self.ws_d), self.ws_d.numel(), st)

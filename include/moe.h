@@ -87,7 +87,9 @@ enum {
 };
 
 /* Which call a workspace is sized for. */
-typedef enum { MOE_WS_DISPATCH = 0, MOE_WS_FFN = 1, MOE_WS_SHARED = 2, MOE_WS_FORWARD = 3 } moe_ws_kind;
+typedef enum {
+    MOE_WS_DISPATCH = 0, MOE_WS_FFN = 1, MOE_WS_SHARED = 2, MOE_WS_FORWARD = 3, MOE_WS_ROUTE = 4
+} moe_ws_kind;
 
 /* ---- host helpers ------------------------------------------------------ */
 
@@ -123,9 +125,12 @@ const char* moe_status_str(int32_t status);
  *   status   [1]    int32 out: set to MOE_OK, or MOE_ERR_NONFINITE_LOGIT if any
  *                   score is NaN/Inf; such a token gets ids 0..k-1 and weights 0
  *                   so that later calls stay in bounds.  Read it after the
- *                   stream synchronises. */
+ *                   stream synchronises.
+ *   ws              >= moe_workspace_bytes(shape, MOE_WS_ROUTE) bytes (fp32 scores
+ *                   [T,E] when E > 64; may be NULL with ws_bytes 0 otherwise) */
 moe_status moe_route(const moe_shape* shape, const void* x, const float* w_r, const float* b_r,
-                     int32_t* topk_ids, float* topk_w, int32_t* status, void* stream);
+                     int32_t* topk_ids, float* topk_w, int32_t* status, void* ws, size_t ws_bytes,
+                     void* stream);
 
 /* Capacity-limited dispatch and load statistics (ch. 36 §36.3, Algorithm
  * 36.1 acceptance step and its invariants; "The real cost of sparse expert

@@ -38,6 +38,7 @@ MOE_WS_DISPATCH = 0
 MOE_WS_FFN = 1
 MOE_WS_SHARED = 2
 MOE_WS_FORWARD = 3
+MOE_WS_ROUTE = 4
 
 
 class MoeShape(ctypes.Structure):
@@ -58,7 +59,7 @@ _SIGS = {
     "moe_check_shape": (c_int32, [POINTER(MoeShape)]),
     "moe_status_str": (c_char_p, [c_int32]),
     "moe_route": (c_int32, [POINTER(MoeShape), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
-                            c_void_p]),
+                            c_void_p, c_size_t, c_void_p]),
     "moe_dispatch": (c_int32, [POINTER(MoeShape), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "moe_expert_ffn": (c_int32, [POINTER(MoeShape), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
@@ -125,8 +126,8 @@ def moe_check_shape(shape: MoeShape) -> int:
     return lib().moe_check_shape(ctypes.byref(shape))
 
 
-def moe_route(shape, x, w_r, b_r, topk_ids, topk_w, status, stream) -> int:
-    return lib().moe_route(ctypes.byref(shape), x, w_r, b_r, topk_ids, topk_w, status, stream)
+def moe_route(shape, x, w_r, b_r, topk_ids, topk_w, status, ws, ws_bytes, stream) -> int:
+    return lib().moe_route(ctypes.byref(shape), x, w_r, b_r, topk_ids, topk_w, status, ws, ws_bytes, stream)
 
 
 def moe_dispatch(shape, x, topk_ids, load, offsets, slot, row_of, src_token, x_perm, stats, ws, ws_bytes,

@@ -71,8 +71,9 @@ def route(shape: L.MoeShape, x, w_r, b_r=None):
     ids = torch.empty((T, k), dtype=torch.int32, device=dev)
     w = torch.empty((T, k), dtype=torch.float32, device=dev)
     status = torch.empty(1, dtype=torch.int32, device=dev)
-    L.check(L.moe_route(shape, _ptr(x), _ptr(w_r), _ptr(b_r), _ptr(ids), _ptr(w), _ptr(status), _stream()),
-            "moe_route")
+    ws = workspace(shape, L.MOE_WS_ROUTE, dev)
+    L.check(L.moe_route(shape, _ptr(x), _ptr(w_r), _ptr(b_r), _ptr(ids), _ptr(w), _ptr(status), _ptr(ws),
+                        ws.numel(), _stream()), "moe_route")
     return ids, w, status
 
 

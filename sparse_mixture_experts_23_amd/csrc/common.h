@@ -79,9 +79,10 @@ struct moe_dims {
 
 namespace moe_kernels {
 
-// Router: scores, softmax, top-k, weights.
+// Router: scores, softmax, top-k, weights.  ws holds the fp32 scores when E > 64.
+size_t route_ws_bytes(const moe_dims& s);
 hipError_t launch_route(const moe_dims& s, const void* x, const float* w_r, const float* b_r,
-                        int32_t* topk_ids, float* topk_w, int32_t* status, hipStream_t st);
+                        int32_t* topk_ids, float* topk_w, int32_t* status, void* ws, hipStream_t st);
 
 // Dispatch.
 size_t dispatch_ws_bytes(const moe_dims& s);

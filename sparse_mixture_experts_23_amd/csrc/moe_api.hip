@@ -54,6 +54,7 @@ struct ForwardWs {
     void* x_perm;
     float* H;
     float* s;
+    void* route;
     void* dispatch;
     void* ffn;
     void* shared;
@@ -76,6 +77,7 @@ ForwardWs carve_forward(const moe_dims& d, void* base) {
     w.x_perm = take((size_t)R * d.d * elem(d));
     w.H = static_cast<float*>(take(sizeof(float) * R * d.d));
     w.s = d.m_shared ? static_cast<float*>(take(sizeof(float) * d.T * d.d)) : nullptr;
+    w.route = take(route_ws_bytes(d));
     w.dispatch = take(dispatch_ws_bytes(d));
     w.ffn = take(ffn_ws(d));
     w.shared = d.m_shared ? take(shared_ws(d)) : nullptr;
@@ -136,6 +138,7 @@ size_t moe_workspace_bytes(const moe_shape* shape, int32_t kind) {
     moe_dims d;
     if (check_shape(shape, &d) != MOE_OK) return 0;
     switch (kind) {
+        case MOE_WS_ROUTE: return align_up(route_ws_bytes(d)) + ALIGN;
         case MOE_WS_DISPATCH: return align_up(dispatch_ws_bytes(d)) + ALIGN;
         case MOE_WS_FFN: return ffn_ws(d);
         case MOE_WS_SHARED: return d.m_shared ? shared_ws(d) : 0;
@@ -157,12 +160,13 @@ const char* moe_status_str(int32_t status) {
 }
 
 moe_status moe_route(const moe_shape* shape, const void* x, const float* w_r, const float* b_r, int32_t* topk_ids,
-                     float* topk_w, int32_t* status, void* stream) {
+                     float* topk_w, int32_t* status, void* ws, size_t ws_bytes, void* stream) {
     moe_dims d;
     moe_status rc = check_shape(shape, &d);
     if (rc != MOE_OK) return rc;
     if (!status || (d.T > 0 && (!x || !w_r || !topk_ids || !topk_w))) return MOE_ERR_INVALID_ARGUMENT;
-    return hip_status(launch_route(d, x, w_r, b_r, topk_ids, topk_w, status, static_cast<hipStream_t>(stream)));
+    if (route_ws_bytes(d) > 0 && (!ws || ws_bytes < route_ws_bytes(d))) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    return hip_status(launch_route(d, x, w_r, b_r, topk_ids, topk_w, status, ws, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_dispatch(const moe_shape* shape, const void* x, const int32_t* topk_ids, int32_t* load,
@@ -245,7 +249,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_r, 
     ForwardWs w = carve_forward(d, ws);
     if (ws_bytes < w.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    MOE_CHECK_HIP(launch_route(d, x, w_r, b_r, topk_ids, topk_w, status, st));
+    MOE_CHECK_HIP(launch_route(d, x, w_r, b_r, topk_ids, topk_w, status, w.route, st));
     MOE_CHECK_HIP(launch_dispatch(d, x, topk_ids, load, w.offsets, slot, w.row_of, w.src_token, w.x_perm, stats,
                                   w.dispatch, st));
     rc = ffn_impl(d, w.x_perm, w.offsets, w_gate, w_up, w_down, w.H, w.ffn, st);

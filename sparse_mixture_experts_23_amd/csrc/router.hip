@@ -8,18 +8,32 @@
 //            full softmax within S_t, "MoE token routing" §2; ch. 36 eq. (36.5))
 //            SWITCH: the full-softmax probability p_te (ch. 36 §36.2)
 //
-// One workgroup (4 waves) owns 16 tokens.  With bf16 activations the score GEMM
-// runs on the bf16 MFMA units: w_r is fp32, so each 8-wide k-slice of w_r is split
-// on the fly into three bf16 parts (hi + mid + lo carries all 24 significand bits)
-// and x * w_r is formed as three exact bf16 x bf16 products accumulated in fp32.
-// The 16 x E fp32 score tile is then reduced in LDS and every wave selects the
-// top-k of its tokens with 64-bit (score-key, ~id) wave arg-max reductions.
+// Score GEMM with bf16 activations: w_r is fp32, so it is first split into three
+// bf16 planes (hi + mid + lo carries all 24 significand bits of each weight), and
+// x * w_r is formed as three exact bf16 x bf16 products accumulated in fp32 on the
+// MFMA units -- an fp32 dot product up to summation order.
+//
+// E <= 64: one fused kernel; 8 waves share 16 tokens, each wave takes one K
+//   slice with all its loads in flight at once, the slices are summed in LDS in a
+//   fixed order and the waves select.
+// E > 64: a split-K score kernel (256 tokens x 64 experts x one K slice per
+//   workgroup) writes fp32 partial scores to the workspace, and a selection
+//   kernel with one wave per token sums the slices in a fixed order.
+// Selection: k rounds of a 64-bit (order-preserving score key, ~id) wave arg-max.
+// Everything is deterministic: no atomics, fixed summation orders.
+#include <algorithm>
+
 #include "common.h"
 
 namespace {
 
-constexpr int RT_TOK = 16;
-constexpr int RT_THREADS = 256;
+constexpr int RT_TOK = 16;       // fused kernel: tokens per workgroup
+constexpr int RT_WAVES = 8;       //               waves (K slices) per workgroup
+constexpr int RT_THREADS = 64 * RT_WAVES;
+
+constexpr int SC_TOK = 256;       // score kernel: tokens per workgroup (64 per wave)
+constexpr int SC_EXP = 64;        //               experts per workgroup
+constexpr int SC_KU = 2;          //               k-steps of 32 per load batch
 
 __global__ void zero_i32_kernel(int32_t* p, int n) {
     int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -27,8 +41,7 @@ __global__ void zero_i32_kernel(int32_t* p, int n) {
 }
 
 // Split 8 fp32 weights into three bf16 vectors whose sum reproduces them.
-__device__ __forceinline__ void split3(const float4 w0, const float4 w1, bf16x8_t& hi, bf16x8_t& mid,
-                                       bf16x8_t& lo) {
+__device__ __forceinline__ void split3(const float4 w0, const float4 w1, uint4& H, uint4& M, uint4& L) {
     float v[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
     uint32_t h[8], m[8], l[8];
 #pragma unroll
@@ -39,100 +52,167 @@ __device__ __forceinline__ void split3(const float4 w0, const float4 w1, bf16x8_
         float r2 = r1 - bf16_bits_to_f32(m[j]);
         l[j] = f32_to_bf16_bits(r2);
     }
-    uint4 H = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-    uint4 M = {m[0] | (m[1] << 16), m[2] | (m[3] << 16), m[4] | (m[5] << 16), m[6] | (m[7] << 16)};
-    uint4 L = {l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)};
-    hi = as_bf16x8(H);
-    mid = as_bf16x8(M);
-    lo = as_bf16x8(L);
+    H = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+    M = {m[0] | (m[1] << 16), m[2] | (m[3] << 16), m[4] | (m[5] << 16), m[6] | (m[7] << 16)};
+    L = {l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)};
 }
 
-// Scores of 16 tokens x E experts into lg[16][E] (bf16 x, MFMA 16x16x32).
-template <int MAXT>
-__device__ void scores_bf16_mfma(const uint16_t* __restrict__ x, const float* __restrict__ w_r, int64_t t0,
-                                 int64_t T, int d, int E, float* lg, float* part) {
-    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-    const int NT = (E + 15) / 16;
-    const int CG = NT < 4 ? NT : 4;
-    const int KS = 4 / CG;
-    const int cg = wave % CG, ks = wave / CG;
-    const int kchunks = (d + 31) / 32;
-    const int per = (kchunks + KS - 1) / KS;
-    const int kbeg = ks * per * 32;
-    const int kend = min(d, (ks + 1) * per * 32);
-    const bool active = ks < KS;
+// w3[p][e][i] = plane p (hi, mid, lo) of w_r[e][i]; 8 weights per thread.
+__global__ __launch_bounds__(256) void split_router_kernel(const float* __restrict__ w_r, int64_t n8,
+                                                           uint4* __restrict__ w3) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n8) return;
+    const float4* src = reinterpret_cast<const float4*>(w_r) + 2 * i;
+    uint4 H, M, L;
+    split3(src[0], src[1], H, M, L);
+    w3[i] = H;
+    w3[n8 + i] = M;
+    w3[2 * n8 + i] = L;
+}
 
-    floatx4_t acc[MAXT];
+__device__ __forceinline__ floatx4_t mfma3(const bf16x8_t a, const uint4 H, const uint4 M, const uint4 L,
+                                           floatx4_t acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(L), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(M), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(H), acc, 0, 0, 0);
+    return acc;
+}
+
+// ---------------------------------------------------------------------------
+// selection and weights for one token (called by a whole wave)
+// ---------------------------------------------------------------------------
+template <int EPL>
+__device__ void select_token(const float* __restrict__ row, const float* __restrict__ b_r, int E, int k, int mode,
+                             int64_t t, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
+                             int32_t* __restrict__ status) {
+    const int lane = threadIdx.x % 64;
+    float v[EPL];
+    bool bad = false;
 #pragma unroll
-    for (int j = 0; j < MAXT; ++j) acc[j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < EPL; ++j) {
+        const int e = lane + 64 * j;
+        float g = -INFINITY;
+        if (e < E) {
+            g = row[e] + (b_r ? b_r[e] : 0.f);
+            bad |= !isfinite(g);
+        }
+        v[j] = g;
+    }
+    if (__any(bad)) {
+        if (lane < k) {
+            topk_ids[t * k + lane] = lane;
+            topk_w[t * k + lane] = 0.f;
+        }
+        if (lane == 0) *status = MOE_ERR_NONFINITE_LOGIT;
+        return;
+    }
+    // k rounds of a wave arg-max over (score key, lower id first).
+    uint32_t taken = 0;
+    int my_e = 0;
+    float my_g = 0.f;
+    for (int s = 0; s < k; ++s) {
+        unsigned long long best = 0ull;
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+            const int e = lane + 64 * j;
+            if (e < E && !((taken >> j) & 1u)) {
+                const unsigned long long key =
+                    ((unsigned long long)float_order_key(v[j]) << 32) | (unsigned long long)(0xffffffffu - (uint32_t)e);
+                best = key > best ? key : best;
+            }
+        }
+        best = wave_max_u64(best);
+        const int e_sel = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffull));
+        if ((e_sel & 63) == lane) taken |= 1u << (e_sel >> 6);
+        float g_sel = 0.f;
+#pragma unroll
+        for (int j = 0; j < EPL; ++j)
+            if (lane + 64 * j == e_sel) g_sel = v[j];
+        g_sel = __shfl(g_sel, e_sel & 63, MOE_WAVE);
+        if (lane == s) {
+            my_e = e_sel;
+            my_g = g_sel;
+        }
+    }
+    const float g_top = __shfl(my_g, 0, MOE_WAVE);   // the largest score
+    float wgt;
+    if (mode == MOE_GATE_SWITCH) {
+        float z = 0.f;
+#pragma unroll
+        for (int j = 0; j < EPL; ++j)
+            if (lane + 64 * j < E) z += expf(v[j] - g_top);
+        z = wave_sum(z);
+        wgt = expf(my_g - g_top) / z;
+    } else {
+        const float ez = lane < k ? expf(my_g - g_top) : 0.f;
+        const float z = wave_sum(ez);
+        wgt = ez / z;
+    }
+    if (lane < k) {
+        topk_ids[t * k + lane] = my_e;
+        topk_w[t * k + lane] = wgt;
+    }
+}
 
+// ---------------------------------------------------------------------------
+// E <= 64: fused scores + selection, 16 tokens per workgroup, 8 K slices
+// ---------------------------------------------------------------------------
+
+// Wave `wave` adds x[t0..t0+15] . w3[e] over its K slice for every expert column
+// tile; results land in part[wave][16][Epad].  All loads of the slice are issued
+// before the first MFMA.
+template <int NT>
+__device__ void scores_bf16_small(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w3, int64_t t0,
+                                  int64_t T, int d, int E, float* part) {
+    constexpr int KU = 8 / NT;                     // k-steps of 32 in flight (x + 3 planes per column tile)
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
     const int row = lane % 16, grp = lane / 16;
     const int64_t t = t0 + row;
     const bool tok_ok = t < T;
-    const uint16_t* xrow = x + (tok_ok ? t : 0) * (int64_t)d;
+    const uint16_t* xrow = x + (tok_ok ? t : 0) * (int64_t)d + grp * 8;
+    const int64_t plane = (int64_t)E * d;
+    const int kchunks = (d + 31) / 32;
+    const int per = (kchunks + RT_WAVES - 1) / RT_WAVES;
+    const int kbeg = wave * per * 32, kend = min(d, (wave + 1) * per * 32);
 
-    if (active) {
-        for (int k0 = kbeg; k0 < kend; k0 += 32) {
-            const int kk = k0 + grp * 8;
+    floatx4_t acc[NT];
+#pragma unroll
+    for (int c = 0; c < NT; ++c) acc[c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = kbeg; k0 < kend; k0 += 32 * KU) {
+        uint4 av[KU], bw[KU][NT][3];
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+            const int kk = k0 + 32 * u + grp * 8;
             const bool k_ok = kk < kend;
-            uint4 av = {0u, 0u, 0u, 0u};
-            if (tok_ok && k_ok) av = *reinterpret_cast<const uint4*>(xrow + kk);
-            const bf16x8_t a = as_bf16x8(av);
+            av[u] = (tok_ok && k_ok) ? *reinterpret_cast<const uint4*>(xrow + k0 + 32 * u) : uint4{0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int j = 0; j < MAXT; ++j) {
-                const int ct = cg + j * CG;
-                if (ct < NT) {
-                    const int e = ct * 16 + row;
-                    float4 w0 = {0.f, 0.f, 0.f, 0.f}, w1 = {0.f, 0.f, 0.f, 0.f};
-                    if (e < E && k_ok) {
-                        const float4* wp = reinterpret_cast<const float4*>(w_r + (int64_t)e * d + kk);
-                        w0 = wp[0];
-                        w1 = wp[1];
-                    }
-                    bf16x8_t hi, mid, lo;
-                    split3(w0, w1, hi, mid, lo);
-                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, lo, acc[j], 0, 0, 0);
-                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, mid, acc[j], 0, 0, 0);
-                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, hi, acc[j], 0, 0, 0);
-                }
+            for (int c = 0; c < NT; ++c) {
+                const int e = c * 16 + row;
+#pragma unroll
+                for (int p = 0; p < 3; ++p)
+                    bw[u][c][p] = (e < E && k_ok)
+                                      ? *reinterpret_cast<const uint4*>(w3 + p * plane + (int64_t)e * d + kk)
+                                      : uint4{0u, 0u, 0u, 0u};
             }
         }
-    }
-    // Accumulator layout: lane holds column (lane % 16), rows 4*(lane/16) + i.
-    const int Epad = NT * 16;
-    if (active) {
 #pragma unroll
-        for (int j = 0; j < MAXT; ++j) {
-            const int ct = cg + j * CG;
-            if (ct < NT) {
-                const int e = ct * 16 + (lane % 16);
+        for (int u = 0; u < KU; ++u)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 4 * (lane / 16) + i;
-                    if (KS == 1) {
-                        if (e < E) lg[r * E + e] = acc[j][i];
-                    } else {
-                        part[(ks * RT_TOK + r) * Epad + e] = acc[j][i];
-                    }
-                }
-            }
-        }
+            for (int c = 0; c < NT; ++c)
+                acc[c] = mfma3(as_bf16x8(av[u]), bw[u][c][0], bw[u][c][1], bw[u][c][2], acc[c]);
     }
-    if (KS > 1) {
-        __syncthreads();
-        for (int p = threadIdx.x; p < RT_TOK * E; p += RT_THREADS) {
-            const int r = p / E, e = p % E;
-            float s = 0.f;
-            for (int q = 0; q < KS; ++q) s += part[(q * RT_TOK + r) * Epad + e];
-            lg[p] = s;
-        }
-    }
+    // lane holds expert column (lane % 16) of tile c, token rows 4*(lane/16) + i
+    constexpr int Epad = NT * 16;
+#pragma unroll
+    for (int c = 0; c < NT; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part[(wave * RT_TOK + 4 * grp + i) * Epad + c * 16 + row] = acc[c][i];
 }
 
 // Scores with fp32 activations: plain fp32 fused multiply-add dot products.
 __device__ void scores_f32(const float* __restrict__ x, const float* __restrict__ w_r, int64_t t0, int64_t T,
-                           int d, int E, float* lg) {
-    for (int p = threadIdx.x; p < RT_TOK * E; p += RT_THREADS) {
+                           int d, int E, int ntok, float* lg) {
+    for (int p = threadIdx.x; p < ntok * E; p += blockDim.x) {
         const int r = p / E, e = p % E;
         const int64_t t = t0 + r;
         float s = 0.f;
@@ -145,129 +225,240 @@ __device__ void scores_f32(const float* __restrict__ x, const float* __restrict_
     }
 }
 
-template <int EPL, bool BF16>
-__global__ __launch_bounds__(RT_THREADS) void route_kernel(const void* __restrict__ xv, const float* __restrict__ w_r,
-                                                           const float* __restrict__ b_r, int64_t T, int d, int E,
-                                                           int k, int mode, int32_t* __restrict__ topk_ids,
-                                                           float* __restrict__ topk_w, int32_t* __restrict__ status) {
-    extern __shared__ float smem[];
-    float* lg = smem;                       // [RT_TOK][E]
-    float* part = smem + RT_TOK * E;        // split-K partials (small E only)
+template <bool BF16, int NT>
+__global__ __launch_bounds__(RT_THREADS) void route_small_kernel(const void* __restrict__ xv,
+                                                                 const float* __restrict__ w_r,
+                                                                 const uint16_t* __restrict__ w3,
+                                                                 const float* __restrict__ b_r, int64_t T, int d,
+                                                                 int E, int k, int mode, int32_t* __restrict__ topk_ids,
+                                                                 float* __restrict__ topk_w,
+                                                                 int32_t* __restrict__ status) {
+    __shared__ float lg[RT_TOK * NT * 16];
+    __shared__ float part[BF16 ? RT_WAVES * RT_TOK * NT * 16 : 1];
     const int64_t t0 = (int64_t)blockIdx.x * RT_TOK;
-
-    if (BF16)
-        scores_bf16_mfma<EPL>(static_cast<const uint16_t*>(xv), w_r, t0, T, d, E, lg, part);
-    else
-        scores_f32(static_cast<const float*>(xv), w_r, t0, T, d, E, lg);
+    if (BF16) {
+        scores_bf16_small<NT>(static_cast<const uint16_t*>(xv), w3, t0, T, d, E, part);
+        __syncthreads();
+        for (int p = threadIdx.x; p < RT_TOK * E; p += RT_THREADS) {
+            const int r = p / E, e = p % E;
+            float s = 0.f;
+#pragma unroll
+            for (int q = 0; q < RT_WAVES; ++q) s += part[(q * RT_TOK + r) * NT * 16 + e];
+            lg[p] = s;
+        }
+    } else {
+        scores_f32(static_cast<const float*>(xv), w_r, t0, T, d, E, RT_TOK, lg);
+    }
     __syncthreads();
-
-    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-    for (int r = wave; r < RT_TOK; r += RT_THREADS / 64) {
+    const int wave = threadIdx.x / 64;
+    for (int r = wave; r < RT_TOK; r += RT_WAVES) {
         const int64_t t = t0 + r;
         if (t >= T) break;
-        float v[EPL];
-        bool bad = false;
-#pragma unroll
-        for (int j = 0; j < EPL; ++j) {
-            const int e = lane + 64 * j;
-            float g = -INFINITY;
-            if (e < E) {
-                g = lg[r * E + e] + (b_r ? b_r[e] : 0.f);
-                bad |= !isfinite(g);
-            }
-            v[j] = g;
-        }
-        bad = __any(bad);
-        if (bad) {
-            if (lane < k) {
-                topk_ids[t * k + lane] = lane;
-                topk_w[t * k + lane] = 0.f;
-            }
-            if (lane == 0) *status = MOE_ERR_NONFINITE_LOGIT;
-            continue;
-        }
-        // k rounds of a wave arg-max over (score key, lower id first).
-        uint32_t taken = 0;
-        int my_e = 0;
-        float my_g = 0.f;
-        for (int s = 0; s < k; ++s) {
-            unsigned long long best = 0ull;
-#pragma unroll
-            for (int j = 0; j < EPL; ++j) {
-                const int e = lane + 64 * j;
-                if (e < E && !((taken >> j) & 1u)) {
-                    const unsigned long long key =
-                        ((unsigned long long)float_order_key(v[j]) << 32) | (unsigned long long)(0xffffffffu - (uint32_t)e);
-                    best = key > best ? key : best;
-                }
-            }
-            best = wave_max_u64(best);
-            const int e_sel = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffull));
-            if ((e_sel & 63) == lane) taken |= 1u << (e_sel >> 6);
-            // recover the score of the winner from its owner lane
-            float g_sel = 0.f;
-#pragma unroll
-            for (int j = 0; j < EPL; ++j)
-                if (lane + 64 * j == e_sel) g_sel = v[j];
-            g_sel = __shfl(g_sel, e_sel & 63, MOE_WAVE);
-            if (lane == s) {
-                my_e = e_sel;
-                my_g = g_sel;
-            }
-        }
-        const float g_top = __shfl(my_g, 0, MOE_WAVE);   // the largest score
-        float wgt;
-        if (mode == MOE_GATE_SWITCH) {
-            float z = 0.f;
-#pragma unroll
-            for (int j = 0; j < EPL; ++j)
-                if (lane + 64 * j < E) z += expf(v[j] - g_top);
-            z = wave_sum(z);
-            wgt = expf(my_g - g_top) / z;
-        } else {
-            const float ez = lane < k ? expf(my_g - g_top) : 0.f;
-            const float z = wave_sum(ez);
-            wgt = ez / z;
-        }
-        if (lane < k) {
-            topk_ids[t * k + lane] = my_e;
-            topk_w[t * k + lane] = wgt;
-        }
+        select_token<1>(lg + r * E, b_r, E, k, mode, t, topk_ids, topk_w, status);
     }
 }
 
+// ---------------------------------------------------------------------------
+// E > 64: split-K score kernel + selection kernel
+// ---------------------------------------------------------------------------
+
+// Workgroup = 4 waves: 256 tokens x 64 experts x K slice ks; wave w owns tokens
+// 64 w .. 64 w + 63 (4 row tiles) x the 64 experts (4 column tiles).
+// part[ks][t][e] = sum over the slice of x[t] . w_r[e].
+__global__ __launch_bounds__(256) void router_scores_kernel(const uint16_t* __restrict__ x,
+                                                            const uint16_t* __restrict__ w3, int64_t T, int d, int E,
+                                                            int kslice, float* __restrict__ part) {
+    const int ntb = (int)((T + SC_TOK - 1) / SC_TOK);
+    const int neb = (E + SC_EXP - 1) / SC_EXP;
+    const int ks = blockIdx.x / (ntb * neb);
+    const int rem = blockIdx.x % (ntb * neb);
+    const int eb = rem / ntb, tb = rem % ntb;      // token blocks of one expert group are adjacent
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    const int row = lane % 16, grp = lane / 16;
+    const int kbeg = ks * kslice, kend = min(d, kbeg + kslice);
+    const int64_t plane = (int64_t)E * d;
+
+    const uint16_t* xr[4];
+    bool tok_ok[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t t = (int64_t)tb * SC_TOK + wave * 64 + i * 16 + row;
+        tok_ok[i] = t < T;
+        xr[i] = x + (tok_ok[i] ? t : 0) * (int64_t)d + grp * 8;
+    }
+    const uint16_t* wr[4];
+    bool e_ok[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int e = eb * SC_EXP + c * 16 + row;
+        e_ok[c] = e < E;
+        wr[c] = w3 + (int64_t)(e_ok[c] ? e : 0) * d + grp * 8;
+    }
+
+    floatx4_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[i][c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (int k0 = kbeg; k0 < kend; k0 += 32 * SC_KU) {
+        uint4 av[SC_KU][4], bw[SC_KU][4][3];
+#pragma unroll
+        for (int u = 0; u < SC_KU; ++u) {
+            const int kk = k0 + 32 * u;
+            const bool k_ok = kk + grp * 8 < kend;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                av[u][i] = (tok_ok[i] && k_ok) ? *reinterpret_cast<const uint4*>(xr[i] + kk) : uint4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int p = 0; p < 3; ++p)
+                    bw[u][c][p] = (e_ok[c] && k_ok) ? *reinterpret_cast<const uint4*>(wr[c] + p * plane + kk)
+                                                    : uint4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < SC_KU; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    acc[i][c] = mfma3(as_bf16x8(av[u][i]), bw[u][c][0], bw[u][c][1], bw[u][c][2], acc[i][c]);
+    }
+    float* out = part + (int64_t)ks * T * E;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int e = eb * SC_EXP + c * 16 + row;
+        if (!e_ok[c]) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t t = (int64_t)tb * SC_TOK + wave * 64 + i * 16 + 4 * grp + v;
+                if (t < T) out[t * E + e] = acc[i][c][v];
+            }
+    }
+}
+
+__global__ __launch_bounds__(256) void router_scores_f32_kernel(const float* __restrict__ x,
+                                                                const float* __restrict__ w_r, int64_t T, int d,
+                                                                int E, float* __restrict__ scores) {
+    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (p >= T * E) return;
+    const int64_t t = p / E;
+    const int e = (int)(p % E);
+    const float* xr = x + t * (int64_t)d;
+    const float* wr = w_r + (int64_t)e * d;
+    float s = 0.f;
+    for (int i = 0; i < d; ++i) s = fmaf(xr[i], wr[i], s);
+    scores[p] = s;
+}
+
+// One wave per token: sums the KS partial score rows in slice order, then selects.
 template <int EPL>
-hipError_t launch_route_epl(const moe_dims& s, const void* x, const float* w_r, const float* b_r, int32_t* ids,
-                            float* w, int32_t* status, hipStream_t st) {
-    const int NT = (s.E + 15) / 16;
-    const int CG = NT < 4 ? NT : 4;
-    const int KS = 4 / CG;
-    size_t lds = sizeof(float) * RT_TOK * s.E;
-    if (s.dtype == MOE_BF16 && KS > 1) lds += sizeof(float) * KS * RT_TOK * NT * 16;
-    const unsigned grid = (unsigned)((s.T + RT_TOK - 1) / RT_TOK);
-    if (s.dtype == MOE_BF16)
-        hipLaunchKernelGGL((route_kernel<EPL, true>), dim3(grid), dim3(RT_THREADS), lds, st, x, w_r, b_r, s.T, s.d,
-                           s.E, s.k, s.gate_mode, ids, w, status);
-    else
-        hipLaunchKernelGGL((route_kernel<EPL, false>), dim3(grid), dim3(RT_THREADS), lds, st, x, w_r, b_r, s.T, s.d,
-                           s.E, s.k, s.gate_mode, ids, w, status);
-    return hipGetLastError();
+__global__ __launch_bounds__(256) void route_select_kernel(const float* __restrict__ part, int KS,
+                                                           const float* __restrict__ b_r, int64_t T, int E, int k,
+                                                           int mode, int32_t* __restrict__ topk_ids,
+                                                           float* __restrict__ topk_w, int32_t* __restrict__ status) {
+    __shared__ float rows[4][EPL * 64];
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+    if (t >= T) return;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+        const int e = lane + 64 * j;
+        float s = 0.f;
+        if (e < E)
+            for (int q = 0; q < KS; ++q) s += part[((int64_t)q * T + t) * E + e];
+        rows[wave][e] = s;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    select_token<EPL>(rows[wave], b_r, E, k, mode, t, topk_ids, topk_w, status);
+}
+
+template <int EPL>
+void launch_select(const moe_dims& s, const float* part, int KS, const float* b_r, int32_t* ids, float* w,
+                   int32_t* status, hipStream_t st) {
+    hipLaunchKernelGGL((route_select_kernel<EPL>), dim3((unsigned)((s.T + 3) / 4)), dim3(256), 0, st, part, KS, b_r,
+                       s.T, s.E, s.k, s.gate_mode, ids, w, status);
+}
+
+// K slices of the split-K score kernel: enough workgroups to fill the GPU,
+// slices of at least 256 (a multiple of 32).
+int score_slices(const moe_dims& s, int* kslice) {
+    const int64_t tiles = ((s.T + SC_TOK - 1) / SC_TOK) * ((s.E + SC_EXP - 1) / SC_EXP);
+    int KS = (int)std::max<int64_t>(1, (256 + tiles - 1) / tiles);
+    KS = std::min(KS, std::max(1, s.d / 256));
+    int ksl = (s.d + KS - 1) / KS;
+    ksl = (ksl + 31) / 32 * 32;
+    KS = (s.d + ksl - 1) / ksl;
+    if (kslice) *kslice = ksl;
+    return KS;
 }
 
 }  // namespace
 
 namespace moe_kernels {
 
+size_t route_ws_bytes(const moe_dims& s) {
+    if (s.dtype != MOE_BF16) return s.E > 64 ? (size_t)s.T * s.E * sizeof(float) : 0;
+    size_t planes = ((size_t)3 * s.E * s.d * 2 + 255) & ~(size_t)255;
+    if (s.E <= 64) return planes;
+    return planes + (size_t)score_slices(s, nullptr) * s.T * s.E * sizeof(float);
+}
+
 hipError_t launch_route(const moe_dims& s, const void* x, const float* w_r, const float* b_r, int32_t* topk_ids,
-                        float* topk_w, int32_t* status, hipStream_t st) {
+                        float* topk_w, int32_t* status, void* ws, hipStream_t st) {
     hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(64), 0, st, status, 1);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || s.T == 0) return e;
-    if (s.E <= 64) return launch_route_epl<1>(s, x, w_r, b_r, topk_ids, topk_w, status, st);
-    if (s.E <= 128) return launch_route_epl<2>(s, x, w_r, b_r, topk_ids, topk_w, status, st);
-    if (s.E <= 256) return launch_route_epl<4>(s, x, w_r, b_r, topk_ids, topk_w, status, st);
-    if (s.E <= 512) return launch_route_epl<8>(s, x, w_r, b_r, topk_ids, topk_w, status, st);
-    return launch_route_epl<16>(s, x, w_r, b_r, topk_ids, topk_w, status, st);
+    uint16_t* w3 = static_cast<uint16_t*>(ws);
+    if (s.dtype == MOE_BF16) {
+        const int64_t n8 = (int64_t)s.E * s.d / 8;
+        hipLaunchKernelGGL(split_router_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, w_r, n8,
+                           reinterpret_cast<uint4*>(w3));
+    }
+    if (s.E <= 64) {
+        const unsigned grid = (unsigned)((s.T + RT_TOK - 1) / RT_TOK);
+        const int NT = (s.E + 15) / 16;
+#define MOE_SMALL(NTV)                                                                                          \
+    do {                                                                                                       \
+        if (s.dtype == MOE_BF16)                                                                               \
+            hipLaunchKernelGGL((route_small_kernel<true, NTV>), dim3(grid), dim3(RT_THREADS), 0, st, x, w_r, w3, \
+                               b_r, s.T, s.d, s.E, s.k, s.gate_mode, topk_ids, topk_w, status);                \
+        else                                                                                                   \
+            hipLaunchKernelGGL((route_small_kernel<false, NTV>), dim3(grid), dim3(RT_THREADS), 0, st, x, w_r, w3, \
+                               b_r, s.T, s.d, s.E, s.k, s.gate_mode, topk_ids, topk_w, status);                \
+    } while (0)
+        if (NT == 1) MOE_SMALL(1);
+        else if (NT == 2) MOE_SMALL(2);
+        else MOE_SMALL(4);
+#undef MOE_SMALL
+        return hipGetLastError();
+    }
+    float* part;
+    int KS = 1;
+    if (s.dtype == MOE_BF16) {
+        part = reinterpret_cast<float*>(static_cast<char*>(ws) + (((size_t)3 * s.E * s.d * 2 + 255) & ~(size_t)255));
+        int ksl = 0;
+        KS = score_slices(s, &ksl);
+        const unsigned grid =
+            (unsigned)(((s.T + SC_TOK - 1) / SC_TOK) * ((s.E + SC_EXP - 1) / SC_EXP) * KS);
+        hipLaunchKernelGGL(router_scores_kernel, dim3(grid), dim3(256), 0, st, static_cast<const uint16_t*>(x), w3,
+                           s.T, s.d, s.E, ksl, part);
+    } else {
+        part = static_cast<float*>(ws);
+        const unsigned grid = (unsigned)((s.T * s.E + 255) / 256);
+        hipLaunchKernelGGL(router_scores_f32_kernel, dim3(grid), dim3(256), 0, st, static_cast<const float*>(x), w_r,
+                           s.T, s.d, s.E, part);
+    }
+    if (s.E <= 128) launch_select<2>(s, part, KS, b_r, topk_ids, topk_w, status, st);
+    else if (s.E <= 256) launch_select<4>(s, part, KS, b_r, topk_ids, topk_w, status, st);
+    else if (s.E <= 512) launch_select<8>(s, part, KS, b_r, topk_ids, topk_w, status, st);
+    else launch_select<16>(s, part, KS, b_r, topk_ids, topk_w, status, st);
+    return hipGetLastError();
 }
 
 }  // namespace moe_kernels

@@ -59,7 +59,7 @@ def test_max_rows_and_workspace():
     assert L.moe_max_rows(_shape(T=1024, k=1, capacity=160)) == 1024
     assert L.moe_max_rows(_shape(T=1024, k=1, capacity=100)) == 800
     assert L.moe_max_rows(_shape(k=0)) == 0
-    for kind in (L.MOE_WS_DISPATCH, L.MOE_WS_FFN, L.MOE_WS_FORWARD):
+    for kind in (L.MOE_WS_DISPATCH, L.MOE_WS_FFN, L.MOE_WS_FORWARD, L.MOE_WS_ROUTE):
         assert L.moe_workspace_bytes(_shape(), kind) > 0
         assert L.moe_workspace_bytes(_shape(), kind) % 256 == 0
     assert L.moe_workspace_bytes(_shape(), L.MOE_WS_SHARED) == 0
@@ -74,8 +74,11 @@ def test_max_rows_and_workspace():
 def test_argument_errors_return_before_any_launch():
     s = _shape(T=16, d=64, m=64)
     fake = 4096  # never dereferenced: every call below fails its host-side checks
-    assert L.moe_route(s, fake, fake, None, fake, fake, None, None) == L.MOE_ERR_INVALID_ARGUMENT
-    assert L.moe_route(_shape(k=0), fake, fake, None, fake, fake, fake, None) == L.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_route(s, fake, fake, None, fake, fake, None, None, 0, None) == L.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_route(_shape(k=0), fake, fake, None, fake, fake, fake, None, 0, None) == L.MOE_ERR_INVALID_ARGUMENT
+    big = _shape(T=16, d=64, m=64, E=128, k=8)
+    assert L.moe_workspace_bytes(big, L.MOE_WS_ROUTE) >= 16 * 128 * 4
+    assert L.moe_route(big, fake, fake, None, fake, fake, fake, None, 0, None) == L.MOE_ERR_WORKSPACE_TOO_SMALL
     assert L.moe_dispatch(s, fake, fake, None, fake, fake, fake, fake, fake, fake, fake, 1 << 20,
                           None) == L.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_dispatch(s, fake, fake, fake, fake, fake, fake, fake, fake, fake, fake, 1,
