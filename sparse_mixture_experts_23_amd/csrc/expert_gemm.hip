@@ -13,15 +13,15 @@
 //     BN up rows of the weights into one B tile so that each lane owns the gate
 //     and the up value of the same output element and applies SiLU(g) * u in
 //     registers before a single bf16 store.
-//   * main kernel (K % 32 == 0): 8 waves (2 per SIMD), K tiles of 64 (or 32)
-//     streamed into an LDS ring by gfx950's direct global->LDS loads; see
-//     gemm_bf16_ring_kernel.
+//   * main kernel (K % 64 == 0): 8 waves (2 per SIMD), K tiles of 64 streamed
+//     into two LDS stages by gfx950's direct global->LDS loads, the steady-state
+//     K tile written as one scheduled asm block; see gemm_bf16_asm_kernel.
 //   * fallback kernel (any K % 8 == 0): 4 waves, register-staged loads, K tiles
 //     of 64 double-buffered in LDS, zero-filled K tail.
 //   * LDS rows are stored with their 16-byte chunks XOR-swizzled by row, so the
 //     16-byte operand reads of 32 consecutive rows hit distinct banks.
 //   * Workgroups are renumbered so that every XCD (workgroup id mod 8) receives
-//     a contiguous run of the work list, ordered (n super-tile of 8, m tile,
+//     a contiguous run of the work list, ordered (n super-tile of 4, m tile,
 //     n tile): the workgroups an XCD runs together share A row tiles and expert
 //     weight tiles in its own L2.
 // fp32 path: a plain LDS-tiled fp32 FMA kernel (64 x 64 tiles, 4 x 4 per thread).
@@ -271,15 +271,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const uint16_t* __res
 }
 
 // ---------------------------------------------------------------------------
-// helpers of the pipelined bf16 kernel
+// helpers of the scheduled bf16 kernel
 // ---------------------------------------------------------------------------
 
-// Swizzle of the 4 chunks of a 64-byte tile row: any 8 consecutive rows read at
-// one chunk hit 8 different 16-byte bank groups of a 128-byte window, and any 16
-// consecutive rows 16 different groups of a 256-byte window.
-__device__ __forceinline__ int lds_swz4(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
-
-// The same global->LDS load issued from a tiny asm statement.  It has no
+// gfx950's direct global->LDS load (16 bytes per lane to M0 + 16 * lane) issued
+// from a tiny asm statement.  It has no
 // register outputs (the data goes to LDS), so it does not touch the rule that
 // asm loads must wait for their outputs; what it changes is that the compiler
 // no longer sees an LDS write it cannot place, and so it stops making every LDS
@@ -301,20 +297,6 @@ __device__ __forceinline__ uint32_t lds_byte_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// ---------------------------------------------------------------------------
-// bf16 MFMA grouped GEMM: 8 waves, global->LDS ring, barrier per K tile
-// ---------------------------------------------------------------------------
-//
-// Workgroup tile 256 rows x BN output columns (GEMM1: 128 gate + 128 up weight
-// rows in one B tile), 8 waves = 2 per SIMD, each owning a 64 x 128 tile of
-// 32x32x16 MFMA accumulators.  K tiles (BK = 64: 2 LDS stages; BK = 32: 4
-// stages; 128 KB either way) are written straight into LDS by dma16_async, one
-// full 128-byte line per row segment at BK = 64.  The compiler schedules the
-// ordinary LDS operand reads of the next K substep between the MFMAs of the
-// current one.  The barrier sits before the last substep of a tile: by then
-// every wave has read all of tile kt, so its stage is refilled with tile
-// kt + STAGES at once, and the next tile's first operands are read while the
-// last substep multiplies.
 // Wait until at most n K tiles of LOADS global->LDS loads each are still in flight.
 template <int LOADS>
 __device__ __forceinline__ void wait_tiles(int n) {
@@ -330,169 +312,260 @@ __device__ __forceinline__ void lds_barrier_reads_done() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int BM, int BN, bool SWIGLU, int WGM, int WGN, int BK>
-__global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_bf16_ring_kernel(const uint16_t* __restrict__ A,
-                                                                         const uint16_t* __restrict__ B0,
-                                                                         const uint16_t* __restrict__ B1,
-                                                                         void* __restrict__ Cout,
-                                                                         const int32_t* __restrict__ offsets,
-                                                                         const int32_t* __restrict__ tprefix, int G,
-                                                                         int64_t nrows, int N, int K) {
-    constexpr int NTHR = WGM * WGN * 64;
-    constexpr int CPR = BK / 8;                     // 16-byte chunks per tile row (4 or 8)
-    constexpr int RPI = 64 / CPR;                   // tile rows per wave load instruction
-    constexpr int STAGES = BK == 32 ? 4 : 2;        // 128 KB of LDS either way
-    constexpr int SUB = BK / 16;                    // MFMA K substeps per tile
-    constexpr int NOPS = SWIGLU ? 2 : 1;
-    constexpr int BROWS = NOPS * BN;
-    constexpr int WM = BM / WGM, WN = BN / WGN;
-    constexpr int MT = WM / 32, NTW = WN / 32;
-    constexpr int A_CH = BM * CPR, B_CH = BROWS * CPR;
-    constexpr int A_LD = A_CH / NTHR, B_LD = B_CH / NTHR;    // DMA per thread per tile
-    constexpr int LOADS = A_LD + B_LD;
-    constexpr int WAVES = WGM * WGN;
-    static_assert(BK == 32 || BK == 64, "K tile");
-    static_assert(A_CH % NTHR == 0 && B_CH % NTHR == 0 && 3 * LOADS <= 63, "load plan");
 
-    __shared__ uint4 sA[STAGES * A_CH];
-    __shared__ uint4 sB[STAGES * B_CH];
+// ---------------------------------------------------------------------------
+// bf16 MFMA grouped GEMM: 8 waves, global->LDS ring, one scheduled asm block per K tile
+// ---------------------------------------------------------------------------
+//
+// Workgroup tile 256 rows x BN output columns (GEMM1: BN = 128 gate + 128 up
+// weight rows in one B tile; GEMM2: BN = 256), 8 waves = 2 per SIMD in a 4 x 2
+// grid, each wave owning 64 rows x 4 B fragments of 32 columns (8 accumulators of
+// 32x32, held in AGPRs).  K advances in tiles of 64 through two LDS stages of
+// 2 x 32 KB, filled by gfx950's direct global->LDS loads (8 per wave per tile,
+// one full 128-byte line per row segment).
+//
+// The steady-state K tile is one asm block with a fixed instruction order; the
+// compiler, left to itself, reuses operand registers and serialises LDS reads
+// with the MFMAs that consume them.  Per substep of K 16 the wave waits for its
+// operands, then alternates one MFMA with one LDS read of the next substep's
+// operands.  Before the last substep it waits for its own loads of the next tile
+// and meets the other waves at a barrier (after which the stage just consumed is
+// free), then alternates the last MFMAs with the refill loads of tile kt + 2 and
+// the reads of the next tile's first operands.  Every LDS read the block issues
+// is waited for inside the block.
+//
+// The MFMAs take the weight fragment as their first operand (C^T = B^T A^T), so a
+// lane's accumulator holds one output row and, per group of 4 registers, 4
+// consecutive output columns: the epilogue stores 8 (bf16) or 16 (fp32) bytes
+// per lane and group.  Each output element is still the same fp32 sum over k in
+// the same order.
+
+#define MOE_MF(c, a, b) "v_mfma_f32_32x32x16_bf16 %[" #c "], %[" #b "], %[" #a "], %[" #c "]\n\t"
+#define MOE_DSR(dst, addr, off) "ds_read_b128 %[" #dst "], %[" #addr "] offset:" off "\n\t"
+#define MOE_DSRI(dst, addr, off) "ds_read_b128 %[" #dst "], %[" #addr "] offset:%[" #off "]\n\t"
+#define MOE_DMA(vo, sb, lds, imm) \
+    "s_add_u32 m0, %[" #lds "], " imm "\n\tglobal_load_lds_dwordx4 %[" #vo "], %[" #sb "]\n\t"
+// One substep: multiply operand set P (A fragments a0 a1, B fragments b0..b3) while
+// reading the next substep into Q (in the order a0 b0 a1 b1 b2 b3).
+#define MOE_SUBSTEP(P, Q, RA, RB)                                 \
+    "s_waitcnt lgkmcnt(0)\n\t"                                    \
+    MOE_MF(c0, P##a0, P##b0) MOE_DSR(Q##a0, RA, "0")              \
+    MOE_MF(c1, P##a1, P##b0) MOE_DSR(Q##b0, RB, "0")              \
+    MOE_MF(c2, P##a0, P##b1) MOE_DSR(Q##a1, RA, "4096")           \
+    MOE_MF(c3, P##a1, P##b1) MOE_DSRI(Q##b1, RB, ob1)             \
+    MOE_MF(c4, P##a0, P##b2) MOE_DSRI(Q##b2, RB, ob2)             \
+    MOE_MF(c5, P##a1, P##b2) MOE_DSRI(Q##b3, RB, ob3)             \
+    MOE_MF(c6, P##a0, P##b3)                                      \
+    MOE_MF(c7, P##a1, P##b3)
+#define MOE_LASTSUB                                                                      \
+    "s_waitcnt lgkmcnt(0)\n\t"                                                           \
+    "s_waitcnt vmcnt(0)\n\t"                                                             \
+    "s_barrier\n\t"                                                                      \
+    MOE_MF(c0, ya0, yb0) MOE_DMA(vo0, sa, ldsA, "0")                                     \
+    MOE_MF(c1, ya1, yb0) MOE_DMA(vo1, sa, ldsA, "8192") MOE_DSR(xa0, na0, "0")           \
+    MOE_MF(c2, ya0, yb1) MOE_DMA(vo2, sa, ldsA, "16384") MOE_DSR(xb0, nb0, "0")          \
+    MOE_MF(c3, ya1, yb1) MOE_DMA(vo3, sa, ldsA, "24576") MOE_DSR(xa1, na0, "4096")       \
+    MOE_MF(c4, ya0, yb2) MOE_DMA(vo4, sb0, ldsB, "0") MOE_DSRI(xb1, nb0, ob1)            \
+    MOE_MF(c5, ya1, yb2) MOE_DMA(vo5, sb1, ldsB, "8192") MOE_DSRI(xb2, nb0, ob2)         \
+    MOE_MF(c6, ya0, yb3) MOE_DMA(vo6, sb2, ldsB, "16384") MOE_DSRI(xb3, nb0, ob3)        \
+    MOE_MF(c7, ya1, yb3) MOE_DMA(vo7, sb3, ldsB, "24576")                                \
+    "s_waitcnt lgkmcnt(0)\n\t"
+
+// One steady-state K tile.  x: operands of substep 0 of this tile on entry, of
+// the next tile on exit.  ra*/rb*: LDS byte addresses of the A / B fragment 0 of
+// substeps 1..3 of this tile; na0/nb0: of substep 0 of the next tile.  OB1..3:
+// byte offsets of B fragments 1..3.  vo: per-lane byte offsets of the 8 refill
+// loads from the SGPR bases sa (A) and sb0..3 (B) of tile kt + 2; ldsA/ldsB:
+// this wave's LDS destination of load 0 in the stage being refilled (load i lands
+// 8 KB further on).
+template <int OB1, int OB2, int OB3>
+__device__ __forceinline__ void gemm_tile_asm(floatx16_t (&c)[8], bf16x8_t (&x)[6], uint32_t ra1, uint32_t rb1,
+                                              uint32_t ra2, uint32_t rb2, uint32_t ra3, uint32_t rb3,
+                                              uint32_t na0, uint32_t nb0, const uint32_t (&vo)[8], const void* sa,
+                                              const void* sb0, const void* sb1, const void* sb2, const void* sb3,
+                                              uint32_t ldsA, uint32_t ldsB) {
+    bf16x8_t y[6];
+    uint32_t saved_m0;
+    asm volatile("s_mov_b32 %[sv], m0\n\t"
+                 MOE_SUBSTEP(x, y, ra1, rb1)
+                 MOE_SUBSTEP(y, x, ra2, rb2)
+                 MOE_SUBSTEP(x, y, ra3, rb3)
+                 MOE_LASTSUB
+                 "s_mov_b32 m0, %[sv]"
+                 : [c0] "+a"(c[0]), [c1] "+a"(c[1]), [c2] "+a"(c[2]), [c3] "+a"(c[3]), [c4] "+a"(c[4]),
+                   [c5] "+a"(c[5]), [c6] "+a"(c[6]), [c7] "+a"(c[7]), [xa0] "+v"(x[0]), [xa1] "+v"(x[1]),
+                   [xb0] "+v"(x[2]), [xb1] "+v"(x[3]), [xb2] "+v"(x[4]), [xb3] "+v"(x[5]), [ya0] "=&v"(y[0]),
+                   [ya1] "=&v"(y[1]), [yb0] "=&v"(y[2]), [yb1] "=&v"(y[3]), [yb2] "=&v"(y[4]), [yb3] "=&v"(y[5]),
+                   [sv] "=&s"(saved_m0)
+                 : [ra1] "v"(ra1), [rb1] "v"(rb1), [ra2] "v"(ra2), [rb2] "v"(rb2), [ra3] "v"(ra3), [rb3] "v"(rb3),
+                   [na0] "v"(na0), [nb0] "v"(nb0), [ob1] "i"(OB1), [ob2] "i"(OB2), [ob3] "i"(OB3),
+                   [vo0] "v"(vo[0]), [vo1] "v"(vo[1]), [vo2] "v"(vo[2]), [vo3] "v"(vo[3]), [vo4] "v"(vo[4]),
+                   [vo5] "v"(vo[5]), [vo6] "v"(vo[6]), [vo7] "v"(vo[7]), [sa] "s"(sa), [sb0] "s"(sb0),
+                   [sb1] "s"(sb1), [sb2] "s"(sb2), [sb3] "s"(sb3), [ldsA] "s"(ldsA), [ldsB] "s"(ldsB)
+                 : "memory");
+}
+
+// Requires K % 64 == 0, N % 8 == 0 and 512 K < 2^32 (32-bit load offsets).
+template <int BN, bool SWIGLU>
+__global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* __restrict__ A,
+                                                               const uint16_t* __restrict__ B0,
+                                                               const uint16_t* __restrict__ B1,
+                                                               void* __restrict__ Cout,
+                                                               const int32_t* __restrict__ offsets,
+                                                               const int32_t* __restrict__ tprefix, int G,
+                                                               int64_t nrows, int N, int K) {
+    constexpr int BM = 256, BK = 64, WGN = 2, WAVES = 8;
+    constexpr int NOPS = SWIGLU ? 2 : 1;
+    constexpr int WM = 64, WN = BN / WGN;       // wave tile: 64 rows x WN columns of each operand
+    constexpr int NTW = WN / 32;                // B fragments per operand per wave
+    static_assert(NOPS * NTW == 4, "4 B fragments per wave");
+    constexpr int STAGE = BM * BK * 2;          // bytes of one operand stage (256 rows x 64 bf16)
+    // B fragment f = (operand o, j) starts at B tile row o * BN + j * 32 (plus the wave's offset)
+    constexpr int OB1 = 32 * 128;
+    constexpr int OB2 = (NOPS == 2 ? BN : 64) * 128;
+    constexpr int OB3 = (NOPS == 2 ? BN + 32 : 96) * 128;
+    constexpr int OBF[4] = {0, OB1, OB2, OB3};
+
+    __shared__ uint4 sA[2 * STAGE / 16];
+    __shared__ uint4 sB[2 * STAGE / 16];
 
     TileCoord tc;
     const int NT = (N + BN - 1) / BN;
     if (!tile_coords(blockIdx.x, offsets, tprefix, G, nrows, BM, NT, tc)) return;
 
-    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+    const int tid = threadIdx.x, lane = tid % 64;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
     const int wm = wave / WGN, wn = wave % WGN;
     const int n0 = tc.nt * BN;
     const int64_t wstride = (int64_t)N * K;
-    const uint16_t* Bg = B0 + (int64_t)tc.g * wstride;
-    const uint16_t* Bu = SWIGLU ? B1 + (int64_t)tc.g * wstride : Bg;
+    const uint16_t* Bg = B0 + (int64_t)tc.g * wstride + (int64_t)n0 * K;
+    const uint16_t* Bu = SWIGLU ? B1 + (int64_t)tc.g * wstride + (int64_t)n0 * K : Bg;
+    const uint16_t* At = A + tc.row_start * K;
 
-    auto swz = [](int r) { return CPR == 4 ? lds_swz4(r) : lds_swz(r); };
-    // DMA plan: instruction i of wave w fills chunks [(WAVES i + w) * 64, +64) =
-    // RPI tile rows; this lane fills row (WAVES i + w) * RPI + lane / CPR at
-    // physical chunk lane % CPR, i.e. logical chunk (lane % CPR) ^ swz(row).
-    const uint16_t* a_src[A_LD];
-    const uint16_t* b_src[B_LD];
+    // Load plan: load i of wave w fills tile rows (8 i + w) * 8 + lane / 8 at
+    // physical chunk lane % 8, i.e. logical chunk (lane % 8) ^ swz(row).  A rows
+    // past the group end and weight rows past N read tile row 0 instead (their
+    // outputs are never stored).  Offsets are bytes from At / the weight base.
+    uint32_t vo[8];
+    const uint16_t* bbase[4];
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-        const int row = (WAVES * i + wave) * RPI + lane / CPR;
-        int64_t gr = tc.row_start + row;
-        if (gr >= tc.row_end) gr = tc.row_start;
-        a_src[i] = A + gr * K + ((lane % CPR) ^ swz(row)) * 8;
+    for (int i = 0; i < 4; ++i) {
+        const int row = (WAVES * i + wave) * 8 + lane / 8;
+        const int ch = (lane % 8) ^ lds_swz(row);
+        const int r = tc.row_start + row < tc.row_end ? row : 0;
+        vo[i] = (uint32_t)(((int64_t)r * K + ch * 8) * 2);
     }
 #pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-        const int row = (WAVES * i + wave) * RPI + lane / CPR;
-        const int op = row / BN;
-        int n = n0 + row % BN;
-        if (n >= N) n = n0;
-        b_src[i] = (op ? Bu : Bg) + (int64_t)n * K + ((lane % CPR) ^ swz(row)) * 8;
+    for (int i = 0; i < 4; ++i) {
+        const int row = (WAVES * i + wave) * 8 + lane / 8;   // B tile row
+        const int op = row / BN, rr = row % BN;
+        const int ch = (lane % 8) ^ lds_swz(row);
+        const int r = n0 + rr < N ? rr : 0;
+        vo[4 + i] = (uint32_t)(((int64_t)r * K + ch * 8) * 2);
+        bbase[i] = op ? Bu : Bg;
     }
     const uint32_t sA_addr = lds_byte_addr(sA), sB_addr = lds_byte_addr(sB);
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    auto issue = [&](int kt, int stage) {
-        const int k0 = kt * BK;
+    auto load_tile = [&](int kt, int stage) {
+        const uint32_t la = sA_addr + stage * STAGE + wave * 1024, lb = sB_addr + stage * STAGE + wave * 1024;
 #pragma unroll
-        for (int i = 0; i < A_LD; ++i)
-            dma16_async(a_src[i] + k0, sA_addr + (uint32_t)((stage * A_CH + (WAVES * i + wave_u) * 64) * 16));
+        for (int i = 0; i < 4; ++i) dma16_async(At + (int64_t)kt * BK + vo[i] / 2, la + i * 8192);
 #pragma unroll
-        for (int i = 0; i < B_LD; ++i)
-            dma16_async(b_src[i] + k0, sB_addr + (uint32_t)((stage * B_CH + (WAVES * i + wave_u) * 64) * 16));
+        for (int i = 0; i < 4; ++i) dma16_async(bbase[i] + (int64_t)kt * BK + vo[4 + i] / 2, lb + i * 8192);
     };
 
-    floatx16_t acc[NOPS][MT][NTW];
+    floatx16_t c[8];
 #pragma unroll
-    for (int o = 0; o < NOPS; ++o)
+    for (int q = 0; q < 8; ++q)
 #pragma unroll
-        for (int i = 0; i < MT; ++i)
-#pragma unroll
-            for (int j = 0; j < NTW; ++j)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc[o][i][j][v] = 0.f;
+        for (int v = 0; v < 16; ++v) c[q][v] = 0.f;
 
     const int KT = K / BK;
-    for (int t = 0; t < STAGES && t < KT; ++t) issue(t, t);
+    load_tile(0, 0);
+    if (KT > 1) load_tile(1, 1);
 
     const int lrow = lane % 32, lhalf = lane / 32;
-    const int rswz = swz(lrow);    // operand rows are lrow + multiples of 32
-    auto read_ops = [&](int stage, int s, bf16x8_t (&a)[MT], bf16x8_t (&b)[NOPS][NTW]) {
-        const uint4* As = sA + stage * A_CH;
-        const uint4* Bs = sB + stage * B_CH;
+    const int rswz = lds_swz(lrow);
+    // LDS byte address of fragment 0 of substep s in stage 0 (32 rows per fragment: A
+    // fragment 1 is 4096 bytes on, B fragments at OBF)
+    uint32_t ra[4], rb[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
         const int cc = (2 * s + lhalf) ^ rswz;
+        ra[s] = sA_addr + ((wm * WM + lrow) * 8 + cc) * 16;
+        rb[s] = sB_addr + ((wn * WN + lrow) * 8 + cc) * 16;
+    }
+    auto read_sub = [&](int stage, int s, bf16x8_t (&o)[6]) {
+        const char* pa = reinterpret_cast<const char*>(sA) + (ra[s] - sA_addr) + stage * STAGE;
+        const char* pb = reinterpret_cast<const char*>(sB) + (rb[s] - sB_addr) + stage * STAGE;
+        o[0] = as_bf16x8(*reinterpret_cast<const uint4*>(pa));
+        o[1] = as_bf16x8(*reinterpret_cast<const uint4*>(pa + 4096));
 #pragma unroll
-        for (int i = 0; i < MT; ++i) a[i] = as_bf16x8(As[(wm * WM + i * 32 + lrow) * CPR + cc]);
-#pragma unroll
-        for (int o = 0; o < NOPS; ++o)
-#pragma unroll
-            for (int j = 0; j < NTW; ++j) b[o][j] = as_bf16x8(Bs[(o * BN + wn * WN + j * 32 + lrow) * CPR + cc]);
+        for (int f = 0; f < 4; ++f) o[2 + f] = as_bf16x8(*reinterpret_cast<const uint4*>(pb + OBF[f]));
     };
-    auto mma = [&](const bf16x8_t (&a)[MT], const bf16x8_t (&b)[NOPS][NTW]) {
+    // accumulator q = (A fragment q % 2, B fragment q / 2); weight fragment first (C^T)
+    auto mma = [&](const bf16x8_t (&o)[6]) {
 #pragma unroll
-        for (int o = 0; o < NOPS; ++o)
-#pragma unroll
-            for (int j = 0; j < NTW; ++j)
-#pragma unroll
-                for (int i = 0; i < MT; ++i)
-                    acc[o][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[o][j], acc[o][i][j], 0, 0, 0);
+        for (int q = 0; q < 8; ++q)
+            c[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o[2 + q / 2], o[q % 2], c[q], 0, 0, 0);
     };
 
-    wait_tiles<LOADS>(min(STAGES - 1, KT - 1));
+    wait_tiles<8>(KT > 1 ? 1 : 0);
     lds_barrier_reads_done();
-    bf16x8_t xa[MT], xb[NOPS][NTW], ya[MT], yb[NOPS][NTW];
-    read_ops(0, 0, xa, xb);
-    for (int kt = 0; kt < KT; ++kt) {
-        const int stage = kt % STAGES;
-        // substeps 0 .. SUB-2: multiply x while reading the next substep into y, then swap
-#pragma unroll
-        for (int s = 0; s + 1 < SUB; ++s) {
-            if (s % 2 == 0) {
-                read_ops(stage, s + 1, ya, yb);
-                mma(xa, xb);
-            } else {
-                read_ops(stage, s + 1, xa, xb);
-                mma(ya, yb);
-            }
-        }
-        // last substep: every wave has now read all of tile kt -> barrier, refill its
-        // stage, and read the next tile's first substep while multiplying
-        auto& la = (SUB % 2 == 0) ? ya : xa;
-        auto& lb = (SUB % 2 == 0) ? yb : xb;
-        auto& na = (SUB % 2 == 0) ? xa : ya;
-        auto& nb = (SUB % 2 == 0) ? xb : yb;
+    bf16x8_t x[6];
+    read_sub(0, 0, x);
+    int kt = 0;
+    for (; kt + 2 < KT; ++kt) {
+        const uint32_t so = (kt & 1) * STAGE, no = STAGE - so;
+        const int64_t koff = (int64_t)(kt + 2) * BK;
+        gemm_tile_asm<OB1, OB2, OB3>(c, x, ra[1] + so, rb[1] + so, ra[2] + so, rb[2] + so, ra[3] + so, rb[3] + so,
+                                     ra[0] + no, rb[0] + no, vo, At + koff, bbase[0] + koff, bbase[1] + koff,
+                                     bbase[2] + koff, bbase[3] + koff, sA_addr + so + wave * 1024,
+                                     sB_addr + so + wave * 1024);
+    }
+    // the last (up to) two tiles: nothing left to load
+    for (; kt < KT; ++kt) {
+        const int stage = kt & 1;
+        bf16x8_t y[6];
+        read_sub(stage, 1, y);
+        mma(x);
+        read_sub(stage, 2, x);
+        mma(y);
+        read_sub(stage, 3, y);
+        mma(x);
         if (kt + 1 < KT) {
-            wait_tiles<LOADS>(min(STAGES - 2, KT - 2 - kt));
+            wait_tiles<8>(0);
             lds_barrier_reads_done();
-            if (kt + STAGES < KT) issue(kt + STAGES, stage);
-            read_ops((kt + 1) % STAGES, 0, na, nb);
+            read_sub(stage ^ 1, 0, x);
         }
-        mma(la, lb);
-        if (SUB % 2 == 1) {   // keep "x = operands of substep 0" for the next tile
-#pragma unroll
-            for (int i = 0; i < MT; ++i) xa[i] = ya[i];
-#pragma unroll
-            for (int o = 0; o < NOPS; ++o)
-#pragma unroll
-                for (int j = 0; j < NTW; ++j) xb[o][j] = yb[o][j];
-        }
+        mma(y);
     }
 
+    // Epilogue: the lane holds output row (.. + lrow) of accumulator q and, in
+    // register group g, columns 8 g + 4 lhalf + 0..3 of its 32-column fragment.
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
+    for (int q = 0; q < 8; ++q) {
+        const int i = q % 2, f = q / 2;
+        const int o = NOPS == 2 ? f / NTW : 0, j = NOPS == 2 ? f % NTW : f;
+        if (SWIGLU && o == 1) continue;
+        const int64_t row = tc.row_start + wm * WM + i * 32 + lrow;
+        if (row >= tc.row_end) continue;
 #pragma unroll
-        for (int j = 0; j < NTW; ++j) {
-            const int col = n0 + wn * WN + j * 32 + lrow;
+        for (int g = 0; g < 4; ++g) {
+            const int col = n0 + wn * WN + j * 32 + 8 * g + 4 * lhalf;
+            if (col >= N) continue;   // N % 8 == 0: a group of 4 is wholly in or out
+            if (SWIGLU) {
+                uint32_t p[2];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int64_t row = tc.row_start + wm * WM + i * 32 + 8 * (v / 4) + 4 * lhalf + (v % 4);
-                if (row < tc.row_end && col < N) {
-                    if (SWIGLU) {
-                        const float hval = silu_f32(acc[0][i][j][v]) * acc[NOPS - 1][i][j][v];
-                        static_cast<uint16_t*>(Cout)[row * N + col] = (uint16_t)f32_to_bf16_bits(hval);
-                    } else {
-                        static_cast<float*>(Cout)[row * N + col] = acc[0][i][j][v];
-                    }
+                for (int e = 0; e < 2; ++e) {
+                    const int v = 4 * g + 2 * e;
+                    const float h0 = silu_f32(c[q][v]) * c[q + 2 * NTW][v];
+                    const float h1 = silu_f32(c[q][v + 1]) * c[q + 2 * NTW][v + 1];
+                    p[e] = f32_to_bf16_bits(h0) | (f32_to_bf16_bits(h1) << 16);
                 }
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(Cout) + row * N + col) = make_uint2(p[0], p[1]);
+            } else {
+                *reinterpret_cast<float4*>(static_cast<float*>(Cout) + row * N + col) =
+                    make_float4(c[q][4 * g], c[q][4 * g + 1], c[q][4 * g + 2], c[q][4 * g + 3]);
             }
         }
     }
@@ -560,16 +633,9 @@ constexpr int BF16_BN1 = 128;   // GEMM1 output columns per tile (256 weight row
 constexpr int BF16_BN2 = 256;   // GEMM2 output columns per tile
 constexpr int F32_BM = 64, F32_BN = 64;
 
-template <int BM, int BN, bool SWIGLU>
-void launch_ring(unsigned grid, hipStream_t st, const uint16_t* A, const uint16_t* B0, const uint16_t* B1, void* C,
-                 const int32_t* offsets, const int32_t* tp, int G, int64_t nrows, int N, int K) {
-    if (K % 64 == 0)
-        hipLaunchKernelGGL((gemm_bf16_ring_kernel<BM, BN, SWIGLU, 4, 2, 64>), dim3(grid), dim3(512), 0, st, A, B0, B1,
-                           C, offsets, tp, G, nrows, N, K);
-    else
-        hipLaunchKernelGGL((gemm_bf16_ring_kernel<BM, BN, SWIGLU, 4, 2, 32>), dim3(grid), dim3(512), 0, st, A, B0, B1,
-                           C, offsets, tp, G, nrows, N, K);
-}
+// The scheduled kernel's conditions: whole K tiles of 64, 4-column output groups,
+// 32-bit load offsets within a 256-row tile.
+bool asm_path_ok(int N, int K) { return K % 64 == 0 && N % 8 == 0 && (int64_t)K * 512 < ((int64_t)1 << 32); }
 
 hipError_t prep_tiles(const int32_t* offsets, int G, int BM, void* ws, hipStream_t st) {
     if (!offsets) return hipSuccess;
@@ -598,8 +664,8 @@ hipError_t launch_gemm1(int dtype, const void* A, const int32_t* offsets, int G,
     const unsigned grid = grid_size(offsets, G, max_rows, BM, N, BN);
     if (grid == 0) return hipSuccess;
     const int32_t* tp = static_cast<const int32_t*>(ws);
-    if (dtype == MOE_BF16 && K % 32 == 0)
-        launch_ring<BF16_BM, BF16_BN1, true>(grid, st,
+    if (dtype == MOE_BF16 && asm_path_ok(N, K))
+        hipLaunchKernelGGL((gemm_bf16_asm_kernel<BF16_BN1, true>), dim3(grid), dim3(512), 0, st,
                            static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(w_gate),
                            static_cast<const uint16_t*>(w_up), h, offsets, tp, G, max_rows, N, K);
     else if (dtype == MOE_BF16)
@@ -622,8 +688,8 @@ hipError_t launch_gemm2(int dtype, const void* h, const int32_t* offsets, int G,
     const unsigned grid = grid_size(offsets, G, max_rows, BM, N, BN);
     if (grid == 0) return hipSuccess;
     const int32_t* tp = static_cast<const int32_t*>(ws);
-    if (dtype == MOE_BF16 && K % 32 == 0)
-        launch_ring<BF16_BM, BF16_BN2, false>(grid, st,
+    if (dtype == MOE_BF16 && asm_path_ok(N, K))
+        hipLaunchKernelGGL((gemm_bf16_asm_kernel<BF16_BN2, false>), dim3(grid), dim3(512), 0, st,
                            static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w_down), nullptr, H,
                            offsets, tp, G, max_rows, N, K);
     else if (dtype == MOE_BF16)

@@ -184,6 +184,10 @@ RAGGED = MoEConfig("ragged_bf16", T=2000, d=328, m=200, E=4, k=2, dtype="bf16", 
               cfg_id=17),
     MoEConfig("many_experts", T=333, d=64, m=64, E=200, k=7, dtype="bf16", gate_mode=0, cf=None, cfg_id=18),
     MoEConfig("max_experts", T=70, d=64, m=32, E=1024, k=32, dtype="bf16", gate_mode=0, cf=None, cfg_id=19),
+    # K multiples of 64 (5 and 7 K tiles): the scheduled bf16 kernel's steady state, with
+    # ragged groups, drops, partial column tiles in both GEMMs and a shared expert
+    MoEConfig("kernel_steady_state", T=1500, d=320, m=448, E=6, k=2, dtype="bf16", gate_mode=0, cf=(5, 4),
+              bias="zipf", m_shared=192, cfg_id=23),
 ], ids=lambda c: c.name)
 def test_parity_small(cfg):
     run_layer(cfg)
