@@ -13,8 +13,11 @@
 
 namespace {
 
+// H1 (nullable): the second K-split partial of H; the row used is H + H1 (one
+// fp32 add, the same value a caller that folded H1 into H first would read).
 template <bool VEC4>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ H, const int32_t* __restrict__ row_of,
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ H, const float* __restrict__ H1,
+                                                      const int32_t* __restrict__ row_of,
                                                       const float* __restrict__ w, const float* __restrict__ shared_out,
                                                       float* __restrict__ y, int64_t T, int d, int k) {
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
@@ -36,7 +39,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                 const int row = lane_value(myrow, r);
                 const float a = lane_value(myw, r);
                 if (row >= 0 && ok) {
-                    const float4 h = H4[(int64_t)row * nv + c];
+                    float4 h = H4[(int64_t)row * nv + c];
+                    if (H1) {
+                        const float4 h1 = reinterpret_cast<const float4*>(H1)[(int64_t)row * nv + c];
+                        h.x += h1.x;
+                        h.y += h1.y;
+                        h.z += h1.z;
+                        h.w += h1.w;
+                    }
                     acc.x = fmaf(a, h.x, acc.x);
                     acc.y = fmaf(a, h.y, acc.y);
                     acc.z = fmaf(a, h.z, acc.z);
@@ -53,7 +63,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
             for (int r = 0; r < k; ++r) {
                 const int row = lane_value(myrow, r);
                 const float a = lane_value(myw, r);
-                if (row >= 0 && ok) acc = fmaf(a, H[(int64_t)row * d + c], acc);
+                if (row >= 0 && ok) {
+                    float h = H[(int64_t)row * d + c];
+                    if (H1) h += H1[(int64_t)row * d + c];
+                    acc = fmaf(a, h, acc);
+                }
             }
             if (ok) y[t * d + c] = acc;
         }
@@ -64,15 +78,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 namespace moe_kernels {
 
-hipError_t launch_combine(const moe_dims& s, const float* H, const int32_t* row_of, const float* topk_w,
+hipError_t launch_combine(const moe_dims& s, const float* H, const float* H1, const int32_t* row_of, const float* topk_w,
                           const float* shared_out, float* y, hipStream_t st) {
     if (s.T == 0) return hipSuccess;
     const unsigned grid = (unsigned)((s.T + 3) / 4);
     if (s.d % 4 == 0)
-        hipLaunchKernelGGL(combine_kernel<true>, dim3(grid), dim3(256), 0, st, H, row_of, topk_w, shared_out, y, s.T,
+        hipLaunchKernelGGL(combine_kernel<true>, dim3(grid), dim3(256), 0, st, H, H1, row_of, topk_w, shared_out, y, s.T,
                            s.d, s.k);
     else
-        hipLaunchKernelGGL(combine_kernel<false>, dim3(grid), dim3(256), 0, st, H, row_of, topk_w, shared_out, y, s.T,
+        hipLaunchKernelGGL(combine_kernel<false>, dim3(grid), dim3(256), 0, st, H, H1, row_of, topk_w, shared_out, y, s.T,
                            s.d, s.k);
     return hipGetLastError();
 }

@@ -95,11 +95,18 @@ size_t gemm_ws_bytes(int G);
 hipError_t launch_gemm1(int dtype, const void* A, const int32_t* offsets, int G, int64_t max_rows,
                         const void* w_gate, const void* w_up, void* h, int N, int K,
                         void* ws, hipStream_t st);
+// GEMM2 may split K in two (gemm2_splits == 2, decided from the shape alone):
+// then H receives the partial sum over the first half of K and H1 the second;
+// with H1 == nullptr it never splits.
+int gemm2_splits(int dtype, int64_t max_rows, int G, int N, int K);
 hipError_t launch_gemm2(int dtype, const void* h, const int32_t* offsets, int G, int64_t max_rows,
-                        const void* w_down, float* H, int N, int K, void* ws, hipStream_t st);
+                        const void* w_down, float* H, float* H1, int N, int K, void* ws, hipStream_t st);
+// H += H1 over the rows [0, offsets[G]) (or [0, max_rows) without offsets); N % 4 == 0.
+hipError_t launch_add_partial(float* H, const float* H1, const int32_t* offsets, int G, int64_t max_rows, int N,
+                              hipStream_t st);
 
-// Combine.
-hipError_t launch_combine(const moe_dims& s, const float* H, const int32_t* row_of,
+// Combine.  H1 (nullable): second K-split partial of H, added to H row by row.
+hipError_t launch_combine(const moe_dims& s, const float* H, const float* H1, const int32_t* row_of,
                           const float* topk_w, const float* shared_out, float* y, hipStream_t st);
 
 }  // namespace moe_kernels

@@ -25,6 +25,7 @@
 //     n tile): the workgroups an XCD runs together share A row tiles and expert
 //     weight tiles in its own L2.
 // fp32 path: a plain LDS-tiled fp32 FMA kernel (64 x 64 tiles, 4 x 4 per thread).
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -32,6 +33,9 @@
 namespace {
 
 constexpr int XCDS = 8;
+// CUs the GEMM2 K-split rule plans for (MI355X; a fixed figure, so that workspace
+// sizes depend on the shape alone)
+constexpr int MOE_GEMM_CUS = 256;
 constexpr int NSUPER = 4;
 
 struct TileCoord {
@@ -405,15 +409,91 @@ __device__ __forceinline__ void gemm_tile_asm(floatx16_t (&c)[8], bf16x8_t (&x)[
                  : "memory");
 }
 
-// Requires K % 64 == 0, N % 8 == 0 and 512 K < 2^32 (32-bit load offsets).
+// Waves whose 64 rows hold at most 32 valid ones run only the MFMAs of A fragment 0
+// (and read no A fragment 1); waves with no valid row run no MFMA and read
+// nothing.  Both still issue their share of the refill loads and meet the same
+// barrier, so the workgroup's load plan and synchronisation are unchanged.
+#define MOE_SUBSTEP_HALF(P, Q, RA, RB)                            \
+    "s_waitcnt lgkmcnt(0)\n\t"                                    \
+    MOE_MF(c0, P##a0, P##b0) MOE_DSR(Q##a0, RA, "0")              \
+    MOE_MF(c2, P##a0, P##b1) MOE_DSR(Q##b0, RB, "0")              \
+    MOE_MF(c4, P##a0, P##b2) MOE_DSRI(Q##b1, RB, ob1)             \
+    MOE_MF(c6, P##a0, P##b3) MOE_DSRI(Q##b2, RB, ob2)             \
+    MOE_DSRI(Q##b3, RB, ob3)
+#define MOE_LASTSUB_HALF                                                                 \
+    "s_waitcnt lgkmcnt(0)\n\t"                                                           \
+    "s_waitcnt vmcnt(0)\n\t"                                                             \
+    "s_barrier\n\t"                                                                      \
+    MOE_MF(c0, ya0, yb0) MOE_DMA(vo0, sa, ldsA, "0") MOE_DMA(vo1, sa, ldsA, "8192")      \
+    MOE_DSR(xa0, na0, "0")                                                               \
+    MOE_MF(c2, ya0, yb1) MOE_DMA(vo2, sa, ldsA, "16384") MOE_DMA(vo3, sa, ldsA, "24576") \
+    MOE_DSR(xb0, nb0, "0") MOE_DSRI(xb1, nb0, ob1)                                       \
+    MOE_MF(c4, ya0, yb2) MOE_DMA(vo4, sb0, ldsB, "0") MOE_DMA(vo5, sb1, ldsB, "8192")    \
+    MOE_DSRI(xb2, nb0, ob2) MOE_DSRI(xb3, nb0, ob3)                                      \
+    MOE_MF(c6, ya0, yb3) MOE_DMA(vo6, sb2, ldsB, "16384") MOE_DMA(vo7, sb3, ldsB, "24576") \
+    "s_waitcnt lgkmcnt(0)\n\t"
+
+template <int OB1, int OB2, int OB3>
+__device__ __forceinline__ void gemm_tile_asm_half(floatx16_t (&c)[8], bf16x8_t (&x)[6], uint32_t ra1, uint32_t rb1,
+                                                   uint32_t ra2, uint32_t rb2, uint32_t ra3, uint32_t rb3,
+                                                   uint32_t na0, uint32_t nb0, const uint32_t (&vo)[8],
+                                                   const void* sa, const void* sb0, const void* sb1,
+                                                   const void* sb2, const void* sb3, uint32_t ldsA, uint32_t ldsB) {
+    bf16x8_t y[6];
+    uint32_t saved_m0;
+    asm volatile("s_mov_b32 %[sv], m0\n\t"
+                 MOE_SUBSTEP_HALF(x, y, ra1, rb1)
+                 MOE_SUBSTEP_HALF(y, x, ra2, rb2)
+                 MOE_SUBSTEP_HALF(x, y, ra3, rb3)
+                 MOE_LASTSUB_HALF
+                 "s_mov_b32 m0, %[sv]"
+                 : [c0] "+a"(c[0]), [c1] "+a"(c[1]), [c2] "+a"(c[2]), [c3] "+a"(c[3]), [c4] "+a"(c[4]),
+                   [c5] "+a"(c[5]), [c6] "+a"(c[6]), [c7] "+a"(c[7]), [xa0] "+v"(x[0]), [xa1] "+v"(x[1]),
+                   [xb0] "+v"(x[2]), [xb1] "+v"(x[3]), [xb2] "+v"(x[4]), [xb3] "+v"(x[5]), [ya0] "=&v"(y[0]),
+                   [ya1] "=&v"(y[1]), [yb0] "=&v"(y[2]), [yb1] "=&v"(y[3]), [yb2] "=&v"(y[4]), [yb3] "=&v"(y[5]),
+                   [sv] "=&s"(saved_m0)
+                 : [ra1] "v"(ra1), [rb1] "v"(rb1), [ra2] "v"(ra2), [rb2] "v"(rb2), [ra3] "v"(ra3), [rb3] "v"(rb3),
+                   [na0] "v"(na0), [nb0] "v"(nb0), [ob1] "i"(OB1), [ob2] "i"(OB2), [ob3] "i"(OB3),
+                   [vo0] "v"(vo[0]), [vo1] "v"(vo[1]), [vo2] "v"(vo[2]), [vo3] "v"(vo[3]), [vo4] "v"(vo[4]),
+                   [vo5] "v"(vo[5]), [vo6] "v"(vo[6]), [vo7] "v"(vo[7]), [sa] "s"(sa), [sb0] "s"(sb0),
+                   [sb1] "s"(sb1), [sb2] "s"(sb2), [sb3] "s"(sb3), [ldsA] "s"(ldsA), [ldsB] "s"(ldsB)
+                 : "memory");
+}
+
+__device__ __forceinline__ void gemm_tile_asm_loads_only(floatx16_t (&c)[8], bf16x8_t (&x)[6], const uint32_t (&vo)[8],
+                                                         const void* sa, const void* sb0, const void* sb1,
+                                                         const void* sb2, const void* sb3, uint32_t ldsA,
+                                                         uint32_t ldsB) {
+    uint32_t saved_m0;
+    asm volatile("s_mov_b32 %[sv], m0\n\t"
+                 "s_waitcnt vmcnt(0)\n\t"
+                 "s_barrier\n\t"
+                 MOE_DMA(vo0, sa, ldsA, "0") MOE_DMA(vo1, sa, ldsA, "8192") MOE_DMA(vo2, sa, ldsA, "16384")
+                 MOE_DMA(vo3, sa, ldsA, "24576") MOE_DMA(vo4, sb0, ldsB, "0") MOE_DMA(vo5, sb1, ldsB, "8192")
+                 MOE_DMA(vo6, sb2, ldsB, "16384") MOE_DMA(vo7, sb3, ldsB, "24576")
+                 "s_mov_b32 m0, %[sv]"
+                 : [c0] "+a"(c[0]), [c1] "+a"(c[1]), [c2] "+a"(c[2]), [c3] "+a"(c[3]), [c4] "+a"(c[4]),
+                   [c5] "+a"(c[5]), [c6] "+a"(c[6]), [c7] "+a"(c[7]), [xa0] "+v"(x[0]), [xa1] "+v"(x[1]),
+                   [xb0] "+v"(x[2]), [xb1] "+v"(x[3]), [xb2] "+v"(x[4]), [xb3] "+v"(x[5]), [sv] "=&s"(saved_m0)
+                 : [vo0] "v"(vo[0]), [vo1] "v"(vo[1]), [vo2] "v"(vo[2]), [vo3] "v"(vo[3]), [vo4] "v"(vo[4]),
+                   [vo5] "v"(vo[5]), [vo6] "v"(vo[6]), [vo7] "v"(vo[7]), [sa] "s"(sa), [sb0] "s"(sb0),
+                   [sb1] "s"(sb1), [sb2] "s"(sb2), [sb3] "s"(sb3), [ldsA] "s"(ldsA), [ldsB] "s"(ldsB)
+                 : "memory");
+}
+
+// Requires K % (64 * S) == 0, N % 8 == 0 and 512 K < 2^32 (32-bit load offsets).
+// K split: the grid is S copies of a tile grid of gridDim.x / S workgroups (a
+// multiple of 8, so every copy keeps the XCD order); copy s sums k in
+// [s K / S, (s + 1) K / S) and writes its fp32 partial to Cout (s = 0) or Cout1
+// (s = 1).  S is 1 or 2, and 1 for SwiGLU.
 template <int BN, bool SWIGLU>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* __restrict__ A,
                                                                const uint16_t* __restrict__ B0,
                                                                const uint16_t* __restrict__ B1,
-                                                               void* __restrict__ Cout,
+                                                               void* __restrict__ Cout, void* __restrict__ Cout1,
                                                                const int32_t* __restrict__ offsets,
                                                                const int32_t* __restrict__ tprefix, int G,
-                                                               int64_t nrows, int N, int K) {
+                                                               int64_t nrows, int N, int K, int S) {
     constexpr int BM = 256, BK = 64, WGN = 2, WAVES = 8;
     constexpr int NOPS = SWIGLU ? 2 : 1;
     constexpr int WM = 64, WN = BN / WGN;       // wave tile: 64 rows x WN columns of each operand
@@ -431,16 +511,21 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* _
 
     TileCoord tc;
     const int NT = (N + BN - 1) / BN;
-    if (!tile_coords(blockIdx.x, offsets, tprefix, G, nrows, BM, NT, tc)) return;
+    const int tiles_grid = gridDim.x / S;
+    const int split = blockIdx.x / tiles_grid;
+    if (!tile_coords(blockIdx.x - split * tiles_grid, offsets, tprefix, G, nrows, BM, NT, tc)) return;
+    const int Ks = K / S;                       // this split's K range starts at split * Ks
+    void* C = split ? Cout1 : Cout;
 
     const int tid = threadIdx.x, lane = tid % 64;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
     const int wm = wave / WGN, wn = wave % WGN;
     const int n0 = tc.nt * BN;
     const int64_t wstride = (int64_t)N * K;
-    const uint16_t* Bg = B0 + (int64_t)tc.g * wstride + (int64_t)n0 * K;
-    const uint16_t* Bu = SWIGLU ? B1 + (int64_t)tc.g * wstride + (int64_t)n0 * K : Bg;
-    const uint16_t* At = A + tc.row_start * K;
+    const int64_t k0 = (int64_t)split * Ks;
+    const uint16_t* Bg = B0 + (int64_t)tc.g * wstride + (int64_t)n0 * K + k0;
+    const uint16_t* Bu = SWIGLU ? B1 + (int64_t)tc.g * wstride + (int64_t)n0 * K + k0 : Bg;
+    const uint16_t* At = A + tc.row_start * K + k0;
 
     // Load plan: load i of wave w fills tile rows (8 i + w) * 8 + lane / 8 at
     // physical chunk lane % 8, i.e. logical chunk (lane % 8) ^ swz(row).  A rows
@@ -479,7 +564,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* _
 #pragma unroll
         for (int v = 0; v < 16; ++v) c[q][v] = 0.f;
 
-    const int KT = K / BK;
+    const int KT = Ks / BK;
     load_tile(0, 0);
     if (KT > 1) load_tile(1, 1);
 
@@ -502,6 +587,9 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* _
 #pragma unroll
         for (int f = 0; f < 4; ++f) o[2 + f] = as_bf16x8(*reinterpret_cast<const uint4*>(pb + OBF[f]));
     };
+    // valid rows of this wave's 64: > 32 -> all MFMAs, 1..32 -> A fragment 0 only, 0 -> none
+    const int64_t wave_rows = tc.row_end - (tc.row_start + wm * WM);
+    const int mode = wave_rows > 32 ? 2 : (wave_rows > 0 ? 1 : 0);
     // accumulator q = (A fragment q % 2, B fragment q / 2); weight fragment first (C^T)
     auto mma = [&](const bf16x8_t (&o)[6]) {
 #pragma unroll
@@ -513,15 +601,36 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* _
     lds_barrier_reads_done();
     bf16x8_t x[6];
     read_sub(0, 0, x);
+    // steady state: one loop per wave mode (the mode is uniform across the wave)
     int kt = 0;
-    for (; kt + 2 < KT; ++kt) {
-        const uint32_t so = (kt & 1) * STAGE, no = STAGE - so;
-        const int64_t koff = (int64_t)(kt + 2) * BK;
-        gemm_tile_asm<OB1, OB2, OB3>(c, x, ra[1] + so, rb[1] + so, ra[2] + so, rb[2] + so, ra[3] + so, rb[3] + so,
-                                     ra[0] + no, rb[0] + no, vo, At + koff, bbase[0] + koff, bbase[1] + koff,
-                                     bbase[2] + koff, bbase[3] + koff, sA_addr + so + wave * 1024,
-                                     sB_addr + so + wave * 1024);
+#define MOE_TILE_ARGS(kt_)                                                                               \
+    const uint32_t so = ((kt_) & 1) * STAGE, no = STAGE - so;                                            \
+    const int64_t koff = (int64_t)((kt_) + 2) * BK;
+    if (mode == 2) {
+        for (; kt + 2 < KT; ++kt) {
+            MOE_TILE_ARGS(kt)
+            gemm_tile_asm<OB1, OB2, OB3>(c, x, ra[1] + so, rb[1] + so, ra[2] + so, rb[2] + so, ra[3] + so,
+                                         rb[3] + so, ra[0] + no, rb[0] + no, vo, At + koff, bbase[0] + koff,
+                                         bbase[1] + koff, bbase[2] + koff, bbase[3] + koff,
+                                         sA_addr + so + wave * 1024, sB_addr + so + wave * 1024);
+        }
+    } else if (mode == 1) {
+        for (; kt + 2 < KT; ++kt) {
+            MOE_TILE_ARGS(kt)
+            gemm_tile_asm_half<OB1, OB2, OB3>(c, x, ra[1] + so, rb[1] + so, ra[2] + so, rb[2] + so, ra[3] + so,
+                                              rb[3] + so, ra[0] + no, rb[0] + no, vo, At + koff, bbase[0] + koff,
+                                              bbase[1] + koff, bbase[2] + koff, bbase[3] + koff,
+                                              sA_addr + so + wave * 1024, sB_addr + so + wave * 1024);
+        }
+    } else {
+        for (; kt + 2 < KT; ++kt) {
+            MOE_TILE_ARGS(kt)
+            (void)no;
+            gemm_tile_asm_loads_only(c, x, vo, At + koff, bbase[0] + koff, bbase[1] + koff, bbase[2] + koff,
+                                     bbase[3] + koff, sA_addr + so + wave * 1024, sB_addr + so + wave * 1024);
+        }
     }
+#undef MOE_TILE_ARGS
     // the last (up to) two tiles: nothing left to load
     for (; kt < KT; ++kt) {
         const int stage = kt & 1;
@@ -562,12 +671,30 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* _
                     const float h1 = silu_f32(c[q][v + 1]) * c[q + 2 * NTW][v + 1];
                     p[e] = f32_to_bf16_bits(h0) | (f32_to_bf16_bits(h1) << 16);
                 }
-                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(Cout) + row * N + col) = make_uint2(p[0], p[1]);
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(C) + row * N + col) = make_uint2(p[0], p[1]);
             } else {
-                *reinterpret_cast<float4*>(static_cast<float*>(Cout) + row * N + col) =
+                *reinterpret_cast<float4*>(static_cast<float*>(C) + row * N + col) =
                     make_float4(c[q][4 * g], c[q][4 * g + 1], c[q][4 * g + 2], c[q][4 * g + 3]);
             }
         }
+    }
+}
+
+// H[r] += H1[r] for the rows r < offsets[G] (or nrows without offsets): folds the
+// second K-split partial into the first where the caller wants H itself.
+__global__ __launch_bounds__(256) void add_partial_kernel(float* __restrict__ H, const float* __restrict__ H1,
+                                                          const int32_t* __restrict__ offsets, int G, int64_t nrows,
+                                                          int N) {
+    const int64_t rows = offsets ? offsets[G] : nrows;
+    const int64_t n4 = rows * (N / 4);
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+        float4 a = reinterpret_cast<float4*>(H)[i];
+        const float4 b = reinterpret_cast<const float4*>(H1)[i];
+        a.x += b.x;
+        a.y += b.y;
+        a.z += b.z;
+        a.w += b.w;
+        reinterpret_cast<float4*>(H)[i] = a;
     }
 }
 
@@ -667,7 +794,7 @@ hipError_t launch_gemm1(int dtype, const void* A, const int32_t* offsets, int G,
     if (dtype == MOE_BF16 && asm_path_ok(N, K))
         hipLaunchKernelGGL((gemm_bf16_asm_kernel<BF16_BN1, true>), dim3(grid), dim3(512), 0, st,
                            static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(w_gate),
-                           static_cast<const uint16_t*>(w_up), h, offsets, tp, G, max_rows, N, K);
+                           static_cast<const uint16_t*>(w_up), h, nullptr, offsets, tp, G, max_rows, N, K, 1);
     else if (dtype == MOE_BF16)
         hipLaunchKernelGGL((gemm_bf16_kernel<BF16_BM, BF16_BN1, true>), dim3(grid), dim3(256), 0, st,
                            static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(w_gate),
@@ -679,26 +806,50 @@ hipError_t launch_gemm1(int dtype, const void* A, const int32_t* offsets, int G,
     return hipGetLastError();
 }
 
+int gemm2_splits(int dtype, int64_t max_rows, int G, int N, int K) {
+    if (dtype != MOE_BF16 || !asm_path_ok(N, K) || K % 128 != 0 || K < 2048) return 1;
+    // expected row tiles: full tiles plus about half a partial tile per group
+    const int64_t mt = (max_rows + BF16_BM - 1) / BF16_BM + (G + 1) / 2;
+    const int64_t tiles = mt * ((N + BF16_BN2 - 1) / BF16_BN2);
+    auto fill = [](int64_t t) {   // fraction of the CU slots the workgroups' rounds use
+        const int64_t rounds = (t + MOE_GEMM_CUS - 1) / MOE_GEMM_CUS;
+        return rounds ? (double)t / (double)(rounds * MOE_GEMM_CUS) : 1.0;
+    };
+    return fill(2 * tiles) > 1.05 * fill(tiles) ? 2 : 1;
+}
+
 hipError_t launch_gemm2(int dtype, const void* h, const int32_t* offsets, int G, int64_t max_rows,
-                        const void* w_down, float* H, int N, int K, void* ws, hipStream_t st) {
+                        const void* w_down, float* H, float* H1, int N, int K, void* ws, hipStream_t st) {
     const int BM = dtype == MOE_BF16 ? BF16_BM : F32_BM;
     const int BN = dtype == MOE_BF16 ? BF16_BN2 : F32_BN;
     hipError_t e = prep_tiles(offsets, G, BM, ws, st);
     if (e != hipSuccess) return e;
-    const unsigned grid = grid_size(offsets, G, max_rows, BM, N, BN);
+    unsigned grid = grid_size(offsets, G, max_rows, BM, N, BN);
     if (grid == 0) return hipSuccess;
     const int32_t* tp = static_cast<const int32_t*>(ws);
-    if (dtype == MOE_BF16 && asm_path_ok(N, K))
+    const int S = H1 ? gemm2_splits(dtype, max_rows, G, N, K) : 1;
+    if (dtype == MOE_BF16 && asm_path_ok(N, K)) {
+        if (S > 1) grid = (grid + XCDS - 1) / XCDS * XCDS * S;
         hipLaunchKernelGGL((gemm_bf16_asm_kernel<BF16_BN2, false>), dim3(grid), dim3(512), 0, st,
-                           static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w_down), nullptr, H,
-                           offsets, tp, G, max_rows, N, K);
-    else if (dtype == MOE_BF16)
+                           static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w_down), nullptr, H, H1,
+                           offsets, tp, G, max_rows, N, K, S);
+    } else if (dtype == MOE_BF16) {
         hipLaunchKernelGGL((gemm_bf16_kernel<BF16_BM, BF16_BN2, false>), dim3(grid), dim3(256), 0, st,
                            static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w_down), nullptr, H,
                            offsets, tp, G, max_rows, N, K);
-    else
+    } else {
         hipLaunchKernelGGL((gemm_f32_kernel<false>), dim3(grid), dim3(256), 0, st, static_cast<const float*>(h),
                            static_cast<const float*>(w_down), nullptr, H, offsets, tp, G, max_rows, N, K);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_add_partial(float* H, const float* H1, const int32_t* offsets, int G, int64_t max_rows, int N,
+                              hipStream_t st) {
+    const int64_t n4 = max_rows * (N / 4);
+    if (n4 == 0) return hipSuccess;
+    const unsigned grid = (unsigned)std::min<int64_t>((n4 + 255) / 256, 8192);
+    hipLaunchKernelGGL(add_partial_kernel, dim3(grid), dim3(256), 0, st, H, H1, offsets, G, max_rows, N);
     return hipGetLastError();
 }
 

@@ -42,7 +42,17 @@ int64_t max_rows(const moe_dims& d) {
 
 size_t elem(const moe_dims& d) { return d.dtype == MOE_BF16 ? 2 : 4; }
 
-size_t ffn_ws(const moe_dims& d) { return align_up(gemm_ws_bytes(d.E)) + align_up((size_t)max_rows(d) * d.m * elem(d)); }
+// Bytes of the second K-split partial of H when GEMM2 splits K for this shape.
+size_t partial_bytes(const moe_dims& d) {
+    const int64_t R = max_rows(d);
+    return gemm2_splits(d.dtype, R, d.E, d.d, d.m) > 1 ? align_up(sizeof(float) * R * d.d) : 0;
+}
+// [tile prefix | h | H partial]
+size_t ffn_ws(const moe_dims& d) {
+    return align_up(gemm_ws_bytes(d.E)) + align_up((size_t)max_rows(d) * d.m * elem(d)) + partial_bytes(d);
+}
+// moe_expert_gemm2 alone: [tile prefix | H partial]
+size_t gemm2_ws(const moe_dims& d) { return align_up(gemm_ws_bytes(d.E)) + partial_bytes(d); }
 size_t shared_ws(const moe_dims& d) {
     return align_up(gemm_ws_bytes(1)) + align_up((size_t)d.T * d.m_shared * elem(d));
 }
@@ -93,14 +103,27 @@ inline moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : M
         if (e_ != hipSuccess) return MOE_ERR_HIP;  \
     } while (0)
 
+// GEMM2 into H, splitting K when the shape calls for it; the second partial goes
+// to `part` and is then either handed back (*H1_out, for the combine to add) or
+// folded into H.
+moe_status gemm2_impl(const moe_dims& d, const void* h, const int32_t* offsets, const void* w_down, float* H,
+                      void* tp, float* part, float** H1_out, hipStream_t st) {
+    const int64_t R = max_rows(d);
+    float* H1 = partial_bytes(d) ? part : nullptr;
+    MOE_CHECK_HIP(launch_gemm2(d.dtype, h, offsets, d.E, R, w_down, H, H1, d.d, d.m, tp, st));
+    if (H1_out) *H1_out = H1;
+    else if (H1) MOE_CHECK_HIP(launch_add_partial(H, H1, offsets, d.E, R, d.d, st));
+    return MOE_OK;
+}
+
 moe_status ffn_impl(const moe_dims& d, const void* x_perm, const int32_t* offsets, const void* w_gate,
-                    const void* w_up, const void* w_down, float* H, void* ws, hipStream_t st) {
+                    const void* w_up, const void* w_down, float* H, void* ws, float** H1_out, hipStream_t st) {
     void* tp = ws;
     void* h = static_cast<char*>(ws) + align_up(gemm_ws_bytes(d.E));
+    float* part = reinterpret_cast<float*>(static_cast<char*>(h) + align_up((size_t)max_rows(d) * d.m * elem(d)));
     const int64_t R = max_rows(d);
     MOE_CHECK_HIP(launch_gemm1(d.dtype, x_perm, offsets, d.E, R, w_gate, w_up, h, d.m, d.d, tp, st));
-    MOE_CHECK_HIP(launch_gemm2(d.dtype, h, offsets, d.E, R, w_down, H, d.d, d.m, tp, st));
-    return MOE_OK;
+    return gemm2_impl(d, h, offsets, w_down, H, tp, part, H1_out, st);
 }
 
 moe_status shared_impl(const moe_dims& d, const void* x, const void* s_gate, const void* s_up, const void* s_down,
@@ -108,7 +131,7 @@ moe_status shared_impl(const moe_dims& d, const void* x, const void* s_gate, con
     void* tp = ws;
     void* h = static_cast<char*>(ws) + align_up(gemm_ws_bytes(1));
     MOE_CHECK_HIP(launch_gemm1(d.dtype, x, nullptr, 1, d.T, s_gate, s_up, h, d.m_shared, d.d, tp, st));
-    MOE_CHECK_HIP(launch_gemm2(d.dtype, h, nullptr, 1, d.T, s_down, s, d.d, d.m_shared, tp, st));
+    MOE_CHECK_HIP(launch_gemm2(d.dtype, h, nullptr, 1, d.T, s_down, s, nullptr, d.d, d.m_shared, tp, st));
     return MOE_OK;
 }
 
@@ -199,9 +222,9 @@ moe_status moe_expert_gemm2(const moe_shape* shape, const void* h, const int32_t
     moe_status rc = check_shape(shape, &d);
     if (rc != MOE_OK) return rc;
     if (!offsets || !ws || !w_down || (max_rows(d) > 0 && (!h || !H))) return MOE_ERR_INVALID_ARGUMENT;
-    if (ws_bytes < align_up(gemm_ws_bytes(d.E))) return MOE_ERR_WORKSPACE_TOO_SMALL;
-    return hip_status(launch_gemm2(d.dtype, h, offsets, d.E, max_rows(d), w_down, H, d.d, d.m, ws,
-                                   static_cast<hipStream_t>(stream)));
+    if (ws_bytes < gemm2_ws(d)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(gemm_ws_bytes(d.E)));
+    return gemm2_impl(d, h, offsets, w_down, H, ws, part, nullptr, static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_expert_ffn(const moe_shape* shape, const void* x_perm, const int32_t* offsets, const void* w_gate,
@@ -212,7 +235,7 @@ moe_status moe_expert_ffn(const moe_shape* shape, const void* x_perm, const int3
     if (!offsets || !ws || !w_gate || !w_up || !w_down || (max_rows(d) > 0 && (!x_perm || !H)))
         return MOE_ERR_INVALID_ARGUMENT;
     if (ws_bytes < ffn_ws(d)) return MOE_ERR_WORKSPACE_TOO_SMALL;
-    return ffn_impl(d, x_perm, offsets, w_gate, w_up, w_down, H, ws, static_cast<hipStream_t>(stream));
+    return ffn_impl(d, x_perm, offsets, w_gate, w_up, w_down, H, ws, nullptr, static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_shared_ffn(const moe_shape* shape, const void* x, const void* s_gate, const void* s_up,
@@ -232,7 +255,7 @@ moe_status moe_combine(const moe_shape* shape, const float* H, const int32_t* ro
     moe_status rc = check_shape(shape, &d);
     if (rc != MOE_OK) return rc;
     if (d.T > 0 && (!row_of || !topk_w || !y || (!H && max_rows(d) > 0))) return MOE_ERR_INVALID_ARGUMENT;
-    return hip_status(launch_combine(d, H, row_of, topk_w, shared_out, y, static_cast<hipStream_t>(stream)));
+    return hip_status(launch_combine(d, H, nullptr, row_of, topk_w, shared_out, y, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_r, const float* b_r,
@@ -252,13 +275,14 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_r, 
     MOE_CHECK_HIP(launch_route(d, x, w_r, b_r, topk_ids, topk_w, status, w.route, st));
     MOE_CHECK_HIP(launch_dispatch(d, x, topk_ids, load, w.offsets, slot, w.row_of, w.src_token, w.x_perm, stats,
                                   w.dispatch, st));
-    rc = ffn_impl(d, w.x_perm, w.offsets, w_gate, w_up, w_down, w.H, w.ffn, st);
+    float* H1 = nullptr;   // second K-split partial of H, added by the combine
+    rc = ffn_impl(d, w.x_perm, w.offsets, w_gate, w_up, w_down, w.H, w.ffn, &H1, st);
     if (rc != MOE_OK) return rc;
     if (d.m_shared) {
         rc = shared_impl(d, x, s_gate, s_up, s_down, w.s, w.shared, st);
         if (rc != MOE_OK) return rc;
     }
-    return hip_status(launch_combine(d, w.H, w.row_of, topk_w, w.s, y, st));
+    return hip_status(launch_combine(d, w.H, H1, w.row_of, topk_w, w.s, y, st));
 }
 
 }  // extern "C"
