@@ -21,9 +21,10 @@
 //   * LDS rows are stored with their 16-byte chunks XOR-swizzled by row, so the
 //     16-byte operand reads of 32 consecutive rows hit distinct banks.
 //   * Workgroups are renumbered so that every XCD (workgroup id mod 8) receives
-//     a contiguous run of the work list, ordered (n super-tile of 4, m tile,
-//     n tile): the workgroups an XCD runs together share A row tiles and expert
-//     weight tiles in its own L2.
+//     a contiguous run of the work list, ordered (n super-tile, m tile, n tile):
+//     the workgroups an XCD runs together share A row tiles and expert weight
+//     tiles in its own L2.  The super-tile is 4 column tiles wide, 16 for GEMM2
+//     when the groups average at most one row tile.
 // fp32 path: a plain LDS-tiled fp32 FMA kernel (64 x 64 tiles, 4 x 4 per thread).
 #include <algorithm>
 #include <type_traits>
@@ -45,14 +46,13 @@ struct TileCoord {
 
 __device__ __forceinline__ bool tile_coords(int b, const int32_t* __restrict__ offsets,
                                             const int32_t* __restrict__ tprefix, int G, int64_t nrows, int BM, int NT,
-                                            TileCoord& tc) {
+                                            TileCoord& tc, int nsup = NSUPER) {
     const int MT = offsets ? tprefix[G] : (int)((nrows + BM - 1) / BM);
     const int total = MT * NT;
     if (b >= total) return false;
     const int x = b % XCDS, j = b / XCDS;
     const int q = total / XCDS, rmd = total % XCDS;
     const int w = x * q + min(x, rmd) + j;
-    constexpr int nsup = NSUPER;
     const int per_super = MT * nsup;
     const int ns = w / per_super;
     const int rem = w - ns * per_super;
@@ -290,6 +290,7 @@ __device__ __forceinline__ void dma16_async(const uint16_t* src, uint32_t lds_wa
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
         "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"   // one wait state between the M0 write and the LDS-DMA load
         "global_load_lds_dwordx4 %1, off\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
@@ -347,8 +348,11 @@ __device__ __forceinline__ void lds_barrier_reads_done() {
 #define MOE_MF(c, a, b) "v_mfma_f32_32x32x16_bf16 %[" #c "], %[" #b "], %[" #a "], %[" #c "]\n\t"
 #define MOE_DSR(dst, addr, off) "ds_read_b128 %[" #dst "], %[" #addr "] offset:" off "\n\t"
 #define MOE_DSRI(dst, addr, off) "ds_read_b128 %[" #dst "], %[" #addr "] offset:%[" #off "]\n\t"
-#define MOE_DMA(vo, sb, lds, imm) \
-    "s_add_u32 m0, %[" #lds "], " imm "\n\tglobal_load_lds_dwordx4 %[" #vo "], %[" #sb "]\n\t"
+// A load's M0 (LDS destination) is written one instruction or more before the
+// load itself: the ISA requires a wait state between the two.
+#define MOE_M0(lds, imm) "s_add_u32 m0, %[" #lds "], " imm "\n\t"
+#define MOE_LD(vo, sb) "global_load_lds_dwordx4 %[" #vo "], %[" #sb "]\n\t"
+#define MOE_DMA(vo, sb, lds, imm) MOE_M0(lds, imm) "s_nop 0\n\t" MOE_LD(vo, sb)
 // One substep: multiply operand set P (A fragments a0 a1, B fragments b0..b3) while
 // reading the next substep into Q (in the order a0 b0 a1 b1 b2 b3).
 #define MOE_SUBSTEP(P, Q, RA, RB)                                 \
@@ -365,14 +369,14 @@ __device__ __forceinline__ void lds_barrier_reads_done() {
     "s_waitcnt lgkmcnt(0)\n\t"                                                           \
     "s_waitcnt vmcnt(0)\n\t"                                                             \
     "s_barrier\n\t"                                                                      \
-    MOE_MF(c0, ya0, yb0) MOE_DMA(vo0, sa, ldsA, "0")                                     \
-    MOE_MF(c1, ya1, yb0) MOE_DMA(vo1, sa, ldsA, "8192") MOE_DSR(xa0, na0, "0")           \
-    MOE_MF(c2, ya0, yb1) MOE_DMA(vo2, sa, ldsA, "16384") MOE_DSR(xb0, nb0, "0")          \
-    MOE_MF(c3, ya1, yb1) MOE_DMA(vo3, sa, ldsA, "24576") MOE_DSR(xa1, na0, "4096")       \
-    MOE_MF(c4, ya0, yb2) MOE_DMA(vo4, sb0, ldsB, "0") MOE_DSRI(xb1, nb0, ob1)            \
-    MOE_MF(c5, ya1, yb2) MOE_DMA(vo5, sb1, ldsB, "8192") MOE_DSRI(xb2, nb0, ob2)         \
-    MOE_MF(c6, ya0, yb3) MOE_DMA(vo6, sb2, ldsB, "16384") MOE_DSRI(xb3, nb0, ob3)        \
-    MOE_MF(c7, ya1, yb3) MOE_DMA(vo7, sb3, ldsB, "24576")                                \
+    MOE_M0(ldsA, "0") MOE_MF(c0, ya0, yb0) MOE_LD(vo0, sa)                                  \
+    MOE_M0(ldsA, "8192") MOE_MF(c1, ya1, yb0) MOE_LD(vo1, sa) MOE_DSR(xa0, na0, "0")        \
+    MOE_M0(ldsA, "16384") MOE_MF(c2, ya0, yb1) MOE_LD(vo2, sa) MOE_DSR(xb0, nb0, "0")       \
+    MOE_M0(ldsA, "24576") MOE_MF(c3, ya1, yb1) MOE_LD(vo3, sa) MOE_DSR(xa1, na0, "4096")    \
+    MOE_M0(ldsB, "0") MOE_MF(c4, ya0, yb2) MOE_LD(vo4, sb0) MOE_DSRI(xb1, nb0, ob1)         \
+    MOE_M0(ldsB, "8192") MOE_MF(c5, ya1, yb2) MOE_LD(vo5, sb1) MOE_DSRI(xb2, nb0, ob2)      \
+    MOE_M0(ldsB, "16384") MOE_MF(c6, ya0, yb3) MOE_LD(vo6, sb2) MOE_DSRI(xb3, nb0, ob3)     \
+    MOE_M0(ldsB, "24576") MOE_MF(c7, ya1, yb3) MOE_LD(vo7, sb3)                             \
     "s_waitcnt lgkmcnt(0)\n\t"
 
 // One steady-state K tile.  x: operands of substep 0 of this tile on entry, of
@@ -424,13 +428,15 @@ __device__ __forceinline__ void gemm_tile_asm(floatx16_t (&c)[8], bf16x8_t (&x)[
     "s_waitcnt lgkmcnt(0)\n\t"                                                           \
     "s_waitcnt vmcnt(0)\n\t"                                                             \
     "s_barrier\n\t"                                                                      \
-    MOE_MF(c0, ya0, yb0) MOE_DMA(vo0, sa, ldsA, "0") MOE_DMA(vo1, sa, ldsA, "8192")      \
-    MOE_DSR(xa0, na0, "0")                                                               \
-    MOE_MF(c2, ya0, yb1) MOE_DMA(vo2, sa, ldsA, "16384") MOE_DMA(vo3, sa, ldsA, "24576") \
-    MOE_DSR(xb0, nb0, "0") MOE_DSRI(xb1, nb0, ob1)                                       \
-    MOE_MF(c4, ya0, yb2) MOE_DMA(vo4, sb0, ldsB, "0") MOE_DMA(vo5, sb1, ldsB, "8192")    \
-    MOE_DSRI(xb2, nb0, ob2) MOE_DSRI(xb3, nb0, ob3)                                      \
-    MOE_MF(c6, ya0, yb3) MOE_DMA(vo6, sb2, ldsB, "16384") MOE_DMA(vo7, sb3, ldsB, "24576") \
+    MOE_M0(ldsA, "0") MOE_MF(c0, ya0, yb0) MOE_LD(vo0, sa)                                  \
+    MOE_M0(ldsA, "8192") MOE_DSR(xa0, na0, "0") MOE_LD(vo1, sa)                             \
+    MOE_M0(ldsA, "16384") MOE_MF(c2, ya0, yb1) MOE_LD(vo2, sa)                              \
+    MOE_M0(ldsA, "24576") MOE_DSR(xb0, nb0, "0") MOE_LD(vo3, sa)                            \
+    MOE_M0(ldsB, "0") MOE_MF(c4, ya0, yb2) MOE_LD(vo4, sb0)                                 \
+    MOE_M0(ldsB, "8192") MOE_DSRI(xb1, nb0, ob1) MOE_LD(vo5, sb1)                           \
+    MOE_M0(ldsB, "16384") MOE_MF(c6, ya0, yb3) MOE_LD(vo6, sb2)                             \
+    MOE_M0(ldsB, "24576") MOE_DSRI(xb2, nb0, ob2) MOE_LD(vo7, sb3)                          \
+    MOE_DSRI(xb3, nb0, ob3)                                                              \
     "s_waitcnt lgkmcnt(0)\n\t"
 
 template <int OB1, int OB2, int OB3>
@@ -493,7 +499,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* _
                                                                void* __restrict__ Cout, void* __restrict__ Cout1,
                                                                const int32_t* __restrict__ offsets,
                                                                const int32_t* __restrict__ tprefix, int G,
-                                                               int64_t nrows, int N, int K, int S) {
+                                                               int64_t nrows, int N, int K, int S, int nsup) {
     constexpr int BM = 256, BK = 64, WGN = 2, WAVES = 8;
     constexpr int NOPS = SWIGLU ? 2 : 1;
     constexpr int WM = 64, WN = BN / WGN;       // wave tile: 64 rows x WN columns of each operand
@@ -513,7 +519,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* _
     const int NT = (N + BN - 1) / BN;
     const int tiles_grid = gridDim.x / S;
     const int split = blockIdx.x / tiles_grid;
-    if (!tile_coords(blockIdx.x - split * tiles_grid, offsets, tprefix, G, nrows, BM, NT, tc)) return;
+    if (!tile_coords(blockIdx.x - split * tiles_grid, offsets, tprefix, G, nrows, BM, NT, tc, nsup)) return;
     const int Ks = K / S;                       // this split's K range starts at split * Ks
     void* C = split ? Cout1 : Cout;
 
@@ -762,6 +768,14 @@ constexpr int F32_BM = 64, F32_BN = 64;
 
 // The scheduled kernel's conditions: whole K tiles of 64, 4-column output groups,
 // 32-bit load offsets within a 256-row tile.
+// Width of the column super-tiles an XCD walks through (see tile_coords).  With
+// groups of at most one row tile on average, a wide super-tile lets the
+// workgroups an XCD runs together reuse the same activation rows across many
+// weight tiles; otherwise 4 keeps both operands' tiles shared.
+int super_width(int64_t max_rows, int G, int NT) {
+    return (G > 1 && max_rows <= (int64_t)G * 256) ? std::min(NT, 16) : NSUPER;
+}
+
 bool asm_path_ok(int N, int K) { return K % 64 == 0 && N % 8 == 0 && (int64_t)K * 512 < ((int64_t)1 << 32); }
 
 hipError_t prep_tiles(const int32_t* offsets, int G, int BM, void* ws, hipStream_t st) {
@@ -794,7 +808,7 @@ hipError_t launch_gemm1(int dtype, const void* A, const int32_t* offsets, int G,
     if (dtype == MOE_BF16 && asm_path_ok(N, K))
         hipLaunchKernelGGL((gemm_bf16_asm_kernel<BF16_BN1, true>), dim3(grid), dim3(512), 0, st,
                            static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(w_gate),
-                           static_cast<const uint16_t*>(w_up), h, nullptr, offsets, tp, G, max_rows, N, K, 1);
+                           static_cast<const uint16_t*>(w_up), h, nullptr, offsets, tp, G, max_rows, N, K, 1, NSUPER);
     else if (dtype == MOE_BF16)
         hipLaunchKernelGGL((gemm_bf16_kernel<BF16_BM, BF16_BN1, true>), dim3(grid), dim3(256), 0, st,
                            static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(w_gate),
@@ -832,7 +846,7 @@ hipError_t launch_gemm2(int dtype, const void* h, const int32_t* offsets, int G,
         if (S > 1) grid = (grid + XCDS - 1) / XCDS * XCDS * S;
         hipLaunchKernelGGL((gemm_bf16_asm_kernel<BF16_BN2, false>), dim3(grid), dim3(512), 0, st,
                            static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w_down), nullptr, H, H1,
-                           offsets, tp, G, max_rows, N, K, S);
+                           offsets, tp, G, max_rows, N, K, S, super_width(max_rows, G, (N + BN - 1) / BN));
     } else if (dtype == MOE_BF16) {
         hipLaunchKernelGGL((gemm_bf16_kernel<BF16_BM, BF16_BN2, false>), dim3(grid), dim3(256), 0, st,
                            static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w_down), nullptr, H,
