@@ -33,10 +33,34 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 METRIC = "MoE-layer tokens/sec on 1 MI355X (Mixtral shape); expert-GEMM % of MFMA peak"
 
-# HBM counter calibration: FETCH_SIZE / WRITE_SIZE of the expert GEMM1 kernel over
-# one launch (KiB per dispatch), scaled by the ratio measured on a plain copy
-# kernel of known size.  None until taken for the current kernel.
-GEMM1_TRAFFIC_BYTES = None
+# HBM bytes of one expert GEMM1 launch on the Mixtral-shaped layer: the rocprofv3
+# FETCH_SIZE + WRITE_SIZE counters of the kernel (KiB per dispatch), each scaled by
+# the bytes-per-KiB that the same counter reports for a plain device copy of known
+# size (`bench.py --copy-calibration`).  Valid only for the GEMM source it was
+# taken on: reported as null once expert_gemm.hip differs from that hash.
+GEMM1_TRAFFIC = {"bytes": 7443403218, "source_sha256": "1b5e15b7b357cfa3e8757f3be7da48758a6da7a73ed63b7a2d228a81b6228018"}
+GEMM_SOURCE = os.path.join(ROOT, "sparse_mixture_experts_23_amd", "csrc", "expert_gemm.hip")
+
+
+def gemm1_traffic_bytes():
+    if not GEMM1_TRAFFIC:
+        return None
+    import hashlib
+    with open(GEMM_SOURCE, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    return GEMM1_TRAFFIC["bytes"] if sha == GEMM1_TRAFFIC["source_sha256"] else None
+
+
+def copy_calibration(nbytes: int, reps: int):
+    """A plain device-to-device copy of nbytes, `reps` times: the reference whose
+    FETCH_SIZE / WRITE_SIZE counters calibrate the GEMM's."""
+    src = torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
 
 
 def log(msg):
@@ -127,9 +151,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mixtral", choices=sorted(CONFIGS))
-    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--phases", default="1", help="0 disables the per-phase timing loop")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (counter calibration) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -137,6 +163,9 @@ def main():
               "runs on more than one GPU are not supported.", file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs the MI355X"
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, max(args.steps, 1))
+        return
 
     cfg = CONFIGS[args.workload]
     log(f"[bench] workload {cfg.name}: generating inputs on the GPU")
@@ -202,7 +231,7 @@ def main():
         roofline = {"bound": "mfma", "kernel": "expert GEMM1 (gate/up + SwiGLU, bf16 MFMA)",
                     "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                    "traffic": GEMM1_TRAFFIC_BYTES}
+                    "traffic": gemm1_traffic_bytes()}
         # algorithmic bytes of the memory-bound phases
         route_bytes = T * d * es + 4 * cfg.E * d + 8 * T * k
         disp_bytes = T * d * es + A * d * es + 12 * T * k + 4 * A
