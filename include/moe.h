@@ -126,8 +126,10 @@ const char* moe_status_str(int32_t status);
  *                   score is NaN/Inf; such a token gets ids 0..k-1 and weights 0
  *                   so that later calls stay in bounds.  Read it after the
  *                   stream synchronises.
- *   ws              >= moe_workspace_bytes(shape, MOE_WS_ROUTE) bytes (fp32 scores
- *                   [T,E] when E > 64; may be NULL with ws_bytes 0 otherwise) */
+ *   ws              >= moe_workspace_bytes(shape, MOE_WS_ROUTE) bytes: none for bf16
+ *                   activations with E <= 8 (may then be NULL with ws_bytes 0); else
+ *                   the bf16 split of w_r (bf16, E <= 64), plus fp32 partial scores
+ *                   when E > 64 (fp32 activations: only the [T,E] scores, E > 64) */
 moe_status moe_route(const moe_shape* shape, const void* x, const float* w_r, const float* b_r,
                      int32_t* topk_ids, float* topk_w, int32_t* status, void* ws, size_t ws_bytes,
                      void* stream);

@@ -13,6 +13,8 @@
 // x * w_r is formed as three exact bf16 x bf16 products accumulated in fp32 on the
 // MFMA units -- an fp32 dot product up to summation order.
 //
+// E <= 8 (bf16 activations): one fused kernel of fp32 fused multiply-adds with the
+//   fp32 weights held in registers (route_valu_kernel); no split of w_r.
 // E <= 64: one fused kernel; 8 waves share 16 tokens, each wave takes one K
 //   slice with all its loads in flight at once, the slices are summed in LDS in a
 //   fixed order and the waves select.
@@ -151,6 +153,119 @@ __device__ void select_token(const float* __restrict__ row, const float* __restr
     if (lane < k) {
         topk_ids[t * k + lane] = my_e;
         topk_w[t * k + lane] = wgt;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// E <= 8, bf16 activations: fp32 FMA dot products, weights held in registers
+// ---------------------------------------------------------------------------
+//
+// 512 threads; thread j owns the K chunk [kr + 8 j, kr + 8 j + 8) of each K range
+// kr (steps of 4096) and keeps that chunk of all E weight rows in registers (fp32,
+// exactly as given).  Loads are unconditional (addresses clamped, invalid values
+// zeroed afterwards), so the wave's VT activation rows stream in while the first
+// tokens are already being multiplied.  Per token the lane's 8 expert partials
+// are reduce-scattered across each 16-lane row with DPP moves (no LDS round
+// trip), one value per (row, expert) goes to LDS, and the scores are summed over
+// (K range, wave, row) in a fixed order.
+
+constexpr int VT = 16;             // tokens per workgroup
+constexpr int V_THREADS = 512;
+constexpr int V_WAVES = V_THREADS / 64;
+constexpr int V_KR = 8 * V_THREADS;    // K elements per range
+constexpr int V_MAXKR = 2;             // d <= 8192
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// v[e], e < 8, summed over the 16 lanes of a row; lane l ends with expert l & 7.
+// Pairings: l <-> 7 - l within 8 lanes (row half mirror), l <-> l ^ 2, l <-> l ^ 1
+// (quad permutes), then l <-> l + 8 mod 16 (row rotate by 8).
+__device__ __forceinline__ float reduce_row8(const float (&v)[8]) {
+    const int lane = threadIdx.x % 64;
+    const bool b0 = lane & 1, b1 = lane & 2, b2 = lane & 4;
+    float u[4], w2[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {   // keep experts 4 b2 + 0..3
+        const float keep = b2 ? v[4 + i] : v[i], give = b2 ? v[i] : v[4 + i];
+        u[i] = keep + dpp_mov<0x141>(give);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {   // keep experts 4 b2 + 2 b1 + 0..1
+        const float keep = b1 ? u[2 + i] : u[i], give = b1 ? u[i] : u[2 + i];
+        w2[i] = keep + dpp_mov<0x4E>(give);
+    }
+    float r = (b0 ? w2[1] : w2[0]) + dpp_mov<0xB1>(b0 ? w2[0] : w2[1]);
+    return r + dpp_mov<0x128>(r);
+}
+
+__global__ __launch_bounds__(V_THREADS) void route_valu_kernel(const uint16_t* __restrict__ x,
+                                                               const float* __restrict__ w_r,
+                                                               const float* __restrict__ b_r, int64_t T, int d,
+                                                               int E, int k, int mode, int32_t* __restrict__ topk_ids,
+                                                               float* __restrict__ topk_w,
+                                                               int32_t* __restrict__ status) {
+    constexpr int NPART = V_WAVES * 4;                // (wave, row) partials per K range
+    __shared__ float part[V_MAXKR * NPART * VT * 8];
+    __shared__ float lg[VT * 8];
+    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+    const int64_t t0 = (int64_t)blockIdx.x * VT;
+    const int nkr = (d + V_KR - 1) / V_KR;
+    for (int kr = 0; kr < nkr; ++kr) {
+        const int c = kr * V_KR + 8 * tid;            // this thread's chunk (d % 8 == 0: wholly in or out)
+        const bool c_ok = c < d;
+        const int cc = c_ok ? c : d - 8;
+        float w[8][8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float* src = w_r + (int64_t)min(e, E - 1) * d + cc;
+            const float4 lo = *reinterpret_cast<const float4*>(src);
+            const float4 hi = *reinterpret_cast<const float4*>(src + 4);
+            const bool ok = c_ok && e < E;
+            w[e][0] = ok ? lo.x : 0.f; w[e][1] = ok ? lo.y : 0.f; w[e][2] = ok ? lo.z : 0.f; w[e][3] = ok ? lo.w : 0.f;
+            w[e][4] = ok ? hi.x : 0.f; w[e][5] = ok ? hi.y : 0.f; w[e][6] = ok ? hi.z : 0.f; w[e][7] = ok ? hi.w : 0.f;
+        }
+        uint4 xv[VT];
+#pragma unroll
+        for (int r = 0; r < VT; ++r) {
+            const int64_t t = min(t0 + r, T - 1);       // rows past T repeat row T - 1 (never selected)
+            xv[r] = *reinterpret_cast<const uint4*>(x + t * (int64_t)d + cc);
+        }
+#pragma unroll
+        for (int r = 0; r < VT; ++r) {
+            const uint32_t q[4] = {xv[r].x, xv[r].y, xv[r].z, xv[r].w};
+            float xf[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {   // a chunk past d contributes 0 (not 0 * x, which may be NaN)
+                xf[2 * j] = c_ok ? __uint_as_float(q[j] << 16) : 0.f;
+                xf[2 * j + 1] = c_ok ? __uint_as_float(q[j] & 0xffff0000u) : 0.f;
+            }
+            float acc[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float s = 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) s = fmaf(xf[j], w[e][j], s);
+                acc[e] = s;
+            }
+            const float sum = reduce_row8(acc);
+            if ((lane & 15) < 8) part[((kr * NPART + wave * 4 + lane / 16) * VT + r) * 8 + (lane & 7)] = sum;
+        }
+    }
+    __syncthreads();
+    if (tid < VT * 8) {
+        const int r = tid / 8, e = tid % 8;
+        float sc = 0.f;
+        for (int p = 0; p < nkr * NPART; ++p) sc += part[(p * VT + r) * 8 + e];
+        lg[r * 8 + e] = sc;
+    }
+    __syncthreads();
+    for (int r = wave; r < VT; r += V_WAVES) {
+        const int64_t t = t0 + r;
+        if (t >= T) break;
+        select_token<1>(lg + r * 8, b_r, E, k, mode, t, topk_ids, topk_w, status);
     }
 }
 
@@ -404,6 +519,7 @@ namespace moe_kernels {
 
 size_t route_ws_bytes(const moe_dims& s) {
     if (s.dtype != MOE_BF16) return s.E > 64 ? (size_t)s.T * s.E * sizeof(float) : 0;
+    if (s.E <= 8 && s.d <= V_MAXKR * V_KR) return 0;   // route_valu_kernel
     size_t planes = ((size_t)3 * s.E * s.d * 2 + 255) & ~(size_t)255;
     if (s.E <= 64) return planes;
     return planes + (size_t)score_slices(s, nullptr) * s.T * s.E * sizeof(float);
@@ -414,6 +530,12 @@ hipError_t launch_route(const moe_dims& s, const void* x, const float* w_r, cons
     hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(64), 0, st, status, 1);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || s.T == 0) return e;
+    if (s.dtype == MOE_BF16 && s.E <= 8 && s.d <= V_MAXKR * V_KR) {
+        const unsigned grid = (unsigned)((s.T + VT - 1) / VT);
+        hipLaunchKernelGGL(route_valu_kernel, dim3(grid), dim3(V_THREADS), 0, st, static_cast<const uint16_t*>(x), w_r,
+                           b_r, s.T, s.d, s.E, s.k, s.gate_mode, topk_ids, topk_w, status);
+        return hipGetLastError();
+    }
     uint16_t* w3 = static_cast<uint16_t*>(ws);
     if (s.dtype == MOE_BF16) {
         const int64_t n8 = (int64_t)s.E * s.d / 8;
