@@ -188,6 +188,9 @@ RAGGED = MoEConfig("ragged_bf16", T=2000, d=328, m=200, E=4, k=2, dtype="bf16", 
     # ragged groups, drops, partial column tiles in both GEMMs and a shared expert
     MoEConfig("kernel_steady_state", T=1500, d=320, m=448, E=6, k=2, dtype="bf16", gate_mode=0, cf=(5, 4),
               bias="zipf", m_shared=192, cfg_id=23),
+    # router with E < 8 experts over two K ranges of 4096 (d > 4096), T not a multiple of 16
+    MoEConfig("router_two_k_ranges", T=101, d=4160, m=64, E=6, k=2, dtype="bf16", gate_mode=1, cf=None,
+              cfg_id=24),
 ], ids=lambda c: c.name)
 def test_parity_small(cfg):
     run_layer(cfg)
