@@ -27,7 +27,17 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_ca
 
 // SiLU(z) = z * sigmoid(z) = z / (1 + e^-z); e^-z from the hardware exp2.
 __device__ __forceinline__ float silu_f32(float z) {
-    return z / (1.0f + __expf(-z));
+    // hardware exp2 and reciprocal (<= 1 ulp each) instead of an IEEE division
+    return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+
+// Two floats to packed bf16 (lo in the low half), round to nearest even: one
+// v_cvt_pk_bf16_f32 on gfx950.
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) float floatx2_t;
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const floatx2_t f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
 // Total order on finite floats as unsigned keys (larger float -> larger key);

@@ -675,7 +675,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* _
                     const int v = 4 * g + 2 * e;
                     const float h0 = silu_f32(c[q][v]) * c[q + 2 * NTW][v];
                     const float h1 = silu_f32(c[q][v + 1]) * c[q + 2 * NTW][v + 1];
-                    p[e] = f32_to_bf16_bits(h0) | (f32_to_bf16_bits(h1) << 16);
+                    p[e] = pack_bf16x2(h0, h1);
                 }
                 *reinterpret_cast<uint2*>(static_cast<uint16_t*>(C) + row * N + col) = make_uint2(p[0], p[1]);
             } else {
