@@ -96,21 +96,29 @@ hipError_t launch_route(const moe_dims& s, const void* x, const float* w_r, cons
 
 // Dispatch.
 size_t dispatch_ws_bytes(const moe_dims& s);
+// tprefix (nullable): also write the grouped GEMMs' tile prefix for tiles of
+// tile_rows rows (gemm_tile_rows), so the GEMM launches can skip computing it.
 hipError_t launch_dispatch(const moe_dims& s, const void* x, const int32_t* ids, int32_t* load,
                            int32_t* offsets, int32_t* slot, int32_t* row_of, int32_t* src_token,
-                           void* x_perm, int32_t* stats, void* ws, hipStream_t st);
+                           void* x_perm, int32_t* stats, void* ws, hipStream_t st,
+                           int32_t* tprefix = nullptr, int tile_rows = 0);
 
 // Grouped expert GEMMs.  offsets == nullptr means one group covering rows [0, nrows).
 size_t gemm_ws_bytes(int G);
+// ws starts with the tile prefix of `offsets` (G + 1 int32, gemm_ws_bytes); it is
+// computed by the launch unless prefix_ready (then the caller wrote it, e.g. the
+// dispatch scan).
+int gemm_tile_rows(int dtype);
 hipError_t launch_gemm1(int dtype, const void* A, const int32_t* offsets, int G, int64_t max_rows,
                         const void* w_gate, const void* w_up, void* h, int N, int K,
-                        void* ws, hipStream_t st);
+                        void* ws, hipStream_t st, bool prefix_ready = false);
 // GEMM2 may split K in two (gemm2_splits == 2, decided from the shape alone):
 // then H receives the partial sum over the first half of K and H1 the second;
 // with H1 == nullptr it never splits.
 int gemm2_splits(int dtype, int64_t max_rows, int G, int N, int K);
 hipError_t launch_gemm2(int dtype, const void* h, const int32_t* offsets, int G, int64_t max_rows,
-                        const void* w_down, float* H, float* H1, int N, int K, void* ws, hipStream_t st);
+                        const void* w_down, float* H, float* H1, int N, int K, void* ws, hipStream_t st,
+                        bool prefix_ready = false);
 // H += H1 over the rows [0, offsets[G]) (or [0, max_rows) without offsets); N % 4 == 0.
 hipError_t launch_add_partial(float* H, const float* H1, const int32_t* offsets, int G, int64_t max_rows, int N,
                               hipStream_t st);

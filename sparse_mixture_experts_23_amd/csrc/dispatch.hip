@@ -50,10 +50,13 @@ __global__ __launch_bounds__(DB_TOK) void dispatch_count_kernel(const int32_t* _
 }
 
 // One workgroup of 1024 threads (E <= 1024): thread e scans expert e over blocks.
+// tprefix (nullable): also writes the grouped GEMMs' tile prefix,
+// tprefix[e] = sum_{e' < e} ceil(accepted(e') / tile_rows), tprefix[E] = total.
 __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict__ hist, int NB, int E, int C,
                                                              int32_t* __restrict__ load, int32_t* __restrict__ offsets,
-                                                             int32_t* __restrict__ stats) {
-    __shared__ int s_sum[16], s_over[16], s_max[16];
+                                                             int32_t* __restrict__ stats, int32_t* __restrict__ tprefix,
+                                                             int tile_rows) {
+    __shared__ int s_sum[16], s_over[16], s_max[16], s_tiles[16];
     const int e = threadIdx.x, wave = e / 64, lane = e % 64;
     int L = 0;
     if (e < E) {
@@ -66,12 +69,17 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict
     }
     const int acc = e < E ? min(L, C) : 0;
     const int over = e < E ? max(L - C, 0) : 0;
-    // inclusive wave scan of acc
-    int incl = acc;
+    const int tiles = tprefix ? (acc + tile_rows - 1) / tile_rows : 0;
+    // inclusive wave scans of acc and of the tile counts
+    int incl = acc, tincl = tiles;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
         const int v = __shfl_up(incl, o, MOE_WAVE);
-        if (lane >= o) incl += v;
+        const int tv = __shfl_up(tincl, o, MOE_WAVE);
+        if (lane >= o) {
+            incl += v;
+            tincl += tv;
+        }
     }
     int ov = over, mx = L;
 #pragma unroll
@@ -79,20 +87,29 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict
         ov += __shfl_xor(ov, o, MOE_WAVE);
         mx = max(mx, __shfl_xor(mx, o, MOE_WAVE));
     }
-    if (lane == 63) s_sum[wave] = incl;
+    if (lane == 63) {
+        s_sum[wave] = incl;
+        s_tiles[wave] = tincl;
+    }
     if (lane == 0) {
         s_over[wave] = ov;
         s_max[wave] = mx;
     }
     __syncthreads();
-    int before = 0, total = 0, otot = 0, mtot = 0;
+    int before = 0, total = 0, otot = 0, mtot = 0, tbefore = 0, ttotal = 0;
     for (int w = 0; w < 16; ++w) {
-        if (w < wave) before += s_sum[w];
+        if (w < wave) {
+            before += s_sum[w];
+            tbefore += s_tiles[w];
+        }
         total += s_sum[w];
+        ttotal += s_tiles[w];
         otot += s_over[w];
         mtot = max(mtot, s_max[w]);
     }
     if (e < E) offsets[e] = before + incl - acc;
+    if (tprefix && e < E) tprefix[e] = tbefore + tincl - tiles;
+    if (tprefix && e == 0) tprefix[E] = ttotal;
     if (e == 0) {
         offsets[E] = total;
         stats[MOE_STAT_OVERFLOW] = otot;
@@ -189,14 +206,15 @@ size_t dispatch_ws_bytes(const moe_dims& s) {
 
 hipError_t launch_dispatch(const moe_dims& s, const void* x, const int32_t* ids, int32_t* load, int32_t* offsets,
                            int32_t* slot, int32_t* row_of, int32_t* src_token, void* x_perm, int32_t* stats, void* ws,
-                           hipStream_t st) {
+                           hipStream_t st, int32_t* tprefix, int tile_rows) {
     const int NB = (int)((s.T + DB_TOK - 1) / DB_TOK);
     int32_t* hist = static_cast<int32_t*>(ws);
     const size_t mask_lds = sizeof(unsigned long long) * 4 * s.E;
     if (NB > 0) {
         hipLaunchKernelGGL(dispatch_count_kernel, dim3(NB), dim3(DB_TOK), mask_lds, st, ids, s.T, s.k, s.E, hist);
     }
-    hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, st, hist, NB, s.E, s.C, load, offsets, stats);
+    hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, st, hist, NB, s.E, s.C, load, offsets, stats,
+                       tprefix, tile_rows);
     if (NB == 0) return hipGetLastError();
     hipLaunchKernelGGL(dispatch_place_kernel, dim3(NB), dim3(DB_TOK), mask_lds, st, ids, s.T, s.k, s.E, s.C, hist,
                        offsets, slot, row_of, src_token, stats);

@@ -796,11 +796,13 @@ namespace moe_kernels {
 
 size_t gemm_ws_bytes(int G) { return (((size_t)(G + 1) * sizeof(int32_t)) + 255) & ~(size_t)255; }
 
+int gemm_tile_rows(int dtype) { return dtype == MOE_BF16 ? BF16_BM : F32_BM; }
+
 hipError_t launch_gemm1(int dtype, const void* A, const int32_t* offsets, int G, int64_t max_rows, const void* w_gate,
-                        const void* w_up, void* h, int N, int K, void* ws, hipStream_t st) {
+                        const void* w_up, void* h, int N, int K, void* ws, hipStream_t st, bool prefix_ready) {
     const int BM = dtype == MOE_BF16 ? BF16_BM : F32_BM;
     const int BN = dtype == MOE_BF16 ? BF16_BN1 : F32_BN;
-    hipError_t e = prep_tiles(offsets, G, BM, ws, st);
+    hipError_t e = prefix_ready ? hipSuccess : prep_tiles(offsets, G, BM, ws, st);
     if (e != hipSuccess) return e;
     const unsigned grid = grid_size(offsets, G, max_rows, BM, N, BN);
     if (grid == 0) return hipSuccess;
@@ -833,10 +835,11 @@ int gemm2_splits(int dtype, int64_t max_rows, int G, int N, int K) {
 }
 
 hipError_t launch_gemm2(int dtype, const void* h, const int32_t* offsets, int G, int64_t max_rows,
-                        const void* w_down, float* H, float* H1, int N, int K, void* ws, hipStream_t st) {
+                        const void* w_down, float* H, float* H1, int N, int K, void* ws, hipStream_t st,
+                        bool prefix_ready) {
     const int BM = dtype == MOE_BF16 ? BF16_BM : F32_BM;
     const int BN = dtype == MOE_BF16 ? BF16_BN2 : F32_BN;
-    hipError_t e = prep_tiles(offsets, G, BM, ws, st);
+    hipError_t e = prefix_ready ? hipSuccess : prep_tiles(offsets, G, BM, ws, st);
     if (e != hipSuccess) return e;
     unsigned grid = grid_size(offsets, G, max_rows, BM, N, BN);
     if (grid == 0) return hipSuccess;

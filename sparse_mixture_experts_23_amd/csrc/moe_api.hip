@@ -107,23 +107,26 @@ inline moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : M
 // to `part` and is then either handed back (*H1_out, for the combine to add) or
 // folded into H.
 moe_status gemm2_impl(const moe_dims& d, const void* h, const int32_t* offsets, const void* w_down, float* H,
-                      void* tp, float* part, float** H1_out, hipStream_t st) {
+                      void* tp, float* part, float** H1_out, hipStream_t st, bool prefix_ready = false) {
     const int64_t R = max_rows(d);
     float* H1 = partial_bytes(d) ? part : nullptr;
-    MOE_CHECK_HIP(launch_gemm2(d.dtype, h, offsets, d.E, R, w_down, H, H1, d.d, d.m, tp, st));
+    MOE_CHECK_HIP(launch_gemm2(d.dtype, h, offsets, d.E, R, w_down, H, H1, d.d, d.m, tp, st, prefix_ready));
     if (H1_out) *H1_out = H1;
     else if (H1) MOE_CHECK_HIP(launch_add_partial(H, H1, offsets, d.E, R, d.d, st));
     return MOE_OK;
 }
 
+// prefix_ready: the tile prefix at the start of ws was written by the dispatch scan.
 moe_status ffn_impl(const moe_dims& d, const void* x_perm, const int32_t* offsets, const void* w_gate,
-                    const void* w_up, const void* w_down, float* H, void* ws, float** H1_out, hipStream_t st) {
+                    const void* w_up, const void* w_down, float* H, void* ws, float** H1_out, hipStream_t st,
+                    bool prefix_ready = false) {
     void* tp = ws;
     void* h = static_cast<char*>(ws) + align_up(gemm_ws_bytes(d.E));
     float* part = reinterpret_cast<float*>(static_cast<char*>(h) + align_up((size_t)max_rows(d) * d.m * elem(d)));
     const int64_t R = max_rows(d);
-    MOE_CHECK_HIP(launch_gemm1(d.dtype, x_perm, offsets, d.E, R, w_gate, w_up, h, d.m, d.d, tp, st));
-    return gemm2_impl(d, h, offsets, w_down, H, tp, part, H1_out, st);
+    MOE_CHECK_HIP(launch_gemm1(d.dtype, x_perm, offsets, d.E, R, w_gate, w_up, h, d.m, d.d, tp, st, prefix_ready));
+    // GEMM2 uses the same row tiles: the prefix GEMM1 found (or was given) stays valid
+    return gemm2_impl(d, h, offsets, w_down, H, tp, part, H1_out, st, true);
 }
 
 moe_status shared_impl(const moe_dims& d, const void* x, const void* s_gate, const void* s_up, const void* s_down,
@@ -273,10 +276,11 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_r, 
     if (ws_bytes < w.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
     hipStream_t st = static_cast<hipStream_t>(stream);
     MOE_CHECK_HIP(launch_route(d, x, w_r, b_r, topk_ids, topk_w, status, w.route, st));
+    // the dispatch scan also writes the GEMMs' tile prefix at the start of the FFN workspace
     MOE_CHECK_HIP(launch_dispatch(d, x, topk_ids, load, w.offsets, slot, w.row_of, w.src_token, w.x_perm, stats,
-                                  w.dispatch, st));
+                                  w.dispatch, st, static_cast<int32_t*>(w.ffn), gemm_tile_rows(d.dtype)));
     float* H1 = nullptr;   // second K-split partial of H, added by the combine
-    rc = ffn_impl(d, w.x_perm, w.offsets, w_gate, w_up, w_down, w.H, w.ffn, &H1, st);
+    rc = ffn_impl(d, w.x_perm, w.offsets, w_gate, w_up, w_down, w.H, w.ffn, &H1, st, true);
     if (rc != MOE_OK) return rc;
     if (d.m_shared) {
         rc = shared_impl(d, x, s_gate, s_up, s_down, w.s, w.shared, st);
