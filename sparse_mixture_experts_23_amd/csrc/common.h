@@ -123,6 +123,11 @@ hipError_t launch_gemm2(int dtype, const void* h, const int32_t* offsets, int G,
 hipError_t launch_add_partial(float* H, const float* H1, const int32_t* offsets, int G, int64_t max_rows, int N,
                               hipStream_t st);
 
+// Ungrouped bf16 GEMM part[s] = x[T,K] . w[N,K]^T over the K split s of
+// scores_splits(T, N, K) splits; part holds S consecutive fp32 [T,N] blocks.
+int scores_splits(int64_t T, int N, int K);
+hipError_t launch_scores_gemm(const void* x, const void* w, int64_t T, int N, int K, float* part, hipStream_t st);
+
 // Combine.  H1 (nullable): second K-split partial of H, added to H row by row.
 hipError_t launch_combine(const moe_dims& s, const float* H, const float* H1, const int32_t* row_of,
                           const float* topk_w, const float* shared_out, float* y, hipStream_t st);

@@ -487,16 +487,17 @@ __device__ __forceinline__ void gemm_tile_asm_loads_only(floatx16_t (&c)[8], bf1
                  : "memory");
 }
 
-// Requires K % (64 * S) == 0, N % 8 == 0 and 512 K < 2^32 (32-bit load offsets).
+// Requires K % 64 == 0, N % 8 == 0 and 512 K < 2^32 (32-bit load offsets).
 // K split: the grid is S copies of a tile grid of gridDim.x / S workgroups (a
-// multiple of 8, so every copy keeps the XCD order); copy s sums k in
-// [s K / S, (s + 1) K / S) and writes its fp32 partial to Cout (s = 0) or Cout1
-// (s = 1).  S is 1 or 2, and 1 for SwiGLU.
+// multiple of 8, so every copy keeps the XCD order); copy s sums the K tiles
+// [s KT / S, (s + 1) KT / S) of the KT = K / 64 and writes its fp32 partial to
+// Cout (s = 0) or Cpart + (s - 1) part_stride (s >= 1).  S = 1 for SwiGLU.
 template <int BN, bool SWIGLU>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* __restrict__ A,
                                                                const uint16_t* __restrict__ B0,
                                                                const uint16_t* __restrict__ B1,
-                                                               void* __restrict__ Cout, void* __restrict__ Cout1,
+                                                               void* __restrict__ Cout, float* __restrict__ Cpart,
+                                                               int64_t part_stride,
                                                                const int32_t* __restrict__ offsets,
                                                                const int32_t* __restrict__ tprefix, int G,
                                                                int64_t nrows, int N, int K, int S, int nsup) {
@@ -520,15 +521,16 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* _
     const int tiles_grid = gridDim.x / S;
     const int split = blockIdx.x / tiles_grid;
     if (!tile_coords(blockIdx.x - split * tiles_grid, offsets, tprefix, G, nrows, BM, NT, tc, nsup)) return;
-    const int Ks = K / S;                       // this split's K range starts at split * Ks
-    void* C = split ? Cout1 : Cout;
+    const int KTall = K / BK;
+    const int kt_begin = split * KTall / S, kt_end = (split + 1) * KTall / S;
+    void* C = split ? static_cast<void*>(Cpart + (int64_t)(split - 1) * part_stride) : Cout;
 
     const int tid = threadIdx.x, lane = tid % 64;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
     const int wm = wave / WGN, wn = wave % WGN;
     const int n0 = tc.nt * BN;
     const int64_t wstride = (int64_t)N * K;
-    const int64_t k0 = (int64_t)split * Ks;
+    const int64_t k0 = (int64_t)kt_begin * BK;
     const uint16_t* Bg = B0 + (int64_t)tc.g * wstride + (int64_t)n0 * K + k0;
     const uint16_t* Bu = SWIGLU ? B1 + (int64_t)tc.g * wstride + (int64_t)n0 * K + k0 : Bg;
     const uint16_t* At = A + tc.row_start * K + k0;
@@ -570,7 +572,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* _
 #pragma unroll
         for (int v = 0; v < 16; ++v) c[q][v] = 0.f;
 
-    const int KT = Ks / BK;
+    const int KT = kt_end - kt_begin;
     load_tile(0, 0);
     if (KT > 1) load_tile(1, 1);
 
@@ -810,7 +812,8 @@ hipError_t launch_gemm1(int dtype, const void* A, const int32_t* offsets, int G,
     if (dtype == MOE_BF16 && asm_path_ok(N, K))
         hipLaunchKernelGGL((gemm_bf16_asm_kernel<BF16_BN1, true>), dim3(grid), dim3(512), 0, st,
                            static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(w_gate),
-                           static_cast<const uint16_t*>(w_up), h, nullptr, offsets, tp, G, max_rows, N, K, 1, NSUPER);
+                           static_cast<const uint16_t*>(w_up), h, nullptr, (int64_t)0, offsets, tp, G, max_rows, N, K, 1,
+                           NSUPER);
     else if (dtype == MOE_BF16)
         hipLaunchKernelGGL((gemm_bf16_kernel<BF16_BM, BF16_BN1, true>), dim3(grid), dim3(256), 0, st,
                            static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(w_gate),
@@ -849,7 +852,7 @@ hipError_t launch_gemm2(int dtype, const void* h, const int32_t* offsets, int G,
         if (S > 1) grid = (grid + XCDS - 1) / XCDS * XCDS * S;
         hipLaunchKernelGGL((gemm_bf16_asm_kernel<BF16_BN2, false>), dim3(grid), dim3(512), 0, st,
                            static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w_down), nullptr, H, H1,
-                           offsets, tp, G, max_rows, N, K, S, super_width(max_rows, G, (N + BN - 1) / BN));
+                           (int64_t)0, offsets, tp, G, max_rows, N, K, S, super_width(max_rows, G, (N + BN - 1) / BN));
     } else if (dtype == MOE_BF16) {
         hipLaunchKernelGGL((gemm_bf16_kernel<BF16_BM, BF16_BN2, false>), dim3(grid), dim3(256), 0, st,
                            static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w_down), nullptr, H,
@@ -857,6 +860,31 @@ hipError_t launch_gemm2(int dtype, const void* h, const int32_t* offsets, int G,
     } else {
         hipLaunchKernelGGL((gemm_f32_kernel<false>), dim3(grid), dim3(256), 0, st, static_cast<const float*>(h),
                            static_cast<const float*>(w_down), nullptr, H, offsets, tp, G, max_rows, N, K);
+    }
+    return hipGetLastError();
+}
+
+int scores_splits(int64_t T, int N, int K) {
+    if (!asm_path_ok(N, K)) return 1;
+    const int64_t tiles = ((T + BF16_BM - 1) / BF16_BM) * ((N + BF16_BN2 - 1) / BF16_BN2);
+    const int KT = K / 64;
+    int S = (int)std::min<int64_t>(16, std::max<int64_t>(1, MOE_GEMM_CUS / std::max<int64_t>(tiles, 1)));
+    return std::max(1, std::min(S, KT / 4));   // at least 4 K tiles per split
+}
+
+hipError_t launch_scores_gemm(const void* x, const void* w, int64_t T, int N, int K, float* part, hipStream_t st) {
+    const unsigned tiles = grid_size(nullptr, 1, T, BF16_BM, N, BF16_BN2);
+    if (tiles == 0) return hipSuccess;
+    const int S = scores_splits(T, N, K);
+    if (asm_path_ok(N, K)) {
+        const unsigned grid = (tiles + XCDS - 1) / XCDS * XCDS * S;
+        hipLaunchKernelGGL((gemm_bf16_asm_kernel<BF16_BN2, false>), dim3(grid), dim3(512), 0, st,
+                           static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), nullptr, part,
+                           part + T * N, T * N, nullptr, nullptr, 1, T, N, K, S, NSUPER);
+    } else {
+        hipLaunchKernelGGL((gemm_bf16_kernel<BF16_BM, BF16_BN2, false>), dim3(tiles), dim3(256), 0, st,
+                           static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), nullptr, part, nullptr,
+                           nullptr, 1, T, N, K);
     }
     return hipGetLastError();
 }

@@ -18,9 +18,11 @@
 // E <= 64: one fused kernel; 8 waves share 16 tokens, each wave takes one K
 //   slice with all its loads in flight at once, the slices are summed in LDS in a
 //   fixed order and the waves select.
-// E > 64: a split-K score kernel (256 tokens x 64 experts x one K slice per
-//   workgroup) writes fp32 partial scores to the workspace, and a selection
-//   kernel with one wave per token sums the slices in a fixed order.
+// E > 64: the three planes stacked as a [3E (padded to a multiple of 8), d]
+//   bf16 matrix make the scores one ungrouped GEMM on the expert-GEMM kernel
+//   ([T, 3E] fp32 per K split, the K range split so that the work fills the
+//   GPU); a selection kernel with one wave per token adds, per expert, the three
+//   plane columns of every split in a fixed order.
 // Selection: k rounds of a 64-bit (order-preserving score key, ~id) wave arg-max.
 // Everything is deterministic: no atomics, fixed summation orders.
 #include <algorithm>
@@ -33,9 +35,6 @@ constexpr int RT_TOK = 16;       // fused kernel: tokens per workgroup
 constexpr int RT_WAVES = 8;       //               waves (K slices) per workgroup
 constexpr int RT_THREADS = 64 * RT_WAVES;
 
-constexpr int SC_TOK = 256;       // score kernel: tokens per workgroup (64 per wave)
-constexpr int SC_EXP = 64;        //               experts per workgroup
-constexpr int SC_KU = 2;          //               k-steps of 32 per load batch
 
 __global__ void zero_i32_kernel(int32_t* p, int n) {
     int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -59,10 +58,13 @@ __device__ __forceinline__ void split3(const float4 w0, const float4 w1, uint4& 
     L = {l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)};
 }
 
-// w3[p][e][i] = plane p (hi, mid, lo) of w_r[e][i]; 8 weights per thread.
+// w3[p][e][i] = plane p (hi, mid, lo) of w_r[e][i]; 8 weights per thread.  The
+// pad8 chunks after the three planes are zeroed (rows that round 3E up to a
+// multiple of 8 for the score GEMM).
 __global__ __launch_bounds__(256) void split_router_kernel(const float* __restrict__ w_r, int64_t n8,
-                                                           uint4* __restrict__ w3) {
+                                                           uint4* __restrict__ w3, int64_t pad8) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < pad8) w3[3 * n8 + i] = uint4{0u, 0u, 0u, 0u};
     if (i >= n8) return;
     const float4* src = reinterpret_cast<const float4*>(w_r) + 2 * i;
     uint4 H, M, L;
@@ -71,6 +73,9 @@ __global__ __launch_bounds__(256) void split_router_kernel(const float* __restri
     w3[n8 + i] = M;
     w3[2 * n8 + i] = L;
 }
+
+// Rows of the score GEMM's weight matrix: the three planes of w_r, padded to a multiple of 8.
+inline int score_cols(int E) { return (3 * E + 7) / 8 * 8; }
 
 __device__ __forceinline__ floatx4_t mfma3(const bf16x8_t a, const uint4 H, const uint4 M, const uint4 L,
                                            floatx4_t acc) {
@@ -377,84 +382,6 @@ __global__ __launch_bounds__(RT_THREADS) void route_small_kernel(const void* __r
 // E > 64: split-K score kernel + selection kernel
 // ---------------------------------------------------------------------------
 
-// Workgroup = 4 waves: 256 tokens x 64 experts x K slice ks; wave w owns tokens
-// 64 w .. 64 w + 63 (4 row tiles) x the 64 experts (4 column tiles).
-// part[ks][t][e] = sum over the slice of x[t] . w_r[e].
-__global__ __launch_bounds__(256) void router_scores_kernel(const uint16_t* __restrict__ x,
-                                                            const uint16_t* __restrict__ w3, int64_t T, int d, int E,
-                                                            int kslice, float* __restrict__ part) {
-    const int ntb = (int)((T + SC_TOK - 1) / SC_TOK);
-    const int neb = (E + SC_EXP - 1) / SC_EXP;
-    const int ks = blockIdx.x / (ntb * neb);
-    const int rem = blockIdx.x % (ntb * neb);
-    const int eb = rem / ntb, tb = rem % ntb;      // token blocks of one expert group are adjacent
-    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-    const int row = lane % 16, grp = lane / 16;
-    const int kbeg = ks * kslice, kend = min(d, kbeg + kslice);
-    const int64_t plane = (int64_t)E * d;
-
-    const uint16_t* xr[4];
-    bool tok_ok[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t t = (int64_t)tb * SC_TOK + wave * 64 + i * 16 + row;
-        tok_ok[i] = t < T;
-        xr[i] = x + (tok_ok[i] ? t : 0) * (int64_t)d + grp * 8;
-    }
-    const uint16_t* wr[4];
-    bool e_ok[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const int e = eb * SC_EXP + c * 16 + row;
-        e_ok[c] = e < E;
-        wr[c] = w3 + (int64_t)(e_ok[c] ? e : 0) * d + grp * 8;
-    }
-
-    floatx4_t acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[i][c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-
-    for (int k0 = kbeg; k0 < kend; k0 += 32 * SC_KU) {
-        uint4 av[SC_KU][4], bw[SC_KU][4][3];
-#pragma unroll
-        for (int u = 0; u < SC_KU; ++u) {
-            const int kk = k0 + 32 * u;
-            const bool k_ok = kk + grp * 8 < kend;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                av[u][i] = (tok_ok[i] && k_ok) ? *reinterpret_cast<const uint4*>(xr[i] + kk) : uint4{0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-#pragma unroll
-                for (int p = 0; p < 3; ++p)
-                    bw[u][c][p] = (e_ok[c] && k_ok) ? *reinterpret_cast<const uint4*>(wr[c] + p * plane + kk)
-                                                    : uint4{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int u = 0; u < SC_KU; ++u)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    acc[i][c] = mfma3(as_bf16x8(av[u][i]), bw[u][c][0], bw[u][c][1], bw[u][c][2], acc[i][c]);
-    }
-    float* out = part + (int64_t)ks * T * E;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const int e = eb * SC_EXP + c * 16 + row;
-        if (!e_ok[c]) continue;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int64_t t = (int64_t)tb * SC_TOK + wave * 64 + i * 16 + 4 * grp + v;
-                if (t < T) out[t * E + e] = acc[i][c][v];
-            }
-    }
-}
-
 __global__ __launch_bounds__(256) void router_scores_f32_kernel(const float* __restrict__ x,
                                                                 const float* __restrict__ w_r, int64_t T, int d,
                                                                 int E, float* __restrict__ scores) {
@@ -469,9 +396,11 @@ __global__ __launch_bounds__(256) void router_scores_f32_kernel(const float* __r
     scores[p] = s;
 }
 
-// One wave per token: sums the KS partial score rows in slice order, then selects.
+// One wave per token: part holds KS blocks [T][NP]; the score of expert e is the
+// sum over the blocks (in order) of its P plane columns p E + e, added lowest
+// plane first; then selects.
 template <int EPL>
-__global__ __launch_bounds__(256) void route_select_kernel(const float* __restrict__ part, int KS,
+__global__ __launch_bounds__(256) void route_select_kernel(const float* __restrict__ part, int KS, int P, int NP,
                                                            const float* __restrict__ b_r, int64_t T, int E, int k,
                                                            int mode, int32_t* __restrict__ topk_ids,
                                                            float* __restrict__ topk_w, int32_t* __restrict__ status) {
@@ -484,7 +413,8 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
         const int e = lane + 64 * j;
         float s = 0.f;
         if (e < E)
-            for (int q = 0; q < KS; ++q) s += part[((int64_t)q * T + t) * E + e];
+            for (int q = 0; q < KS; ++q)
+                for (int pl = P - 1; pl >= 0; --pl) s += part[((int64_t)q * T + t) * NP + pl * E + e];
         rows[wave][e] = s;
     }
     __builtin_amdgcn_wave_barrier();
@@ -494,23 +424,10 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
 }
 
 template <int EPL>
-void launch_select(const moe_dims& s, const float* part, int KS, const float* b_r, int32_t* ids, float* w,
-                   int32_t* status, hipStream_t st) {
-    hipLaunchKernelGGL((route_select_kernel<EPL>), dim3((unsigned)((s.T + 3) / 4)), dim3(256), 0, st, part, KS, b_r,
-                       s.T, s.E, s.k, s.gate_mode, ids, w, status);
-}
-
-// K slices of the split-K score kernel: enough workgroups to fill the GPU,
-// slices of at least 256 (a multiple of 32).
-int score_slices(const moe_dims& s, int* kslice) {
-    const int64_t tiles = ((s.T + SC_TOK - 1) / SC_TOK) * ((s.E + SC_EXP - 1) / SC_EXP);
-    int KS = (int)std::max<int64_t>(1, (256 + tiles - 1) / tiles);
-    KS = std::min(KS, std::max(1, s.d / 256));
-    int ksl = (s.d + KS - 1) / KS;
-    ksl = (ksl + 31) / 32 * 32;
-    KS = (s.d + ksl - 1) / ksl;
-    if (kslice) *kslice = ksl;
-    return KS;
+void launch_select(const moe_dims& s, const float* part, int KS, int P, int NP, const float* b_r, int32_t* ids,
+                   float* w, int32_t* status, hipStream_t st) {
+    hipLaunchKernelGGL((route_select_kernel<EPL>), dim3((unsigned)((s.T + 3) / 4)), dim3(256), 0, st, part, KS, P, NP,
+                       b_r, s.T, s.E, s.k, s.gate_mode, ids, w, status);
 }
 
 }  // namespace
@@ -520,9 +437,10 @@ namespace moe_kernels {
 size_t route_ws_bytes(const moe_dims& s) {
     if (s.dtype != MOE_BF16) return s.E > 64 ? (size_t)s.T * s.E * sizeof(float) : 0;
     if (s.E <= 8 && s.d <= V_MAXKR * V_KR) return 0;   // route_valu_kernel
-    size_t planes = ((size_t)3 * s.E * s.d * 2 + 255) & ~(size_t)255;
+    const int N3 = score_cols(s.E);
+    size_t planes = ((size_t)N3 * s.d * 2 + 255) & ~(size_t)255;
     if (s.E <= 64) return planes;
-    return planes + (size_t)score_slices(s, nullptr) * s.T * s.E * sizeof(float);
+    return planes + (size_t)scores_splits(s.T, N3, s.d) * s.T * N3 * sizeof(float);
 }
 
 hipError_t launch_route(const moe_dims& s, const void* x, const float* w_r, const float* b_r, int32_t* topk_ids,
@@ -539,8 +457,9 @@ hipError_t launch_route(const moe_dims& s, const void* x, const float* w_r, cons
     uint16_t* w3 = static_cast<uint16_t*>(ws);
     if (s.dtype == MOE_BF16) {
         const int64_t n8 = (int64_t)s.E * s.d / 8;
-        hipLaunchKernelGGL(split_router_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, w_r, n8,
-                           reinterpret_cast<uint4*>(w3));
+        const int64_t pad8 = s.E > 64 ? (int64_t)(score_cols(s.E) - 3 * s.E) * s.d / 8 : 0;
+        hipLaunchKernelGGL(split_router_kernel, dim3((unsigned)((std::max(n8, pad8) + 255) / 256)), dim3(256), 0, st,
+                           w_r, n8, reinterpret_cast<uint4*>(w3), pad8);
     }
     if (s.E <= 64) {
         const unsigned grid = (unsigned)((s.T + RT_TOK - 1) / RT_TOK);
@@ -560,26 +479,28 @@ hipError_t launch_route(const moe_dims& s, const void* x, const float* w_r, cons
 #undef MOE_SMALL
         return hipGetLastError();
     }
+    // E > 64: scores as one ungrouped GEMM (bf16: x against the three planes, [T, 3E]
+    // padded to N3 columns, K split over KS blocks; fp32: plain dot products)
     float* part;
-    int KS = 1;
+    int KS = 1, P = 1, NP = s.E;
     if (s.dtype == MOE_BF16) {
-        part = reinterpret_cast<float*>(static_cast<char*>(ws) + (((size_t)3 * s.E * s.d * 2 + 255) & ~(size_t)255));
-        int ksl = 0;
-        KS = score_slices(s, &ksl);
-        const unsigned grid =
-            (unsigned)(((s.T + SC_TOK - 1) / SC_TOK) * ((s.E + SC_EXP - 1) / SC_EXP) * KS);
-        hipLaunchKernelGGL(router_scores_kernel, dim3(grid), dim3(256), 0, st, static_cast<const uint16_t*>(x), w3,
-                           s.T, s.d, s.E, ksl, part);
+        const int N3 = score_cols(s.E);
+        part = reinterpret_cast<float*>(static_cast<char*>(ws) + (((size_t)N3 * s.d * 2 + 255) & ~(size_t)255));
+        KS = scores_splits(s.T, N3, s.d);
+        P = 3;
+        NP = N3;
+        e = launch_scores_gemm(x, w3, s.T, N3, s.d, part, st);
+        if (e != hipSuccess) return e;
     } else {
         part = static_cast<float*>(ws);
         const unsigned grid = (unsigned)((s.T * s.E + 255) / 256);
         hipLaunchKernelGGL(router_scores_f32_kernel, dim3(grid), dim3(256), 0, st, static_cast<const float*>(x), w_r,
                            s.T, s.d, s.E, part);
     }
-    if (s.E <= 128) launch_select<2>(s, part, KS, b_r, topk_ids, topk_w, status, st);
-    else if (s.E <= 256) launch_select<4>(s, part, KS, b_r, topk_ids, topk_w, status, st);
-    else if (s.E <= 512) launch_select<8>(s, part, KS, b_r, topk_ids, topk_w, status, st);
-    else launch_select<16>(s, part, KS, b_r, topk_ids, topk_w, status, st);
+    if (s.E <= 128) launch_select<2>(s, part, KS, P, NP, b_r, topk_ids, topk_w, status, st);
+    else if (s.E <= 256) launch_select<4>(s, part, KS, P, NP, b_r, topk_ids, topk_w, status, st);
+    else if (s.E <= 512) launch_select<8>(s, part, KS, P, NP, b_r, topk_ids, topk_w, status, st);
+    else launch_select<16>(s, part, KS, P, NP, b_r, topk_ids, topk_w, status, st);
     return hipGetLastError();
 }
 
