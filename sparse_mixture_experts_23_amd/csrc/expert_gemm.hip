@@ -14,8 +14,10 @@
 //     and the up value of the same output element and applies SiLU(g) * u in
 //     registers before a single bf16 store.
 //   * main kernel (K % 64 == 0): 8 waves (2 per SIMD), K tiles of 64 streamed
-//     into two LDS stages by gfx950's direct global->LDS loads, the steady-state
-//     K tile written as one scheduled asm block; see gemm_bf16_asm_kernel.
+//     into LDS by gfx950's direct global->LDS loads (two activation stages,
+//     three weight stages, so the weights stream two K tiles ahead), the
+//     steady-state K tile written as one scheduled asm block; see
+//     gemm_bf16_asm_kernel.
 //   * fallback kernel (any K % 8 == 0): 4 waves, register-staged loads, K tiles
 //     of 64 double-buffered in LDS, zero-filled K tail.
 //   * LDS rows are stored with their 16-byte chunks XOR-swizzled by row, so the
@@ -325,19 +327,22 @@ __device__ __forceinline__ void lds_barrier_reads_done() {
 // Workgroup tile 256 rows x BN output columns (GEMM1: BN = 128 gate + 128 up
 // weight rows in one B tile; GEMM2: BN = 256), 8 waves = 2 per SIMD in a 4 x 2
 // grid, each wave owning 64 rows x 4 B fragments of 32 columns (8 accumulators of
-// 32x32, held in AGPRs).  K advances in tiles of 64 through two LDS stages of
-// 2 x 32 KB, filled by gfx950's direct global->LDS loads (8 per wave per tile,
-// one full 128-byte line per row segment).
+// 32x32, held in AGPRs).  K advances in tiles of 64 through LDS: two 32 KB
+// activation stages and three 32 KB weight stages (all 160 KB), filled by
+// gfx950's direct global->LDS loads (8 per wave per tile, one full 128-byte
+// line per row segment); the weights, the operand streamed from HBM, run two K
+// tiles ahead.
 //
 // The steady-state K tile is one asm block with a fixed instruction order; the
 // compiler, left to itself, reuses operand registers and serialises LDS reads
 // with the MFMAs that consume them.  Per substep of K 16 the wave waits for its
 // operands, then alternates one MFMA with one LDS read of the next substep's
 // operands.  Before the last substep it waits for its own loads of the next tile
-// and meets the other waves at a barrier (after which the stage just consumed is
-// free), then alternates the last MFMAs with the refill loads of tile kt + 2 and
-// the reads of the next tile's first operands.  Every LDS read the block issues
-// is waited for inside the block.
+// (the newest 4, the weights of tile kt + 2, may stay in flight) and meets the
+// other waves at a barrier (after which the stages just consumed are free), then
+// alternates the last MFMAs with the refill loads (activations of tile kt + 2,
+// weights of tile kt + 3) and the reads of the next tile's first operands.
+// Every LDS read the block issues is waited for inside the block.
 //
 // The MFMAs take the weight fragment as their first operand (C^T = B^T A^T), so a
 // lane's accumulator holds one output row and, per group of 4 registers, 4
@@ -367,7 +372,7 @@ __device__ __forceinline__ void lds_barrier_reads_done() {
     MOE_MF(c7, P##a1, P##b3)
 #define MOE_LASTSUB                                                                      \
     "s_waitcnt lgkmcnt(0)\n\t"                                                           \
-    "s_waitcnt vmcnt(0)\n\t"                                                             \
+    "s_waitcnt vmcnt(4)\n\t"                                                             \
     "s_barrier\n\t"                                                                      \
     MOE_M0(ldsA, "0") MOE_MF(c0, ya0, yb0) MOE_LD(vo0, sa)                                  \
     MOE_M0(ldsA, "8192") MOE_MF(c1, ya1, yb0) MOE_LD(vo1, sa) MOE_DSR(xa0, na0, "0")        \
@@ -426,7 +431,7 @@ __device__ __forceinline__ void gemm_tile_asm(floatx16_t (&c)[8], bf16x8_t (&x)[
     MOE_DSRI(Q##b3, RB, ob3)
 #define MOE_LASTSUB_HALF                                                                 \
     "s_waitcnt lgkmcnt(0)\n\t"                                                           \
-    "s_waitcnt vmcnt(0)\n\t"                                                             \
+    "s_waitcnt vmcnt(4)\n\t"                                                             \
     "s_barrier\n\t"                                                                      \
     MOE_M0(ldsA, "0") MOE_MF(c0, ya0, yb0) MOE_LD(vo0, sa)                                  \
     MOE_M0(ldsA, "8192") MOE_DSR(xa0, na0, "0") MOE_LD(vo1, sa)                             \
@@ -472,7 +477,7 @@ __device__ __forceinline__ void gemm_tile_asm_loads_only(floatx16_t (&c)[8], bf1
                                                          uint32_t ldsB) {
     uint32_t saved_m0;
     asm volatile("s_mov_b32 %[sv], m0\n\t"
-                 "s_waitcnt vmcnt(0)\n\t"
+                 "s_waitcnt vmcnt(4)\n\t"
                  "s_barrier\n\t"
                  MOE_DMA(vo0, sa, ldsA, "0") MOE_DMA(vo1, sa, ldsA, "8192") MOE_DMA(vo2, sa, ldsA, "16384")
                  MOE_DMA(vo3, sa, ldsA, "24576") MOE_DMA(vo4, sb0, ldsB, "0") MOE_DMA(vo5, sb1, ldsB, "8192")
@@ -513,8 +518,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* _
     constexpr int OB3 = (NOPS == 2 ? BN + 32 : 96) * 128;
     constexpr int OBF[4] = {0, OB1, OB2, OB3};
 
-    __shared__ uint4 sA[2 * STAGE / 16];
-    __shared__ uint4 sB[2 * STAGE / 16];
+    __shared__ uint4 sA[2 * STAGE / 16];   // activation K tiles: 2 stages
+    __shared__ uint4 sB[3 * STAGE / 16];   // weight K tiles: 3 stages (all 160 KB of LDS)
 
     TileCoord tc;
     const int NT = (N + BN - 1) / BN;
@@ -558,10 +563,13 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* _
         bbase[i] = op ? Bu : Bg;
     }
     const uint32_t sA_addr = lds_byte_addr(sA), sB_addr = lds_byte_addr(sB);
-    auto load_tile = [&](int kt, int stage) {
-        const uint32_t la = sA_addr + stage * STAGE + wave * 1024, lb = sB_addr + stage * STAGE + wave * 1024;
+    auto load_a = [&](int kt, int stage) {
+        const uint32_t la = sA_addr + stage * STAGE + wave * 1024;
 #pragma unroll
         for (int i = 0; i < 4; ++i) dma16_async(At + (int64_t)kt * BK + vo[i] / 2, la + i * 8192);
+    };
+    auto load_b = [&](int kt, int stage) {
+        const uint32_t lb = sB_addr + stage * STAGE + wave * 1024;
 #pragma unroll
         for (int i = 0; i < 4; ++i) dma16_async(bbase[i] + (int64_t)kt * BK + vo[4 + i] / 2, lb + i * 8192);
     };
@@ -572,9 +580,18 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* _
 #pragma unroll
         for (int v = 0; v < 16; ++v) c[q][v] = 0.f;
 
+    // K tile kt lives in activation stage kt % 2 and weight stage kt % 3.  The
+    // refill at the end of tile kt loads activations of kt + 2 and weights of
+    // kt + 3 (the last tile again once kt + 3 runs past the end: it lands in a
+    // stage nobody reads any more), so weights stream two tiles ahead.
     const int KT = kt_end - kt_begin;
-    load_tile(0, 0);
-    if (KT > 1) load_tile(1, 1);
+    load_a(0, 0);
+    load_b(0, 0);
+    if (KT > 1) {
+        load_a(1, 1);
+        load_b(1, 1);
+    }
+    if (KT > 2) load_b(2, 2);
 
     const int lrow = lane % 32, lhalf = lane / 32;
     const int rswz = lds_swz(lrow);
@@ -587,9 +604,9 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* _
         ra[s] = sA_addr + ((wm * WM + lrow) * 8 + cc) * 16;
         rb[s] = sB_addr + ((wn * WN + lrow) * 8 + cc) * 16;
     }
-    auto read_sub = [&](int stage, int s, bf16x8_t (&o)[6]) {
-        const char* pa = reinterpret_cast<const char*>(sA) + (ra[s] - sA_addr) + stage * STAGE;
-        const char* pb = reinterpret_cast<const char*>(sB) + (rb[s] - sB_addr) + stage * STAGE;
+    auto read_sub = [&](int sta, int stb, int s, bf16x8_t (&o)[6]) {
+        const char* pa = reinterpret_cast<const char*>(sA) + (ra[s] - sA_addr) + sta * STAGE;
+        const char* pb = reinterpret_cast<const char*>(sB) + (rb[s] - sB_addr) + stb * STAGE;
         o[0] = as_bf16x8(*reinterpret_cast<const uint4*>(pa));
         o[1] = as_bf16x8(*reinterpret_cast<const uint4*>(pa + 4096));
 #pragma unroll
@@ -605,56 +622,66 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* _
             c[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o[2 + q / 2], o[q % 2], c[q], 0, 0, 0);
     };
 
-    wait_tiles<8>(KT > 1 ? 1 : 0);
+    // tile 0 must have landed; the loads issued after it may still be in flight
+    if (KT > 2) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    else if (KT == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier_reads_done();
     bf16x8_t x[6];
-    read_sub(0, 0, x);
+    read_sub(0, 0, 0, x);
     // steady state: one loop per wave mode (the mode is uniform across the wave)
-    int kt = 0;
+    int kt = 0, sb = 0;   // sb = kt % 3
 #define MOE_TILE_ARGS(kt_)                                                                               \
     const uint32_t so = ((kt_) & 1) * STAGE, no = STAGE - so;                                            \
-    const int64_t koff = (int64_t)((kt_) + 2) * BK;
+    const uint32_t sbo = sb * STAGE, nbo = (sb == 2 ? 0 : sb + 1) * STAGE;                               \
+    const int64_t koff = (int64_t)((kt_) + 2) * BK;                                                      \
+    const int64_t kbo = (int64_t)min((kt_) + 3, KT - 1) * BK;
     if (mode == 2) {
         for (; kt + 2 < KT; ++kt) {
             MOE_TILE_ARGS(kt)
-            gemm_tile_asm<OB1, OB2, OB3>(c, x, ra[1] + so, rb[1] + so, ra[2] + so, rb[2] + so, ra[3] + so,
-                                         rb[3] + so, ra[0] + no, rb[0] + no, vo, At + koff, bbase[0] + koff,
-                                         bbase[1] + koff, bbase[2] + koff, bbase[3] + koff,
-                                         sA_addr + so + wave * 1024, sB_addr + so + wave * 1024);
+            gemm_tile_asm<OB1, OB2, OB3>(c, x, ra[1] + so, rb[1] + sbo, ra[2] + so, rb[2] + sbo, ra[3] + so,
+                                         rb[3] + sbo, ra[0] + no, rb[0] + nbo, vo, At + koff, bbase[0] + kbo,
+                                         bbase[1] + kbo, bbase[2] + kbo, bbase[3] + kbo,
+                                         sA_addr + so + wave * 1024, sB_addr + sbo + wave * 1024);
+            sb = sb == 2 ? 0 : sb + 1;
         }
     } else if (mode == 1) {
         for (; kt + 2 < KT; ++kt) {
             MOE_TILE_ARGS(kt)
-            gemm_tile_asm_half<OB1, OB2, OB3>(c, x, ra[1] + so, rb[1] + so, ra[2] + so, rb[2] + so, ra[3] + so,
-                                              rb[3] + so, ra[0] + no, rb[0] + no, vo, At + koff, bbase[0] + koff,
-                                              bbase[1] + koff, bbase[2] + koff, bbase[3] + koff,
-                                              sA_addr + so + wave * 1024, sB_addr + so + wave * 1024);
+            gemm_tile_asm_half<OB1, OB2, OB3>(c, x, ra[1] + so, rb[1] + sbo, ra[2] + so, rb[2] + sbo, ra[3] + so,
+                                              rb[3] + sbo, ra[0] + no, rb[0] + nbo, vo, At + koff, bbase[0] + kbo,
+                                              bbase[1] + kbo, bbase[2] + kbo, bbase[3] + kbo,
+                                              sA_addr + so + wave * 1024, sB_addr + sbo + wave * 1024);
+            sb = sb == 2 ? 0 : sb + 1;
         }
     } else {
         for (; kt + 2 < KT; ++kt) {
             MOE_TILE_ARGS(kt)
             (void)no;
-            gemm_tile_asm_loads_only(c, x, vo, At + koff, bbase[0] + koff, bbase[1] + koff, bbase[2] + koff,
-                                     bbase[3] + koff, sA_addr + so + wave * 1024, sB_addr + so + wave * 1024);
+            (void)nbo;
+            gemm_tile_asm_loads_only(c, x, vo, At + koff, bbase[0] + kbo, bbase[1] + kbo, bbase[2] + kbo,
+                                     bbase[3] + kbo, sA_addr + so + wave * 1024, sB_addr + sbo + wave * 1024);
+            sb = sb == 2 ? 0 : sb + 1;
         }
     }
 #undef MOE_TILE_ARGS
     // the last (up to) two tiles: nothing left to load
     for (; kt < KT; ++kt) {
-        const int stage = kt & 1;
+        const int sa = kt & 1, sbn = sb == 2 ? 0 : sb + 1;
         bf16x8_t y[6];
-        read_sub(stage, 1, y);
+        read_sub(sa, sb, 1, y);
         mma(x);
-        read_sub(stage, 2, x);
+        read_sub(sa, sb, 2, x);
         mma(y);
-        read_sub(stage, 3, y);
+        read_sub(sa, sb, 3, y);
         mma(x);
         if (kt + 1 < KT) {
             wait_tiles<8>(0);
             lds_barrier_reads_done();
-            read_sub(stage ^ 1, 0, x);
+            read_sub(sa ^ 1, sbn, 0, x);
         }
         mma(y);
+        sb = sbn;
     }
 
     // Epilogue: the lane holds output row (.. + lrow) of accumulator q and, in
