@@ -513,6 +513,85 @@ __device__ __forceinline__ void gemm_tile_asm_loads_only(floatx16_t (&c)[8], bf1
                  : "memory");
 }
 
+// Thin tiles: the last row tile of a group that also has full tiles, holding at
+// most 64 valid rows.  Its weight tiles are the ones its sibling tiles read at
+// about the same time, so they mostly hit in L2 and the K loop is bound by load
+// latency, not bandwidth: it gets a deeper prefetch.  (A group of at most 64 rows
+// in all streams its weights from HBM alone; there the standard pipeline was as
+// fast, and faster for the layer as a whole, so it keeps it.)  The rows are split
+// into two 32-row halves over the waves of A row slots 0 and 1, so four waves on
+// four SIMDs each run the A-fragment-0 MFMAs; the others only load.
+// An activation tile needs just 8 KB, so the activation stages become four 8 KB
+// slots and the freed 32 KB holds a fourth weight stage: both operands stream
+// three K tiles ahead.  Block kt loads the weights of kt + 3 in its first substep
+// and the activations of kt + 3 (one load per wave) in its second; at its barrier
+// the wave's loads of tile kt + 1 are complete when at most the 10 issued after
+// them (tiles kt + 2 and kt + 3) are in flight.
+#define MOE_SUBSTEP_HALF_A1(P, Q, RA, RB)                                                \
+    "s_waitcnt lgkmcnt(0)\n\t"                                                           \
+    MOE_M0(ldsA, "0") MOE_MF(c0, P##a0, P##b0) MOE_LD(vo0, sa) MOE_DSR(Q##a0, RA, "0")   \
+    MOE_MF(c2, P##a0, P##b1) MOE_DSR(Q##b0, RB, "0")                                     \
+    MOE_MF(c4, P##a0, P##b2) MOE_DSRI(Q##b1, RB, ob1)                                    \
+    MOE_MF(c6, P##a0, P##b3) MOE_DSRI(Q##b2, RB, ob2)                                    \
+    MOE_DSRI(Q##b3, RB, ob3)
+#define MOE_LASTSUB_HALF_THIN                                                            \
+    "s_waitcnt lgkmcnt(0)\n\t"                                                           \
+    "s_waitcnt vmcnt(10)\n\t"                                                            \
+    "s_barrier\n\t"                                                                      \
+    MOE_MF(c0, ya0, yb0) MOE_DSR(xa0, na0, "0")                                          \
+    MOE_MF(c2, ya0, yb1) MOE_DSR(xb0, nb0, "0")                                          \
+    MOE_MF(c4, ya0, yb2) MOE_DSRI(xb1, nb0, ob1) MOE_DSRI(xb2, nb0, ob2)                 \
+    MOE_MF(c6, ya0, yb3) MOE_DSRI(xb3, nb0, ob3)                                         \
+    "s_waitcnt lgkmcnt(0)\n\t"
+
+template <int OB1, int OB2, int OB3>
+__device__ __forceinline__ void gemm_tile_asm_thin(floatx16_t (&c)[8], bf16x8_t (&x)[6], uint32_t ra1, uint32_t rb1,
+                                                   uint32_t ra2, uint32_t rb2, uint32_t ra3, uint32_t rb3,
+                                                   uint32_t na0, uint32_t nb0, const uint32_t (&vo)[8],
+                                                   const void* sa, const void* sb0, const void* sb1,
+                                                   const void* sb2, const void* sb3, uint32_t ldsA, uint32_t ldsB) {
+    bf16x8_t y[6];
+    uint32_t saved_m0;
+    asm volatile("s_mov_b32 %[sv], m0\n\t"
+                 MOE_SUBSTEP_HALF_B(x, y, ra1, rb1)
+                 MOE_SUBSTEP_HALF_A1(y, x, ra2, rb2)
+                 MOE_SUBSTEP_HALF(x, y, ra3, rb3)
+                 MOE_LASTSUB_HALF_THIN
+                 "s_mov_b32 m0, %[sv]"
+                 : [c0] "+a"(c[0]), [c1] "+a"(c[1]), [c2] "+a"(c[2]), [c3] "+a"(c[3]), [c4] "+a"(c[4]),
+                   [c5] "+a"(c[5]), [c6] "+a"(c[6]), [c7] "+a"(c[7]), [xa0] "+v"(x[0]), [xa1] "+v"(x[1]),
+                   [xb0] "+v"(x[2]), [xb1] "+v"(x[3]), [xb2] "+v"(x[4]), [xb3] "+v"(x[5]), [ya0] "=&v"(y[0]),
+                   [ya1] "=&v"(y[1]), [yb0] "=&v"(y[2]), [yb1] "=&v"(y[3]), [yb2] "=&v"(y[4]), [yb3] "=&v"(y[5]),
+                   [sv] "=&s"(saved_m0)
+                 : [ra1] "v"(ra1), [rb1] "v"(rb1), [ra2] "v"(ra2), [rb2] "v"(rb2), [ra3] "v"(ra3), [rb3] "v"(rb3),
+                   [na0] "v"(na0), [nb0] "v"(nb0), [ob1] "i"(OB1), [ob2] "i"(OB2), [ob3] "i"(OB3),
+                   [vo0] "v"(vo[0]), [vo1] "v"(vo[1]), [vo2] "v"(vo[2]), [vo3] "v"(vo[3]), [vo4] "v"(vo[4]),
+                   [vo5] "v"(vo[5]), [vo6] "v"(vo[6]), [vo7] "v"(vo[7]), [sa] "s"(sa), [sb0] "s"(sb0),
+                   [sb1] "s"(sb1), [sb2] "s"(sb2), [sb3] "s"(sb3), [ldsA] "s"(ldsA), [ldsB] "s"(ldsB)
+                 : "memory");
+}
+
+__device__ __forceinline__ void gemm_tile_asm_loads_only_thin(floatx16_t (&c)[8], bf16x8_t (&x)[6],
+                                                              const uint32_t (&vo)[8], const void* sa,
+                                                              const void* sb0, const void* sb1, const void* sb2,
+                                                              const void* sb3, uint32_t ldsA, uint32_t ldsB) {
+    uint32_t saved_m0;
+    asm volatile("s_mov_b32 %[sv], m0\n\t"
+                 MOE_DMA(vo4, sb0, ldsB, "0") MOE_DMA(vo5, sb1, ldsB, "8192")
+                 MOE_DMA(vo6, sb2, ldsB, "16384") MOE_DMA(vo7, sb3, ldsB, "24576")
+                 MOE_DMA(vo0, sa, ldsA, "0")
+                 "s_waitcnt vmcnt(10)\n\t"
+                 "s_barrier\n\t"
+                 "s_mov_b32 m0, %[sv]"
+                 : [c0] "+a"(c[0]), [c1] "+a"(c[1]), [c2] "+a"(c[2]), [c3] "+a"(c[3]), [c4] "+a"(c[4]),
+                   [c5] "+a"(c[5]), [c6] "+a"(c[6]), [c7] "+a"(c[7]), [xa0] "+v"(x[0]), [xa1] "+v"(x[1]),
+                   [xb0] "+v"(x[2]), [xb1] "+v"(x[3]), [xb2] "+v"(x[4]), [xb3] "+v"(x[5]), [sv] "=&s"(saved_m0)
+                 : [vo0] "v"(vo[0]), [vo4] "v"(vo[4]), [vo5] "v"(vo[5]), [vo6] "v"(vo[6]), [vo7] "v"(vo[7]),
+                   [sa] "s"(sa), [sb0] "s"(sb0), [sb1] "s"(sb1), [sb2] "s"(sb2), [sb3] "s"(sb3), [ldsA] "s"(ldsA),
+                   [ldsB] "s"(ldsB)
+                 : "memory");
+}
+
 // Requires K % 64 == 0, N % 8 == 0 and 512 K < 2^32 (32-bit load offsets).
 // K split: the grid is S copies of a tile grid of gridDim.x / S workgroups (a
 // multiple of 8, so every copy keeps the XCD order); copy s sums the K tiles
@@ -539,8 +618,10 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* _
     constexpr int OB3 = (NOPS == 2 ? BN + 32 : 96) * 128;
     constexpr int OBF[4] = {0, OB1, OB2, OB3};
 
-    __shared__ uint4 sA[2 * STAGE / 16];   // activation K tiles: 2 stages
-    __shared__ uint4 sB[3 * STAGE / 16];   // weight K tiles: 3 stages (all 160 KB of LDS)
+    // activation K tiles: 2 stages, then weight K tiles: 3 stages (all 160 KB of LDS)
+    __shared__ uint4 lds[5 * STAGE / 16];
+    uint4* const sA = lds;
+    uint4* const sB = lds + 2 * STAGE / 16;
 
     TileCoord tc;
     const int NT = (N + BN - 1) / BN;
@@ -554,6 +635,9 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* _
     const int tid = threadIdx.x, lane = tid % 64;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
     const int wm = wave / WGN, wn = wave % WGN;
+    // thin: a last row tile of <= 64 rows behind full tiles of the same group
+    const bool thin = tc.row_end - tc.row_start <= 64 && tc.row_start > (offsets ? offsets[tc.g] : 0);
+    const int arow = thin ? 32 * wm : WM * wm;   // first tile row of this wave's A fragment 0
     const int n0 = tc.nt * BN;
     const int64_t wstride = (int64_t)N * K;
     const int64_t k0 = (int64_t)kt_begin * BK;
@@ -594,6 +678,17 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* _
 #pragma unroll
         for (int i = 0; i < 4; ++i) dma16_async(bbase[i] + (int64_t)kt * BK + vo[4 + i] / 2, lb + i * 8192);
     };
+    // thin tiles: activation tile t in 8 KB slot t % 4; weight stage 3 is the upper
+    // half of the activation area (byte offset from weight stage 0: -STAGE)
+    auto thin_boff = [&](int t) -> int { return (t & 3) == 3 ? -STAGE : (t & 3) * STAGE; };
+    auto load_a_thin = [&](int kt, int t) {
+        dma16_async(At + (int64_t)kt * BK + vo[0] / 2, sA_addr + (t & 3) * 8192 + wave * 1024);
+    };
+    auto load_b_thin = [&](int kt, int t) {
+        const uint32_t lb = sB_addr + thin_boff(t) + wave * 1024;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma16_async(bbase[i] + (int64_t)kt * BK + vo[4 + i] / 2, lb + i * 8192);
+    };
 
     floatx16_t c[8];
 #pragma unroll
@@ -603,13 +698,23 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* _
 
     // K tile kt lives in activation stage kt % 2 and weight stage kt % 3.  Block
     // kt loads the weights of kt + 2 in its first substep and the activations of
-    // kt + 2 after its barrier, so weights stream ~2 tiles ahead.
+    // kt + 2 after its barrier, so weights stream ~2 tiles ahead.  Thin tiles:
+    // activation slot kt % 4, weight stage kt % 4, both loaded 3 tiles ahead.
     const int KT = kt_end - kt_begin;
-    load_a(0, 0);
-    load_b(0, 0);
-    if (KT > 1) {
-        load_a(1, 1);
-        load_b(1, 1);
+    if (thin) {
+        // tiles 0..2 of both operands (indices past the end reload the last tile
+        // into a slot nobody reads, so the wait counts below always hold)
+        for (int t = 0; t < 3; ++t) {
+            load_b_thin(min(t, KT - 1), t);
+            load_a_thin(min(t, KT - 1), t);
+        }
+    } else {
+        load_a(0, 0);
+        load_b(0, 0);
+        if (KT > 1) {
+            load_a(1, 1);
+            load_b(1, 1);
+        }
     }
 
     const int lrow = lane % 32, lhalf = lane / 32;
@@ -620,20 +725,25 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* _
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         const int cc = (2 * s + lhalf) ^ rswz;
-        ra[s] = sA_addr + ((wm * WM + lrow) * 8 + cc) * 16;
+        ra[s] = sA_addr + ((arow + lrow) * 8 + cc) * 16;   // arow % 16 == 0: same swizzle
         rb[s] = sB_addr + ((wn * WN + lrow) * 8 + cc) * 16;
     }
-    auto read_sub = [&](int sta, int stb, int s, bf16x8_t (&o)[6]) {
-        const char* pa = reinterpret_cast<const char*>(sA) + (ra[s] - sA_addr) + sta * STAGE;
-        const char* pb = reinterpret_cast<const char*>(sB) + (rb[s] - sB_addr) + stb * STAGE;
+    // aoff / boff: byte offset of the stage from activation / weight stage 0
+    auto read_sub = [&](int aoff, int boff, int s, bf16x8_t (&o)[6]) {
+        const char* base = reinterpret_cast<const char*>(lds);
+        const char* pa = base + (int)(ra[s] - sA_addr) + aoff;
+        const char* pb = base + (int)(rb[s] - sA_addr) + boff;
         o[0] = as_bf16x8(*reinterpret_cast<const uint4*>(pa));
         o[1] = as_bf16x8(*reinterpret_cast<const uint4*>(pa + 4096));
 #pragma unroll
         for (int f = 0; f < 4; ++f) o[2 + f] = as_bf16x8(*reinterpret_cast<const uint4*>(pb + OBF[f]));
     };
+    auto aoff_of = [&](int t) -> int { return thin ? (t & 3) * 8192 : (t & 1) * STAGE; };
+    auto boff_of = [&](int t) -> int { return thin ? thin_boff(t) : (t % 3) * STAGE; };
     // valid rows of this wave's 64: > 32 -> all MFMAs, 1..32 -> A fragment 0 only, 0 -> none
-    const int64_t wave_rows = tc.row_end - (tc.row_start + wm * WM);
-    const int mode = wave_rows > 32 ? 2 : (wave_rows > 0 ? 1 : 0);
+    // (thin tiles: 32 rows per wave, so never more than A fragment 0)
+    const int64_t wave_rows = tc.row_end - (tc.row_start + arow);
+    const int mode = thin ? (wave_rows > 0 ? 1 : 0) : (wave_rows > 32 ? 2 : (wave_rows > 0 ? 1 : 0));
     // accumulator q = (A fragment q % 2, B fragment q / 2); weight fragment first (C^T)
     auto mma = [&](const bf16x8_t (&o)[6]) {
 #pragma unroll
@@ -642,13 +752,43 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* _
     };
 
     // tile 0 must have landed; the loads issued after it may still be in flight
-    if (KT > 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    if (thin) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+    else if (KT > 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier_reads_done();
     bf16x8_t x[6];
     read_sub(0, 0, 0, x);
     // steady state: one loop per wave mode (the mode is uniform across the wave)
     int kt = 0, sb = 0;   // sb = kt % 3
+    if (thin) {
+        // every block but the last; loads past the last tile reload it into a free slot
+#define MOE_THIN_ARGS(kt_)                                                                              \
+    const uint32_t so = ((kt_) & 3) * 8192, no = (((kt_) + 1) & 3) * 8192;                              \
+    const uint32_t sbo = (uint32_t)thin_boff(kt_), nbo = (uint32_t)thin_boff((kt_) + 1);                \
+    const int64_t koff = (int64_t)min((kt_) + 3, KT - 1) * BK;                                          \
+    const uint32_t ldsA = sA_addr + (((kt_) + 3) & 3) * 8192 + wave * 1024;                             \
+    const uint32_t ldsB = sB_addr + (uint32_t)thin_boff((kt_) + 3) + wave * 1024;
+        if (mode == 1) {
+            for (; kt + 1 < KT; ++kt) {
+                MOE_THIN_ARGS(kt)
+                gemm_tile_asm_thin<OB1, OB2, OB3>(c, x, ra[1] + so, rb[1] + sbo, ra[2] + so, rb[2] + sbo,
+                                                  ra[3] + so, rb[3] + sbo, ra[0] + no, rb[0] + nbo, vo, At + koff,
+                                                  bbase[0] + koff, bbase[1] + koff, bbase[2] + koff,
+                                                  bbase[3] + koff, ldsA, ldsB);
+            }
+        } else {
+            for (; kt + 1 < KT; ++kt) {
+                MOE_THIN_ARGS(kt)
+                (void)so;
+                (void)no;
+                (void)sbo;
+                (void)nbo;
+                gemm_tile_asm_loads_only_thin(c, x, vo, At + koff, bbase[0] + koff, bbase[1] + koff,
+                                              bbase[2] + koff, bbase[3] + koff, ldsA, ldsB);
+            }
+        }
+#undef MOE_THIN_ARGS
+    } else {
 #define MOE_TILE_ARGS(kt_)                                                                               \
     const uint32_t so = ((kt_) & 1) * STAGE, no = STAGE - so;                                            \
     const uint32_t sbo = sb * STAGE, nbo = (sb == 2 ? 0 : sb + 1) * STAGE;                               \
@@ -684,24 +824,27 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* _
         }
     }
 #undef MOE_TILE_ARGS
+    }
     // the last (up to) two tiles: nothing left to load
     for (; kt < KT; ++kt) {
-        const int sa = kt & 1, sbn = sb == 2 ? 0 : sb + 1;
+        const int ao = aoff_of(kt), bo = boff_of(kt);
         bf16x8_t y[6];
-        read_sub(sa, sb, 1, y);
+        read_sub(ao, bo, 1, y);
         mma(x);
-        read_sub(sa, sb, 2, x);
+        read_sub(ao, bo, 2, x);
         mma(y);
-        read_sub(sa, sb, 3, y);
+        read_sub(ao, bo, 3, y);
         mma(x);
         if (kt + 1 < KT) {
             wait_tiles<8>(0);
             lds_barrier_reads_done();
-            read_sub(sa ^ 1, sbn, 0, x);
+            read_sub(aoff_of(kt + 1), boff_of(kt + 1), 0, x);
         }
         mma(y);
-        sb = sbn;
     }
+    // thin tiles may still have loads past the last tile in flight: they must land
+    // before the workgroup's LDS is released
+    if (thin) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // Epilogue: the lane holds output row (.. + lrow) of accumulator q and, in
     // register group g, columns 8 g + 4 lhalf + 0..3 of its 32-column fragment.
@@ -710,7 +853,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* _
         const int i = q % 2, f = q / 2;
         const int o = NOPS == 2 ? f / NTW : 0, j = NOPS == 2 ? f % NTW : f;
         if (SWIGLU && o == 1) continue;
-        const int64_t row = tc.row_start + wm * WM + i * 32 + lrow;
+        if (thin && i == 1) continue;   // rows of the next wave's half
+        const int64_t row = tc.row_start + arow + i * 32 + lrow;
         if (row >= tc.row_end) continue;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {

@@ -188,6 +188,8 @@ RAGGED = MoEConfig("ragged_bf16", T=2000, d=328, m=200, E=4, k=2, dtype="bf16", 
     # ragged groups, drops, partial column tiles in both GEMMs and a shared expert
     MoEConfig("kernel_steady_state", T=1500, d=320, m=448, E=6, k=2, dtype="bf16", gate_mode=0, cf=(5, 4),
               bias="zipf", m_shared=192, cfg_id=23),
+    # E > 64: router scores on the expert-GEMM kernel; 300 rows end in a 44-row tile
+    MoEConfig("router_thin_tail", T=300, d=1024, m=64, E=100, k=4, dtype="bf16", gate_mode=0, cf=None, cfg_id=26),
     # router with E < 8 experts over two K ranges of 4096 (d > 4096), T not a multiple of 16
     MoEConfig("router_two_k_ranges", T=101, d=4160, m=64, E=6, k=2, dtype="bf16", gate_mode=1, cf=None,
               cfg_id=24),
@@ -262,3 +264,41 @@ def test_run_twice_bitwise_and_causal_prefix():
     sp = api.make_shape(tp, cfg.d, cfg.m, cfg.E, cfg.k, shape.capacity, cfg.gate_mode, cfg.torch_dtype)
     c = api.forward(sp, inp.x[:tp].contiguous(), inp.w_r, inp.b_r, inp.w_gate, inp.w_up, inp.w_down)
     assert torch.equal(c.slot, a.slot[:tp])
+
+
+# ---------------------------------------------------------------------------
+# expert GEMMs on chosen group sizes: small groups, groups whose last row tile
+# holds 1..64 rows behind full tiles (the thin-tile pipeline), short K
+# ---------------------------------------------------------------------------
+
+THIN_GROUPS = [1, 5, 31, 33, 64, 0, 257, 288, 300, 320, 517, 552]
+
+
+@pytest.mark.parametrize("d,m", [(64, 192), (128, 64), (192, 2048), (1088, 2176)])
+def test_expert_gemms_thin_tiles(d, m):
+    """Both expert GEMMs through the C-ABI on fixed group sizes.  These include
+    groups of at most 64 rows, groups that end in a row tile of 1, 32, 40, 44, 5
+    or 64 rows behind full tiles, an empty group, K of 1..34 tiles of 64, and a
+    down projection long enough to be split over K.  Every output row is checked
+    against the oracle's SwiGLU expert."""
+    E = len(THIN_GROUPS)
+    A = sum(THIN_GROUPS)
+    cfg = MoEConfig("thin_tiles", T=A, d=d, m=m, E=E, k=1, dtype="bf16", gate_mode=0, cf=None, cfg_id=25)
+    log(f"[parity] expert GEMMs, groups {THIN_GROUPS}, d={d} m={m}")
+    inp = make_inputs(cfg, 0, DEV)
+    shape = shape_of(cfg)
+    offs = np.concatenate([[0], np.cumsum(THIN_GROUPS)]).astype(np.int32)
+    offsets = torch.from_numpy(offs).to(DEV)
+    h = api.expert_gemm1(shape, inp.x, offsets, inp.w_gate, inp.w_up)
+    H = api.expert_gemm2(shape, h, offsets, inp.w_down)
+    torch.cuda.synchronize()
+    x64, H64 = np64(inp.x), np64(H)
+    worst = 0.0
+    for g in range(E):
+        lo, hi = int(offs[g]), int(offs[g + 1])
+        if hi == lo:
+            continue
+        ref = O.swiglu_ffn(x64[lo:hi], np64(inp.w_gate[g]), np64(inp.w_up[g]), np64(inp.w_down[g]),
+                           round_h_bf16=True)
+        worst = max(worst, check_output(H64[lo:hi], ref, BF16_TOL, f"group {g} ({hi - lo} rows)"))
+    log(f"[parity] expert GEMMs d={d} m={m}: ok  max rel err {worst:.2e}")
