@@ -38,7 +38,7 @@ METRIC = "MoE-layer tokens/sec on 1 MI355X (Mixtral shape); expert-GEMM % of MFM
 # the bytes-per-KiB that the same counter reports for a plain device copy of known
 # size (`bench.py --copy-calibration`).  Valid only for the GEMM source it was
 # taken on: reported as null once expert_gemm.hip differs from that hash.
-GEMM1_TRAFFIC = {"bytes": 7443403218, "source_sha256": "1b5e15b7b357cfa3e8757f3be7da48758a6da7a73ed63b7a2d228a81b6228018"}
+GEMM1_TRAFFIC = {"bytes": 6548048402, "source_sha256": "004d66eadeeb5e8d0ed9d376d535fdf29a97137c911deaaee407b956209c317c"}
 GEMM_SOURCE = os.path.join(ROOT, "sparse_mixture_experts_23_amd", "csrc", "expert_gemm.hip")
 
 

@@ -26,34 +26,56 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     const int myrow = lane < k ? row_of[t * k + lane] : -1;
     const float myw = lane < k ? w[t * k + lane] : 0.f;
     if (VEC4) {
+        // U column chunks of 64 float4 per pass: a path's U loads (and H1's) are in
+        // flight together; per element the sum is still s + a0 h0 + a1 h1 + ...
+        constexpr int U = 4;
         const int nv = d / 4;
         const float4* H4 = reinterpret_cast<const float4*>(H);
+        const float4* H14 = reinterpret_cast<const float4*>(H1);
         const float4* S4 = reinterpret_cast<const float4*>(shared_out);
         float4* Y4 = reinterpret_cast<float4*>(y);
         // uniform trip count: every lane stays active around lane_value
-        for (int c0 = 0; c0 < nv; c0 += 64) {
-            const int c = c0 + lane;
-            const bool ok = c < nv;
-            float4 acc = (shared_out && ok) ? S4[t * nv + c] : float4{0.f, 0.f, 0.f, 0.f};
+        for (int c0 = 0; c0 < nv; c0 += 64 * U) {
+            float4 acc[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 + u * 64 + lane;
+                acc[u] = (shared_out && c < nv) ? S4[t * nv + c] : float4{0.f, 0.f, 0.f, 0.f};
+            }
             for (int r = 0; r < k; ++r) {
                 const int row = lane_value(myrow, r);
                 const float a = lane_value(myw, r);
-                if (row >= 0 && ok) {
-                    float4 h = H4[(int64_t)row * nv + c];
-                    if (H1) {
-                        const float4 h1 = reinterpret_cast<const float4*>(H1)[(int64_t)row * nv + c];
-                        h.x += h1.x;
-                        h.y += h1.y;
-                        h.z += h1.z;
-                        h.w += h1.w;
+                if (row < 0) continue;   // uniform across the wave
+                float4 h[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int c = c0 + u * 64 + lane;
+                    h[u] = c < nv ? H4[(int64_t)row * nv + c] : float4{0.f, 0.f, 0.f, 0.f};
+                }
+                if (H1) {
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int c = c0 + u * 64 + lane;
+                        const float4 h1 = c < nv ? H14[(int64_t)row * nv + c] : float4{0.f, 0.f, 0.f, 0.f};
+                        h[u].x += h1.x;
+                        h[u].y += h1.y;
+                        h[u].z += h1.z;
+                        h[u].w += h1.w;
                     }
-                    acc.x = fmaf(a, h.x, acc.x);
-                    acc.y = fmaf(a, h.y, acc.y);
-                    acc.z = fmaf(a, h.z, acc.z);
-                    acc.w = fmaf(a, h.w, acc.w);
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    acc[u].x = fmaf(a, h[u].x, acc[u].x);
+                    acc[u].y = fmaf(a, h[u].y, acc[u].y);
+                    acc[u].z = fmaf(a, h[u].z, acc[u].z);
+                    acc[u].w = fmaf(a, h[u].w, acc[u].w);
                 }
             }
-            if (ok) Y4[t * nv + c] = acc;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 + u * 64 + lane;
+                if (c < nv) Y4[t * nv + c] = acc[u];
+            }
         }
     } else {
         for (int c0 = 0; c0 < d; c0 += 64) {

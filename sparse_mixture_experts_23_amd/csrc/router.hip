@@ -174,7 +174,7 @@ __device__ void select_token(const float* __restrict__ row, const float* __restr
 // trip), one value per (row, expert) goes to LDS, and the scores are summed over
 // (K range, wave, row) in a fixed order.
 
-constexpr int VT = 16;             // tokens per workgroup
+constexpr int VT = 8;              // tokens per workgroup
 constexpr int V_THREADS = 512;
 constexpr int V_WAVES = V_THREADS / 64;
 constexpr int V_KR = 8 * V_THREADS;    // K elements per range
