@@ -188,6 +188,9 @@ RAGGED = MoEConfig("ragged_bf16", T=2000, d=328, m=200, E=4, k=2, dtype="bf16", 
     # ragged groups, drops, partial column tiles in both GEMMs and a shared expert
     MoEConfig("kernel_steady_state", T=1500, d=320, m=448, E=6, k=2, dtype="bf16", gate_mode=0, cf=(5, 4),
               bias="zipf", m_shared=192, cfg_id=23),
+    # 34 token blocks x 1000 experts: the dispatch scan runs as its own kernel
+    MoEConfig("dispatch_large_table", T=8500, d=64, m=64, E=1000, k=2, dtype="bf16", gate_mode=0, cf=(5, 4),
+              cfg_id=27),
     # E > 64: router scores on the expert-GEMM kernel; 300 rows end in a 44-row tile
     MoEConfig("router_thin_tail", T=300, d=1024, m=64, E=100, k=4, dtype="bf16", gate_mode=0, cf=None, cfg_id=26),
     # router with E < 8 experts over two K ranges of 4096 (d > 4096), T not a multiple of 16
