@@ -88,6 +88,10 @@ class Stages:
         self.ws_d = api.workspace(shape, L.MOE_WS_DISPATCH, dev)
         self.ws_f = api.workspace(shape, L.MOE_WS_FFN, dev)
         self.ws_s = api.workspace(shape, L.MOE_WS_SHARED, dev) if shape.m_shared else None
+        # load-balance statistics (opt-in diagnostics, timed beside the layer)
+        self.prob_sum = z(E, dt=torch.float32)
+        self.bal = z(2 * E + L.MOE_BAL_COUNT, dt=torch.float32)
+        self.ws_rs = api.workspace(shape, L.MOE_WS_ROUTE_STATS, dev)
 
     def run(self, phase, st):
         s, i, p = self.shape, self.inp, lambda t: None if t is None else t.data_ptr()  # noqa: E731
@@ -108,6 +112,11 @@ class Stages:
                                   self.ws_s.numel(), st)
         elif phase == "combine":
             rc = L.moe_combine(s, p(self.H), p(self.row_of), p(self.w), p(self.s), p(self.y), st)
+        elif phase == "route_stats":
+            rc = L.moe_route_stats(s, p(i.x), p(i.w_r), p(i.b_r), p(self.ids), p(self.w), p(self.status),
+                                   p(self.prob_sum), p(self.ws_rs), self.ws_rs.numel(), st)
+        elif phase == "balance":
+            rc = L.moe_balance(s, p(self.load), p(self.stats), p(self.prob_sum), p(self.bal), st)
         else:
             raise ValueError(phase)
         L.check(rc, phase)
@@ -199,7 +208,8 @@ def main():
     if args.phases != "0":
         stg = Stages(shape, inp)
         st = torch.cuda.current_stream()
-        names = ["route", "dispatch", "gemm1", "gemm2"] + (["shared"] if cfg.m_shared else []) + ["combine"]
+        names = (["route", "dispatch", "gemm1", "gemm2"] + (["shared"] if cfg.m_shared else []) + ["combine"]
+                 + ["route_stats", "balance"])
         for n in names:   # warm each stage once
             stg.run(n, st.cuda_stream)
         torch.cuda.synchronize()

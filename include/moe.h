@@ -86,9 +86,21 @@ enum {
     MOE_STAT_COUNT = 8
 };
 
+/* Indices, after the 2E per-expert values, of the fp32 vector written by
+ * moe_balance. */
+enum {
+    MOE_BAL_VALUE = 0,            /* E * sum_e f_e * p_bar_e (1 at the uniform point) */
+    MOE_BAL_PATH_REJECTION = 1,   /* O / (T k)                                        */
+    MOE_BAL_TOKENS_AFFECTED = 2,  /* tokens with at least one path rejected / T       */
+    MOE_BAL_TOKENS_DROPPED = 3,   /* tokens with every path rejected / T              */
+    MOE_BAL_RHO_MAX = 4,          /* max_e L_e / (T k / E)                            */
+    MOE_BAL_COUNT = 5
+};
+
 /* Which call a workspace is sized for. */
 typedef enum {
-    MOE_WS_DISPATCH = 0, MOE_WS_FFN = 1, MOE_WS_SHARED = 2, MOE_WS_FORWARD = 3, MOE_WS_ROUTE = 4
+    MOE_WS_DISPATCH = 0, MOE_WS_FFN = 1, MOE_WS_SHARED = 2, MOE_WS_FORWARD = 3, MOE_WS_ROUTE = 4,
+    MOE_WS_ROUTE_STATS = 5
 } moe_ws_kind;
 
 /* ---- host helpers ------------------------------------------------------ */
@@ -133,6 +145,31 @@ const char* moe_status_str(int32_t status);
 moe_status moe_route(const moe_shape* shape, const void* x, const float* w_r, const float* b_r,
                      int32_t* topk_ids, float* topk_w, int32_t* status, void* ws, size_t ws_bytes,
                      void* stream);
+
+/* moe_route plus the router's probability mass per expert, the summable half of
+ * the load-balance statistics (ch. 36 §36.4: merge probability sums and token
+ * counts first, then form means over the chosen scope).
+ *   prob_sum [E] fp32 out: sum over the T tokens of the full softmax p_e(x_t)
+ *                          of the (biased) fp32 scores, in a fixed order; a token
+ *                          with a non-finite score adds 0
+ *   ws       >= moe_workspace_bytes(shape, MOE_WS_ROUTE_STATS) bytes: moe_route's
+ *            workspace followed by the [T,E] fp32 probabilities
+ * Other arguments as moe_route; same ids, weights and status. */
+moe_status moe_route_stats(const moe_shape* shape, const void* x, const float* w_r, const float* b_r,
+                           int32_t* topk_ids, float* topk_w, int32_t* status, float* prob_sum, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/* Load-balance and rejection statistics (ch. 36 §36.4 definitions of f_e and
+ * p_bar_e and the auxiliary balance product, its worked example's rejection
+ * rates; "The real cost of sparse expert models" rho_max):
+ *   load     [E] int32 in: L_e from moe_dispatch
+ *   stats    [MOE_STAT_COUNT] int32 in: from moe_dispatch
+ *   prob_sum [E] fp32 in: from moe_route_stats
+ *   out      [2E + MOE_BAL_COUNT] fp32 out: f_e = L_e / (T k) for e < E, then
+ *            p_bar_e = prob_sum_e / T, then the MOE_BAL_* values (all 0 for T = 0)
+ * One small kernel on stream; nothing is read back to the host. */
+moe_status moe_balance(const moe_shape* shape, const int32_t* load, const int32_t* stats,
+                       const float* prob_sum, float* out, void* stream);
 
 /* Capacity-limited dispatch and load statistics (ch. 36 §36.3, Algorithm
  * 36.1 acceptance step and its invariants; "The real cost of sparse expert

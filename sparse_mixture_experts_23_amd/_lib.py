@@ -39,6 +39,14 @@ MOE_WS_FFN = 1
 MOE_WS_SHARED = 2
 MOE_WS_FORWARD = 3
 MOE_WS_ROUTE = 4
+MOE_WS_ROUTE_STATS = 5
+
+MOE_BAL_VALUE = 0
+MOE_BAL_PATH_REJECTION = 1
+MOE_BAL_TOKENS_AFFECTED = 2
+MOE_BAL_TOKENS_DROPPED = 3
+MOE_BAL_RHO_MAX = 4
+MOE_BAL_COUNT = 5
 
 
 class MoeShape(ctypes.Structure):
@@ -60,6 +68,9 @@ _SIGS = {
     "moe_status_str": (c_char_p, [c_int32]),
     "moe_route": (c_int32, [POINTER(MoeShape), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                             c_void_p, c_size_t, c_void_p]),
+    "moe_route_stats": (c_int32, [POINTER(MoeShape), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                  c_void_p, c_void_p, c_size_t, c_void_p]),
+    "moe_balance": (c_int32, [POINTER(MoeShape), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "moe_dispatch": (c_int32, [POINTER(MoeShape), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "moe_expert_ffn": (c_int32, [POINTER(MoeShape), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
@@ -128,6 +139,15 @@ def moe_check_shape(shape: MoeShape) -> int:
 
 def moe_route(shape, x, w_r, b_r, topk_ids, topk_w, status, ws, ws_bytes, stream) -> int:
     return lib().moe_route(ctypes.byref(shape), x, w_r, b_r, topk_ids, topk_w, status, ws, ws_bytes, stream)
+
+
+def moe_route_stats(shape, x, w_r, b_r, topk_ids, topk_w, status, prob_sum, ws, ws_bytes, stream) -> int:
+    return lib().moe_route_stats(ctypes.byref(shape), x, w_r, b_r, topk_ids, topk_w, status, prob_sum, ws, ws_bytes,
+                                 stream)
+
+
+def moe_balance(shape, load, stats, prob_sum, out, stream) -> int:
+    return lib().moe_balance(ctypes.byref(shape), load, stats, prob_sum, out, stream)
 
 
 def moe_dispatch(shape, x, topk_ids, load, offsets, slot, row_of, src_token, x_perm, stats, ws, ws_bytes,

@@ -77,6 +77,35 @@ def route(shape: L.MoeShape, x, w_r, b_r=None):
     return ids, w, status
 
 
+def route_stats(shape: L.MoeShape, x, w_r, b_r=None):
+    """moe_route_stats: (topk_ids, topk_w, status, prob_sum [E] fp32)."""
+    dev = x.device
+    T, k = shape.T, shape.k
+    _need(x, "x", _torch_dtype(shape), (T, shape.d))
+    _need(w_r, "w_r", torch.float32, (shape.E, shape.d))
+    if b_r is not None:
+        _need(b_r, "b_r", torch.float32, (shape.E,))
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    status = torch.empty(1, dtype=torch.int32, device=dev)
+    prob_sum = torch.empty(shape.E, dtype=torch.float32, device=dev)
+    ws = workspace(shape, L.MOE_WS_ROUTE_STATS, dev)
+    L.check(L.moe_route_stats(shape, _ptr(x), _ptr(w_r), _ptr(b_r), _ptr(ids), _ptr(w), _ptr(status),
+                              _ptr(prob_sum), _ptr(ws), ws.numel(), _stream()), "moe_route_stats")
+    return ids, w, status, prob_sum
+
+
+def balance(shape: L.MoeShape, load, stats, prob_sum):
+    """moe_balance: fp32 [2E + MOE_BAL_COUNT] = f_e, p_bar_e, then the MOE_BAL_* values."""
+    E = shape.E
+    _need(load, "load", torch.int32, (E,))
+    _need(stats, "stats", torch.int32, (L.MOE_STAT_COUNT,))
+    _need(prob_sum, "prob_sum", torch.float32, (E,))
+    out = torch.empty(2 * E + L.MOE_BAL_COUNT, dtype=torch.float32, device=load.device)
+    L.check(L.moe_balance(shape, _ptr(load), _ptr(stats), _ptr(prob_sum), _ptr(out), _stream()), "moe_balance")
+    return out
+
+
 @dataclass
 class DispatchOut:
     load: torch.Tensor

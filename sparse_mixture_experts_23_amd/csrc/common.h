@@ -90,9 +90,16 @@ struct moe_dims {
 namespace moe_kernels {
 
 // Router: scores, softmax, top-k, weights.  ws holds the fp32 scores when E > 64.
+// probs (nullable): also write every token's full softmax, probs[t E + e].
 size_t route_ws_bytes(const moe_dims& s);
 hipError_t launch_route(const moe_dims& s, const void* x, const float* w_r, const float* b_r,
-                        int32_t* topk_ids, float* topk_w, int32_t* status, void* ws, hipStream_t st);
+                        int32_t* topk_ids, float* topk_w, int32_t* status, void* ws, hipStream_t st,
+                        float* probs = nullptr);
+// prob_sum[e] = sum_t probs[t E + e] in a fixed order.
+hipError_t launch_prob_sum(const moe_dims& s, const float* probs, float* prob_sum, hipStream_t st);
+// Balance statistics from the loads, the dispatch statistics and prob_sum (out: see moe_balance).
+hipError_t launch_balance(const moe_dims& s, const int32_t* load, const int32_t* stats, const float* prob_sum,
+                          float* out, hipStream_t st);
 
 // Dispatch.
 size_t dispatch_ws_bytes(const moe_dims& s);

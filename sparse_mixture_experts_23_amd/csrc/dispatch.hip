@@ -195,9 +195,56 @@ __global__ __launch_bounds__(256) void dispatch_gather_kernel(const V* __restric
     }
 }
 
+// Load-balance statistics ("LLM from scratch" ch. 36 §36.4 and its worked
+// example): f_e = L_e / (T k), the pre-capacity share of routing records;
+// p_bar_e = prob_sum_e / T, the mean full-softmax probability; the balance value
+// E sum_e f_e p_bar_e (1 at the uniform point); the path rejection rate O / (T k),
+// the shares of tokens with some / all paths rejected, and rho_max = max_e L_e /
+// (T k / E) ("The real cost of sparse expert models", load ratio).  One
+// workgroup, E <= 1024; the sum over e runs in a fixed order.
+__global__ __launch_bounds__(1024) void balance_kernel(const int32_t* __restrict__ load,
+                                                       const int32_t* __restrict__ stats,
+                                                       const float* __restrict__ prob_sum, int64_t T, int E, int k,
+                                                       float* __restrict__ out) {
+    __shared__ float part[16];
+    const int e = threadIdx.x, wave = e / 64, lane = e % 64;
+    const double paths = (double)T * k;
+    float f = 0.f, p = 0.f;
+    if (e < E && T > 0) {
+        f = (float)(load[e] / paths);
+        p = (float)(prob_sum[e] / (double)T);
+    }
+    if (e < E) {
+        out[e] = f;
+        out[E + e] = p;
+    }
+    float fp = f * p;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) fp += __shfl_xor(fp, o, MOE_WAVE);
+    if (lane == 0) part[wave] = fp;
+    __syncthreads();
+    if (e == 0) {
+        float sum = 0.f;
+        for (int w = 0; w < 16; ++w) sum += part[w];
+        const bool any = T > 0;
+        out[2 * E + MOE_BAL_VALUE] = (float)E * sum;
+        out[2 * E + MOE_BAL_PATH_REJECTION] = any ? (float)(stats[MOE_STAT_OVERFLOW] / paths) : 0.f;
+        out[2 * E + MOE_BAL_TOKENS_AFFECTED] = any ? (float)(stats[MOE_STAT_TOKENS_AFFECTED] / (double)T) : 0.f;
+        out[2 * E + MOE_BAL_TOKENS_DROPPED] = any ? (float)(stats[MOE_STAT_TOKENS_DROPPED] / (double)T) : 0.f;
+        out[2 * E + MOE_BAL_RHO_MAX] = any ? (float)(stats[MOE_STAT_MAX_LOAD] / (paths / E)) : 0.f;
+    }
+}
+
 }  // namespace
 
 namespace moe_kernels {
+
+hipError_t launch_balance(const moe_dims& s, const int32_t* load, const int32_t* stats, const float* prob_sum,
+                          float* out, hipStream_t st) {
+    hipLaunchKernelGGL(balance_kernel, dim3(1), dim3(1024), 0, st, load, stats, prob_sum, s.T, s.E, s.k, out);
+    return hipGetLastError();
+}
+
 
 size_t dispatch_ws_bytes(const moe_dims& s) {
     const int64_t NB = (s.T + DB_TOK - 1) / DB_TOK;

@@ -53,6 +53,10 @@ size_t ffn_ws(const moe_dims& d) {
 }
 // moe_expert_gemm2 alone: [tile prefix | H partial]
 size_t gemm2_ws(const moe_dims& d) { return align_up(gemm_ws_bytes(d.E)) + partial_bytes(d); }
+// moe_route's workspace, then the [T, E] fp32 probabilities
+size_t route_stats_ws(const moe_dims& d) {
+    return align_up(route_ws_bytes(d)) + align_up((size_t)d.T * d.E * sizeof(float));
+}
 size_t shared_ws(const moe_dims& d) {
     return align_up(gemm_ws_bytes(1)) + align_up((size_t)d.T * d.m_shared * elem(d));
 }
@@ -165,6 +169,7 @@ size_t moe_workspace_bytes(const moe_shape* shape, int32_t kind) {
     if (check_shape(shape, &d) != MOE_OK) return 0;
     switch (kind) {
         case MOE_WS_ROUTE: return align_up(route_ws_bytes(d)) + ALIGN;
+        case MOE_WS_ROUTE_STATS: return route_stats_ws(d) + ALIGN;
         case MOE_WS_DISPATCH: return align_up(dispatch_ws_bytes(d)) + ALIGN;
         case MOE_WS_FFN: return ffn_ws(d);
         case MOE_WS_SHARED: return d.m_shared ? shared_ws(d) : 0;
@@ -183,6 +188,29 @@ const char* moe_status_str(int32_t status) {
         case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP runtime call or kernel launch failed";
         default: return "unknown moe_status";
     }
+}
+
+moe_status moe_route_stats(const moe_shape* shape, const void* x, const float* w_r, const float* b_r,
+                           int32_t* topk_ids, float* topk_w, int32_t* status, float* prob_sum, void* ws,
+                           size_t ws_bytes, void* stream) {
+    moe_dims d;
+    moe_status rc = check_shape(shape, &d);
+    if (rc != MOE_OK) return rc;
+    if (!status || !prob_sum || (d.T > 0 && (!x || !w_r || !topk_ids || !topk_w))) return MOE_ERR_INVALID_ARGUMENT;
+    if (!ws || ws_bytes < route_stats_ws(d)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    float* probs = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(route_ws_bytes(d)));
+    MOE_CHECK_HIP(launch_route(d, x, w_r, b_r, topk_ids, topk_w, status, ws, st, probs));
+    return hip_status(launch_prob_sum(d, probs, prob_sum, st));
+}
+
+moe_status moe_balance(const moe_shape* shape, const int32_t* load, const int32_t* stats, const float* prob_sum,
+                       float* out, void* stream) {
+    moe_dims d;
+    moe_status rc = check_shape(shape, &d);
+    if (rc != MOE_OK) return rc;
+    if (!load || !stats || !prob_sum || !out) return MOE_ERR_INVALID_ARGUMENT;
+    return hip_status(launch_balance(d, load, stats, prob_sum, out, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_route(const moe_shape* shape, const void* x, const float* w_r, const float* b_r, int32_t* topk_ids,

@@ -91,7 +91,7 @@ __device__ __forceinline__ floatx4_t mfma3(const bf16x8_t a, const uint4 H, cons
 template <int EPL>
 __device__ void select_token(const float* __restrict__ row, const float* __restrict__ b_r, int E, int k, int mode,
                              int64_t t, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
-                             int32_t* __restrict__ status) {
+                             int32_t* __restrict__ status, float* __restrict__ probs) {
     const int lane = threadIdx.x % 64;
     float v[EPL];
     bool bad = false;
@@ -111,6 +111,11 @@ __device__ void select_token(const float* __restrict__ row, const float* __restr
             topk_w[t * k + lane] = 0.f;
         }
         if (lane == 0) *status = MOE_ERR_NONFINITE_LOGIT;
+        if (probs) {
+#pragma unroll
+            for (int j = 0; j < EPL; ++j)
+                if (lane + 64 * j < E) probs[t * E + lane + 64 * j] = 0.f;
+        }
         return;
     }
     // k rounds of a wave arg-max over (score key, lower id first).
@@ -142,6 +147,16 @@ __device__ void select_token(const float* __restrict__ row, const float* __restr
         }
     }
     const float g_top = __shfl(my_g, 0, MOE_WAVE);   // the largest score
+    if (probs) {   // full softmax over the E scores, for the balance statistics
+        float z = 0.f;
+#pragma unroll
+        for (int j = 0; j < EPL; ++j)
+            if (lane + 64 * j < E) z += expf(v[j] - g_top);
+        z = wave_sum(z);
+#pragma unroll
+        for (int j = 0; j < EPL; ++j)
+            if (lane + 64 * j < E) probs[t * E + lane + 64 * j] = expf(v[j] - g_top) / z;
+    }
     float wgt;
     if (mode == MOE_GATE_SWITCH) {
         float z = 0.f;
@@ -211,7 +226,8 @@ __global__ __launch_bounds__(V_THREADS) void route_valu_kernel(const uint16_t* _
                                                                const float* __restrict__ b_r, int64_t T, int d,
                                                                int E, int k, int mode, int32_t* __restrict__ topk_ids,
                                                                float* __restrict__ topk_w,
-                                                               int32_t* __restrict__ status) {
+                                                               int32_t* __restrict__ status,
+                                                               float* __restrict__ probs) {
     constexpr int NPART = V_WAVES * 4;                // (wave, row) partials per K range
     __shared__ float part[V_MAXKR * NPART * VT * 8];
     __shared__ float lg[VT * 8];
@@ -270,7 +286,7 @@ __global__ __launch_bounds__(V_THREADS) void route_valu_kernel(const uint16_t* _
     for (int r = wave; r < VT; r += V_WAVES) {
         const int64_t t = t0 + r;
         if (t >= T) break;
-        select_token<1>(lg + r * 8, b_r, E, k, mode, t, topk_ids, topk_w, status);
+        select_token<1>(lg + r * 8, b_r, E, k, mode, t, topk_ids, topk_w, status, probs);
     }
 }
 
@@ -352,7 +368,8 @@ __global__ __launch_bounds__(RT_THREADS) void route_small_kernel(const void* __r
                                                                  const float* __restrict__ b_r, int64_t T, int d,
                                                                  int E, int k, int mode, int32_t* __restrict__ topk_ids,
                                                                  float* __restrict__ topk_w,
-                                                                 int32_t* __restrict__ status) {
+                                                                 int32_t* __restrict__ status,
+                                                                 float* __restrict__ probs) {
     __shared__ float lg[RT_TOK * NT * 16];
     __shared__ float part[BF16 ? RT_WAVES * RT_TOK * NT * 16 : 1];
     const int64_t t0 = (int64_t)blockIdx.x * RT_TOK;
@@ -374,7 +391,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_small_kernel(const void* __r
     for (int r = wave; r < RT_TOK; r += RT_WAVES) {
         const int64_t t = t0 + r;
         if (t >= T) break;
-        select_token<1>(lg + r * E, b_r, E, k, mode, t, topk_ids, topk_w, status);
+        select_token<1>(lg + r * E, b_r, E, k, mode, t, topk_ids, topk_w, status, probs);
     }
 }
 
@@ -403,7 +420,8 @@ template <int EPL>
 __global__ __launch_bounds__(256) void route_select_kernel(const float* __restrict__ part, int KS, int P, int NP,
                                                            const float* __restrict__ b_r, int64_t T, int E, int k,
                                                            int mode, int32_t* __restrict__ topk_ids,
-                                                           float* __restrict__ topk_w, int32_t* __restrict__ status) {
+                                                           float* __restrict__ topk_w, int32_t* __restrict__ status,
+                                                           float* __restrict__ probs) {
     __shared__ float rows[4][EPL * 64];
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
     const int64_t t = (int64_t)blockIdx.x * 4 + wave;
@@ -420,14 +438,42 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    select_token<EPL>(rows[wave], b_r, E, k, mode, t, topk_ids, topk_w, status);
+    select_token<EPL>(rows[wave], b_r, E, k, mode, t, topk_ids, topk_w, status, probs);
 }
 
 template <int EPL>
 void launch_select(const moe_dims& s, const float* part, int KS, int P, int NP, const float* b_r, int32_t* ids,
-                   float* w, int32_t* status, hipStream_t st) {
+                   float* w, int32_t* status, float* probs, hipStream_t st) {
     hipLaunchKernelGGL((route_select_kernel<EPL>), dim3((unsigned)((s.T + 3) / 4)), dim3(256), 0, st, part, KS, P, NP,
-                       b_r, s.T, s.E, s.k, s.gate_mode, ids, w, status);
+                       b_r, s.T, s.E, s.k, s.gate_mode, ids, w, status, probs);
+}
+
+// prob_sum[e] = sum over t of probs[t E + e]: 16 waves per 64 experts, wave w
+// sums a contiguous sixteenth of the tokens (four interleaved partial
+// sums per lane), then the waves' sums are added in wave order.  Fixed order.
+__global__ __launch_bounds__(1024) void prob_column_sum_kernel(const float* __restrict__ probs, int64_t T, int E,
+                                                               float* __restrict__ prob_sum) {
+    __shared__ float ws[16][64];
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    const int e = blockIdx.x * 64 + lane;
+    const int64_t per = (T + 15) / 16;
+    const int64_t t0 = min((int64_t)wave * per, T), t1 = min(t0 + per, T);
+    float a[4] = {0.f, 0.f, 0.f, 0.f};
+    if (e < E) {
+        int64_t t = t0;
+        for (; t + 4 <= t1; t += 4) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] += probs[(t + i) * E + e];
+        }
+        for (int i = 0; t < t1; ++t, ++i) a[i] += probs[t * E + e];
+    }
+    ws[wave][lane] = (a[0] + a[1]) + (a[2] + a[3]);
+    __syncthreads();
+    if (wave == 0 && e < E) {
+        float sum = 0.f;
+        for (int w = 0; w < 16; ++w) sum += ws[w][lane];
+        prob_sum[e] = sum;
+    }
 }
 
 }  // namespace
@@ -444,14 +490,14 @@ size_t route_ws_bytes(const moe_dims& s) {
 }
 
 hipError_t launch_route(const moe_dims& s, const void* x, const float* w_r, const float* b_r, int32_t* topk_ids,
-                        float* topk_w, int32_t* status, void* ws, hipStream_t st) {
+                        float* topk_w, int32_t* status, void* ws, hipStream_t st, float* probs) {
     hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(64), 0, st, status, 1);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || s.T == 0) return e;
     if (s.dtype == MOE_BF16 && s.E <= 8 && s.d <= V_MAXKR * V_KR) {
         const unsigned grid = (unsigned)((s.T + VT - 1) / VT);
         hipLaunchKernelGGL(route_valu_kernel, dim3(grid), dim3(V_THREADS), 0, st, static_cast<const uint16_t*>(x), w_r,
-                           b_r, s.T, s.d, s.E, s.k, s.gate_mode, topk_ids, topk_w, status);
+                           b_r, s.T, s.d, s.E, s.k, s.gate_mode, topk_ids, topk_w, status, probs);
         return hipGetLastError();
     }
     uint16_t* w3 = static_cast<uint16_t*>(ws);
@@ -468,10 +514,10 @@ hipError_t launch_route(const moe_dims& s, const void* x, const float* w_r, cons
     do {                                                                                                       \
         if (s.dtype == MOE_BF16)                                                                               \
             hipLaunchKernelGGL((route_small_kernel<true, NTV>), dim3(grid), dim3(RT_THREADS), 0, st, x, w_r, w3, \
-                               b_r, s.T, s.d, s.E, s.k, s.gate_mode, topk_ids, topk_w, status);                \
+                               b_r, s.T, s.d, s.E, s.k, s.gate_mode, topk_ids, topk_w, status, probs);         \
         else                                                                                                   \
             hipLaunchKernelGGL((route_small_kernel<false, NTV>), dim3(grid), dim3(RT_THREADS), 0, st, x, w_r, w3, \
-                               b_r, s.T, s.d, s.E, s.k, s.gate_mode, topk_ids, topk_w, status);                \
+                               b_r, s.T, s.d, s.E, s.k, s.gate_mode, topk_ids, topk_w, status, probs);         \
     } while (0)
         if (NT == 1) MOE_SMALL(1);
         else if (NT == 2) MOE_SMALL(2);
@@ -497,10 +543,16 @@ hipError_t launch_route(const moe_dims& s, const void* x, const float* w_r, cons
         hipLaunchKernelGGL(router_scores_f32_kernel, dim3(grid), dim3(256), 0, st, static_cast<const float*>(x), w_r,
                            s.T, s.d, s.E, part);
     }
-    if (s.E <= 128) launch_select<2>(s, part, KS, P, NP, b_r, topk_ids, topk_w, status, st);
-    else if (s.E <= 256) launch_select<4>(s, part, KS, P, NP, b_r, topk_ids, topk_w, status, st);
-    else if (s.E <= 512) launch_select<8>(s, part, KS, P, NP, b_r, topk_ids, topk_w, status, st);
-    else launch_select<16>(s, part, KS, P, NP, b_r, topk_ids, topk_w, status, st);
+    if (s.E <= 128) launch_select<2>(s, part, KS, P, NP, b_r, topk_ids, topk_w, status, probs, st);
+    else if (s.E <= 256) launch_select<4>(s, part, KS, P, NP, b_r, topk_ids, topk_w, status, probs, st);
+    else if (s.E <= 512) launch_select<8>(s, part, KS, P, NP, b_r, topk_ids, topk_w, status, probs, st);
+    else launch_select<16>(s, part, KS, P, NP, b_r, topk_ids, topk_w, status, probs, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_prob_sum(const moe_dims& s, const float* probs, float* prob_sum, hipStream_t st) {
+    hipLaunchKernelGGL(prob_column_sum_kernel, dim3((unsigned)((s.E + 63) / 64)), dim3(1024), 0, st, probs, s.T, s.E,
+                       prob_sum);
     return hipGetLastError();
 }
 

@@ -305,3 +305,78 @@ def test_expert_gemms_thin_tiles(d, m):
                            round_h_bf16=True)
         worst = max(worst, check_output(H64[lo:hi], ref, BF16_TOL, f"group {g} ({hi - lo} rows)"))
     log(f"[parity] expert GEMMs d={d} m={m}: ok  max rel err {worst:.2e}")
+
+
+# ---------------------------------------------------------------------------
+# load-balance statistics (moe_route_stats + moe_balance)
+# ---------------------------------------------------------------------------
+
+def test_gpu_balance_w2_worked_example():
+    """ch. 36 §36.4 worked example: f = requested load / 8 paths, p_bar = the
+    column means of the printed probability table, the balance value E sum f p_bar,
+    and the printed rejection rates 1/8, 1/4, 0 with rho_max 1.5 (C = 3)."""
+    g = _golden("w2_ch36_worked_example.json")
+    P = np.array(g["probs"])
+    x = torch.eye(4, dtype=torch.float32, device=DEV)
+    w_r = torch.tensor(np.log(P).T.astype(np.float32).copy(), device=DEV)
+    shape = api.make_shape(4, 4, 1, 3, 2, g["capacity"], L.MOE_GATE_RENORM, torch.float32)
+    ids, w, status, prob_sum = api.route_stats(shape, x, w_r)
+    ids0, w0, _ = api.route(shape, x, w_r)
+    assert torch.equal(ids, ids0) and torch.equal(w, w0) and int(status.item()) == L.MOE_OK
+    disp = api.dispatch(shape, x, ids)
+    out = api.balance(shape, disp.load, disp.stats, prob_sum).cpu().numpy().astype(np.float64)
+    E = 3
+    f_want = np.array(g["requested_load"], dtype=np.float64) / g["total_paths"]
+    p_want = P.mean(axis=0)
+    np.testing.assert_array_equal(out[:E], f_want)                 # 3/8, 1/2, 1/8 exactly
+    np.testing.assert_allclose(out[E:2 * E], p_want, atol=1e-6)    # 0.4875, 0.2625, 0.25
+    np.testing.assert_allclose(out[2 * E + L.MOE_BAL_VALUE], E * np.dot(f_want, p_want), atol=1e-6)
+    bal = out[2 * E:]
+    assert bal[L.MOE_BAL_PATH_REJECTION] == g["path_rejection_rate"][0] / g["path_rejection_rate"][1]
+    assert bal[L.MOE_BAL_TOKENS_AFFECTED] == g["tokens_affected_rate"][0] / g["tokens_affected_rate"][1]
+    assert bal[L.MOE_BAL_TOKENS_DROPPED] == g["tokens_fully_skipped_rate"]
+    assert bal[L.MOE_BAL_RHO_MAX] == g["rho_max"]
+
+
+BALANCE_CASES = [
+    MoEConfig("bal_valu", T=777, d=512, m=64, E=8, k=2, dtype="bf16", gate_mode=0, cf=(5, 4), bias="zipf",
+              cfg_id=28),
+    MoEConfig("bal_small", T=600, d=256, m=64, E=40, k=4, dtype="bf16", gate_mode=1, cf=(1, 1), cfg_id=29),
+    MoEConfig("bal_select", T=900, d=256, m=64, E=300, k=8, dtype="bf16", gate_mode=0, cf=(5, 4), bias="zipf",
+              cfg_id=30),
+    MoEConfig("bal_f32_small", T=300, d=96, m=64, E=16, k=2, dtype="f32", gate_mode=0, cf=None, cfg_id=31),
+    MoEConfig("bal_f32_select", T=300, d=96, m=64, E=130, k=3, dtype="f32", gate_mode=0, cf=(1, 1), cfg_id=32),
+]
+
+
+@pytest.mark.parametrize("cfg", BALANCE_CASES, ids=lambda c: c.name)
+def test_gpu_balance_matches_oracle(cfg):
+    """moe_route_stats ids/weights equal moe_route's; f, p_bar and the balance
+    value equal the oracle's balance_stats on the GPU's ids (p_bar within 1e-5:
+    fp32 softmax of fp32 scores that differ from the oracle's by rounding), the
+    rates and rho_max equal the oracle dispatch's."""
+    inp = make_inputs(cfg, 0, DEV)
+    shape = shape_of(cfg)
+    ids, w, status, prob_sum = api.route_stats(shape, inp.x, inp.w_r, inp.b_r)
+    ids0, w0, _ = api.route(shape, inp.x, inp.w_r, inp.b_r)
+    assert torch.equal(ids, ids0) and torch.equal(w, w0) and int(status.item()) == L.MOE_OK
+    disp = api.dispatch(shape, inp.x, ids)
+    out = api.balance(shape, disp.load, disp.stats, prob_sum).cpu().numpy().astype(np.float64)
+    E = cfg.E
+    ids_np = ids.cpu().numpy()
+    b = None if inp.b_r is None else inp.b_r.cpu().numpy()
+    _, g32 = O.router_logits(np64(inp.x), inp.w_r.cpu().numpy(), b)
+    f, p_bar, aux = O.balance_stats(g32, ids_np, E)
+    np.testing.assert_allclose(out[:E], f, rtol=0, atol=1e-7)
+    np.testing.assert_allclose(out[E:2 * E], p_bar, rtol=0, atol=1e-5)
+    np.testing.assert_allclose(out[2 * E + L.MOE_BAL_VALUE], aux, rtol=1e-5)
+    C = oracle_capacity(cfg) or cfg.T
+    d = O.assign_slots(ids_np, E, C)
+    T, k = cfg.T, cfg.k
+    bal = out[2 * E:]
+    np.testing.assert_allclose(bal[L.MOE_BAL_PATH_REJECTION], d.overflow / (T * k), rtol=1e-6)
+    np.testing.assert_allclose(bal[L.MOE_BAL_TOKENS_AFFECTED], d.tokens_affected / T, rtol=1e-6)
+    np.testing.assert_allclose(bal[L.MOE_BAL_TOKENS_DROPPED], d.tokens_dropped / T, rtol=1e-6)
+    np.testing.assert_allclose(bal[L.MOE_BAL_RHO_MAX], d.rho_max, rtol=1e-6)
+    log(f"[parity] {cfg.name}: balance value {bal[L.MOE_BAL_VALUE]:.6f} (oracle {aux:.6f}), "
+        f"rho_max {bal[L.MOE_BAL_RHO_MAX]:.4f}, path rejection {bal[L.MOE_BAL_PATH_REJECTION]:.4f}")
