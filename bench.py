@@ -160,6 +160,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="mixtral", choices=sorted(CONFIGS))
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="override the workload's token count T (e.g. 1..64 for decode-sized batches)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--phases", default="1", help="0 disables the per-phase timing loop")
@@ -177,6 +179,8 @@ def main():
         return
 
     cfg = CONFIGS[args.workload]
+    if args.tokens:
+        cfg = cfg.with_tokens(args.tokens)
     log(f"[bench] workload {cfg.name}: generating inputs on the GPU")
     inp = make_inputs(cfg, seed=0, device="cuda")
     C = 0 if cfg.cf is None else api.capacity(cfg.T, cfg.k, cfg.E, *cfg.cf)

@@ -13,11 +13,12 @@
 
 namespace {
 
-// H1 (nullable): the second K-split partial of H; the row used is H + H1 (one
-// fp32 add, the same value a caller that folded H1 into H first would read).
+// H1 (nullable): np further K-split partials of H, block p at H1 + p ps; the row
+// used is ((H + P_0) + P_1) + ... (the value a caller that folded them into H in
+// that order would read).
 template <bool VEC4>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ H, const float* __restrict__ H1,
-                                                      const int32_t* __restrict__ row_of,
+                                                      int np, int64_t ps, const int32_t* __restrict__ row_of,
                                                       const float* __restrict__ w, const float* __restrict__ shared_out,
                                                       float* __restrict__ y, int64_t T, int d, int k) {
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
@@ -52,11 +53,24 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                     const int c = c0 + u * 64 + lane;
                     h[u] = c < nv ? H4[(int64_t)row * nv + c] : float4{0.f, 0.f, 0.f, 0.f};
                 }
-                if (H1) {
+                // the first partial's loads are issued with H's (no loop in between)
+                if (np > 0) {
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
                         const int c = c0 + u * 64 + lane;
                         const float4 h1 = c < nv ? H14[(int64_t)row * nv + c] : float4{0.f, 0.f, 0.f, 0.f};
+                        h[u].x += h1.x;
+                        h[u].y += h1.y;
+                        h[u].z += h1.z;
+                        h[u].w += h1.w;
+                    }
+                }
+                for (int p = 1; p < np; ++p) {
+                    const float4* P4 = H14 + p * (ps / 4);
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int c = c0 + u * 64 + lane;
+                        const float4 h1 = c < nv ? P4[(int64_t)row * nv + c] : float4{0.f, 0.f, 0.f, 0.f};
                         h[u].x += h1.x;
                         h[u].y += h1.y;
                         h[u].z += h1.z;
@@ -87,7 +101,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                 const float a = lane_value(myw, r);
                 if (row >= 0 && ok) {
                     float h = H[(int64_t)row * d + c];
-                    if (H1) h += H1[(int64_t)row * d + c];
+                    for (int p = 0; p < np; ++p) h += H1[p * ps + (int64_t)row * d + c];
                     acc = fmaf(a, h, acc);
                 }
             }
@@ -100,16 +114,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 namespace moe_kernels {
 
-hipError_t launch_combine(const moe_dims& s, const float* H, const float* H1, const int32_t* row_of, const float* topk_w,
-                          const float* shared_out, float* y, hipStream_t st) {
+hipError_t launch_combine(const moe_dims& s, const float* H, const float* H1, int np, int64_t part_stride,
+                          const int32_t* row_of, const float* topk_w, const float* shared_out, float* y,
+                          hipStream_t st) {
     if (s.T == 0) return hipSuccess;
+    if (!H1) np = 0;
     const unsigned grid = (unsigned)((s.T + 3) / 4);
     if (s.d % 4 == 0)
-        hipLaunchKernelGGL(combine_kernel<true>, dim3(grid), dim3(256), 0, st, H, H1, row_of, topk_w, shared_out, y, s.T,
-                           s.d, s.k);
+        hipLaunchKernelGGL(combine_kernel<true>, dim3(grid), dim3(256), 0, st, H, H1, np, part_stride, row_of, topk_w,
+                           shared_out, y, s.T, s.d, s.k);
     else
-        hipLaunchKernelGGL(combine_kernel<false>, dim3(grid), dim3(256), 0, st, H, H1, row_of, topk_w, shared_out, y, s.T,
-                           s.d, s.k);
+        hipLaunchKernelGGL(combine_kernel<false>, dim3(grid), dim3(256), 0, st, H, H1, np, part_stride, row_of,
+                           topk_w, shared_out, y, s.T, s.d, s.k);
     return hipGetLastError();
 }
 

@@ -116,27 +116,36 @@ size_t gemm_ws_bytes(int G);
 // computed by the launch unless prefix_ready (then the caller wrote it, e.g. the
 // dispatch scan).
 int gemm_tile_rows(int dtype);
+// GEMM1 may split K over S = gemm1_splits(...) workgroups per tile when few row
+// tiles exist (decided from the shape alone); it then needs `part`, fp32 scratch
+// of gemm1_part_bytes(...) (S gate and S up partials), and forms h from their
+// sums.  With part == nullptr it never splits.
+int gemm1_splits(int dtype, int64_t max_rows, int G, int N, int K);
+size_t gemm1_part_bytes(int dtype, int64_t max_rows, int G, int N, int K);
 hipError_t launch_gemm1(int dtype, const void* A, const int32_t* offsets, int G, int64_t max_rows,
                         const void* w_gate, const void* w_up, void* h, int N, int K,
-                        void* ws, hipStream_t st, bool prefix_ready = false);
-// GEMM2 may split K in two (gemm2_splits == 2, decided from the shape alone):
-// then H receives the partial sum over the first half of K and H1 the second;
-// with H1 == nullptr it never splits.
+                        void* ws, hipStream_t st, bool prefix_ready = false, float* part = nullptr);
+// GEMM2 may split K over S = gemm2_splits(...) (decided from the shape alone):
+// then H receives the partial sum over the first K range and H1 + (s - 1) max_rows N
+// the sum over range s = 1..S-1; with H1 == nullptr it never splits.
 int gemm2_splits(int dtype, int64_t max_rows, int G, int N, int K);
 hipError_t launch_gemm2(int dtype, const void* h, const int32_t* offsets, int G, int64_t max_rows,
                         const void* w_down, float* H, float* H1, int N, int K, void* ws, hipStream_t st,
                         bool prefix_ready = false);
-// H += H1 over the rows [0, offsets[G]) (or [0, max_rows) without offsets); N % 4 == 0.
-hipError_t launch_add_partial(float* H, const float* H1, const int32_t* offsets, int G, int64_t max_rows, int N,
-                              hipStream_t st);
+// H += H1[0] + ... + H1[np - 1] (blocks of max_rows N floats, added in order) over the
+// rows [0, offsets[G]) (or [0, max_rows) without offsets); N % 4 == 0.
+hipError_t launch_add_partial(float* H, const float* H1, int np, const int32_t* offsets, int G, int64_t max_rows,
+                              int N, hipStream_t st);
 
 // Ungrouped bf16 GEMM part[s] = x[T,K] . w[N,K]^T over the K split s of
 // scores_splits(T, N, K) splits; part holds S consecutive fp32 [T,N] blocks.
 int scores_splits(int64_t T, int N, int K);
 hipError_t launch_scores_gemm(const void* x, const void* w, int64_t T, int N, int K, float* part, hipStream_t st);
 
-// Combine.  H1 (nullable): second K-split partial of H, added to H row by row.
-hipError_t launch_combine(const moe_dims& s, const float* H, const float* H1, const int32_t* row_of,
-                          const float* topk_w, const float* shared_out, float* y, hipStream_t st);
+// Combine.  H1 (nullable): np further K-split partials of H (blocks of
+// part_stride floats), added to the H row in order before weighting.
+hipError_t launch_combine(const moe_dims& s, const float* H, const float* H1, int np, int64_t part_stride,
+                          const int32_t* row_of, const float* topk_w, const float* shared_out, float* y,
+                          hipStream_t st);
 
 }  // namespace moe_kernels

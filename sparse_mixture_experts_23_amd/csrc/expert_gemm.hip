@@ -596,8 +596,10 @@ __device__ __forceinline__ void gemm_tile_asm_loads_only_thin(floatx16_t (&c)[8]
 // K split: the grid is S copies of a tile grid of gridDim.x / S workgroups (a
 // multiple of 8, so every copy keeps the XCD order); copy s sums the K tiles
 // [s KT / S, (s + 1) KT / S) of the KT = K / 64 and writes its fp32 partial to
-// Cout (s = 0) or Cpart + (s - 1) part_stride (s >= 1).  S = 1 for SwiGLU.
-template <int BN, bool SWIGLU>
+// Cout (s = 0) or Cpart + (s - 1) part_stride (s >= 1).  SwiGLU with S > 1
+// writes the fp32 gate and up partials instead (see swiglu_part), and
+// swiglu_reduce_kernel forms h from them.
+template <int BN, bool SWIGLU, bool SPLIT_GU = false>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* __restrict__ A,
                                                                const uint16_t* __restrict__ B0,
                                                                const uint16_t* __restrict__ B1,
@@ -630,6 +632,10 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* _
     if (!tile_coords(blockIdx.x - split * tiles_grid, offsets, tprefix, G, nrows, BM, NT, tc, nsup)) return;
     const int KTall = K / BK;
     const int kt_begin = split * KTall / S, kt_end = (split + 1) * KTall / S;
+    // SPLIT_GU (SwiGLU, S > 1): fp32 gate / up partials, gate of split s at Cpart + s
+    // part_stride, up at Cpart + (S + s) part_stride; otherwise split 0 writes Cout
+    // and split s >= 1 its fp32 partial at Cpart + (s - 1) part_stride.
+    constexpr bool swiglu_part = SWIGLU && SPLIT_GU;
     void* C = split ? static_cast<void*>(Cpart + (int64_t)(split - 1) * part_stride) : Cout;
 
     const int tid = threadIdx.x, lane = tid % 64;
@@ -860,7 +866,13 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* _
         for (int g = 0; g < 4; ++g) {
             const int col = n0 + wn * WN + j * 32 + 8 * g + 4 * lhalf;
             if (col >= N) continue;   // N % 8 == 0: a group of 4 is wholly in or out
-            if (SWIGLU) {
+            if (swiglu_part) {
+                const int v = 4 * g, qu = q + 2 * NTW;
+                float* Gp = Cpart + (int64_t)split * part_stride + row * N + col;
+                float* Up = Cpart + (int64_t)(S + split) * part_stride + row * N + col;
+                *reinterpret_cast<float4*>(Gp) = make_float4(c[q][v], c[q][v + 1], c[q][v + 2], c[q][v + 3]);
+                *reinterpret_cast<float4*>(Up) = make_float4(c[qu][v], c[qu][v + 1], c[qu][v + 2], c[qu][v + 3]);
+            } else if (SWIGLU) {
                 uint32_t p[2];
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
@@ -878,21 +890,53 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* _
     }
 }
 
-// H[r] += H1[r] for the rows r < offsets[G] (or nrows without offsets): folds the
-// second K-split partial into the first where the caller wants H itself.
-__global__ __launch_bounds__(256) void add_partial_kernel(float* __restrict__ H, const float* __restrict__ H1,
-                                                          const int32_t* __restrict__ offsets, int G, int64_t nrows,
-                                                          int N) {
+// H[r] += P_0[r] + P_1[r] + ... (P_p = H1 + p stride, added in that order) for the
+// rows r < offsets[G] (or nrows without offsets): folds the K-split partials into
+// the first where the caller wants H itself.
+__global__ __launch_bounds__(256) void add_partial_kernel(float* __restrict__ H, const float* __restrict__ H1, int np,
+                                                          int64_t stride, const int32_t* __restrict__ offsets, int G,
+                                                          int64_t nrows, int N) {
     const int64_t rows = offsets ? offsets[G] : nrows;
     const int64_t n4 = rows * (N / 4);
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
         float4 a = reinterpret_cast<float4*>(H)[i];
-        const float4 b = reinterpret_cast<const float4*>(H1)[i];
-        a.x += b.x;
-        a.y += b.y;
-        a.z += b.z;
-        a.w += b.w;
+        for (int p = 0; p < np; ++p) {
+            const float4 b = reinterpret_cast<const float4*>(H1 + (int64_t)p * stride)[i];
+            a.x += b.x;
+            a.y += b.y;
+            a.z += b.z;
+            a.w += b.w;
+        }
         reinterpret_cast<float4*>(H)[i] = a;
+    }
+}
+
+// h = SiLU(g) * u rounded to bf16, g and u the sums over the S K-split partials
+// (gate partial s at part + s stride, up at part + (S + s) stride, added in split
+// order), for the rows r < offsets[G] (or nrows); N % 8 == 0.
+__global__ __launch_bounds__(256) void swiglu_reduce_kernel(const float* __restrict__ part, int S, int64_t stride,
+                                                            const int32_t* __restrict__ offsets, int G,
+                                                            int64_t nrows, int N, uint16_t* __restrict__ h) {
+    const int64_t rows = offsets ? offsets[G] : nrows;
+    const int64_t n4 = rows * (N / 4);
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+        float4 g = reinterpret_cast<const float4*>(part)[i];
+        float4 u = reinterpret_cast<const float4*>(part + (int64_t)S * stride)[i];
+        for (int s = 1; s < S; ++s) {
+            const float4 gs = reinterpret_cast<const float4*>(part + (int64_t)s * stride)[i];
+            const float4 us = reinterpret_cast<const float4*>(part + (int64_t)(S + s) * stride)[i];
+            g.x += gs.x;
+            g.y += gs.y;
+            g.z += gs.z;
+            g.w += gs.w;
+            u.x += us.x;
+            u.y += us.y;
+            u.z += us.z;
+            u.w += us.w;
+        }
+        const uint32_t p0 = pack_bf16x2(silu_f32(g.x) * u.x, silu_f32(g.y) * u.y);
+        const uint32_t p1 = pack_bf16x2(silu_f32(g.z) * u.z, silu_f32(g.w) * u.w);
+        reinterpret_cast<uint2*>(h)[i] = make_uint2(p0, p1);
     }
 }
 
@@ -990,16 +1034,52 @@ size_t gemm_ws_bytes(int G) { return (((size_t)(G + 1) * sizeof(int32_t)) + 255)
 
 int gemm_tile_rows(int dtype) { return dtype == MOE_BF16 ? BF16_BM : F32_BM; }
 
+// K splits for a grouped GEMM with few row tiles (small batches: every active
+// group then holds about one row tile, and the tiles stream weights from HBM):
+// as many copies of the tile grid as still fit in one round on the CUs — a round
+// of fewer, longer workgroups streamed faster than several rounds of short ones —
+// at most 16 and at least 4 K tiles per split.  Depends on the shape only
+// (workspace sizes follow from it).
+int small_splits(int64_t max_rows, int G, int N, int BN, int K) {
+    const int64_t groups = std::max<int64_t>(std::min<int64_t>(G, max_rows), (max_rows + BF16_BM - 1) / BF16_BM);
+    const int64_t tiles = std::max<int64_t>(1, groups * ((N + BN - 1) / BN));
+    const int S = (int)std::min<int64_t>(16, MOE_GEMM_CUS / tiles);
+    return std::max(1, std::min(S, (K / 64) / 4));
+}
+
+int gemm1_splits(int dtype, int64_t max_rows, int G, int N, int K) {
+    if (dtype != MOE_BF16 || !asm_path_ok(N, K)) return 1;
+    return small_splits(max_rows, G, N, BF16_BN1, K);
+}
+
+size_t gemm1_part_bytes(int dtype, int64_t max_rows, int G, int N, int K) {
+    const int S = gemm1_splits(dtype, max_rows, G, N, K);
+    return S > 1 ? (size_t)2 * S * max_rows * N * sizeof(float) : 0;
+}
+
 hipError_t launch_gemm1(int dtype, const void* A, const int32_t* offsets, int G, int64_t max_rows, const void* w_gate,
-                        const void* w_up, void* h, int N, int K, void* ws, hipStream_t st, bool prefix_ready) {
+                        const void* w_up, void* h, int N, int K, void* ws, hipStream_t st, bool prefix_ready,
+                        float* part) {
     const int BM = dtype == MOE_BF16 ? BF16_BM : F32_BM;
     const int BN = dtype == MOE_BF16 ? BF16_BN1 : F32_BN;
     hipError_t e = prefix_ready ? hipSuccess : prep_tiles(offsets, G, BM, ws, st);
     if (e != hipSuccess) return e;
-    const unsigned grid = grid_size(offsets, G, max_rows, BM, N, BN);
+    unsigned grid = grid_size(offsets, G, max_rows, BM, N, BN);
     if (grid == 0) return hipSuccess;
     const int32_t* tp = static_cast<const int32_t*>(ws);
-    if (dtype == MOE_BF16 && asm_path_ok(N, K))
+    const int S = part ? gemm1_splits(dtype, max_rows, G, N, K) : 1;
+    if (dtype == MOE_BF16 && asm_path_ok(N, K) && S > 1) {
+        // fp32 gate / up partials per K split, then SiLU(g) * u from their sums
+        grid = (grid + XCDS - 1) / XCDS * XCDS * S;
+        const int64_t stride = max_rows * N;
+        hipLaunchKernelGGL((gemm_bf16_asm_kernel<BF16_BN1, true, true>), dim3(grid), dim3(512), 0, st,
+                           static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(w_gate),
+                           static_cast<const uint16_t*>(w_up), h, part, stride, offsets, tp, G, max_rows, N, K, S,
+                           NSUPER);
+        const int64_t n4 = max_rows * (N / 4);
+        hipLaunchKernelGGL(swiglu_reduce_kernel, dim3((unsigned)std::min<int64_t>((n4 + 255) / 256, 8192)),
+                           dim3(256), 0, st, part, S, stride, offsets, G, max_rows, N, static_cast<uint16_t*>(h));
+    } else if (dtype == MOE_BF16 && asm_path_ok(N, K))
         hipLaunchKernelGGL((gemm_bf16_asm_kernel<BF16_BN1, true>), dim3(grid), dim3(512), 0, st,
                            static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(w_gate),
                            static_cast<const uint16_t*>(w_up), h, nullptr, (int64_t)0, offsets, tp, G, max_rows, N, K, 1,
@@ -1016,7 +1096,10 @@ hipError_t launch_gemm1(int dtype, const void* A, const int32_t* offsets, int G,
 }
 
 int gemm2_splits(int dtype, int64_t max_rows, int G, int N, int K) {
-    if (dtype != MOE_BF16 || !asm_path_ok(N, K) || K % 128 != 0 || K < 2048) return 1;
+    if (dtype != MOE_BF16 || !asm_path_ok(N, K)) return 1;
+    const int s_small = small_splits(max_rows, G, N, BF16_BN2, K);
+    if (s_small > 1) return s_small;
+    if (K % 128 != 0 || K < 2048) return 1;
     // expected row tiles: full tiles plus about half a partial tile per group
     const int64_t mt = (max_rows + BF16_BM - 1) / BF16_BM + (G + 1) / 2;
     const int64_t tiles = mt * ((N + BF16_BN2 - 1) / BF16_BN2);
@@ -1042,7 +1125,8 @@ hipError_t launch_gemm2(int dtype, const void* h, const int32_t* offsets, int G,
         if (S > 1) grid = (grid + XCDS - 1) / XCDS * XCDS * S;
         hipLaunchKernelGGL((gemm_bf16_asm_kernel<BF16_BN2, false>), dim3(grid), dim3(512), 0, st,
                            static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w_down), nullptr, H, H1,
-                           (int64_t)0, offsets, tp, G, max_rows, N, K, S, super_width(max_rows, G, (N + BN - 1) / BN));
+                           max_rows * N, offsets, tp, G, max_rows, N, K, S,
+                           super_width(max_rows, G, (N + BN - 1) / BN));
     } else if (dtype == MOE_BF16) {
         hipLaunchKernelGGL((gemm_bf16_kernel<BF16_BM, BF16_BN2, false>), dim3(grid), dim3(256), 0, st,
                            static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w_down), nullptr, H,
@@ -1079,12 +1163,13 @@ hipError_t launch_scores_gemm(const void* x, const void* w, int64_t T, int N, in
     return hipGetLastError();
 }
 
-hipError_t launch_add_partial(float* H, const float* H1, const int32_t* offsets, int G, int64_t max_rows, int N,
-                              hipStream_t st) {
+hipError_t launch_add_partial(float* H, const float* H1, int np, const int32_t* offsets, int G, int64_t max_rows,
+                              int N, hipStream_t st) {
     const int64_t n4 = max_rows * (N / 4);
-    if (n4 == 0) return hipSuccess;
+    if (n4 == 0 || np == 0) return hipSuccess;
     const unsigned grid = (unsigned)std::min<int64_t>((n4 + 255) / 256, 8192);
-    hipLaunchKernelGGL(add_partial_kernel, dim3(grid), dim3(256), 0, st, H, H1, offsets, G, max_rows, N);
+    hipLaunchKernelGGL(add_partial_kernel, dim3(grid), dim3(256), 0, st, H, H1, np, max_rows * N, offsets, G,
+                       max_rows, N);
     return hipGetLastError();
 }
 

@@ -42,23 +42,36 @@ int64_t max_rows(const moe_dims& d) {
 
 size_t elem(const moe_dims& d) { return d.dtype == MOE_BF16 ? 2 : 4; }
 
-// Bytes of the second K-split partial of H when GEMM2 splits K for this shape.
+// Bytes of the K-split partials of H beyond the first (S - 1 blocks of R d fp32)
+// when GEMM2 splits K for this shape; of GEMM1's gate / up partials.
 size_t partial_bytes(const moe_dims& d) {
     const int64_t R = max_rows(d);
-    return gemm2_splits(d.dtype, R, d.E, d.d, d.m) > 1 ? align_up(sizeof(float) * R * d.d) : 0;
+    const int S = gemm2_splits(d.dtype, R, d.E, d.d, d.m);
+    return S > 1 ? align_up(sizeof(float) * (S - 1) * R * d.d) : 0;
 }
-// [tile prefix | h | H partial]
+size_t g1_part_bytes(const moe_dims& d) { return align_up(gemm1_part_bytes(d.dtype, max_rows(d), d.E, d.m, d.d)); }
+// [tile prefix | h | GEMM1 partials | H partials]
 size_t ffn_ws(const moe_dims& d) {
-    return align_up(gemm_ws_bytes(d.E)) + align_up((size_t)max_rows(d) * d.m * elem(d)) + partial_bytes(d);
+    return align_up(gemm_ws_bytes(d.E)) + align_up((size_t)max_rows(d) * d.m * elem(d)) + g1_part_bytes(d) +
+           partial_bytes(d);
 }
-// moe_expert_gemm2 alone: [tile prefix | H partial]
+// moe_expert_gemm1 alone: [tile prefix | GEMM1 partials]
+size_t gemm1_ws(const moe_dims& d) { return align_up(gemm_ws_bytes(d.E)) + g1_part_bytes(d); }
+// moe_expert_gemm2 alone: [tile prefix | H partials]
 size_t gemm2_ws(const moe_dims& d) { return align_up(gemm_ws_bytes(d.E)) + partial_bytes(d); }
 // moe_route's workspace, then the [T, E] fp32 probabilities
 size_t route_stats_ws(const moe_dims& d) {
     return align_up(route_ws_bytes(d)) + align_up((size_t)d.T * d.E * sizeof(float));
 }
+// shared expert: [tile prefix | h | GEMM1 partials | s partials] (one group of T rows)
+size_t shared_g1_bytes(const moe_dims& d) { return align_up(gemm1_part_bytes(d.dtype, d.T, 1, d.m_shared, d.d)); }
+size_t shared_g2_bytes(const moe_dims& d) {
+    const int S = gemm2_splits(d.dtype, d.T, 1, d.d, d.m_shared);
+    return S > 1 ? align_up(sizeof(float) * (S - 1) * d.T * d.d) : 0;
+}
 size_t shared_ws(const moe_dims& d) {
-    return align_up(gemm_ws_bytes(1)) + align_up((size_t)d.T * d.m_shared * elem(d));
+    return align_up(gemm_ws_bytes(1)) + align_up((size_t)d.T * d.m_shared * elem(d)) + shared_g1_bytes(d) +
+           shared_g2_bytes(d);
 }
 
 struct ForwardWs {
@@ -107,38 +120,61 @@ inline moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : M
         if (e_ != hipSuccess) return MOE_ERR_HIP;  \
     } while (0)
 
-// GEMM2 into H, splitting K when the shape calls for it; the second partial goes
-// to `part` and is then either handed back (*H1_out, for the combine to add) or
-// folded into H.
+// K-split partials of H still to be added (np blocks of stride floats from H1).
+struct Partials {
+    float* H1 = nullptr;
+    int np = 0;
+    int64_t stride = 0;
+};
+
+// GEMM2 into H, splitting K when the shape calls for it; the partials beyond the
+// first go to `part` and are then either handed back (*out, for the combine to
+// add) or folded into H.
 moe_status gemm2_impl(const moe_dims& d, const void* h, const int32_t* offsets, const void* w_down, float* H,
-                      void* tp, float* part, float** H1_out, hipStream_t st, bool prefix_ready = false) {
+                      void* tp, float* part, Partials* out, hipStream_t st, bool prefix_ready = false) {
     const int64_t R = max_rows(d);
     float* H1 = partial_bytes(d) ? part : nullptr;
     MOE_CHECK_HIP(launch_gemm2(d.dtype, h, offsets, d.E, R, w_down, H, H1, d.d, d.m, tp, st, prefix_ready));
-    if (H1_out) *H1_out = H1;
-    else if (H1) MOE_CHECK_HIP(launch_add_partial(H, H1, offsets, d.E, R, d.d, st));
+    const int np = H1 ? gemm2_splits(d.dtype, R, d.E, d.d, d.m) - 1 : 0;
+    if (out) {
+        out->H1 = H1;
+        out->np = np;
+        out->stride = R * d.d;
+    } else if (np) {
+        MOE_CHECK_HIP(launch_add_partial(H, H1, np, offsets, d.E, R, d.d, st));
+    }
     return MOE_OK;
 }
 
 // prefix_ready: the tile prefix at the start of ws was written by the dispatch scan.
 moe_status ffn_impl(const moe_dims& d, const void* x_perm, const int32_t* offsets, const void* w_gate,
-                    const void* w_up, const void* w_down, float* H, void* ws, float** H1_out, hipStream_t st,
+                    const void* w_up, const void* w_down, float* H, void* ws, Partials* out, hipStream_t st,
                     bool prefix_ready = false) {
     void* tp = ws;
-    void* h = static_cast<char*>(ws) + align_up(gemm_ws_bytes(d.E));
-    float* part = reinterpret_cast<float*>(static_cast<char*>(h) + align_up((size_t)max_rows(d) * d.m * elem(d)));
+    char* h = static_cast<char*>(ws) + align_up(gemm_ws_bytes(d.E));
+    float* g1part = reinterpret_cast<float*>(h + align_up((size_t)max_rows(d) * d.m * elem(d)));
+    float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(g1part) + g1_part_bytes(d));
     const int64_t R = max_rows(d);
-    MOE_CHECK_HIP(launch_gemm1(d.dtype, x_perm, offsets, d.E, R, w_gate, w_up, h, d.m, d.d, tp, st, prefix_ready));
+    MOE_CHECK_HIP(launch_gemm1(d.dtype, x_perm, offsets, d.E, R, w_gate, w_up, h, d.m, d.d, tp, st, prefix_ready,
+                               g1_part_bytes(d) ? g1part : nullptr));
     // GEMM2 uses the same row tiles: the prefix GEMM1 found (or was given) stays valid
-    return gemm2_impl(d, h, offsets, w_down, H, tp, part, H1_out, st, true);
+    return gemm2_impl(d, h, offsets, w_down, H, tp, part, out, st, true);
 }
 
 moe_status shared_impl(const moe_dims& d, const void* x, const void* s_gate, const void* s_up, const void* s_down,
                        float* s, void* ws, hipStream_t st) {
     void* tp = ws;
-    void* h = static_cast<char*>(ws) + align_up(gemm_ws_bytes(1));
-    MOE_CHECK_HIP(launch_gemm1(d.dtype, x, nullptr, 1, d.T, s_gate, s_up, h, d.m_shared, d.d, tp, st));
-    MOE_CHECK_HIP(launch_gemm2(d.dtype, h, nullptr, 1, d.T, s_down, s, nullptr, d.d, d.m_shared, tp, st));
+    char* h = static_cast<char*>(ws) + align_up(gemm_ws_bytes(1));
+    float* g1part = reinterpret_cast<float*>(h + align_up((size_t)d.T * d.m_shared * elem(d)));
+    float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(g1part) + shared_g1_bytes(d));
+    MOE_CHECK_HIP(launch_gemm1(d.dtype, x, nullptr, 1, d.T, s_gate, s_up, h, d.m_shared, d.d, tp, st, false,
+                               shared_g1_bytes(d) ? g1part : nullptr));
+    float* H1 = shared_g2_bytes(d) ? part : nullptr;
+    MOE_CHECK_HIP(launch_gemm2(d.dtype, h, nullptr, 1, d.T, s_down, s, H1, d.d, d.m_shared, tp, st));
+    if (H1) {
+        const int np = gemm2_splits(d.dtype, d.T, 1, d.d, d.m_shared) - 1;
+        MOE_CHECK_HIP(launch_add_partial(s, H1, np, nullptr, 1, d.T, d.d, st));
+    }
     return MOE_OK;
 }
 
@@ -242,9 +278,10 @@ moe_status moe_expert_gemm1(const moe_shape* shape, const void* x_perm, const in
     moe_status rc = check_shape(shape, &d);
     if (rc != MOE_OK) return rc;
     if (!offsets || !ws || !w_gate || !w_up || (max_rows(d) > 0 && (!x_perm || !h))) return MOE_ERR_INVALID_ARGUMENT;
-    if (ws_bytes < align_up(gemm_ws_bytes(d.E))) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    if (ws_bytes < gemm1_ws(d)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    float* g1part = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(gemm_ws_bytes(d.E)));
     return hip_status(launch_gemm1(d.dtype, x_perm, offsets, d.E, max_rows(d), w_gate, w_up, h, d.m, d.d, ws,
-                                   static_cast<hipStream_t>(stream)));
+                                   static_cast<hipStream_t>(stream), false, g1_part_bytes(d) ? g1part : nullptr));
 }
 
 moe_status moe_expert_gemm2(const moe_shape* shape, const void* h, const int32_t* offsets, const void* w_down,
@@ -286,7 +323,8 @@ moe_status moe_combine(const moe_shape* shape, const float* H, const int32_t* ro
     moe_status rc = check_shape(shape, &d);
     if (rc != MOE_OK) return rc;
     if (d.T > 0 && (!row_of || !topk_w || !y || (!H && max_rows(d) > 0))) return MOE_ERR_INVALID_ARGUMENT;
-    return hip_status(launch_combine(d, H, nullptr, row_of, topk_w, shared_out, y, static_cast<hipStream_t>(stream)));
+    return hip_status(
+        launch_combine(d, H, nullptr, 0, 0, row_of, topk_w, shared_out, y, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_r, const float* b_r,
@@ -307,14 +345,14 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_r, 
     // the dispatch scan also writes the GEMMs' tile prefix at the start of the FFN workspace
     MOE_CHECK_HIP(launch_dispatch(d, x, topk_ids, load, w.offsets, slot, w.row_of, w.src_token, w.x_perm, stats,
                                   w.dispatch, st, static_cast<int32_t*>(w.ffn), gemm_tile_rows(d.dtype)));
-    float* H1 = nullptr;   // second K-split partial of H, added by the combine
-    rc = ffn_impl(d, w.x_perm, w.offsets, w_gate, w_up, w_down, w.H, w.ffn, &H1, st, true);
+    Partials parts;   // K-split partials of H beyond the first, added by the combine
+    rc = ffn_impl(d, w.x_perm, w.offsets, w_gate, w_up, w_down, w.H, w.ffn, &parts, st, true);
     if (rc != MOE_OK) return rc;
     if (d.m_shared) {
         rc = shared_impl(d, x, s_gate, s_up, s_down, w.s, w.shared, st);
         if (rc != MOE_OK) return rc;
     }
-    return hip_status(launch_combine(d, w.H, H1, w.row_of, topk_w, w.s, y, st));
+    return hip_status(launch_combine(d, w.H, parts.H1, parts.np, parts.stride, w.row_of, topk_w, w.s, y, st));
 }
 
 }  // extern "C"

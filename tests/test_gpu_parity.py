@@ -226,6 +226,19 @@ def test_parity_full_size(name, sample):
     assert st[L.MOE_STAT_ACCEPTED] == int(np.minimum(load, out["dref"].capacity).sum())
 
 
+# decode-sized batches: few rows per expert, so both expert GEMMs (and the shared
+# expert's) split K over many workgroups and sum fp32 partials
+DSV3_SMALL = MoEConfig("dsv3_small_decode", T=2, d=1024, m=512, E=64, k=8, dtype="bf16", gate_mode=0, cf=None,
+                       m_shared=512, cfg_id=33)
+
+
+@pytest.mark.parametrize("cfg", [CONFIGS["mixtral"].with_tokens(1), CONFIGS["mixtral"].with_tokens(8),
+                                 DSV3_SMALL, DSV3_SMALL.with_tokens(16)],
+                         ids=["mixtral_T1", "mixtral_T8", "dsv3_small_T2", "dsv3_small_T16"])
+def test_parity_decode(cfg):
+    run_layer(cfg)
+
+
 # ---------------------------------------------------------------------------
 # edge cases and properties
 # ---------------------------------------------------------------------------
