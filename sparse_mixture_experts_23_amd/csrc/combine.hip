@@ -13,6 +13,8 @@
 
 namespace {
 
+constexpr int COMBINE_U = 4;   // 64-lane column blocks per wave (float4 each; scalar path: floats)
+
 // H1 (nullable): np further K-split partials of H, block p at H1 + p ps; the row
 // used is ((H + P_0) + P_1) + ... (the value a caller that folded them into H in
 // that order would read).
@@ -20,23 +22,27 @@ template <bool VEC4>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ H, const float* __restrict__ H1,
                                                       int np, int64_t ps, const int32_t* __restrict__ row_of,
                                                       const float* __restrict__ w, const float* __restrict__ shared_out,
-                                                      float* __restrict__ y, int64_t T, int d, int k) {
+                                                      float* __restrict__ y, int64_t T, int d, int k,
+                                                      int nchunk) {
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-    const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+    const int64_t gw = (int64_t)blockIdx.x * 4 + wave;   // (token, column chunk) of this wave
+    const int64_t t = gw / nchunk;
+    const int chunk = (int)(gw % nchunk);
     if (t >= T) return;
     const int myrow = lane < k ? row_of[t * k + lane] : -1;
     const float myw = lane < k ? w[t * k + lane] : 0.f;
     if (VEC4) {
-        // U column chunks of 64 float4 per pass: a path's U loads (and H1's) are in
-        // flight together; per element the sum is still s + a0 h0 + a1 h1 + ...
-        constexpr int U = 4;
+        // A wave owns U column blocks of 64 float4: a path's U loads (and its
+        // partials') are in flight together; per element the sum is still
+        // s + a0 h0 + a1 h1 + ...
+        constexpr int U = COMBINE_U;
         const int nv = d / 4;
         const float4* H4 = reinterpret_cast<const float4*>(H);
         const float4* H14 = reinterpret_cast<const float4*>(H1);
         const float4* S4 = reinterpret_cast<const float4*>(shared_out);
         float4* Y4 = reinterpret_cast<float4*>(y);
         // uniform trip count: every lane stays active around lane_value
-        for (int c0 = 0; c0 < nv; c0 += 64 * U) {
+        for (int c0 = chunk * 64 * U; c0 < (chunk + 1) * 64 * U; c0 += 64 * U) {
             float4 acc[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -92,7 +98,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
             }
         }
     } else {
-        for (int c0 = 0; c0 < d; c0 += 64) {
+        for (int c0 = chunk * 64 * COMBINE_U; c0 < min(d, (chunk + 1) * 64 * COMBINE_U); c0 += 64) {
             const int c = c0 + lane;
             const bool ok = c < d;
             float acc = (shared_out && ok) ? shared_out[t * d + c] : 0.f;
@@ -119,13 +125,17 @@ hipError_t launch_combine(const moe_dims& s, const float* H, const float* H1, in
                           hipStream_t st) {
     if (s.T == 0) return hipSuccess;
     if (!H1) np = 0;
-    const unsigned grid = (unsigned)((s.T + 3) / 4);
-    if (s.d % 4 == 0)
+    // one wave per (token, chunk of COMBINE_U 64-lane column blocks)
+    const bool vec4 = s.d % 4 == 0;
+    const int cols = vec4 ? s.d / 4 : s.d;
+    const int nchunk = (cols + 64 * COMBINE_U - 1) / (64 * COMBINE_U);
+    const unsigned grid = (unsigned)((s.T * nchunk + 3) / 4);
+    if (vec4)
         hipLaunchKernelGGL(combine_kernel<true>, dim3(grid), dim3(256), 0, st, H, H1, np, part_stride, row_of, topk_w,
-                           shared_out, y, s.T, s.d, s.k);
+                           shared_out, y, s.T, s.d, s.k, nchunk);
     else
         hipLaunchKernelGGL(combine_kernel<false>, dim3(grid), dim3(256), 0, st, H, H1, np, part_stride, row_of,
-                           topk_w, shared_out, y, s.T, s.d, s.k);
+                           topk_w, shared_out, y, s.T, s.d, s.k, nchunk);
     return hipGetLastError();
 }
 

@@ -426,14 +426,37 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
     const int64_t t = (int64_t)blockIdx.x * 4 + wave;
     if (t >= T) return;
+    // s_e = sum over K splits q (in order) of the planes pl = P-1 .. 0 (in that
+    // order); the loads of four splits are issued together, then added in order
+    float sum[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) sum[j] = 0.f;
+    for (int q0 = 0; q0 < KS; q0 += 4) {
+        float v[EPL][4][3];
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+            const int e = lane + 64 * j;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+                for (int pl = 0; pl < 3; ++pl)
+                    v[j][qq][pl] = (e < E && q0 + qq < KS && pl < P)
+                                       ? part[((int64_t)(q0 + qq) * T + t) * NP + pl * E + e]
+                                       : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < EPL; ++j)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq)
+                if (q0 + qq < KS)
+#pragma unroll
+                    for (int pl = 2; pl >= 0; --pl)
+                        if (pl < P) sum[j] += v[j][qq][pl];
+    }
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
         const int e = lane + 64 * j;
-        float s = 0.f;
-        if (e < E)
-            for (int q = 0; q < KS; ++q)
-                for (int pl = P - 1; pl >= 0; --pl) s += part[((int64_t)q * T + t) * NP + pl * E + e];
-        rows[wave][e] = s;
+        if (e < E) rows[wave][e] = sum[j];
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -449,25 +472,35 @@ void launch_select(const moe_dims& s, const float* part, int KS, int P, int NP, 
 }
 
 // prob_sum[e] = sum over t of probs[t E + e]: 16 waves per 64 experts, wave w
-// sums a contiguous sixteenth of the tokens (four interleaved partial
-// sums per lane), then the waves' sums are added in wave order.  Fixed order.
+// sums a contiguous sixteenth of the tokens (16 interleaved partial sums per
+// lane, so 16 loads are in flight, added pairwise at the end), then the waves'
+// sums are added in wave order.  Fixed order.
 __global__ __launch_bounds__(1024) void prob_column_sum_kernel(const float* __restrict__ probs, int64_t T, int E,
                                                                float* __restrict__ prob_sum) {
+    constexpr int NA = 16;
     __shared__ float ws[16][64];
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
     const int e = blockIdx.x * 64 + lane;
     const int64_t per = (T + 15) / 16;
     const int64_t t0 = min((int64_t)wave * per, T), t1 = min(t0 + per, T);
-    float a[4] = {0.f, 0.f, 0.f, 0.f};
+    float a[NA];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) a[i] = 0.f;
     if (e < E) {
         int64_t t = t0;
-        for (; t + 4 <= t1; t += 4) {
+        for (; t + NA <= t1; t += NA) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] += probs[(t + i) * E + e];
+            for (int i = 0; i < NA; ++i) a[i] += probs[(t + i) * E + e];
         }
-        for (int i = 0; t < t1; ++t, ++i) a[i] += probs[t * E + e];
+#pragma unroll
+        for (int i = 0; i < NA; ++i)
+            if (t + i < t1) a[i] += probs[(t + i) * E + e];
     }
-    ws[wave][lane] = (a[0] + a[1]) + (a[2] + a[3]);
+#pragma unroll
+    for (int w = NA / 2; w >= 1; w /= 2)
+#pragma unroll
+        for (int i = 0; i < w; ++i) a[i] += a[i + w];
+    ws[wave][lane] = a[0];
     __syncthreads();
     if (wave == 0 && e < E) {
         float sum = 0.f;
