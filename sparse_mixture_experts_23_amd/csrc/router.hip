@@ -227,11 +227,14 @@ __global__ __launch_bounds__(V_THREADS) void route_valu_kernel(const uint16_t* _
                                                                int E, int k, int mode, int32_t* __restrict__ topk_ids,
                                                                float* __restrict__ topk_w,
                                                                int32_t* __restrict__ status,
-                                                               float* __restrict__ probs) {
+                                                               float* __restrict__ probs, int zero_status) {
     constexpr int NPART = V_WAVES * 4;                // (wave, row) partials per K range
     __shared__ float part[V_MAXKR * NPART * VT * 8];
     __shared__ float lg[VT * 8];
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+    // a one-workgroup launch clears the status word itself (before the barriers
+    // that precede every selection)
+    if (zero_status && tid == 0) *status = MOE_OK;
     const int64_t t0 = (int64_t)blockIdx.x * VT;
     const int nkr = (d + V_KR - 1) / V_KR;
     for (int kr = 0; kr < nkr; ++kr) {
@@ -369,7 +372,8 @@ __global__ __launch_bounds__(RT_THREADS) void route_small_kernel(const void* __r
                                                                  int E, int k, int mode, int32_t* __restrict__ topk_ids,
                                                                  float* __restrict__ topk_w,
                                                                  int32_t* __restrict__ status,
-                                                                 float* __restrict__ probs) {
+                                                                 float* __restrict__ probs, int zero_status) {
+    if (zero_status && threadIdx.x == 0) *status = MOE_OK;   // one-workgroup launch
     __shared__ float lg[RT_TOK * NT * 16];
     __shared__ float part[BF16 ? RT_WAVES * RT_TOK * NT * 16 : 1];
     const int64_t t0 = (int64_t)blockIdx.x * RT_TOK;
@@ -421,9 +425,13 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
                                                            const float* __restrict__ b_r, int64_t T, int E, int k,
                                                            int mode, int32_t* __restrict__ topk_ids,
                                                            float* __restrict__ topk_w, int32_t* __restrict__ status,
-                                                           float* __restrict__ probs) {
+                                                           float* __restrict__ probs, int zero_status) {
     __shared__ float rows[4][EPL * 64];
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    if (zero_status) {   // one-workgroup launch: clear the status word first
+        if (threadIdx.x == 0) *status = MOE_OK;
+        __syncthreads();
+    }
     const int64_t t = (int64_t)blockIdx.x * 4 + wave;
     if (t >= T) return;
     // s_e = sum over K splits q (in order) of the planes pl = P-1 .. 0 (in that
@@ -467,8 +475,9 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
 template <int EPL>
 void launch_select(const moe_dims& s, const float* part, int KS, int P, int NP, const float* b_r, int32_t* ids,
                    float* w, int32_t* status, float* probs, hipStream_t st) {
-    hipLaunchKernelGGL((route_select_kernel<EPL>), dim3((unsigned)((s.T + 3) / 4)), dim3(256), 0, st, part, KS, P, NP,
-                       b_r, s.T, s.E, s.k, s.gate_mode, ids, w, status, probs);
+    const unsigned grid = (unsigned)((s.T + 3) / 4);
+    hipLaunchKernelGGL((route_select_kernel<EPL>), dim3(grid), dim3(256), 0, st, part, KS, P, NP, b_r, s.T, s.E, s.k,
+                       s.gate_mode, ids, w, status, probs, grid == 1 ? 1 : 0);
 }
 
 // prob_sum[e] = sum over t of probs[t E + e]: 16 waves per 64 experts, wave w
@@ -524,13 +533,18 @@ size_t route_ws_bytes(const moe_dims& s) {
 
 hipError_t launch_route(const moe_dims& s, const void* x, const float* w_r, const float* b_r, int32_t* topk_ids,
                         float* topk_w, int32_t* status, void* ws, hipStream_t st, float* probs) {
-    hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(64), 0, st, status, 1);
+    // The status word is cleared before any selection may set it: by the selecting
+    // kernel itself when that is a single workgroup, else by a kernel of its own.
+    const bool valu = s.dtype == MOE_BF16 && s.E <= 8 && s.d <= V_MAXKR * V_KR;
+    const int64_t sel_tokens = valu ? VT : (s.E <= 64 ? RT_TOK : 4);   // tokens per selecting workgroup
+    const bool self_zero = s.T > 0 && s.T <= sel_tokens;
+    if (!self_zero) hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(64), 0, st, status, 1);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || s.T == 0) return e;
-    if (s.dtype == MOE_BF16 && s.E <= 8 && s.d <= V_MAXKR * V_KR) {
+    if (valu) {
         const unsigned grid = (unsigned)((s.T + VT - 1) / VT);
         hipLaunchKernelGGL(route_valu_kernel, dim3(grid), dim3(V_THREADS), 0, st, static_cast<const uint16_t*>(x), w_r,
-                           b_r, s.T, s.d, s.E, s.k, s.gate_mode, topk_ids, topk_w, status, probs);
+                           b_r, s.T, s.d, s.E, s.k, s.gate_mode, topk_ids, topk_w, status, probs, self_zero ? 1 : 0);
         return hipGetLastError();
     }
     uint16_t* w3 = static_cast<uint16_t*>(ws);
@@ -547,10 +561,12 @@ hipError_t launch_route(const moe_dims& s, const void* x, const float* w_r, cons
     do {                                                                                                       \
         if (s.dtype == MOE_BF16)                                                                               \
             hipLaunchKernelGGL((route_small_kernel<true, NTV>), dim3(grid), dim3(RT_THREADS), 0, st, x, w_r, w3, \
-                               b_r, s.T, s.d, s.E, s.k, s.gate_mode, topk_ids, topk_w, status, probs);         \
+                               b_r, s.T, s.d, s.E, s.k, s.gate_mode, topk_ids, topk_w, status, probs,          \
+                               self_zero ? 1 : 0);                                                     \
         else                                                                                                   \
             hipLaunchKernelGGL((route_small_kernel<false, NTV>), dim3(grid), dim3(RT_THREADS), 0, st, x, w_r, w3, \
-                               b_r, s.T, s.d, s.E, s.k, s.gate_mode, topk_ids, topk_w, status, probs);         \
+                               b_r, s.T, s.d, s.E, s.k, s.gate_mode, topk_ids, topk_w, status, probs,          \
+                               self_zero ? 1 : 0);                                                     \
     } while (0)
         if (NT == 1) MOE_SMALL(1);
         else if (NT == 2) MOE_SMALL(2);

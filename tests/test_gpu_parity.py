@@ -268,6 +268,36 @@ def test_nonfinite_score_sets_status_and_keeps_ids_in_range():
         layer.check_status()
 
 
+@pytest.mark.parametrize("T,E", [(4, 8), (10, 40), (3, 100), (40, 100)])
+def test_status_word_set_then_cleared(T, E):
+    """The router's status word: set by a non-finite score, back to MOE_OK on the
+    next clean call — also where the selecting kernel is a single workgroup that
+    clears the word itself (T <= 8 with E <= 8, T <= 16 with E <= 64, T <= 4 above)."""
+    cfg = MoEConfig("status", T=T, d=128, m=64, E=E, k=2, dtype="bf16", gate_mode=0, cf=None, cfg_id=34)
+    inp = make_inputs(cfg, 0, DEV)
+    shape = shape_of(cfg)
+    bad = inp.x.clone()
+    bad[T - 1, 7] = float("inf")
+    _, _, status = api.route(shape, bad, inp.w_r, inp.b_r)
+    torch.cuda.synchronize()
+    assert int(status.item()) == L.MOE_ERR_NONFINITE_LOGIT
+    ids, _, status2 = api.route(shape, inp.x, inp.w_r, inp.b_r)
+    torch.cuda.synchronize()
+    assert int(status2.item()) == L.MOE_OK
+    # the same status buffer, reused: error, then cleared
+    st = torch.empty(1, dtype=torch.int32, device=DEV)
+    ids_b = torch.empty((T, 2), dtype=torch.int32, device=DEV)
+    w_b = torch.empty((T, 2), dtype=torch.float32, device=DEV)
+    ws = api.workspace(shape, L.MOE_WS_ROUTE, DEV)
+    for x_in, want in ((bad, L.MOE_ERR_NONFINITE_LOGIT), (inp.x, L.MOE_OK)):
+        L.check(L.moe_route(shape, x_in.data_ptr(), inp.w_r.data_ptr(), 0, ids_b.data_ptr(), w_b.data_ptr(),
+                            st.data_ptr(), ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream),
+                "moe_route")
+        torch.cuda.synchronize()
+        assert int(st.item()) == want
+    assert torch.equal(ids_b, ids)
+
+
 def test_run_twice_bitwise_and_causal_prefix():
     cfg = RAGGED.scaled(name="det", cfg_id=22)
     inp = make_inputs(cfg, 3, DEV)
