@@ -472,6 +472,79 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
     select_token<EPL>(rows[wave], b_r, E, k, mode, t, topk_ids, topk_w, status, probs);
 }
 
+// ---------------------------------------------------------------------------
+// small batches (T <= DOT_TMAX), bf16 activations, E > 8: direct fp32 dot products
+// ---------------------------------------------------------------------------
+//
+// Workgroup (g, q) owns experts [DOT_EW g, DOT_EW g + DOT_EW) for all T tokens
+// over the K range [2048 q, 2048 q + 2048), so w_r is read once over the grid and
+// every load of a workgroup is in flight at once.  Thread j multiplies the 8-wide
+// K chunk 2048 q + 8 j of its experts' fp32 weights with every token's exactly
+// upcast activations (fp32 FMAs), then the (token, expert) sums are reduced over
+// the wave with a fixed xor pattern and over the 4 waves in order:
+// part[(q T + t) E + e], no bias (the selection adds the K ranges in order, then
+// the bias).  Same arithmetic class as route_valu_kernel: an fp32 dot product up
+// to summation order.
+constexpr int DOT_TMAX = 16;
+constexpr int DOT_EW = 2;
+
+__global__ __launch_bounds__(256) void route_dot_kernel(const uint16_t* __restrict__ x,
+                                                        const float* __restrict__ w_r, int64_t T, int d, int E,
+                                                        float* __restrict__ part) {
+    __shared__ float red[4][DOT_TMAX * DOT_EW];
+    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+    const int e0 = blockIdx.x * DOT_EW;
+    const int q = blockIdx.y;
+    float acc[DOT_TMAX][DOT_EW];
+#pragma unroll
+    for (int t = 0; t < DOT_TMAX; ++t)
+#pragma unroll
+        for (int j = 0; j < DOT_EW; ++j) acc[t][j] = 0.f;
+    const int c = q * 2048 + 8 * tid;
+    if (c < d) {   // d % 8 == 0: a chunk is wholly in
+        float w[DOT_EW][8];
+#pragma unroll
+        for (int j = 0; j < DOT_EW; ++j) {
+            const int e = min(e0 + j, E - 1);
+            const float4 lo = *reinterpret_cast<const float4*>(w_r + (int64_t)e * d + c);
+            const float4 hi = *reinterpret_cast<const float4*>(w_r + (int64_t)e * d + c + 4);
+            w[j][0] = lo.x; w[j][1] = lo.y; w[j][2] = lo.z; w[j][3] = lo.w;
+            w[j][4] = hi.x; w[j][5] = hi.y; w[j][6] = hi.z; w[j][7] = hi.w;
+        }
+#pragma unroll
+        for (int t = 0; t < DOT_TMAX; ++t) {
+            if (t < T) {
+                const uint4 xv = *reinterpret_cast<const uint4*>(x + (int64_t)t * d + c);
+                const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float x0 = __uint_as_float(xw[i] << 16), x1 = __uint_as_float(xw[i] & 0xffff0000u);
+#pragma unroll
+                    for (int j = 0; j < DOT_EW; ++j) {
+                        acc[t][j] = fmaf(x0, w[j][2 * i], acc[t][j]);
+                        acc[t][j] = fmaf(x1, w[j][2 * i + 1], acc[t][j]);
+                    }
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < DOT_TMAX; ++t)
+#pragma unroll
+        for (int j = 0; j < DOT_EW; ++j) {
+            float v = acc[t][j];
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, MOE_WAVE);
+            if (lane == 0) red[wave][t * DOT_EW + j] = v;
+        }
+    __syncthreads();
+    if (tid < DOT_TMAX * DOT_EW) {
+        const int t = tid / DOT_EW, j = tid % DOT_EW, e = e0 + j;
+        if (t < T && e < E)
+            part[((int64_t)q * T + t) * E + e] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+    }
+}
+
 template <int EPL>
 void launch_select(const moe_dims& s, const float* part, int KS, int P, int NP, const float* b_r, int32_t* ids,
                    float* w, int32_t* status, float* probs, hipStream_t st) {
@@ -525,6 +598,7 @@ namespace moe_kernels {
 size_t route_ws_bytes(const moe_dims& s) {
     if (s.dtype != MOE_BF16) return s.E > 64 ? (size_t)s.T * s.E * sizeof(float) : 0;
     if (s.E <= 8 && s.d <= V_MAXKR * V_KR) return 0;   // route_valu_kernel
+    if (s.T <= DOT_TMAX) return (size_t)((s.d + 2047) / 2048) * s.T * s.E * sizeof(float);   // route_dot_kernel
     const int N3 = score_cols(s.E);
     size_t planes = ((size_t)N3 * s.d * 2 + 255) & ~(size_t)255;
     if (s.E <= 64) return planes;
@@ -536,7 +610,9 @@ hipError_t launch_route(const moe_dims& s, const void* x, const float* w_r, cons
     // The status word is cleared before any selection may set it: by the selecting
     // kernel itself when that is a single workgroup, else by a kernel of its own.
     const bool valu = s.dtype == MOE_BF16 && s.E <= 8 && s.d <= V_MAXKR * V_KR;
-    const int64_t sel_tokens = valu ? VT : (s.E <= 64 ? RT_TOK : 4);   // tokens per selecting workgroup
+    const bool dot = !valu && s.dtype == MOE_BF16 && s.T <= DOT_TMAX;
+    // tokens per selecting workgroup
+    const int64_t sel_tokens = valu ? VT : (dot || s.E > 64 ? 4 : RT_TOK);
     const bool self_zero = s.T > 0 && s.T <= sel_tokens;
     if (!self_zero) hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(64), 0, st, status, 1);
     hipError_t e = hipGetLastError();
@@ -545,6 +621,17 @@ hipError_t launch_route(const moe_dims& s, const void* x, const float* w_r, cons
         const unsigned grid = (unsigned)((s.T + VT - 1) / VT);
         hipLaunchKernelGGL(route_valu_kernel, dim3(grid), dim3(V_THREADS), 0, st, static_cast<const uint16_t*>(x), w_r,
                            b_r, s.T, s.d, s.E, s.k, s.gate_mode, topk_ids, topk_w, status, probs, self_zero ? 1 : 0);
+        return hipGetLastError();
+    }
+    if (dot) {
+        float* dpart = static_cast<float*>(ws);
+        const int KS = (s.d + 2047) / 2048;
+        hipLaunchKernelGGL(route_dot_kernel, dim3((unsigned)((s.E + DOT_EW - 1) / DOT_EW), (unsigned)KS), dim3(256), 0,
+                           st, static_cast<const uint16_t*>(x), w_r, s.T, s.d, s.E, dpart);
+        if (s.E <= 128) launch_select<2>(s, dpart, KS, 1, s.E, b_r, topk_ids, topk_w, status, probs, st);
+        else if (s.E <= 256) launch_select<4>(s, dpart, KS, 1, s.E, b_r, topk_ids, topk_w, status, probs, st);
+        else if (s.E <= 512) launch_select<8>(s, dpart, KS, 1, s.E, b_r, topk_ids, topk_w, status, probs, st);
+        else launch_select<16>(s, dpart, KS, 1, s.E, b_r, topk_ids, topk_w, status, probs, st);
         return hipGetLastError();
     }
     uint16_t* w3 = static_cast<uint16_t*>(ws);

@@ -191,6 +191,10 @@ RAGGED = MoEConfig("ragged_bf16", T=2000, d=328, m=200, E=4, k=2, dtype="bf16", 
     # 34 token blocks x 1000 experts: the dispatch scan runs as its own kernel
     MoEConfig("dispatch_large_table", T=8500, d=64, m=64, E=1000, k=2, dtype="bf16", gate_mode=0, cf=(5, 4),
               cfg_id=27),
+    # T <= 16 with E > 8: direct fp32 dot-product router; d not a multiple of the 2048-wide pass
+    MoEConfig("router_dot_small", T=16, d=2056, m=64, E=33, k=3, dtype="bf16", gate_mode=1, cf=None, cfg_id=35),
+    MoEConfig("router_dot_many", T=5, d=512, m=64, E=700, k=8, dtype="bf16", gate_mode=0, cf=None, bias="zipf",
+              cfg_id=36),
     # E > 64: router scores on the expert-GEMM kernel; 300 rows end in a 44-row tile
     MoEConfig("router_thin_tail", T=300, d=1024, m=64, E=100, k=4, dtype="bf16", gate_mode=0, cf=None, cfg_id=26),
     # router with E < 8 experts over two K ranges of 4096 (d > 4096), T not a multiple of 16
@@ -389,6 +393,8 @@ BALANCE_CASES = [
               cfg_id=30),
     MoEConfig("bal_f32_small", T=300, d=96, m=64, E=16, k=2, dtype="f32", gate_mode=0, cf=None, cfg_id=31),
     MoEConfig("bal_f32_select", T=300, d=96, m=64, E=130, k=3, dtype="f32", gate_mode=0, cf=(1, 1), cfg_id=32),
+    MoEConfig("bal_dot", T=13, d=256, m=64, E=70, k=4, dtype="bf16", gate_mode=0, cf=(1, 1), bias="zipf",
+              cfg_id=37),
 ]
 
 
