@@ -263,7 +263,44 @@ def assign_slots(ids: np.ndarray, E: int, C: int) -> Dispatch:
             if counter[e] < C:
                 slot[t, r] = counter[e]
             counter[e] += 1
-    load = np.array(counter, dtype=np.int64)
+    return _dispatch_from_slots(ids, slot, np.array(counter, dtype=np.int64), E, C)
+
+
+def assign_slots_by_gate(ids: np.ndarray, w: np.ndarray, E: int, C: int) -> Dispatch:
+    """Acceptance by routing weight instead of arrival order.
+
+    [CH36] §36.3 (acceptance rules): the capacity competition inside a routing
+    group may be decided by gate weight, so that low-weight paths are the ones
+    that lose compute.  Reading: for each expert, its requests are ranked by
+    their routing weight a_{t,e}, larger first, equal weights in token order;
+    the first C are accepted.  The accepted paths keep token order inside the
+    expert's group of rows (slot = number of accepted earlier tokens of that
+    expert), so the grouped layout is the same as under first-come-first-served.
+    `w` are the routing weights the decision is taken on (fp32 values).
+    """
+    ids = np.asarray(ids, dtype=np.int64)
+    w = np.asarray(w)
+    T, k = ids.shape
+    if C < 1:
+        raise OracleError("capacity must be >= 1")
+    requests = [[] for _ in range(E)]          # (t, r) in token order
+    for t in range(T):
+        for r in range(k):
+            requests[int(ids[t, r])].append((t, r))
+    slot = np.full((T, k), -1, dtype=np.int64)
+    for e in range(E):
+        ranked = sorted(requests[e], key=lambda tr: (-float(w[tr[0], tr[1]]), tr[0]))
+        accepted = sorted(ranked[:C])          # back to token order
+        for c, (t, r) in enumerate(accepted):
+            slot[t, r] = c
+    load = np.array([len(q) for q in requests], dtype=np.int64)
+    return _dispatch_from_slots(ids, slot, load, E, C)
+
+
+def _dispatch_from_slots(ids: np.ndarray, slot: np.ndarray, load: np.ndarray, E: int, C: int) -> Dispatch:
+    """Grouped-row offsets, row map and load statistics from per-path slots
+    ([REVIEW] equations for C_e, O and rho_max; rho_max on the requested load)."""
+    T, k = ids.shape
     accepted = np.minimum(load, C)
     offsets = np.zeros(E + 1, dtype=np.int64)
     offsets[1:] = np.cumsum(accepted)
@@ -327,6 +364,22 @@ def swiglu_ffn(xrows: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray,
     if round_h_bf16:
         h = round_to_bf16(h)
     return h @ np.asarray(w_down, dtype=np.float64).T
+
+
+def survivor_weights(row_of: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """The overflow variant that renormalises over the surviving paths: each
+    accepted weight is divided by the sum of the token's accepted weights
+    ([CH36] §36.4 worked example: with its only surviving expert, token 4's
+    weight becomes one); rejected paths keep weight 0 and a token with no
+    accepted path has no weights."""
+    w = np.asarray(w, dtype=np.float64)
+    acc = np.asarray(row_of) >= 0
+    out = np.zeros_like(w)
+    for t in range(w.shape[0]):
+        tot = float(w[t][acc[t]].sum())
+        if tot > 0:
+            out[t][acc[t]] = w[t][acc[t]] / tot
+    return out
 
 
 def combine(T: int, width: int, row_of: np.ndarray, w: np.ndarray,
@@ -402,7 +455,9 @@ def forward(x, w_r, b_r, experts: WeightsArg, k: int, mode: int,
             round_h_bf16: bool = False,
             renorm_form: str = RENORM_FORM_SOFTMAX_THEN_RENORM,
             tokens: Optional[Sequence[int]] = None,
-            ids_override: Optional[np.ndarray] = None) -> ForwardResult:
+            ids_override: Optional[np.ndarray] = None,
+            accept_by_gate: bool = False, renorm_survivors: bool = False,
+            accept_weights: Optional[np.ndarray] = None) -> ForwardResult:
     """One sparse MoE layer forward, Algorithm 36.1 ([CH36] §36.4) with the
     conventions above.  The output excludes the residual ([CH36] §36.3: a
     token whose every path is rejected keeps only its residual, which the
@@ -416,6 +471,12 @@ def forward(x, w_r, b_r, experts: WeightsArg, k: int, mode: int,
     them), for staged comparisons where a near-tie flipped a selection.
     `shared` is one expert's (w_gate [m_s,d], w_up [m_s,d], w_down [d,m_s]),
     always applied and unweighted ([CH36] §36.6; [SKEWER] DeepSeek-V3 formula).
+    Overflow variants ([CH36] §36.3-§36.4): `accept_by_gate` decides the
+    capacity competition by routing weight (assign_slots_by_gate), on
+    `accept_weights` if given (the fp32 weights of the run being checked, so
+    that both sides take the decision on the same values) else on the weights
+    rounded to fp32; `renorm_survivors` renormalises each token's weights over
+    its accepted paths (survivor_weights).
     """
     x = np.asarray(x)
     T = x.shape[0]
@@ -435,7 +496,12 @@ def forward(x, w_r, b_r, experts: WeightsArg, k: int, mode: int,
         rt.ids = np.asarray(ids_override, dtype=np.int64)
         rt.w = gate_weights(rt.g32, rt.ids, mode, renorm_form)
     cap = T if C is None else C
-    disp = assign_slots(rt.ids, E, cap)
+    if accept_by_gate:
+        aw = round_to_f32(rt.w) if accept_weights is None else np.asarray(accept_weights)
+        disp = assign_slots_by_gate(rt.ids, aw, E, cap)
+    else:
+        disp = assign_slots(rt.ids, E, cap)
+    w_comb = survivor_weights(disp.row_of, rt.w) if renorm_survivors else rt.w
     tok = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
 
     # Expert FFN per accepted path of the requested tokens, evaluated expert
@@ -465,7 +531,7 @@ def forward(x, w_r, b_r, experts: WeightsArg, k: int, mode: int,
         for r in range(k):
             row = int(disp.row_of[t, r])
             if row >= 0:
-                y[i] += float(rt.w[t, r]) * path_out[row]
+                y[i] += float(w_comb[t, r]) * path_out[row]
     stats = dict(load=disp.load, accepted=disp.accepted, overflow=disp.overflow,
                  max_load=disp.max_load, rho_max=disp.rho_max,
                  tokens_dropped=disp.tokens_dropped, tokens_affected=disp.tokens_affected,

@@ -477,3 +477,90 @@ def test_token_subset_matches_full_evaluation():
     full = O.forward(x, w_r, None, ex, k=2, mode=O.GATE_RENORM, C=20)
     sub = O.forward(x, w_r, None, ex, k=2, mode=O.GATE_RENORM, C=20, tokens=[0, 13, 59])
     np.testing.assert_allclose(sub.y, full.y[[0, 13, 59]], atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# overflow variants ([CH36] §36.3 acceptance rules and overflow, §36.4 example)
+# --------------------------------------------------------------------------
+
+def test_w2_renormalised_survivors_gives_printed_3x4():
+    """The worked example's variant: renormalising over the surviving paths
+    gives token 4 the coefficient 3 (its only surviving expert, scale 3, with
+    weight one); the tokens without a rejected path keep their outputs."""
+    g, x, w_r = _w2()
+    rt = O.route(x, w_r, None, k=2, mode=O.GATE_RENORM)
+    disp = O.assign_slots(rt.ids, 3, g["capacity"])
+    outs = _linear_path_outputs(g, x, rt.ids, disp)
+    drop = O.combine(4, 4, disp.row_of, rt.w, outs)
+    ren = O.combine(4, 4, disp.row_of, O.survivor_weights(disp.row_of, rt.w), outs)
+    assert abs(ren[3, 3] - g["token4_renormalise_variant_coefficient"]) < 1e-9
+    np.testing.assert_allclose(ren[:3], drop[:3], atol=1e-12)
+    # without any rejection the renormalised weights are the weights themselves
+    free = O.assign_slots(rt.ids, 3, 4)
+    np.testing.assert_allclose(O.survivor_weights(free.row_of, rt.w), rt.w, atol=1e-12)
+
+
+def test_gate_priority_constructed_example():
+    """tests/golden/w2_gate_priority_variant.json: at expert 1 the four requests
+    carry weights 2/9, 1/3, 7/18, 2/3 in token order; C = 3 rejects the last
+    arrival first-come-first-served but the lowest weight (token 0) by gate
+    weight, and the accepted rows keep token order."""
+    with open(os.path.join(GOLDEN, "w2_gate_priority_variant.json")) as f:
+        g = json.load(f)
+    P = np.array(g["probs"])
+    x = np.eye(4)
+    w_r = np.log(P).T.astype(np.float32)
+    rt = O.route(x, w_r, None, k=2, mode=O.GATE_RENORM)
+    for t in range(4):
+        assert sorted(rt.ids[t].tolist()) == g["selected_sets"][t]
+        by_id = {int(e): float(w) for e, w in zip(rt.ids[t], rt.w[t])}
+        for e, wf in zip(g["selected_sets"][t], g["weights_by_expert_id"][t]):
+            assert abs(by_id[e] - float(_frac(wf))) < 1e-6
+    C = g["capacity"]
+    fcfs = O.assign_slots(rt.ids, 3, C)
+    gate = O.assign_slots_by_gate(rt.ids, O.round_to_f32(rt.w), 3, C)
+
+    def rejected(d):
+        return [[t, int(rt.ids[t, r])] for t in range(4) for r in range(2) if d.slot[t, r] < 0]
+
+    assert rejected(fcfs) == g["first_come_first_served"]["rejected"]
+    assert rejected(gate) == g["by_gate_weight"]["rejected"]
+    for t, c in g["by_gate_weight"]["expert1_slots_by_token"]:
+        r = int(np.where(rt.ids[t] == 1)[0][0])
+        assert gate.slot[t, r] == c
+    cases = ((fcfs, rt.w, "first_come_first_served"), (gate, rt.w, "by_gate_weight"),
+             (gate, O.survivor_weights(gate.row_of, rt.w), "by_gate_weight_renormalised_survivors"))
+    for d, w, key in cases:
+        y = O.combine(4, 4, d.row_of, w, _linear_path_outputs(g, x, rt.ids, d))
+        want = [float(_frac(v)) for v in g[key]["y_diag"]]
+        np.testing.assert_allclose(np.diag(y), want, atol=1e-6)
+        assert np.count_nonzero(y - np.diag(np.diag(y))) == 0
+    # the load statistics do not depend on the acceptance order
+    assert gate.load.tolist() == fcfs.load.tolist()
+    assert gate.overflow == fcfs.overflow == 1
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_gate_priority_invariants(seed):
+    """Brute-force properties on random small groups: per expert exactly
+    min(L_e, C) requests are accepted; no rejected request outweighs an accepted
+    one (equal weights: the earlier token wins); accepted slots run 0.. in token
+    order; with C >= every load nothing changes from first-come-first-served."""
+    rng = np.random.default_rng(100 + seed)
+    T, E, k = int(rng.integers(5, 40)), int(rng.integers(2, 7)), 2
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+    w = rng.choice([0.125, 0.25, 0.375, 0.5], size=(T, k))   # many exact ties
+    C = int(rng.integers(1, 6))
+    d = O.assign_slots_by_gate(ids, w, E, C)
+    for e in range(E):
+        req = [(t, r) for t in range(T) for r in range(k) if ids[t, r] == e]
+        acc = [(t, r) for t, r in req if d.slot[t, r] >= 0]
+        rej = [(t, r) for t, r in req if d.slot[t, r] < 0]
+        assert len(acc) == min(len(req), C)
+        for ta, ra in acc:
+            for tr, rr in rej:
+                assert w[ta, ra] > w[tr, rr] or (w[ta, ra] == w[tr, rr] and ta < tr)
+        assert [int(d.slot[t, r]) for t, r in acc] == list(range(len(acc)))
+    big = O.assign_slots_by_gate(ids, w, E, T)
+    ref = O.assign_slots(ids, E, T)
+    assert np.array_equal(big.slot, ref.slot) and np.array_equal(big.row_of, ref.row_of)
