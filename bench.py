@@ -99,7 +99,8 @@ class Stages:
             rc = L.moe_route(s, p(i.x), p(i.w_r), p(i.b_r), p(self.ids), p(self.w), p(self.status), p(self.ws_r),
                              self.ws_r.numel(), st)
         elif phase == "dispatch":
-            rc = L.moe_dispatch(s, p(i.x), p(self.ids), p(self.load), p(self.offsets), p(self.slot), p(self.row_of),
+            rc = L.moe_dispatch(s, p(i.x), p(self.ids), p(self.w), p(self.load), p(self.offsets), p(self.slot),
+                                p(self.row_of),
                                 p(self.src), p(self.x_perm), p(self.stats), p(self.ws_d), self.ws_d.numel(), st)
         elif phase == "gemm1":
             rc = L.moe_expert_gemm1(s, p(self.x_perm), p(self.offsets), p(i.w_gate), p(i.w_up), p(self.h),

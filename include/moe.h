@@ -74,6 +74,17 @@ typedef struct {
     int32_t gate_mode;   /* moe_gate_mode */
     int32_t dtype;       /* moe_dtype     */
     int32_t m_shared;
+    /* Overflow variants (ch. 36 §36.3 acceptance rules and overflow; §36.4 worked
+     * example); both 0 is the chapter's Algorithm 36.1:
+     *   accept_by_gate   1: an expert over capacity keeps the C requests with the
+     *                    largest routing weight (equal weights: earlier token),
+     *                    instead of the first C in token order; accepted rows
+     *                    still keep token order inside the expert's group
+     *   renorm_survivors 1: the combine divides each accepted weight by the sum
+     *                    of the token's accepted weights (a token with no
+     *                    accepted path still adds nothing) */
+    int32_t accept_by_gate;
+    int32_t renorm_survivors;
 } moe_shape;
 
 /* Indices of the int32 statistics vector written by moe_dispatch. */
@@ -176,10 +187,13 @@ moe_status moe_balance(const moe_shape* shape, const int32_t* load, const int32_
  * models" equations for C_e, O and rho_max).
  *   x         [T,d]      dtype
  *   topk_ids  [T,k]      int32 in (values must lie in [0,E); each row distinct)
+ *   topk_w    [T,k]      fp32 in: the routing weights; read only with
+ *                        shape->accept_by_gate (then required; else may be NULL)
  *   load      [E]        int32 out: requested load L_e
  *   offsets   [E+1]      int32 out: exclusive prefix sum of min(L_e, C)
  *   slot      [T,k]      int32 out: slot c within the expert (number of earlier
- *                        tokens that requested the same expert), or -1 if rejected
+ *                        tokens that requested the same expert; with
+ *                        accept_by_gate, of earlier accepted tokens), or -1 if rejected
  *   row_of    [T,k]      int32 out: offsets[e] + slot, or -1
  *   src_token [max_rows] int32 out: token of each grouped row (rows >= A untouched)
  *   x_perm    [max_rows,d] dtype out: x_perm[row] = x[src_token[row]]; rows are
@@ -187,6 +201,7 @@ moe_status moe_balance(const moe_shape* shape, const int32_t* load, const int32_
  *   stats     [MOE_STAT_COUNT] int32 out (see the MOE_STAT_* indices)
  *   ws        >= moe_workspace_bytes(shape, MOE_WS_DISPATCH) bytes */
 moe_status moe_dispatch(const moe_shape* shape, const void* x, const int32_t* topk_ids,
+                        const float* topk_w,
                         int32_t* load, int32_t* offsets, int32_t* slot, int32_t* row_of,
                         int32_t* src_token, void* x_perm, int32_t* stats,
                         void* ws, size_t ws_bytes, void* stream);

@@ -51,7 +51,8 @@ MOE_BAL_COUNT = 5
 
 class MoeShape(ctypes.Structure):
     _fields_ = [("T", c_int64), ("d", c_int32), ("m", c_int32), ("E", c_int32), ("k", c_int32),
-                ("capacity", c_int32), ("gate_mode", c_int32), ("dtype", c_int32), ("m_shared", c_int32)]
+                ("capacity", c_int32), ("gate_mode", c_int32), ("dtype", c_int32), ("m_shared", c_int32),
+                ("accept_by_gate", c_int32), ("renorm_survivors", c_int32)]
 
 
 class MoeError(RuntimeError):
@@ -72,7 +73,7 @@ _SIGS = {
                                   c_void_p, c_void_p, c_size_t, c_void_p]),
     "moe_balance": (c_int32, [POINTER(MoeShape), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "moe_dispatch": (c_int32, [POINTER(MoeShape), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
-                               c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "moe_expert_ffn": (c_int32, [POINTER(MoeShape), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                  c_void_p, c_size_t, c_void_p]),
     "moe_expert_gemm1": (c_int32, [POINTER(MoeShape), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
@@ -150,9 +151,9 @@ def moe_balance(shape, load, stats, prob_sum, out, stream) -> int:
     return lib().moe_balance(ctypes.byref(shape), load, stats, prob_sum, out, stream)
 
 
-def moe_dispatch(shape, x, topk_ids, load, offsets, slot, row_of, src_token, x_perm, stats, ws, ws_bytes,
+def moe_dispatch(shape, x, topk_ids, topk_w, load, offsets, slot, row_of, src_token, x_perm, stats, ws, ws_bytes,
                  stream) -> int:
-    return lib().moe_dispatch(ctypes.byref(shape), x, topk_ids, load, offsets, slot, row_of, src_token, x_perm,
+    return lib().moe_dispatch(ctypes.byref(shape), x, topk_ids, topk_w, load, offsets, slot, row_of, src_token, x_perm,
                               stats, ws, ws_bytes, stream)
 
 

@@ -37,9 +37,11 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape: tuple):
 
 
 def make_shape(T: int, d: int, m: int, E: int, k: int, capacity: int = 0, gate_mode: int = L.MOE_GATE_RENORM,
-               dtype=torch.bfloat16, m_shared: int = 0) -> L.MoeShape:
+               dtype=torch.bfloat16, m_shared: int = 0, accept_by_gate: bool = False,
+               renorm_survivors: bool = False) -> L.MoeShape:
     s = L.MoeShape(T, d, m, E, k, capacity, gate_mode,
-                   _dtype_code(dtype) if isinstance(dtype, torch.dtype) else int(dtype), m_shared)
+                   _dtype_code(dtype) if isinstance(dtype, torch.dtype) else int(dtype), m_shared,
+                   int(accept_by_gate), int(renorm_survivors))
     L.check(L.moe_check_shape(s), "moe_check_shape")
     return s
 
@@ -117,12 +119,15 @@ class DispatchOut:
     stats: torch.Tensor
 
 
-def dispatch(shape: L.MoeShape, x, topk_ids) -> DispatchOut:
+def dispatch(shape: L.MoeShape, x, topk_ids, topk_w=None) -> DispatchOut:
+    """topk_w (the routing weights) is needed only with shape.accept_by_gate."""
     dev = x.device
     T, k, E = shape.T, shape.k, shape.E
     R = L.moe_max_rows(shape)
     _need(x, "x", _torch_dtype(shape), (T, shape.d))
     _need(topk_ids, "topk_ids", torch.int32, (T, k))
+    if topk_w is not None:
+        _need(topk_w, "topk_w", torch.float32, (T, k))
     out = DispatchOut(
         load=torch.empty(E, dtype=torch.int32, device=dev),
         offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
@@ -133,7 +138,8 @@ def dispatch(shape: L.MoeShape, x, topk_ids) -> DispatchOut:
         stats=torch.empty(L.MOE_STAT_COUNT, dtype=torch.int32, device=dev),
     )
     ws = workspace(shape, L.MOE_WS_DISPATCH, dev)
-    L.check(L.moe_dispatch(shape, _ptr(x), _ptr(topk_ids), _ptr(out.load), _ptr(out.offsets), _ptr(out.slot),
+    L.check(L.moe_dispatch(shape, _ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(out.load), _ptr(out.offsets),
+                           _ptr(out.slot),
                            _ptr(out.row_of), _ptr(out.src_token), _ptr(out.x_perm), _ptr(out.stats), _ptr(ws),
                            ws.numel(), _stream()), "moe_dispatch")
     return out

@@ -8,7 +8,9 @@
 // unweighted, ch. 36 §36.6.)  The scatter-add of the definition is computed as a
 // token-major gather: each token's row is written by exactly one wave, summing
 // its paths in rank order with fp32 fused multiply-adds, so the result is
-// deterministic without atomics.
+// deterministic without atomics.  Overflow variant (ch. 36 §36.4 worked
+// example): with renorm_survivors each accepted weight is first divided by the
+// sum of the token's accepted weights.
 #include "common.h"
 
 namespace {
@@ -23,14 +25,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       int np, int64_t ps, const int32_t* __restrict__ row_of,
                                                       const float* __restrict__ w, const float* __restrict__ shared_out,
                                                       float* __restrict__ y, int64_t T, int d, int k,
-                                                      int nchunk) {
+                                                      int nchunk, int renorm) {
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
     const int64_t gw = (int64_t)blockIdx.x * 4 + wave;   // (token, column chunk) of this wave
     const int64_t t = gw / nchunk;
     const int chunk = (int)(gw % nchunk);
     if (t >= T) return;
     const int myrow = lane < k ? row_of[t * k + lane] : -1;
-    const float myw = lane < k ? w[t * k + lane] : 0.f;
+    float myw = lane < k ? w[t * k + lane] : 0.f;
+    if (renorm) {   // overflow variant: weights over the accepted paths, summed in rank order
+        float tot = 0.f;
+        for (int r = 0; r < k; ++r)
+            if (lane_value(myrow, r) >= 0) tot += lane_value(myw, r);
+        if (tot > 0.f) myw = myw / tot;
+    }
     if (VEC4) {
         // A wave owns U column blocks of 64 float4: a path's U loads (and its
         // partials') are in flight together; per element the sum is still
@@ -132,10 +140,10 @@ hipError_t launch_combine(const moe_dims& s, const float* H, const float* H1, in
     const unsigned grid = (unsigned)((s.T * nchunk + 3) / 4);
     if (vec4)
         hipLaunchKernelGGL(combine_kernel<true>, dim3(grid), dim3(256), 0, st, H, H1, np, part_stride, row_of, topk_w,
-                           shared_out, y, s.T, s.d, s.k, nchunk);
+                           shared_out, y, s.T, s.d, s.k, nchunk, s.renorm_survivors);
     else
         hipLaunchKernelGGL(combine_kernel<false>, dim3(grid), dim3(256), 0, st, H, H1, np, part_stride, row_of,
-                           topk_w, shared_out, y, s.T, s.d, s.k, nchunk);
+                           topk_w, shared_out, y, s.T, s.d, s.k, nchunk, s.renorm_survivors);
     return hipGetLastError();
 }
 

@@ -85,6 +85,8 @@ struct moe_dims {
     int gate_mode;
     int dtype;
     int m_shared;
+    int accept_by_gate;     // overflow variant: acceptance by routing weight
+    int renorm_survivors;   // overflow variant: weights renormalised over accepted paths
 };
 
 namespace moe_kernels {
@@ -105,8 +107,9 @@ hipError_t launch_balance(const moe_dims& s, const int32_t* load, const int32_t*
 size_t dispatch_ws_bytes(const moe_dims& s);
 // tprefix (nullable): also write the grouped GEMMs' tile prefix for tiles of
 // tile_rows rows (gemm_tile_rows), so the GEMM launches can skip computing it.
-hipError_t launch_dispatch(const moe_dims& s, const void* x, const int32_t* ids, int32_t* load,
-                           int32_t* offsets, int32_t* slot, int32_t* row_of, int32_t* src_token,
+// topk_w: the routing weights (read only when s.accept_by_gate).
+hipError_t launch_dispatch(const moe_dims& s, const void* x, const int32_t* ids, const float* topk_w,
+                           int32_t* load, int32_t* offsets, int32_t* slot, int32_t* row_of, int32_t* src_token,
                            void* x_perm, int32_t* stats, void* ws, hipStream_t st,
                            int32_t* tprefix = nullptr, int tile_rows = 0);
 

@@ -52,11 +52,13 @@ __global__ __launch_bounds__(DB_TOK) void dispatch_count_kernel(const int32_t* _
 // One workgroup of 1024 threads (E <= 1024): thread e scans expert e over blocks.
 // tprefix (nullable): also writes the grouped GEMMs' tile prefix,
 // tprefix[e] = sum_{e' < e} ceil(accepted(e') / tile_rows), tprefix[E] = total.
+// roff (nullable): also the exclusive prefix of the requested loads, roff[e] and
+// roff[E] = T k (positions of each expert's requests, acceptance by gate weight).
 __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict__ hist, int NB, int E, int C,
                                                              int32_t* __restrict__ load, int32_t* __restrict__ offsets,
                                                              int32_t* __restrict__ stats, int32_t* __restrict__ tprefix,
-                                                             int tile_rows) {
-    __shared__ int s_sum[16], s_over[16], s_max[16], s_tiles[16];
+                                                             int tile_rows, int32_t* __restrict__ roff) {
+    __shared__ int s_sum[16], s_over[16], s_max[16], s_tiles[16], s_req[16];
     const int e = threadIdx.x, wave = e / 64, lane = e % 64;
     int L = 0;
     if (e < E) {
@@ -70,15 +72,17 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict
     const int acc = e < E ? min(L, C) : 0;
     const int over = e < E ? max(L - C, 0) : 0;
     const int tiles = tprefix ? (acc + tile_rows - 1) / tile_rows : 0;
-    // inclusive wave scans of acc and of the tile counts
-    int incl = acc, tincl = tiles;
+    // inclusive wave scans of acc, of the tile counts and of the requests
+    int incl = acc, tincl = tiles, rincl = L;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
         const int v = __shfl_up(incl, o, MOE_WAVE);
         const int tv = __shfl_up(tincl, o, MOE_WAVE);
+        const int rv = __shfl_up(rincl, o, MOE_WAVE);
         if (lane >= o) {
             incl += v;
             tincl += tv;
+            rincl += rv;
         }
     }
     int ov = over, mx = L;
@@ -90,26 +94,31 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict
     if (lane == 63) {
         s_sum[wave] = incl;
         s_tiles[wave] = tincl;
+        s_req[wave] = rincl;
     }
     if (lane == 0) {
         s_over[wave] = ov;
         s_max[wave] = mx;
     }
     __syncthreads();
-    int before = 0, total = 0, otot = 0, mtot = 0, tbefore = 0, ttotal = 0;
+    int before = 0, total = 0, otot = 0, mtot = 0, tbefore = 0, ttotal = 0, rbefore = 0, rtotal = 0;
     for (int w = 0; w < 16; ++w) {
         if (w < wave) {
             before += s_sum[w];
             tbefore += s_tiles[w];
+            rbefore += s_req[w];
         }
         total += s_sum[w];
         ttotal += s_tiles[w];
+        rtotal += s_req[w];
         otot += s_over[w];
         mtot = max(mtot, s_max[w]);
     }
     if (e < E) offsets[e] = before + incl - acc;
     if (tprefix && e < E) tprefix[e] = tbefore + tincl - tiles;
     if (tprefix && e == 0) tprefix[E] = ttotal;
+    if (roff && e < E) roff[e] = rbefore + rincl - (e < E ? L : 0);
+    if (roff && e == 0) roff[E] = rtotal;
     if (e == 0) {
         offsets[E] = total;
         stats[MOE_STAT_OVERFLOW] = otot;
@@ -303,6 +312,170 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __r
     }
 }
 
+// ---------------------------------------------------------------------------
+// Overflow variant: acceptance by gate weight ("LLM from scratch" ch. 36 §36.3,
+// acceptance rules).  An expert over capacity keeps its C requests of largest
+// routing weight, equal weights in token order; the accepted rows keep token
+// order.  Priority key of request (t, e) = (bits of its fp32 weight << 32) |
+// ~t: the weights are positive, so their bit patterns order like the values,
+// and a larger key is a higher priority; within an expert keys are unique.
+// ---------------------------------------------------------------------------
+
+// Per 256-token block: every request (t, r) goes to position roff[e] + (its
+// first-come position among e's requests) of the request lists (key, path id);
+// paths with an invalid id get slot / row -1 here.
+__global__ __launch_bounds__(DB_TOK) void dispatch_requests_kernel(const int32_t* __restrict__ ids,
+                                                                   const float* __restrict__ w, int64_t T, int k,
+                                                                   int E, const int32_t* __restrict__ base,
+                                                                   const int32_t* __restrict__ roff,
+                                                                   unsigned long long* __restrict__ req_key,
+                                                                   int32_t* __restrict__ req_path,
+                                                                   int32_t* __restrict__ slot,
+                                                                   int32_t* __restrict__ row_of) {
+    extern __shared__ unsigned long long masks[];
+    build_masks(masks, ids, T, k, E);
+    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+    const int64_t t = (int64_t)blockIdx.x * DB_TOK + tid;
+    if (t >= T) return;
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (int r = 0; r < k; ++r) {
+        const int e = ids[t * k + r];
+        if ((unsigned)e >= (unsigned)E) {
+            slot[t * k + r] = -1;
+            row_of[t * k + r] = -1;
+            continue;
+        }
+        int rank = __popcll(masks[wave * E + e] & below);
+        for (int q = 0; q < wave; ++q) rank += __popcll(masks[q * E + e]);
+        const int64_t pos = (int64_t)roff[e] + base[(int64_t)blockIdx.x * E + e] + rank;
+        req_key[pos] = ((unsigned long long)__float_as_uint(w[t * k + r]) << 32) |
+                       (unsigned long long)(0xffffffffu - (uint32_t)t);
+        req_path[pos] = (int32_t)(t * k + r);
+    }
+}
+
+// Workgroup e: the C-th largest key of expert e's requests (radix selection, 8
+// bits a pass from the top: each pass counts the candidates' next digit with LDS
+// atomics and keeps the digit where the count from the top reaches C); 0 (every
+// key passes) when the expert is not over capacity.
+__global__ __launch_bounds__(1024) void dispatch_threshold_kernel(const int32_t* __restrict__ load,
+                                                                  const int32_t* __restrict__ roff, int C,
+                                                                  const unsigned long long* __restrict__ req_key,
+                                                                  unsigned long long* __restrict__ thresh) {
+    __shared__ int hist[256];
+    __shared__ unsigned long long s_prefix;
+    __shared__ int s_need;
+    const int e = blockIdx.x, tid = threadIdx.x;
+    const int L = load[e];
+    if (L <= C) {
+        if (tid == 0) thresh[e] = 0ull;
+        return;
+    }
+    const unsigned long long* key = req_key + roff[e];
+    if (tid == 0) {
+        s_prefix = 0ull;
+        s_need = C;
+    }
+    unsigned long long mask = 0ull;
+    for (int shift = 56; shift >= 0; shift -= 8) {
+        for (int i = tid; i < 256; i += 1024) hist[i] = 0;
+        __syncthreads();
+        const unsigned long long prefix = s_prefix;
+        for (int i = tid; i < L; i += 1024) {
+            const unsigned long long kk = key[i];
+            if ((kk & mask) == prefix) atomicAdd(&hist[(int)((kk >> shift) & 0xffull)], 1);
+        }
+        __syncthreads();
+        if (tid == 0) {
+            int need = s_need, b = 255;
+            for (; b > 0; --b) {   // from the largest digit down
+                if (hist[b] >= need) break;
+                need -= hist[b];
+            }
+            s_need = need;
+            s_prefix = prefix | ((unsigned long long)b << shift);
+        }
+        mask |= 0xffull << shift;
+        __syncthreads();
+    }
+    if (tid == 0) thresh[e] = s_prefix;
+}
+
+// Workgroup e: walks expert e's requests in first-come order; those with key >=
+// thresh[e] are accepted and numbered in that (token) order.
+__global__ __launch_bounds__(1024) void dispatch_assign_kernel(const int32_t* __restrict__ load,
+                                                               const int32_t* __restrict__ roff,
+                                                               const int32_t* __restrict__ offsets, int k,
+                                                               const unsigned long long* __restrict__ req_key,
+                                                               const int32_t* __restrict__ req_path,
+                                                               const unsigned long long* __restrict__ thresh,
+                                                               int32_t* __restrict__ slot,
+                                                               int32_t* __restrict__ row_of,
+                                                               int32_t* __restrict__ src_token) {
+    __shared__ int w_cnt[16];
+    const int e = blockIdx.x, tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+    const int L = load[e], base = roff[e], off = offsets[e];
+    const unsigned long long th = thresh[e];
+    int running = 0;
+    for (int i0 = 0; i0 < L; i0 += 1024) {
+        const int i = i0 + tid;
+        const bool in = i < L;
+        const bool acc = in && req_key[base + i] >= th;
+        const unsigned long long bal = __ballot(acc);
+        const int before_in_wave = __popcll(bal & ((1ull << lane) - 1ull));
+        if (lane == 0) w_cnt[wave] = __popcll(bal);
+        __syncthreads();
+        int before = running + before_in_wave, chunk = 0;
+        for (int q = 0; q < 16; ++q) {
+            if (q < wave) before += w_cnt[q];
+            chunk += w_cnt[q];
+        }
+        if (in) {
+            const int path = req_path[base + i];
+            if (acc) {
+                slot[path] = before;
+                row_of[path] = off + before;
+                src_token[off + before] = path / k;
+            } else {
+                slot[path] = -1;
+                row_of[path] = -1;
+            }
+        }
+        running += chunk;
+        __syncthreads();
+    }
+}
+
+// Tokens with some / all paths rejected, per 256-token block (one atomic add each).
+__global__ __launch_bounds__(DB_TOK) void dispatch_token_stats_kernel(const int32_t* __restrict__ row_of, int64_t T,
+                                                                      int k, int32_t* __restrict__ stats) {
+    __shared__ int s_drop[4], s_aff[4];
+    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+    const int64_t t = (int64_t)blockIdx.x * DB_TOK + tid;
+    int dropped = 0, affected = 0;
+    if (t < T) {
+        int nrej = 0;
+        for (int r = 0; r < k; ++r) nrej += row_of[t * k + r] < 0;
+        dropped = nrej == k;
+        affected = nrej > 0;
+    }
+    for (int o = 32; o >= 1; o >>= 1) {
+        dropped += __shfl_xor(dropped, o, MOE_WAVE);
+        affected += __shfl_xor(affected, o, MOE_WAVE);
+    }
+    if (lane == 0) {
+        s_drop[wave] = dropped;
+        s_aff[wave] = affected;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        const int dsum = s_drop[0] + s_drop[1] + s_drop[2] + s_drop[3];
+        const int asum = s_aff[0] + s_aff[1] + s_aff[2] + s_aff[3];
+        if (dsum) atomicAdd(&stats[MOE_STAT_TOKENS_DROPPED], dsum);
+        if (asum) atomicAdd(&stats[MOE_STAT_TOKENS_AFFECTED], asum);
+    }
+}
+
 // x_perm[row] = x[t] for every accepted path of token t; one wave per token.
 template <typename V>
 __global__ __launch_bounds__(256) void dispatch_gather_kernel(const V* __restrict__ x, int64_t T, int k,
@@ -377,18 +550,50 @@ hipError_t launch_balance(const moe_dims& s, const int32_t* load, const int32_t*
 }
 
 
-size_t dispatch_ws_bytes(const moe_dims& s) {
-    const int64_t NB = (s.T + DB_TOK - 1) / DB_TOK;
-    return (size_t)NB * (size_t)s.E * sizeof(int32_t);
+namespace {
+inline size_t al8(size_t v) { return (v + 7) / 8 * 8; }
 }
 
-hipError_t launch_dispatch(const moe_dims& s, const void* x, const int32_t* ids, int32_t* load, int32_t* offsets,
-                           int32_t* slot, int32_t* row_of, int32_t* src_token, void* x_perm, int32_t* stats, void* ws,
-                           hipStream_t st, int32_t* tprefix, int tile_rows) {
+size_t dispatch_ws_bytes(const moe_dims& s) {
+    const int64_t NB = (s.T + DB_TOK - 1) / DB_TOK;
+    size_t b = al8((size_t)NB * (size_t)s.E * sizeof(int32_t));   // per-block counts / base slots
+    if (s.accept_by_gate) {
+        // request offsets, thresholds, request keys and path ids
+        b += al8(sizeof(int32_t) * (s.E + 1)) + sizeof(unsigned long long) * s.E +
+             (sizeof(unsigned long long) + sizeof(int32_t)) * (size_t)s.T * s.k;
+    }
+    return b;
+}
+
+hipError_t launch_dispatch(const moe_dims& s, const void* x, const int32_t* ids, const float* topk_w, int32_t* load,
+                           int32_t* offsets, int32_t* slot, int32_t* row_of, int32_t* src_token, void* x_perm,
+                           int32_t* stats, void* ws, hipStream_t st, int32_t* tprefix, int tile_rows) {
     const int NB = (int)((s.T + DB_TOK - 1) / DB_TOK);
     int32_t* hist = static_cast<int32_t*>(ws);
     const size_t mask_lds = sizeof(unsigned long long) * 4 * s.E;
-    if (NB == 1) {
+    if (s.accept_by_gate) {
+        char* p = static_cast<char*>(ws) + al8((size_t)NB * s.E * sizeof(int32_t));
+        int32_t* roff = reinterpret_cast<int32_t*>(p);
+        p += al8(sizeof(int32_t) * (s.E + 1));
+        unsigned long long* thresh = reinterpret_cast<unsigned long long*>(p);
+        p += sizeof(unsigned long long) * s.E;
+        unsigned long long* req_key = reinterpret_cast<unsigned long long*>(p);
+        p += sizeof(unsigned long long) * (size_t)s.T * s.k;
+        int32_t* req_path = reinterpret_cast<int32_t*>(p);
+        if (NB > 0)
+            hipLaunchKernelGGL(dispatch_count_kernel, dim3(NB), dim3(DB_TOK), mask_lds, st, ids, s.T, s.k, s.E,
+                               hist);
+        hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, st, hist, NB, s.E, s.C, load, offsets,
+                           stats, tprefix, tile_rows, roff);
+        if (NB == 0) return hipGetLastError();
+        hipLaunchKernelGGL(dispatch_requests_kernel, dim3(NB), dim3(DB_TOK), mask_lds, st, ids, topk_w, s.T, s.k,
+                           s.E, hist, roff, req_key, req_path, slot, row_of);
+        hipLaunchKernelGGL(dispatch_threshold_kernel, dim3(s.E), dim3(1024), 0, st, load, roff, s.C, req_key,
+                           thresh);
+        hipLaunchKernelGGL(dispatch_assign_kernel, dim3(s.E), dim3(1024), 0, st, load, roff, offsets, s.k, req_key,
+                           req_path, thresh, slot, row_of, src_token);
+        hipLaunchKernelGGL(dispatch_token_stats_kernel, dim3(NB), dim3(DB_TOK), 0, st, row_of, s.T, s.k, stats);
+    } else if (NB == 1) {
         hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(1024), mask_lds + sizeof(int) * s.E, st, ids, s.T,
                            s.k, s.E, s.C, load, offsets, stats, tprefix, tile_rows, slot, row_of, src_token);
     } else {
@@ -397,7 +602,7 @@ hipError_t launch_dispatch(const moe_dims& s, const void* x, const int32_t* ids,
                                hist);
         }
         hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, st, hist, NB, s.E, s.C, load, offsets,
-                           stats, tprefix, tile_rows);
+                           stats, tprefix, tile_rows, (int32_t*)nullptr);
         if (NB == 0) return hipGetLastError();
         hipLaunchKernelGGL(dispatch_place_kernel, dim3(NB), dim3(DB_TOK), mask_lds, st, ids, s.T, s.k, s.E, s.C,
                            hist, offsets, slot, row_of, src_token, stats);

@@ -21,6 +21,8 @@ moe_status check_shape(const moe_shape* s, moe_dims* out) {
     if (s->E > 1024 || s->k > 32) return MOE_ERR_UNSUPPORTED;
     if (s->T * (int64_t)s->k > (int64_t)INT_MAX) return MOE_ERR_UNSUPPORTED;
     if (s->dtype == MOE_BF16 && (s->d % 8 || s->m % 8 || s->m_shared % 8)) return MOE_ERR_UNSUPPORTED;
+    if ((s->accept_by_gate != 0 && s->accept_by_gate != 1) || (s->renorm_survivors != 0 && s->renorm_survivors != 1))
+        return MOE_ERR_INVALID_ARGUMENT;
     if (out) {
         out->T = s->T;
         out->d = s->d;
@@ -31,6 +33,8 @@ moe_status check_shape(const moe_shape* s, moe_dims* out) {
         out->gate_mode = s->gate_mode;
         out->dtype = s->dtype;
         out->m_shared = s->m_shared;
+        out->accept_by_gate = s->accept_by_gate;
+        out->renorm_survivors = s->renorm_survivors;
     }
     return MOE_OK;
 }
@@ -259,17 +263,18 @@ moe_status moe_route(const moe_shape* shape, const void* x, const float* w_r, co
     return hip_status(launch_route(d, x, w_r, b_r, topk_ids, topk_w, status, ws, static_cast<hipStream_t>(stream)));
 }
 
-moe_status moe_dispatch(const moe_shape* shape, const void* x, const int32_t* topk_ids, int32_t* load,
-                        int32_t* offsets, int32_t* slot, int32_t* row_of, int32_t* src_token, void* x_perm,
-                        int32_t* stats, void* ws, size_t ws_bytes, void* stream) {
+moe_status moe_dispatch(const moe_shape* shape, const void* x, const int32_t* topk_ids, const float* topk_w,
+                        int32_t* load, int32_t* offsets, int32_t* slot, int32_t* row_of, int32_t* src_token,
+                        void* x_perm, int32_t* stats, void* ws, size_t ws_bytes, void* stream) {
     moe_dims d;
     moe_status rc = check_shape(shape, &d);
     if (rc != MOE_OK) return rc;
     if (!load || !offsets || !stats || !ws) return MOE_ERR_INVALID_ARGUMENT;
     if (d.T > 0 && (!x || !topk_ids || !slot || !row_of || !src_token || !x_perm)) return MOE_ERR_INVALID_ARGUMENT;
+    if (d.T > 0 && d.accept_by_gate && !topk_w) return MOE_ERR_INVALID_ARGUMENT;
     if (ws_bytes < moe_workspace_bytes(shape, MOE_WS_DISPATCH)) return MOE_ERR_WORKSPACE_TOO_SMALL;
-    return hip_status(launch_dispatch(d, x, topk_ids, load, offsets, slot, row_of, src_token, x_perm, stats, ws,
-                                      static_cast<hipStream_t>(stream)));
+    return hip_status(launch_dispatch(d, x, topk_ids, topk_w, load, offsets, slot, row_of, src_token, x_perm, stats,
+                                      ws, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_expert_gemm1(const moe_shape* shape, const void* x_perm, const int32_t* offsets, const void* w_gate,
@@ -343,8 +348,8 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_r, 
     hipStream_t st = static_cast<hipStream_t>(stream);
     MOE_CHECK_HIP(launch_route(d, x, w_r, b_r, topk_ids, topk_w, status, w.route, st));
     // the dispatch scan also writes the GEMMs' tile prefix at the start of the FFN workspace
-    MOE_CHECK_HIP(launch_dispatch(d, x, topk_ids, load, w.offsets, slot, w.row_of, w.src_token, w.x_perm, stats,
-                                  w.dispatch, st, static_cast<int32_t*>(w.ffn), gemm_tile_rows(d.dtype)));
+    MOE_CHECK_HIP(launch_dispatch(d, x, topk_ids, topk_w, load, w.offsets, slot, w.row_of, w.src_token, w.x_perm,
+                                  stats, w.dispatch, st, static_cast<int32_t*>(w.ffn), gemm_tile_rows(d.dtype)));
     Partials parts;   // K-split partials of H beyond the first, added by the combine
     rc = ffn_impl(d, w.x_perm, w.offsets, w_gate, w_up, w_down, w.H, w.ffn, &parts, st, true);
     if (rc != MOE_OK) return rc;

@@ -43,6 +43,8 @@ class MoEConfig:
     m_shared: int = 0
     renorm_form: str = "softmax_then_renorm"   # the oracle's literal weight form
     cfg_id: int = 0
+    accept_by_gate: bool = False      # overflow variant: capacity competition by routing weight
+    renorm_survivors: bool = False    # overflow variant: weights renormalised over accepted paths
 
     @property
     def torch_dtype(self):

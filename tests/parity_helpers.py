@@ -38,7 +38,8 @@ def shape_of(cfg: MoEConfig) -> L.MoeShape:
     if cfg.cf is not None:
         C = api.capacity(cfg.T, cfg.k, cfg.E, *cfg.cf)
         assert C == O.capacity(cfg.T, cfg.k, cfg.E, *cfg.cf)
-    return api.make_shape(cfg.T, cfg.d, cfg.m, cfg.E, cfg.k, C, cfg.gate_mode, cfg.torch_dtype, cfg.m_shared)
+    return api.make_shape(cfg.T, cfg.d, cfg.m, cfg.E, cfg.k, C, cfg.gate_mode, cfg.torch_dtype, cfg.m_shared,
+                          accept_by_gate=cfg.accept_by_gate, renorm_survivors=cfg.renorm_survivors)
 
 
 def oracle_capacity(cfg: MoEConfig):
@@ -86,10 +87,16 @@ def compare_route(cfg: MoEConfig, rt: O.Route, ids_gpu: np.ndarray, w_gpu: np.nd
     return RouteReport(near_ties=int(near.sum()), flipped_tokens=flipped)
 
 
-def compare_dispatch(cfg: MoEConfig, ids_gpu: np.ndarray, C: int, out: api.DispatchOut, x: torch.Tensor):
+def compare_dispatch(cfg: MoEConfig, ids_gpu: np.ndarray, C: int, out: api.DispatchOut, x: torch.Tensor,
+                     w_gpu: np.ndarray = None):
     """Staged check 2: the GPU's ids through the oracle's serial slot loop must give
-    the GPU's slots, row map, loads, offsets, rows and statistics bit for bit."""
-    ref = O.assign_slots(ids_gpu.astype(np.int64), cfg.E, C)
+    the GPU's slots, row map, loads, offsets, rows and statistics bit for bit.
+    With acceptance by gate weight the decision is taken on the GPU's fp32
+    weights w_gpu on both sides (the same values decide the same integers)."""
+    if cfg.accept_by_gate:
+        ref = O.assign_slots_by_gate(ids_gpu.astype(np.int64), np.asarray(w_gpu, dtype=np.float32), cfg.E, C)
+    else:
+        ref = O.assign_slots(ids_gpu.astype(np.int64), cfg.E, C)
     np.testing.assert_array_equal(out.slot.cpu().numpy(), ref.slot)
     np.testing.assert_array_equal(out.row_of.cpu().numpy(), ref.row_of)
     np.testing.assert_array_equal(out.load.cpu().numpy(), ref.load)

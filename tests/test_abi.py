@@ -34,7 +34,8 @@ def test_capacity_helper_exact_ceiling():
 
 
 def _shape(**kw):
-    base = dict(T=4096, d=4096, m=14336, E=8, k=2, capacity=0, gate_mode=0, dtype=1, m_shared=0)
+    base = dict(T=4096, d=4096, m=14336, E=8, k=2, capacity=0, gate_mode=0, dtype=1, m_shared=0,
+                accept_by_gate=0, renorm_survivors=0)
     base.update(kw)
     return L.MoeShape(*[base[f] for f, _ in L.MoeShape._fields_])
 
@@ -52,6 +53,9 @@ def test_shape_checks():
     assert L.moe_check_shape(_shape(E=2048, k=2)) == L.MOE_ERR_UNSUPPORTED
     assert L.moe_check_shape(_shape(E=64, k=33)) == L.MOE_ERR_UNSUPPORTED
     assert L.moe_check_shape(_shape(T=0)) == L.MOE_OK
+    assert L.moe_check_shape(_shape(accept_by_gate=1, renorm_survivors=1)) == L.MOE_OK
+    assert L.moe_check_shape(_shape(accept_by_gate=2)) == L.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_check_shape(_shape(renorm_survivors=-1)) == L.MOE_ERR_INVALID_ARGUMENT
 
 
 def test_max_rows_and_workspace():
@@ -79,10 +83,13 @@ def test_argument_errors_return_before_any_launch():
     big = _shape(T=16, d=64, m=64, E=128, k=8)
     assert L.moe_workspace_bytes(big, L.MOE_WS_ROUTE) >= 16 * 128 * 4
     assert L.moe_route(big, fake, fake, None, fake, fake, fake, None, 0, None) == L.MOE_ERR_WORKSPACE_TOO_SMALL
-    assert L.moe_dispatch(s, fake, fake, None, fake, fake, fake, fake, fake, fake, fake, 1 << 20,
+    assert L.moe_dispatch(s, fake, fake, None, None, fake, fake, fake, fake, fake, fake, fake, 1 << 20,
                           None) == L.MOE_ERR_INVALID_ARGUMENT
-    assert L.moe_dispatch(s, fake, fake, fake, fake, fake, fake, fake, fake, fake, fake, 1,
+    assert L.moe_dispatch(s, fake, fake, None, fake, fake, fake, fake, fake, fake, fake, fake, 1,
                           None) == L.MOE_ERR_WORKSPACE_TOO_SMALL
+    gate = _shape(accept_by_gate=1)   # the routing weights are required for acceptance by gate weight
+    assert L.moe_dispatch(gate, fake, fake, None, fake, fake, fake, fake, fake, fake, fake, fake, 1 << 30,
+                          None) == L.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_expert_ffn(s, fake, fake, fake, fake, fake, fake, fake, 1, None) == L.MOE_ERR_WORKSPACE_TOO_SMALL
     assert L.moe_shared_ffn(s, fake, fake, fake, fake, fake, fake, 1 << 20, None) == L.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_combine(s, fake, None, fake, None, fake, None) == L.MOE_ERR_INVALID_ARGUMENT

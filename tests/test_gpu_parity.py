@@ -9,6 +9,7 @@ same seeded inputs, with the staged protocol:
 """
 import json
 import os
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -40,7 +41,7 @@ def run_layer(cfg: MoEConfig, seed: int = 0, sample: int = 0):
     shape = shape_of(cfg)
     # staged calls through the C-ABI
     ids, w, status = api.route(shape, inp.x, inp.w_r, inp.b_r)
-    disp = api.dispatch(shape, inp.x, ids)
+    disp = api.dispatch(shape, inp.x, ids, w)
     H = api.expert_ffn(shape, disp.x_perm, disp.offsets, inp.w_gate, inp.w_up, inp.w_down)
     s = api.shared_ffn(shape, inp.x, inp.s_gate, inp.s_up, inp.s_down) if cfg.m_shared else None
     y = api.combine(shape, H, disp.row_of, w, s)
@@ -61,14 +62,15 @@ def run_layer(cfg: MoEConfig, seed: int = 0, sample: int = 0):
     rt = O.route(x64, wr, b, cfg.k, cfg.gate_mode, cfg.renorm_form)
     rep = compare_route(cfg, rt, ids_np, w_np)
     C = oracle_capacity(cfg) or cfg.T
-    dref = compare_dispatch(cfg, ids_np, C, disp, inp.x)
+    dref = compare_dispatch(cfg, ids_np, C, disp, inp.x, w_np.astype(np.float32))
     tokens = pick_tokens(cfg.T, sample, dref) if sample else None
     shared = None
     if cfg.m_shared:
         shared = (inp.s_gate.float().cpu().numpy(), inp.s_up.float().cpu().numpy(), inp.s_down.float().cpu().numpy())
     res = O.forward(x64, wr, b, expert_provider(inp), cfg.k, cfg.gate_mode, C=oracle_capacity(cfg), shared=shared,
                     round_h_bf16=cfg.dtype == "bf16", renorm_form=cfg.renorm_form, tokens=tokens,
-                    ids_override=ids_np)
+                    ids_override=ids_np, accept_by_gate=cfg.accept_by_gate,
+                    renorm_survivors=cfg.renorm_survivors, accept_weights=w_np.astype(np.float32))
     y_gpu = np64(y)
     if tokens is not None:
         y_gpu = y_gpu[tokens]
@@ -155,6 +157,48 @@ def test_gpu_worked_example_w2_capacity():
     assert np.count_nonzero(y - np.diag(np.diag(y))) == 0
 
 
+def _linear_combine(shape, g, x, ids, w, disp):
+    """The worked examples' linear experts F_e(x) = scale[e] x on the grouped rows,
+    combined on the GPU."""
+    offs = disp.offsets.cpu().numpy()
+    src = disp.src_token.cpu().numpy()
+    H = np.zeros((max(int(offs[-1]), 1), 4), dtype=np.float32)
+    for e in range(3):
+        for row in range(offs[e], offs[e + 1]):
+            H[row] = g["expert_scale"][e] * np.eye(4)[src[row]]
+    return api.combine(shape, torch.tensor(H, device=DEV), disp.row_of, w).cpu().numpy()
+
+
+def test_gpu_overflow_variants_worked_examples():
+    """Renormalising over the survivors gives the chapter's 3 x4 for token 4; the
+    hand-worked fixture tests/golden/w2_gate_priority_variant.json separates
+    first-come-first-served from acceptance by gate weight."""
+    g = _golden("w2_ch36_worked_example.json")
+    x = torch.eye(4, dtype=torch.float32, device=DEV)
+    w_r = torch.tensor(np.log(np.array(g["probs"])).T.astype(np.float32).copy(), device=DEV)
+    shape = api.make_shape(4, 4, 1, 3, 2, g["capacity"], L.MOE_GATE_RENORM, torch.float32, renorm_survivors=True)
+    ids, w, _ = api.route(shape, x, w_r)
+    y = _linear_combine(shape, g, x, ids, w, api.dispatch(shape, x, ids, w))
+    assert abs(y[3, 3] - g["token4_renormalise_variant_coefficient"]) < 1e-6
+
+    gv = _golden("w2_gate_priority_variant.json")
+    w_r = torch.tensor(np.log(np.array(gv["probs"])).T.astype(np.float32).copy(), device=DEV)
+    for gate, renorm, key in ((False, False, "first_come_first_served"), (True, False, "by_gate_weight"),
+                              (True, True, "by_gate_weight_renormalised_survivors")):
+        shape = api.make_shape(4, 4, 1, 3, 2, gv["capacity"], L.MOE_GATE_RENORM, torch.float32,
+                               accept_by_gate=gate, renorm_survivors=renorm)
+        ids, w, _ = api.route(shape, x, w_r)
+        disp = api.dispatch(shape, x, ids, w)
+        ids_np, slot = ids.cpu().numpy(), disp.slot.cpu().numpy()
+        rej = [[t, int(ids_np[t, r])] for t in range(4) for r in range(2) if slot[t, r] < 0]
+        if key != "by_gate_weight_renormalised_survivors":
+            assert rej == gv[key]["rejected"]
+        y = _linear_combine(shape, gv, x, ids, w, disp)
+        want = [float(Fraction(*v)) for v in gv[key]["y_diag"]]
+        np.testing.assert_allclose(np.diag(y), want, atol=1e-6)
+        assert np.count_nonzero(y - np.diag(np.diag(y))) == 0
+
+
 # ---------------------------------------------------------------------------
 # layers: full element-by-element parity at oracle-friendly sizes
 # ---------------------------------------------------------------------------
@@ -195,6 +239,17 @@ RAGGED = MoEConfig("ragged_bf16", T=2000, d=328, m=200, E=4, k=2, dtype="bf16", 
     MoEConfig("router_dot_small", T=16, d=2056, m=64, E=33, k=3, dtype="bf16", gate_mode=1, cf=None, cfg_id=35),
     MoEConfig("router_dot_many", T=5, d=512, m=64, E=700, k=8, dtype="bf16", gate_mode=0, cf=None, bias="zipf",
               cfg_id=36),
+    # overflow variants: acceptance by gate weight, weights renormalised over the survivors
+    MoEConfig("overflow_gate", T=1500, d=256, m=192, E=8, k=2, dtype="bf16", gate_mode=0, cf=(1, 1), bias="zipf",
+              accept_by_gate=True, cfg_id=38),
+    MoEConfig("overflow_renorm", T=1500, d=256, m=192, E=8, k=2, dtype="bf16", gate_mode=0, cf=(1, 1),
+              bias="zipf", renorm_survivors=True, cfg_id=39),
+    MoEConfig("overflow_both_many", T=700, d=128, m=64, E=100, k=8, dtype="bf16", gate_mode=0, cf=(1, 1),
+              bias="zipf", accept_by_gate=True, renorm_survivors=True, cfg_id=40),
+    MoEConfig("overflow_both_f32", T=300, d=64, m=64, E=6, k=3, dtype="f32", gate_mode=1, cf=(1, 2),
+              accept_by_gate=True, renorm_survivors=True, cfg_id=41),
+    MoEConfig("overflow_gate_one_block", T=200, d=64, m=64, E=16, k=4, dtype="bf16", gate_mode=0, cf=(1, 2),
+              bias="zipf", accept_by_gate=True, cfg_id=42),
     # E > 64: router scores on the expert-GEMM kernel; 300 rows end in a 44-row tile
     MoEConfig("router_thin_tail", T=300, d=1024, m=64, E=100, k=4, dtype="bf16", gate_mode=0, cf=None, cfg_id=26),
     # router with E < 8 experts over two K ranges of 4096 (d > 4096), T not a multiple of 16
