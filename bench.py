@@ -143,7 +143,8 @@ def cpu_baseline(cfg, inp, budget_tokens):
     C = None if cfg.cf is None else O.capacity(Ts, cfg.k, cfg.E, *cfg.cf)
     t0 = time.perf_counter()
     O.forward(x, wr, b, experts, cfg.k, cfg.gate_mode, C=C, shared=shared, round_h_bf16=cfg.dtype == "bf16",
-              renorm_form=cfg.renorm_form)
+              renorm_form=cfg.renorm_form, accept_by_gate=cfg.accept_by_gate,
+              renorm_survivors=cfg.renorm_survivors)
     dt = time.perf_counter() - t0
     threads = 1
     if threadpool_info is not None:
@@ -161,6 +162,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="mixtral", choices=sorted(CONFIGS))
+    ap.add_argument("--accept-by-gate", action="store_true",
+                    help="overflow variant: experts over capacity keep their highest-weight requests")
+    ap.add_argument("--renorm-survivors", action="store_true",
+                    help="overflow variant: weights renormalised over each token's accepted paths")
     ap.add_argument("--tokens", type=int, default=0,
                     help="override the workload's token count T (e.g. 1..64 for decode-sized batches)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
@@ -182,10 +187,13 @@ def main():
     cfg = CONFIGS[args.workload]
     if args.tokens:
         cfg = cfg.with_tokens(args.tokens)
+    if args.accept_by_gate or args.renorm_survivors:
+        cfg = cfg.scaled(accept_by_gate=args.accept_by_gate, renorm_survivors=args.renorm_survivors)
     log(f"[bench] workload {cfg.name}: generating inputs on the GPU")
     inp = make_inputs(cfg, seed=0, device="cuda")
     C = 0 if cfg.cf is None else api.capacity(cfg.T, cfg.k, cfg.E, *cfg.cf)
-    shape = api.make_shape(cfg.T, cfg.d, cfg.m, cfg.E, cfg.k, C, cfg.gate_mode, cfg.torch_dtype, cfg.m_shared)
+    shape = api.make_shape(cfg.T, cfg.d, cfg.m, cfg.E, cfg.k, C, cfg.gate_mode, cfg.torch_dtype, cfg.m_shared,
+                           accept_by_gate=cfg.accept_by_gate, renorm_survivors=cfg.renorm_survivors)
     layer = api.MoELayer(shape, "cuda")
     fwd = lambda: layer.forward(inp.x, inp.w_r, inp.b_r, inp.w_gate, inp.w_up, inp.w_down,  # noqa: E731
                                 inp.s_gate, inp.s_up, inp.s_down)
@@ -287,7 +295,9 @@ def main():
         "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights)",
         "config": {"workload": f"{cfg.name} MoE layer", "T": T, "d": d, "m": m, "E": cfg.E, "k": k,
                    "capacity": C or "unlimited", "gate": "switch" if cfg.gate_mode else "renorm",
-                   "shared_expert_m": cfg.m_shared, "router": "fp32", "accumulate": "fp32"},
+                   "shared_expert_m": cfg.m_shared, "router": "fp32", "accumulate": "fp32",
+                   "acceptance": "gate weight" if cfg.accept_by_gate else "token order",
+                   "rejected_paths": "renormalise survivors" if cfg.renorm_survivors else "drop"},
         "stats": {"accepted_paths": A, "overflow": stats[L.MOE_STAT_OVERFLOW],
                   "max_load": stats[L.MOE_STAT_MAX_LOAD], "rho_max": round(stats[L.MOE_STAT_MAX_LOAD] / (T * k / cfg.E), 4),
                   "tokens_dropped": stats[L.MOE_STAT_TOKENS_DROPPED], "active_experts": active},

@@ -362,9 +362,9 @@ __global__ __launch_bounds__(1024) void dispatch_threshold_kernel(const int32_t*
                                                                   const int32_t* __restrict__ roff, int C,
                                                                   const unsigned long long* __restrict__ req_key,
                                                                   unsigned long long* __restrict__ thresh) {
-    __shared__ int hist[256];
+    __shared__ int hist[256], wsum[4];
     __shared__ unsigned long long s_prefix;
-    __shared__ int s_need;
+    __shared__ int s_need, s_need_next;
     const int e = blockIdx.x, tid = threadIdx.x;
     const int L = load[e];
     if (L <= C) {
@@ -386,16 +386,33 @@ __global__ __launch_bounds__(1024) void dispatch_threshold_kernel(const int32_t*
             if ((kk & mask) == prefix) atomicAdd(&hist[(int)((kk >> shift) & 0xffull)], 1);
         }
         __syncthreads();
-        if (tid == 0) {
-            int need = s_need, b = 255;
-            for (; b > 0; --b) {   // from the largest digit down
-                if (hist[b] >= need) break;
-                need -= hist[b];
+        // counts from the largest digit down: thread i < 256 takes digit 255 - i;
+        // the digit where the running count first reaches `need` is chosen
+        const int need = s_need;
+        const int lane = tid % 64, wave = tid / 64;
+        int v = 0, incl = 0;
+        if (tid < 256) {   // waves 0..3, whole waves
+            v = hist[255 - tid];
+            incl = v;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int u = __shfl_up(incl, o, MOE_WAVE);
+                if (lane >= o) incl += u;
             }
-            s_need = need;
-            s_prefix = prefix | ((unsigned long long)b << shift);
+            if (lane == 63) wsum[wave] = incl;
+        }
+        __syncthreads();   // every wave of the workgroup
+        if (tid < 256) {
+            for (int q = 0; q < wave; ++q) incl += wsum[q];
+            const int excl = incl - v;
+            if (excl < need && incl >= need) {
+                s_need_next = need - excl;
+                s_prefix = prefix | ((unsigned long long)(255 - tid) << shift);
+            }
         }
         mask |= 0xffull << shift;
+        __syncthreads();
+        if (tid == 0) s_need = s_need_next;
         __syncthreads();
     }
     if (tid == 0) thresh[e] = s_prefix;
