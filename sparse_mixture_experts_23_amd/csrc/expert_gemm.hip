@@ -607,7 +607,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* _
                                                                int64_t part_stride,
                                                                const int32_t* __restrict__ offsets,
                                                                const int32_t* __restrict__ tprefix, int G,
-                                                               int64_t nrows, int N, int K, int S, int nsup) {
+                                                               int64_t nrows, int N, int K, int S, int nsup,
+                                                               int thin_all) {
     constexpr int BM = 256, BK = 64, WGN = 2, WAVES = 8;
     constexpr int NOPS = SWIGLU ? 2 : 1;
     constexpr int WM = 64, WN = BN / WGN;       // wave tile: 64 rows x WN columns of each operand
@@ -642,7 +643,10 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* _
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
     const int wm = wave / WGN, wn = wave % WGN;
     // thin: a last row tile of <= 64 rows behind full tiles of the same group
-    const bool thin = tc.row_end - tc.row_start <= 64 && tc.row_start > (offsets ? offsets[tc.g] : 0);
+    // (thin_all: every tile of <= 64 rows, for launches whose whole grid is one
+    // round of workgroups — small batches, where each CU streams one tile)
+    const bool thin = tc.row_end - tc.row_start <= 64 &&
+                      (thin_all || tc.row_start > (offsets ? offsets[tc.g] : 0));
     const int arow = thin ? 32 * wm : WM * wm;   // first tile row of this wave's A fragment 0
     const int n0 = tc.nt * BN;
     const int64_t wstride = (int64_t)N * K;
@@ -1040,11 +1044,19 @@ int gemm_tile_rows(int dtype) { return dtype == MOE_BF16 ? BF16_BM : F32_BM; }
 // of fewer, longer workgroups streamed faster than several rounds of short ones —
 // at most 16 and at least 4 K tiles per split.  Depends on the shape only
 // (workspace sizes follow from it).
-int small_splits(int64_t max_rows, int G, int N, int BN, int K) {
+int64_t est_tiles(int64_t max_rows, int G, int N, int BN) {
     const int64_t groups = std::max<int64_t>(std::min<int64_t>(G, max_rows), (max_rows + BF16_BM - 1) / BF16_BM);
-    const int64_t tiles = std::max<int64_t>(1, groups * ((N + BN - 1) / BN));
-    const int S = (int)std::min<int64_t>(16, MOE_GEMM_CUS / tiles);
+    return std::max<int64_t>(1, groups * ((N + BN - 1) / BN));
+}
+
+int small_splits(int64_t max_rows, int G, int N, int BN, int K) {
+    const int S = (int)std::min<int64_t>(16, MOE_GEMM_CUS / est_tiles(max_rows, G, N, BN));
     return std::max(1, std::min(S, (K / 64) / 4));
+}
+
+// whole grid (tiles x splits) expected to fit in one round on the CUs
+int one_round(int64_t max_rows, int G, int N, int BN, int S) {
+    return est_tiles(max_rows, G, N, BN) * S <= MOE_GEMM_CUS ? 1 : 0;
 }
 
 int gemm1_splits(int dtype, int64_t max_rows, int G, int N, int K) {
@@ -1075,7 +1087,7 @@ hipError_t launch_gemm1(int dtype, const void* A, const int32_t* offsets, int G,
         hipLaunchKernelGGL((gemm_bf16_asm_kernel<BF16_BN1, true, true>), dim3(grid), dim3(512), 0, st,
                            static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(w_gate),
                            static_cast<const uint16_t*>(w_up), h, part, stride, offsets, tp, G, max_rows, N, K, S,
-                           NSUPER);
+                           NSUPER, one_round(max_rows, G, N, BF16_BN1, S));
         const int64_t n4 = max_rows * (N / 4);
         hipLaunchKernelGGL(swiglu_reduce_kernel, dim3((unsigned)std::min<int64_t>((n4 + 255) / 256, 8192)),
                            dim3(256), 0, st, part, S, stride, offsets, G, max_rows, N, static_cast<uint16_t*>(h));
@@ -1083,7 +1095,7 @@ hipError_t launch_gemm1(int dtype, const void* A, const int32_t* offsets, int G,
         hipLaunchKernelGGL((gemm_bf16_asm_kernel<BF16_BN1, true>), dim3(grid), dim3(512), 0, st,
                            static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(w_gate),
                            static_cast<const uint16_t*>(w_up), h, nullptr, (int64_t)0, offsets, tp, G, max_rows, N, K, 1,
-                           NSUPER);
+                           NSUPER, one_round(max_rows, G, N, BF16_BN1, 1));
     else if (dtype == MOE_BF16)
         hipLaunchKernelGGL((gemm_bf16_kernel<BF16_BM, BF16_BN1, true>), dim3(grid), dim3(256), 0, st,
                            static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(w_gate),
@@ -1126,7 +1138,7 @@ hipError_t launch_gemm2(int dtype, const void* h, const int32_t* offsets, int G,
         hipLaunchKernelGGL((gemm_bf16_asm_kernel<BF16_BN2, false>), dim3(grid), dim3(512), 0, st,
                            static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w_down), nullptr, H, H1,
                            max_rows * N, offsets, tp, G, max_rows, N, K, S,
-                           super_width(max_rows, G, (N + BN - 1) / BN));
+                           super_width(max_rows, G, (N + BN - 1) / BN), one_round(max_rows, G, N, BF16_BN2, S));
     } else if (dtype == MOE_BF16) {
         hipLaunchKernelGGL((gemm_bf16_kernel<BF16_BM, BF16_BN2, false>), dim3(grid), dim3(256), 0, st,
                            static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w_down), nullptr, H,
@@ -1154,7 +1166,7 @@ hipError_t launch_scores_gemm(const void* x, const void* w, int64_t T, int N, in
         const unsigned grid = (tiles + XCDS - 1) / XCDS * XCDS * S;
         hipLaunchKernelGGL((gemm_bf16_asm_kernel<BF16_BN2, false>), dim3(grid), dim3(512), 0, st,
                            static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), nullptr, part,
-                           part + T * N, T * N, nullptr, nullptr, 1, T, N, K, S, NSUPER);
+                           part + T * N, T * N, nullptr, nullptr, 1, T, N, K, S, NSUPER, 0);
     } else {
         hipLaunchKernelGGL((gemm_bf16_kernel<BF16_BM, BF16_BN2, false>), dim3(tiles), dim3(256), 0, st,
                            static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), nullptr, part, nullptr,
