@@ -38,7 +38,7 @@ METRIC = "MoE-layer tokens/sec on 1 MI355X (Mixtral shape); expert-GEMM % of MFM
 # the bytes-per-KiB that the same counter reports for a plain device copy of known
 # size (`bench.py --copy-calibration`).  Valid only for the GEMM source it was
 # taken on: reported as null once expert_gemm.hip differs from that hash.
-GEMM1_TRAFFIC = {"bytes": 6409109364, "source_sha256": "92a620d35084fbc9e1b8baf674654bc8cd050a1fc93bb5c0a58281f93c4285a6"}
+GEMM1_TRAFFIC = {"bytes": 6551596715, "source_sha256": "d451bf1e08110b56241a5ce672d30578740ab6c36a8d7bceb7f1d132d1b25473"}
 GEMM_SOURCE = os.path.join(ROOT, "sparse_mixture_experts_23_amd", "csrc", "expert_gemm.hip")
 
 
