@@ -13,7 +13,9 @@
  *                  token order, overflowing paths rejected (contribute 0,
  *                  no second renormalisation)
  *       (ch. 36 §36.3 and Algorithm 36.1; "The real cost of sparse expert
- *        models" equation for C_e and O)
+ *        models" equation for C_e and O); two overflow variants are shape
+ *       fields: acceptance by gate weight, weights renormalised over the
+ *       surviving paths (ch. 36 §36.3-§36.4)
  *   experts        SwiGLU  E_i(x) = [SiLU(x W_gate,i) (*) (x W_up,i)] W_down,i
  *       ("MoE token routing" §3)
  *   shared expert  optional, applied to every token, unweighted
@@ -150,9 +152,11 @@ const char* moe_status_str(int32_t status);
  *                   so that later calls stay in bounds.  Read it after the
  *                   stream synchronises.
  *   ws              >= moe_workspace_bytes(shape, MOE_WS_ROUTE) bytes: none for bf16
- *                   activations with E <= 8 (may then be NULL with ws_bytes 0); else
- *                   the bf16 split of w_r (bf16, E <= 64), plus fp32 partial scores
- *                   when E > 64 (fp32 activations: only the [T,E] scores, E > 64) */
+ *                   activations with E <= 8 (may then be NULL with ws_bytes 0); for
+ *                   bf16 with T <= 16 and E > 8 the fp32 partial scores of each
+ *                   2048-wide K range; else the bf16 split of w_r (bf16, E <= 64),
+ *                   plus fp32 partial scores when E > 64 (fp32 activations: only the
+ *                   [T,E] scores, E > 64) */
 moe_status moe_route(const moe_shape* shape, const void* x, const float* w_r, const float* b_r,
                      int32_t* topk_ids, float* topk_w, int32_t* status, void* ws, size_t ws_bytes,
                      void* stream);
@@ -220,12 +224,16 @@ moe_status moe_expert_ffn(const moe_shape* shape, const void* x_perm, const int3
                           const void* w_gate, const void* w_up, const void* w_down, float* H,
                           void* ws, size_t ws_bytes, void* stream);
 
-/* The first half of moe_expert_ffn alone: h [max_rows,m] (dtype) out. */
+/* The first half of moe_expert_ffn alone: h [max_rows,m] (dtype) out.  ws as for
+ * moe_expert_ffn (MOE_WS_FFN is large enough); small batches use part of it for
+ * the fp32 gate/up partials of a K split. */
 moe_status moe_expert_gemm1(const moe_shape* shape, const void* x_perm, const int32_t* offsets,
                             const void* w_gate, const void* w_up, void* h,
                             void* ws, size_t ws_bytes, void* stream);
 
-/* The second half of moe_expert_ffn alone: H [max_rows,d] fp32 out from h. */
+/* The second half of moe_expert_ffn alone: H [max_rows,d] fp32 out from h.  ws as
+ * for moe_expert_ffn (MOE_WS_FFN is large enough); a K split's extra fp32
+ * partials live there and are added into H before the call's last kernel ends. */
 moe_status moe_expert_gemm2(const moe_shape* shape, const void* h, const int32_t* offsets,
                             const void* w_down, float* H, void* ws, size_t ws_bytes, void* stream);
 
@@ -240,7 +248,9 @@ moe_status moe_shared_ffn(const moe_shape* shape, const void* x, const void* s_g
 /* Weighted combine back into token order (Algorithm 36.1 combine step;
  * "MoE token routing" §3):
  *   y[t] = shared_out[t] + sum_{r=0..k-1, row_of[t,r] >= 0} topk_w[t,r] * H[row_of[t,r]]
- * summed in rank order r = 0..k-1, in fp32.
+ * summed in rank order r = 0..k-1, in fp32.  With shape->renorm_survivors each
+ * topk_w[t,r] is first divided by the sum (rank order) of the token's accepted
+ * weights.
  *   H [max_rows,d] fp32;  row_of, topk_w [T,k];  shared_out [T,d] fp32 or NULL;
  *   y [T,d] fp32 out (fully overwritten). */
 moe_status moe_combine(const moe_shape* shape, const float* H, const int32_t* row_of,
