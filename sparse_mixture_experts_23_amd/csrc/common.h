@@ -89,14 +89,31 @@ struct moe_dims {
     int renorm_survivors;   // overflow variant: weights renormalised over accepted paths
 };
 
+// Tokens per block of the dispatch's per-block expert counts, hist[b][e] = number
+// of tokens in [256 b, 256 b + 256) that selected expert e.
+constexpr int MOE_DISPATCH_BLOCK = 256;
+
 namespace moe_kernels {
 
-// Router: scores, softmax, top-k, weights.  ws holds the fp32 scores when E > 64.
+// Router: scores, softmax, top-k, weights.  ws holds the weight planes or the
+// fp32 scores (route_ws_bytes).
 // probs (nullable): also write every token's full softmax, probs[t E + e].
+// hist (nullable): the dispatch's per-block expert counts ([ceil(T / 256)][E]
+// int32).  Where the router path can count them while it selects (E <= 8, bf16),
+// it zeroes and fills them and sets *hist_done; otherwise it leaves them alone.
 size_t route_ws_bytes(const moe_dims& s);
 hipError_t launch_route(const moe_dims& s, const void* x, const float* w_r, const float* b_r,
                         int32_t* topk_ids, float* topk_w, int32_t* status, void* ws, hipStream_t st,
-                        float* probs = nullptr);
+                        float* probs = nullptr, int32_t* hist = nullptr, bool* hist_done = nullptr);
+// Small batches (bf16, 0 < T <= 16, E <= 256, acceptance in token order): route,
+// dispatch and row gather of the whole layer front in one workgroup (after a
+// split-K dot kernel for E > 8); the same outputs as launch_route followed by
+// launch_dispatch, and the GEMMs' tile prefix in tprefix.  ws: route_ws_bytes.
+bool front_fused_ok(const moe_dims& s);
+hipError_t launch_front(const moe_dims& s, const void* x, const float* w_r, const float* b_r, int32_t* topk_ids,
+                        float* topk_w, int32_t* status, void* ws, hipStream_t st, int32_t* load, int32_t* offsets,
+                        int32_t* slot, int32_t* row_of, int32_t* src_token, void* x_perm, int32_t* stats,
+                        int32_t* tprefix, int tile_rows);
 // prob_sum[e] = sum_t probs[t E + e] in a fixed order.
 hipError_t launch_prob_sum(const moe_dims& s, const float* probs, float* prob_sum, hipStream_t st);
 // Balance statistics from the loads, the dispatch statistics and prob_sum (out: see moe_balance).
@@ -105,13 +122,18 @@ hipError_t launch_balance(const moe_dims& s, const int32_t* load, const int32_t*
 
 // Dispatch.
 size_t dispatch_ws_bytes(const moe_dims& s);
+// Whether launch_dispatch reads the per-block expert counts (more than one token
+// block, or acceptance by gate weight); a single block is counted in place.
+bool dispatch_uses_hist(const moe_dims& s);
 // tprefix (nullable): also write the grouped GEMMs' tile prefix for tiles of
 // tile_rows rows (gemm_tile_rows), so the GEMM launches can skip computing it.
 // topk_w: the routing weights (read only when s.accept_by_gate).
+// ws starts with the per-block expert counts (dispatch_hist); hist_ready: the
+// router has already written them, so the counting kernel is skipped.
 hipError_t launch_dispatch(const moe_dims& s, const void* x, const int32_t* ids, const float* topk_w,
                            int32_t* load, int32_t* offsets, int32_t* slot, int32_t* row_of, int32_t* src_token,
                            void* x_perm, int32_t* stats, void* ws, hipStream_t st,
-                           int32_t* tprefix = nullptr, int tile_rows = 0);
+                           int32_t* tprefix = nullptr, int tile_rows = 0, bool hist_ready = false);
 
 // Grouped expert GEMMs.  offsets == nullptr means one group covering rows [0, nrows).
 size_t gemm_ws_bytes(int G);

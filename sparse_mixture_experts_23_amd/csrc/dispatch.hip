@@ -17,10 +17,11 @@
 //           the result never depends on thread timing
 //   gather: x_perm[row] = x[token], one wave per token, 16-byte vector copies.
 #include "common.h"
+#include "dispatch_block.h"
 
 namespace {
 
-constexpr int DB_TOK = 256;   // tokens per count/place workgroup (4 waves x 64)
+constexpr int DB_TOK = MOE_DISPATCH_BLOCK;   // tokens per count/place workgroup (4 waves x 64)
 
 __device__ __forceinline__ void build_masks(unsigned long long* masks, const int32_t* __restrict__ ids, int64_t T,
                                             int k, int E) {
@@ -182,9 +183,7 @@ __global__ __launch_bounds__(DB_TOK) void dispatch_place_kernel(const int32_t* _
 }
 
 // T <= 256 (one token block): count, scan and place in one workgroup of 1024
-// threads — the same integer results as the three kernels above, with the block
-// base slots all 0 (no earlier block).  masks: 4 E uint64 of dynamic LDS, then
-// s_off[E] int32.
+// threads.  masks: 4 E uint64 of dynamic LDS, then s_off[E] int32.
 __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __restrict__ ids, int64_t T, int k,
                                                               int E, int C, int32_t* __restrict__ load,
                                                               int32_t* __restrict__ offsets,
@@ -195,121 +194,8 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __r
                                                               int32_t* __restrict__ src_token) {
     extern __shared__ unsigned long long masks[];
     int* s_off = reinterpret_cast<int*>(masks + 4 * E);
-    __shared__ int s_sum[16], s_over[16], s_max[16], s_tiles[16], s_drop[16], s_aff[16];
-    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
-    for (int i = tid; i < 4 * E; i += 1024) masks[i] = 0ull;
-    __syncthreads();
-    if (tid < T) {
-        for (int r = 0; r < k; ++r) {
-            const int e = ids[tid * k + r];
-            if ((unsigned)e < (unsigned)E) atomicOr(&masks[(tid / 64) * E + e], 1ull << (tid % 64));
-        }
-    }
-    __syncthreads();
-    // per expert: L_e, accepted, tiles; scans over e (thread e < E <= 1024)
-    const int e = tid;
-    int L = 0;
-    if (e < E) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) L += __popcll(masks[w * E + e]);
-        load[e] = L;
-    }
-    const int acc = e < E ? min(L, C) : 0;
-    const int over = e < E ? max(L - C, 0) : 0;
-    const int tiles = tprefix ? (acc + tile_rows - 1) / tile_rows : 0;
-    int incl = acc, tincl = tiles;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int v = __shfl_up(incl, o, MOE_WAVE);
-        const int tv = __shfl_up(tincl, o, MOE_WAVE);
-        if (lane >= o) {
-            incl += v;
-            tincl += tv;
-        }
-    }
-    int ov = over, mx = L;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        ov += __shfl_xor(ov, o, MOE_WAVE);
-        mx = max(mx, __shfl_xor(mx, o, MOE_WAVE));
-    }
-    if (lane == 63) {
-        s_sum[wave] = incl;
-        s_tiles[wave] = tincl;
-    }
-    if (lane == 0) {
-        s_over[wave] = ov;
-        s_max[wave] = mx;
-    }
-    __syncthreads();
-    int before = 0, total = 0, otot = 0, mtot = 0, tbefore = 0, ttotal = 0;
-    for (int w = 0; w < 16; ++w) {
-        if (w < wave) {
-            before += s_sum[w];
-            tbefore += s_tiles[w];
-        }
-        total += s_sum[w];
-        ttotal += s_tiles[w];
-        otot += s_over[w];
-        mtot = max(mtot, s_max[w]);
-    }
-    if (e < E) {
-        const int off = before + incl - acc;
-        offsets[e] = off;
-        s_off[e] = off;
-        if (tprefix) tprefix[e] = tbefore + tincl - tiles;
-    }
-    if (e == 0) {
-        offsets[E] = total;
-        if (tprefix) tprefix[E] = ttotal;
-        stats[MOE_STAT_OVERFLOW] = otot;
-        stats[MOE_STAT_ACCEPTED] = total;
-        stats[MOE_STAT_MAX_LOAD] = mtot;
-        for (int i = MOE_STAT_TOKENS_AFFECTED + 1; i < MOE_STAT_COUNT; ++i) stats[i] = 0;
-    }
-    __syncthreads();
-    // place: token t = tid, rank = earlier tokens (lower lanes, lower waves) with e
-    int dropped = 0, affected = 0;
-    if (tid < T) {
-        const unsigned long long below = (1ull << lane) - 1ull;
-        int nrej = 0;
-        for (int r = 0; r < k; ++r) {
-            const int ee = ids[tid * k + r];
-            int c = -1, row = -1;
-            if ((unsigned)ee < (unsigned)E) {
-                int rank = __popcll(masks[wave * E + ee] & below);
-                for (int w = 0; w < wave; ++w) rank += __popcll(masks[w * E + ee]);
-                if (rank < C) {
-                    c = rank;
-                    row = s_off[ee] + rank;
-                    src_token[row] = tid;
-                }
-            }
-            slot[tid * k + r] = c;
-            row_of[tid * k + r] = row;
-            nrej += c < 0;
-        }
-        dropped = nrej == k;
-        affected = nrej > 0;
-    }
-    for (int o = 32; o >= 1; o >>= 1) {
-        dropped += __shfl_xor(dropped, o, MOE_WAVE);
-        affected += __shfl_xor(affected, o, MOE_WAVE);
-    }
-    if (lane == 0) {
-        s_drop[wave] = dropped;
-        s_aff[wave] = affected;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        int dsum = 0, asum = 0;
-        for (int w = 0; w < 16; ++w) {
-            dsum += s_drop[w];
-            asum += s_aff[w];
-        }
-        stats[MOE_STAT_TOKENS_DROPPED] = dsum;
-        stats[MOE_STAT_TOKENS_AFFECTED] = asum;
-    }
+    dispatch_one_block(ids, T, k, E, C, load, offsets, stats, tprefix, tile_rows, slot, row_of, src_token, masks,
+                       s_off, nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -571,6 +457,8 @@ namespace {
 inline size_t al8(size_t v) { return (v + 7) / 8 * 8; }
 }
 
+bool dispatch_uses_hist(const moe_dims& s) { return s.accept_by_gate || s.T > DB_TOK; }
+
 size_t dispatch_ws_bytes(const moe_dims& s) {
     const int64_t NB = (s.T + DB_TOK - 1) / DB_TOK;
     size_t b = al8((size_t)NB * (size_t)s.E * sizeof(int32_t));   // per-block counts / base slots
@@ -584,7 +472,8 @@ size_t dispatch_ws_bytes(const moe_dims& s) {
 
 hipError_t launch_dispatch(const moe_dims& s, const void* x, const int32_t* ids, const float* topk_w, int32_t* load,
                            int32_t* offsets, int32_t* slot, int32_t* row_of, int32_t* src_token, void* x_perm,
-                           int32_t* stats, void* ws, hipStream_t st, int32_t* tprefix, int tile_rows) {
+                           int32_t* stats, void* ws, hipStream_t st, int32_t* tprefix, int tile_rows,
+                           bool hist_ready) {
     const int NB = (int)((s.T + DB_TOK - 1) / DB_TOK);
     int32_t* hist = static_cast<int32_t*>(ws);
     const size_t mask_lds = sizeof(unsigned long long) * 4 * s.E;
@@ -597,7 +486,7 @@ hipError_t launch_dispatch(const moe_dims& s, const void* x, const int32_t* ids,
         unsigned long long* req_key = reinterpret_cast<unsigned long long*>(p);
         p += sizeof(unsigned long long) * (size_t)s.T * s.k;
         int32_t* req_path = reinterpret_cast<int32_t*>(p);
-        if (NB > 0)
+        if (NB > 0 && !hist_ready)
             hipLaunchKernelGGL(dispatch_count_kernel, dim3(NB), dim3(DB_TOK), mask_lds, st, ids, s.T, s.k, s.E,
                                hist);
         hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, st, hist, NB, s.E, s.C, load, offsets,
@@ -614,7 +503,7 @@ hipError_t launch_dispatch(const moe_dims& s, const void* x, const int32_t* ids,
         hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(1024), mask_lds + sizeof(int) * s.E, st, ids, s.T,
                            s.k, s.E, s.C, load, offsets, stats, tprefix, tile_rows, slot, row_of, src_token);
     } else {
-        if (NB > 0) {
+        if (NB > 0 && !hist_ready) {
             hipLaunchKernelGGL(dispatch_count_kernel, dim3(NB), dim3(DB_TOK), mask_lds, st, ids, s.T, s.k, s.E,
                                hist);
         }

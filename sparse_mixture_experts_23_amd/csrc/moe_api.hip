@@ -346,10 +346,20 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_r, 
     ForwardWs w = carve_forward(d, ws);
     if (ws_bytes < w.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    MOE_CHECK_HIP(launch_route(d, x, w_r, b_r, topk_ids, topk_w, status, w.route, st));
-    // the dispatch scan also writes the GEMMs' tile prefix at the start of the FFN workspace
-    MOE_CHECK_HIP(launch_dispatch(d, x, topk_ids, topk_w, load, w.offsets, slot, w.row_of, w.src_token, w.x_perm,
-                                  stats, w.dispatch, st, static_cast<int32_t*>(w.ffn), gemm_tile_rows(d.dtype)));
+    // the dispatch (or the one-workgroup front of small batches) also writes the
+    // GEMMs' tile prefix at the start of the FFN workspace
+    int32_t* tprefix = static_cast<int32_t*>(w.ffn);
+    if (front_fused_ok(d)) {
+        MOE_CHECK_HIP(launch_front(d, x, w_r, b_r, topk_ids, topk_w, status, w.route, st, load, w.offsets, slot,
+                                   w.row_of, w.src_token, w.x_perm, stats, tprefix, gemm_tile_rows(d.dtype)));
+    } else {
+        // where it can, the router also counts the dispatch's per-block expert loads
+        bool counted = false;
+        MOE_CHECK_HIP(launch_route(d, x, w_r, b_r, topk_ids, topk_w, status, w.route, st, nullptr,
+                                   dispatch_uses_hist(d) ? static_cast<int32_t*>(w.dispatch) : nullptr, &counted));
+        MOE_CHECK_HIP(launch_dispatch(d, x, topk_ids, topk_w, load, w.offsets, slot, w.row_of, w.src_token,
+                                      w.x_perm, stats, w.dispatch, st, tprefix, gemm_tile_rows(d.dtype), counted));
+    }
     Partials parts;   // K-split partials of H beyond the first, added by the combine
     rc = ffn_impl(d, w.x_perm, w.offsets, w_gate, w_up, w_down, w.H, w.ffn, &parts, st, true);
     if (rc != MOE_OK) return rc;

@@ -13,8 +13,9 @@
 // x * w_r is formed as three exact bf16 x bf16 products accumulated in fp32 on the
 // MFMA units -- an fp32 dot product up to summation order.
 //
-// E <= 8 (bf16 activations): one fused kernel of fp32 fused multiply-adds with the
-//   fp32 weights held in registers (route_valu_kernel); no split of w_r.
+// E <= 8 (bf16 activations): a small kernel writes the planes as ready-made MFMA
+//   operands (two 16-column tiles: hi | mid and lo | 0), then one fused kernel
+//   computes the scores of 16 tokens on 8 waves and selects (route_mfma8_kernel).
 // E <= 64: one fused kernel; 8 waves share 16 tokens, each wave takes one K
 //   slice with all its loads in flight at once, the slices are summed in LDS in a
 //   fixed order and the waves select.
@@ -24,10 +25,12 @@
 //   GPU); a selection kernel with one wave per token adds, per expert, the three
 //   plane columns of every split in a fixed order.
 // Selection: k rounds of a 64-bit (order-preserving score key, ~id) wave arg-max.
-// Everything is deterministic: no atomics, fixed summation orders.
+// Everything is deterministic: fixed summation orders; the only atomics are the
+// integer expert counts the E <= 8 path adds for the dispatch.
 #include <algorithm>
 
 #include "common.h"
+#include "dispatch_block.h"
 
 namespace {
 
@@ -88,10 +91,12 @@ __device__ __forceinline__ floatx4_t mfma3(const bf16x8_t a, const uint4 H, cons
 // ---------------------------------------------------------------------------
 // selection and weights for one token (called by a whole wave)
 // ---------------------------------------------------------------------------
+// b_r, topk_ids and topk_w may point to global memory or LDS.  cnt (nullable,
+// LDS): cnt[e] += 1 for every expert id written.
 template <int EPL>
 __device__ void select_token(const float* __restrict__ row, const float* __restrict__ b_r, int E, int k, int mode,
                              int64_t t, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
-                             int32_t* __restrict__ status, float* __restrict__ probs) {
+                             int32_t* __restrict__ status, float* __restrict__ probs, int* cnt = nullptr) {
     const int lane = threadIdx.x % 64;
     float v[EPL];
     bool bad = false;
@@ -109,6 +114,7 @@ __device__ void select_token(const float* __restrict__ row, const float* __restr
         if (lane < k) {
             topk_ids[t * k + lane] = lane;
             topk_w[t * k + lane] = 0.f;
+            if (cnt) atomicAdd(&cnt[lane], 1);
         }
         if (lane == 0) *status = MOE_ERR_NONFINITE_LOGIT;
         if (probs) {
@@ -173,123 +179,125 @@ __device__ void select_token(const float* __restrict__ row, const float* __restr
     if (lane < k) {
         topk_ids[t * k + lane] = my_e;
         topk_w[t * k + lane] = wgt;
+        if (cnt) atomicAdd(&cnt[my_e], 1);
     }
 }
 
 // ---------------------------------------------------------------------------
-// E <= 8, bf16 activations: fp32 FMA dot products, weights held in registers
+// E <= 8, bf16 activations: fused scores + selection on MFMA, 16 tokens per workgroup
 // ---------------------------------------------------------------------------
 //
-// 512 threads; thread j owns the K chunk [kr + 8 j, kr + 8 j + 8) of each K range
-// kr (steps of 4096) and keeps that chunk of all E weight rows in registers (fp32,
-// exactly as given).  Loads are unconditional (addresses clamped, invalid values
-// zeroed afterwards), so the wave's VT activation rows stream in while the first
-// tokens are already being multiplied.  Per token the lane's 8 expert partials
-// are reduce-scattered across each 16-lane row with DPP moves (no LDS round
-// trip), one value per (row, expert) goes to LDS, and the scores are summed over
-// (K range, wave, row) in a fixed order.
+// route_prep_kernel lays the three bf16 planes of w_r out as the B operands of
+// v_mfma_f32_16x16x32_bf16 for two 16-column tiles, tile 0 = [hi e0..7 | mid e0..7]
+// and tile 1 = [lo e0..7 | 0]: entry (s, tile, lane) is the 8 bf16 that lane
+// `lane` (column lane % 16, K group lane / 16) supplies for the K step of 32 that
+// starts at 32 s, so each operand load of a wave is one contiguous 1 KB read.  The
+// same launch clears the status word and the dispatch's per-block counts.
+//
+// route_mfma8_kernel: 8 waves; wave w takes K steps [16 w, 16 w + 16) of every
+// chunk of 128 steps and issues all activation and operand loads of the chunk
+// before its first MFMA.  Per (token, expert) a lane adds its hi column, the mid
+// column one lane over and its lo column; the waves' partials are summed in wave
+// order in LDS, then each wave selects two tokens and counts the chosen experts
+// into the block's dispatch counts (integer adds: order-independent).
+constexpr int M8_TOK = 16;                        // tokens per workgroup
+constexpr int M8_WAVES = 8;
+constexpr int M8_THREADS = 64 * M8_WAVES;
+constexpr int M8_STEPS = 16;                      // K steps of 32 per wave per chunk
+constexpr int M8_CHUNK = M8_WAVES * M8_STEPS;     // K steps per chunk (4096 elements)
 
-constexpr int VT = 8;              // tokens per workgroup
-constexpr int V_THREADS = 512;
-constexpr int V_WAVES = V_THREADS / 64;
-constexpr int V_KR = 8 * V_THREADS;    // K elements per range
-constexpr int V_MAXKR = 2;             // d <= 8192
+__host__ __device__ inline int m8_steps(int d) { return (d + 31) / 32; }
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+__global__ __launch_bounds__(256) void route_prep_kernel(const float* __restrict__ w_r, int d, int E,
+                                                         uint4* __restrict__ bop, int NS,
+                                                         int32_t* __restrict__ status, int32_t* __restrict__ hist,
+                                                         int64_t nhist) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i == 0) *status = MOE_OK;
+    if (hist)
+        for (int64_t h = i; h < nhist; h += (int64_t)gridDim.x * blockDim.x) hist[h] = 0;
+    if (i >= (int64_t)NS * 128) return;
+    const int s = (int)(i / 128), tile = (int)(i / 64) % 2, lane = (int)(i % 64);
+    const int c = lane % 16, e = c % 8, kk = 32 * s + 8 * (lane / 16);
+    uint4 out = {0u, 0u, 0u, 0u};
+    if (e < E && kk < d && (tile == 0 || c < 8)) {   // d % 8 == 0: a group of 8 is wholly in or out
+        const float4* src = reinterpret_cast<const float4*>(w_r + (int64_t)e * d + kk);
+        uint4 H, M, L;
+        split3(src[0], src[1], H, M, L);
+        out = tile == 1 ? L : (c < 8 ? H : M);
+    }
+    bop[i] = out;
 }
 
-// v[e], e < 8, summed over the 16 lanes of a row; lane l ends with expert l & 7.
-// Pairings: l <-> 7 - l within 8 lanes (row half mirror), l <-> l ^ 2, l <-> l ^ 1
-// (quad permutes), then l <-> l + 8 mod 16 (row rotate by 8).
-__device__ __forceinline__ float reduce_row8(const float (&v)[8]) {
-    const int lane = threadIdx.x % 64;
-    const bool b0 = lane & 1, b1 = lane & 2, b2 = lane & 4;
-    float u[4], w2[2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {   // keep experts 4 b2 + 0..3
-        const float keep = b2 ? v[4 + i] : v[i], give = b2 ? v[i] : v[4 + i];
-        u[i] = keep + dpp_mov<0x141>(give);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {   // keep experts 4 b2 + 2 b1 + 0..1
-        const float keep = b1 ? u[2 + i] : u[i], give = b1 ? u[i] : u[2 + i];
-        w2[i] = keep + dpp_mov<0x4E>(give);
-    }
-    float r = (b0 ? w2[1] : w2[0]) + dpp_mov<0xB1>(b0 ? w2[0] : w2[1]);
-    return r + dpp_mov<0x128>(r);
-}
-
-__global__ __launch_bounds__(V_THREADS) void route_valu_kernel(const uint16_t* __restrict__ x,
-                                                               const float* __restrict__ w_r,
-                                                               const float* __restrict__ b_r, int64_t T, int d,
-                                                               int E, int k, int mode, int32_t* __restrict__ topk_ids,
-                                                               float* __restrict__ topk_w,
-                                                               int32_t* __restrict__ status,
-                                                               float* __restrict__ probs, int zero_status) {
-    constexpr int NPART = V_WAVES * 4;                // (wave, row) partials per K range
-    __shared__ float part[V_MAXKR * NPART * VT * 8];
-    __shared__ float lg[VT * 8];
+__global__ __launch_bounds__(M8_THREADS) void route_mfma8_kernel(const uint16_t* __restrict__ x,
+                                                                 const uint4* __restrict__ bop,
+                                                                 const float* __restrict__ b_r, int64_t T, int d,
+                                                                 int E, int k, int mode,
+                                                                 int32_t* __restrict__ topk_ids,
+                                                                 float* __restrict__ topk_w,
+                                                                 int32_t* __restrict__ status,
+                                                                 float* __restrict__ probs,
+                                                                 int32_t* __restrict__ hist) {
+    __shared__ float part[M8_WAVES * M8_TOK * 8];
+    __shared__ float lg[M8_TOK * 8];
+    __shared__ int cnt[8];
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
-    // a one-workgroup launch clears the status word itself (before the barriers
-    // that precede every selection)
-    if (zero_status && tid == 0) *status = MOE_OK;
-    const int64_t t0 = (int64_t)blockIdx.x * VT;
-    const int nkr = (d + V_KR - 1) / V_KR;
-    for (int kr = 0; kr < nkr; ++kr) {
-        const int c = kr * V_KR + 8 * tid;            // this thread's chunk (d % 8 == 0: wholly in or out)
-        const bool c_ok = c < d;
-        const int cc = c_ok ? c : d - 8;
-        float w[8][8];
+    const int lr = lane % 16, grp = lane / 16;   // A: token row lr; B and D: column lr
+    if (tid < 8) cnt[tid] = 0;
+    const int64_t t0 = (int64_t)blockIdx.x * M8_TOK;
+    // rows past T repeat row T - 1 (never selected)
+    const uint16_t* xrow = x + min(t0 + lr, T - 1) * (int64_t)d;
+    const int NS = m8_steps(d);
+    floatx4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = wave * M8_STEPS; s0 < NS; s0 += M8_CHUNK) {
+        // Every load is unconditional from a clamped, valid address, so all of them
+        // are in flight together; activation groups past d (or past the last step)
+        // are zeroed afterwards, and the operands there are 0 (the prep wrote
+        // zeros) or a repeat of the last step (multiplied by the zeroed activations).
+        uint4 xv[M8_STEPS], b0[M8_STEPS], b1[M8_STEPS];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float* src = w_r + (int64_t)min(e, E - 1) * d + cc;
-            const float4 lo = *reinterpret_cast<const float4*>(src);
-            const float4 hi = *reinterpret_cast<const float4*>(src + 4);
-            const bool ok = c_ok && e < E;
-            w[e][0] = ok ? lo.x : 0.f; w[e][1] = ok ? lo.y : 0.f; w[e][2] = ok ? lo.z : 0.f; w[e][3] = ok ? lo.w : 0.f;
-            w[e][4] = ok ? hi.x : 0.f; w[e][5] = ok ? hi.y : 0.f; w[e][6] = ok ? hi.z : 0.f; w[e][7] = ok ? hi.w : 0.f;
-        }
-        uint4 xv[VT];
-#pragma unroll
-        for (int r = 0; r < VT; ++r) {
-            const int64_t t = min(t0 + r, T - 1);       // rows past T repeat row T - 1 (never selected)
-            xv[r] = *reinterpret_cast<const uint4*>(x + t * (int64_t)d + cc);
+        for (int j = 0; j < M8_STEPS; ++j) {
+            const int kk = min(32 * min(s0 + j, NS - 1) + 8 * grp, d - 8);
+            xv[j] = *reinterpret_cast<const uint4*>(xrow + kk);
         }
 #pragma unroll
-        for (int r = 0; r < VT; ++r) {
-            const uint32_t q[4] = {xv[r].x, xv[r].y, xv[r].z, xv[r].w};
-            float xf[8];
+        for (int j = 0; j < M8_STEPS; ++j) {
+            const int64_t s = min(s0 + j, NS - 1);
+            b0[j] = bop[s * 128 + lane];
+            b1[j] = bop[s * 128 + 64 + lane];
+        }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {   // a chunk past d contributes 0 (not 0 * x, which may be NaN)
-                xf[2 * j] = c_ok ? __uint_as_float(q[j] << 16) : 0.f;
-                xf[2 * j + 1] = c_ok ? __uint_as_float(q[j] & 0xffff0000u) : 0.f;
-            }
-            float acc[8];
+        for (int j = 0; j < M8_STEPS; ++j) {
+            if (!(s0 + j < NS && 32 * (s0 + j) + 8 * grp < d)) xv[j] = uint4{0u, 0u, 0u, 0u};
+        }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float s = 0.f;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) s = fmaf(xf[j], w[e][j], s);
-                acc[e] = s;
-            }
-            const float sum = reduce_row8(acc);
-            if ((lane & 15) < 8) part[((kr * NPART + wave * 4 + lane / 16) * VT + r) * 8 + (lane & 7)] = sum;
+        for (int j = 0; j < M8_STEPS; ++j) {
+            a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xv[j]), as_bf16x8(b0[j]), a0, 0, 0, 0);
+            a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xv[j]), as_bf16x8(b1[j]), a1, 0, 0, 0);
         }
     }
+    // lane (lr, grp) holds column lr of both tiles for tokens 4 grp + i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float mid = __shfl_xor(a0[i], 8, MOE_WAVE);
+        if (lr < 8) part[(wave * M8_TOK + 4 * grp + i) * 8 + lr] = (a0[i] + mid) + a1[i];
+    }
     __syncthreads();
-    if (tid < VT * 8) {
-        const int r = tid / 8, e = tid % 8;
+    if (tid < M8_TOK * 8) {
         float sc = 0.f;
-        for (int p = 0; p < nkr * NPART; ++p) sc += part[(p * VT + r) * 8 + e];
-        lg[r * 8 + e] = sc;
+#pragma unroll
+        for (int w = 0; w < M8_WAVES; ++w) sc += part[w * M8_TOK * 8 + tid];
+        lg[tid] = sc;
     }
     __syncthreads();
-    for (int r = wave; r < VT; r += V_WAVES) {
+    for (int r = wave; r < M8_TOK; r += M8_WAVES) {
         const int64_t t = t0 + r;
         if (t >= T) break;
-        select_token<1>(lg + r * 8, b_r, E, k, mode, t, topk_ids, topk_w, status, probs);
+        select_token<1>(lg + r * 8, b_r, E, k, mode, t, topk_ids, topk_w, status, probs, hist ? cnt : nullptr);
+    }
+    if (hist) {   // uniform: every thread reaches the barrier
+        __syncthreads();
+        if (tid < E && cnt[tid]) atomicAdd(&hist[(t0 / MOE_DISPATCH_BLOCK) * E + tid], cnt[tid]);
     }
 }
 
@@ -483,8 +491,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
 // upcast activations (fp32 FMAs), then the (token, expert) sums are reduced over
 // the wave with a fixed xor pattern and over the 4 waves in order:
 // part[(q T + t) E + e], no bias (the selection adds the K ranges in order, then
-// the bias).  Same arithmetic class as route_valu_kernel: an fp32 dot product up
-// to summation order.
+// the bias).  An fp32 dot product up to summation order, like the plane split.
 constexpr int DOT_TMAX = 16;
 constexpr int DOT_EW = 2;
 
@@ -545,6 +552,176 @@ __global__ __launch_bounds__(256) void route_dot_kernel(const uint16_t* __restri
     }
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// v[e], e < 8, summed over the 16 lanes of a row; lane l ends with expert l & 7.
+// Pairings: l <-> 7 - l within 8 lanes (row half mirror), l <-> l ^ 2, l <-> l ^ 1
+// (quad permutes), then l <-> l + 8 mod 16 (row rotate by 8).
+__device__ __forceinline__ float reduce_row8(const float (&v)[8]) {
+    const int lane = threadIdx.x % 64;
+    const bool b0 = lane & 1, b1 = lane & 2, b2 = lane & 4;
+    float u[4], w2[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {   // keep experts 4 b2 + 0..3
+        const float keep = b2 ? v[4 + i] : v[i], give = b2 ? v[i] : v[4 + i];
+        u[i] = keep + dpp_mov<0x141>(give);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {   // keep experts 4 b2 + 2 b1 + 0..1
+        const float keep = b1 ? u[2 + i] : u[i], give = b1 ? u[i] : u[2 + i];
+        w2[i] = keep + dpp_mov<0x4E>(give);
+    }
+    float r = (b0 ? w2[1] : w2[0]) + dpp_mov<0xB1>(b0 ? w2[0] : w2[1]);
+    return r + dpp_mov<0x128>(r);
+}
+
+// ---------------------------------------------------------------------------
+// T <= 16, bf16, E <= 256: the front of the layer in one workgroup
+// ---------------------------------------------------------------------------
+//
+// One workgroup of 1024 threads clears the status word, forms the scores, selects
+// (wave t takes token t) and, with DISPATCH, dispatches the block (the same
+// integer results as the dispatch kernels) and copies every accepted row to its
+// grouped position -- one launch where the large-batch path takes four or more.
+// Scores for E <= 8: fp32 FMA dot products.  Thread j holds the K chunk [4 j,
+// 4 j + 4) of every K range of 4096 for all E weight rows (fp32, as given) and
+// per token reduces its 8 expert partials over each 16-lane row with DPP moves;
+// the rows' sums are accumulated in LDS over the K ranges in order, then added
+// over the rows in order.  E > 8: the sum, in split order, of route_dot_kernel's
+// partials.
+constexpr int FS_TOK = DOT_TMAX;
+constexpr int FS_EMAX = 256;
+constexpr int FS_THREADS = 1024;
+constexpr int FS_WAVES = FS_THREADS / 64;
+constexpr int FS_KR = 4 * FS_THREADS;   // K elements per range
+
+template <int EPL, bool DISPATCH>
+__global__ __launch_bounds__(FS_THREADS) void front_small_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ w_r, const float* __restrict__ dpart, int KS,
+    const float* __restrict__ b_r, int64_t T, int d, int E, int k, int C, int mode, int32_t* __restrict__ topk_ids,
+    float* __restrict__ topk_w, int32_t* __restrict__ status, float* __restrict__ probs, int32_t* __restrict__ load,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ slot, int32_t* __restrict__ row_of,
+    int32_t* __restrict__ src_token, uint4* __restrict__ x_perm, int32_t* __restrict__ stats,
+    int32_t* __restrict__ tprefix, int tile_rows) {
+    __shared__ float lg[FS_TOK * FS_EMAX];
+    __shared__ float part[64 * FS_TOK * 8];   // (16-lane row, token, expert)
+    __shared__ float s_bias[FS_EMAX];
+    __shared__ unsigned long long masks[DISPATCH ? 4 * FS_EMAX : 1];
+    __shared__ int s_off[DISPATCH ? FS_EMAX : 1];
+    __shared__ int s_ids[DISPATCH ? FS_TOK * 32 : 1];
+    __shared__ float s_w[DISPATCH ? FS_TOK * 32 : 1];
+    __shared__ int s_row[DISPATCH ? FS_TOK * 32 : 1];
+    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+    if (tid == 0) *status = MOE_OK;   // before the barriers that precede every selection
+    const float bias = (tid < E && b_r) ? b_r[tid] : 0.f;   // to LDS before the selection's barrier
+    if (E <= 8) {
+        const int row = tid / 16;   // 16-lane row, 0..63
+        for (int kr = 0; kr * FS_KR < d; ++kr) {
+            const int c = kr * FS_KR + 4 * tid;
+            const bool c_ok = c < d;   // d % 8 == 0: a chunk of 4 is wholly in or out
+            const int cc = c_ok ? c : d - 4;
+            // all loads unconditional (clamped addresses), invalid values zeroed afterwards
+            float w[8][4];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float4 v = *reinterpret_cast<const float4*>(w_r + (int64_t)min(e, E - 1) * d + cc);
+                const bool ok = c_ok && e < E;
+                w[e][0] = ok ? v.x : 0.f;
+                w[e][1] = ok ? v.y : 0.f;
+                w[e][2] = ok ? v.z : 0.f;
+                w[e][3] = ok ? v.w : 0.f;
+            }
+            for (int t0 = 0; t0 < T; t0 += 8) {
+                uint2 xv[8];   // the next eight tokens
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    xv[i] = *reinterpret_cast<const uint2*>(x + min((int64_t)(t0 + i), T - 1) * d + cc);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int t = t0 + i;
+                    if (t >= T) break;
+                    // a chunk past d adds 0 (not 0 * x, which may be NaN)
+                    const float xf[4] = {c_ok ? __uint_as_float(xv[i].x << 16) : 0.f,
+                                         c_ok ? __uint_as_float(xv[i].x & 0xffff0000u) : 0.f,
+                                         c_ok ? __uint_as_float(xv[i].y << 16) : 0.f,
+                                         c_ok ? __uint_as_float(xv[i].y & 0xffff0000u) : 0.f};
+                    float acc[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        float sum = 0.f;
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) sum = fmaf(xf[jj], w[e][jj], sum);
+                        acc[e] = sum;
+                    }
+                    const float sum = reduce_row8(acc);
+                    if ((lane & 15) < 8) {
+                        float* dst = &part[(row * FS_TOK + t) * 8 + (lane & 7)];
+                        *dst = kr ? *dst + sum : sum;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        if (tid < FS_TOK * 8) {
+            const int t = tid / 8, e = tid % 8;
+            if (t < T && e < E) {
+                float sc = 0.f;
+#pragma unroll 16
+                for (int r = 0; r < 64; ++r) sc += part[(r * FS_TOK + t) * 8 + e];
+                lg[t * E + e] = sc;
+            }
+        }
+    } else {
+        for (int p = tid; p < T * E; p += FS_THREADS) {
+            float sc = 0.f;
+            for (int q0 = 0; q0 < KS; q0 += 8) {   // eight splits' loads in flight, added in order
+                float v[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) v[q] = dpart[(int64_t)min(q0 + q, KS - 1) * T * E + p];
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    if (q0 + q < KS) sc += v[q];
+            }
+            lg[p] = sc;
+        }
+    }
+    if (tid < E) s_bias[tid] = bias;
+    __syncthreads();
+    // with DISPATCH the ids and weights go to LDS first and to memory at the end, so
+    // no barrier below waits for their stores
+    if (wave < T)
+        select_token<EPL>(lg + wave * E, s_bias, E, k, mode, wave, DISPATCH ? s_ids : topk_ids,
+                          DISPATCH ? s_w : topk_w, status, probs);
+    if (!DISPATCH) return;
+    __syncthreads();
+    dispatch_one_block(s_ids, T, k, E, C, load, offsets, stats, tprefix, tile_rows, slot, row_of, src_token, masks,
+                       s_off, s_row);
+    for (int p = tid; p < T * k; p += FS_THREADS) {
+        topk_ids[p] = s_ids[p];
+        topk_w[p] = s_w[p];
+    }
+    // copy every accepted row x[t] -> x_perm[row]: one wave per path, 4 x 16 B per lane in flight
+    const int64_t vpr = d / 8;   // 16-byte vectors per bf16 row (d % 8 == 0)
+    const uint4* xv4 = reinterpret_cast<const uint4*>(x);
+    for (int p = wave; p < T * k; p += FS_WAVES) {
+        const int row = s_row[p];
+        if (row < 0) continue;
+        const uint4* src = xv4 + (int64_t)(p / k) * vpr;
+        uint4* dst = x_perm + (int64_t)row * vpr;
+        for (int64_t c0 = lane; c0 < vpr; c0 += 4 * 64) {
+            uint4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = src[min(c0 + 64 * u, vpr - 1)];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (c0 + 64 * u < vpr) dst[c0 + 64 * u] = v[u];
+        }
+    }
+}
+
 template <int EPL>
 void launch_select(const moe_dims& s, const float* part, int KS, int P, int NP, const float* b_r, int32_t* ids,
                    float* w, int32_t* status, float* probs, hipStream_t st) {
@@ -597,32 +774,91 @@ namespace moe_kernels {
 
 size_t route_ws_bytes(const moe_dims& s) {
     if (s.dtype != MOE_BF16) return s.E > 64 ? (size_t)s.T * s.E * sizeof(float) : 0;
-    if (s.E <= 8 && s.d <= V_MAXKR * V_KR) return 0;   // route_valu_kernel
-    if (s.T <= DOT_TMAX) return (size_t)((s.d + 2047) / 2048) * s.T * s.E * sizeof(float);   // route_dot_kernel
+    if (s.T <= DOT_TMAX)   // front_small_kernel (E <= 8), else route_dot_kernel's partials
+        return s.E <= 8 ? 0 : (size_t)((s.d + 2047) / 2048) * s.T * s.E * sizeof(float);
+    if (s.E <= 8) return (size_t)m8_steps(s.d) * 128 * sizeof(uint4);   // route_mfma8_kernel operands
     const int N3 = score_cols(s.E);
     size_t planes = ((size_t)N3 * s.d * 2 + 255) & ~(size_t)255;
     if (s.E <= 64) return planes;
     return planes + (size_t)scores_splits(s.T, N3, s.d) * s.T * N3 * sizeof(float);
 }
 
+bool front_fused_ok(const moe_dims& s) {
+    return s.dtype == MOE_BF16 && s.T > 0 && s.T <= FS_TOK && s.E <= FS_EMAX && !s.accept_by_gate;
+}
+
+namespace {
+
+// T <= 16, bf16, E <= 256: route_dot_kernel (E > 8), then front_small_kernel.
+template <bool DISPATCH>
+hipError_t launch_front_small(const moe_dims& s, const void* x, const float* w_r, const float* b_r,
+                              int32_t* topk_ids, float* topk_w, int32_t* status, float* probs, void* ws,
+                              hipStream_t st, int32_t* load, int32_t* offsets, int32_t* slot, int32_t* row_of,
+                              int32_t* src_token, void* x_perm, int32_t* stats, int32_t* tprefix, int tile_rows) {
+    const float* dpart = nullptr;
+    int KS = 0;
+    if (s.E > 8) {
+        KS = (s.d + 2047) / 2048;
+        hipLaunchKernelGGL(route_dot_kernel, dim3((unsigned)((s.E + DOT_EW - 1) / DOT_EW), (unsigned)KS), dim3(256), 0,
+                           st, static_cast<const uint16_t*>(x), w_r, s.T, s.d, s.E, static_cast<float*>(ws));
+        dpart = static_cast<const float*>(ws);
+    }
+#define MOE_FRONT(EPLV)                                                                                         \
+    hipLaunchKernelGGL((front_small_kernel<EPLV, DISPATCH>), dim3(1), dim3(FS_THREADS), 0, st,                 \
+                       static_cast<const uint16_t*>(x), w_r, dpart, KS, b_r, s.T, s.d, s.E, s.k, s.C, s.gate_mode, \
+                       topk_ids, topk_w, status, probs, load, offsets, slot, row_of, src_token,                \
+                       static_cast<uint4*>(x_perm), stats, tprefix, tile_rows)
+    if (s.E <= 64) MOE_FRONT(1);
+    else if (s.E <= 128) MOE_FRONT(2);
+    else MOE_FRONT(4);
+#undef MOE_FRONT
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_front(const moe_dims& s, const void* x, const float* w_r, const float* b_r, int32_t* topk_ids,
+                        float* topk_w, int32_t* status, void* ws, hipStream_t st, int32_t* load, int32_t* offsets,
+                        int32_t* slot, int32_t* row_of, int32_t* src_token, void* x_perm, int32_t* stats,
+                        int32_t* tprefix, int tile_rows) {
+    return launch_front_small<true>(s, x, w_r, b_r, topk_ids, topk_w, status, nullptr, ws, st, load, offsets, slot,
+                                    row_of, src_token, x_perm, stats, tprefix, tile_rows);
+}
+
 hipError_t launch_route(const moe_dims& s, const void* x, const float* w_r, const float* b_r, int32_t* topk_ids,
-                        float* topk_w, int32_t* status, void* ws, hipStream_t st, float* probs) {
-    // The status word is cleared before any selection may set it: by the selecting
-    // kernel itself when that is a single workgroup, else by a kernel of its own.
-    const bool valu = s.dtype == MOE_BF16 && s.E <= 8 && s.d <= V_MAXKR * V_KR;
-    const bool dot = !valu && s.dtype == MOE_BF16 && s.T <= DOT_TMAX;
-    // tokens per selecting workgroup
-    const int64_t sel_tokens = valu ? VT : (dot || s.E > 64 ? 4 : RT_TOK);
-    const bool self_zero = s.T > 0 && s.T <= sel_tokens;
-    if (!self_zero) hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(64), 0, st, status, 1);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || s.T == 0) return e;
-    if (valu) {
-        const unsigned grid = (unsigned)((s.T + VT - 1) / VT);
-        hipLaunchKernelGGL(route_valu_kernel, dim3(grid), dim3(V_THREADS), 0, st, static_cast<const uint16_t*>(x), w_r,
-                           b_r, s.T, s.d, s.E, s.k, s.gate_mode, topk_ids, topk_w, status, probs, self_zero ? 1 : 0);
+                        float* topk_w, int32_t* status, void* ws, hipStream_t st, float* probs, int32_t* hist,
+                        bool* hist_done) {
+    if (s.T == 0) {
+        hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(64), 0, st, status, 1);
         return hipGetLastError();
     }
+    if (s.dtype == MOE_BF16 && s.T <= FS_TOK && s.E <= FS_EMAX)
+        return launch_front_small<false>(s, x, w_r, b_r, topk_ids, topk_w, status, probs, ws, st, nullptr, nullptr,
+                                         nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0);
+    if (s.dtype == MOE_BF16 && s.E <= 8) {
+        const int NS = m8_steps(s.d);
+        const bool count = hist != nullptr;
+        const int64_t nhist = count ? (s.T + MOE_DISPATCH_BLOCK - 1) / MOE_DISPATCH_BLOCK * s.E : 0;
+        hipLaunchKernelGGL(route_prep_kernel, dim3((unsigned)((NS * 128 + 255) / 256)), dim3(256), 0, st, w_r, s.d,
+                           s.E, static_cast<uint4*>(ws), NS, status, count ? hist : nullptr, nhist);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(route_mfma8_kernel, dim3((unsigned)((s.T + M8_TOK - 1) / M8_TOK)), dim3(M8_THREADS), 0,
+                           st, static_cast<const uint16_t*>(x), static_cast<const uint4*>(ws), b_r, s.T, s.d, s.E,
+                           s.k, s.gate_mode, topk_ids, topk_w, status, probs, count ? hist : nullptr);
+        e = hipGetLastError();
+        if (e == hipSuccess && count && hist_done) *hist_done = true;
+        return e;
+    }
+    // The status word is cleared before any selection may set it: by the selecting
+    // kernel itself when that is a single workgroup, else by a kernel of its own.
+    const bool dot = s.dtype == MOE_BF16 && s.T <= DOT_TMAX;   // here E > 256
+    // tokens per selecting workgroup
+    const int64_t sel_tokens = dot || s.E > 64 ? 4 : RT_TOK;
+    const bool self_zero = s.T <= sel_tokens;
+    if (!self_zero) hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(64), 0, st, status, 1);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     if (dot) {
         float* dpart = static_cast<float*>(ws);
         const int KS = (s.d + 2047) / 2048;

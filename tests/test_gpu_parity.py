@@ -235,7 +235,8 @@ RAGGED = MoEConfig("ragged_bf16", T=2000, d=328, m=200, E=4, k=2, dtype="bf16", 
     # 34 token blocks x 1000 experts: the dispatch scan runs as its own kernel
     MoEConfig("dispatch_large_table", T=8500, d=64, m=64, E=1000, k=2, dtype="bf16", gate_mode=0, cf=(5, 4),
               cfg_id=27),
-    # T <= 16 with E > 8: direct fp32 dot-product router; d not a multiple of the 2048-wide pass
+    # T <= 16 with E > 8: split-K fp32 dot-product kernel, then the one-workgroup front;
+    # d not a multiple of the 2048-wide pass
     MoEConfig("router_dot_small", T=16, d=2056, m=64, E=33, k=3, dtype="bf16", gate_mode=1, cf=None, cfg_id=35),
     MoEConfig("router_dot_many", T=5, d=512, m=64, E=700, k=8, dtype="bf16", gate_mode=0, cf=None, bias="zipf",
               cfg_id=36),
@@ -252,7 +253,14 @@ RAGGED = MoEConfig("ragged_bf16", T=2000, d=328, m=200, E=4, k=2, dtype="bf16", 
               bias="zipf", accept_by_gate=True, cfg_id=42),
     # E > 64: router scores on the expert-GEMM kernel; 300 rows end in a 44-row tile
     MoEConfig("router_thin_tail", T=300, d=1024, m=64, E=100, k=4, dtype="bf16", gate_mode=0, cf=None, cfg_id=26),
-    # router with E < 8 experts over two K ranges of 4096 (d > 4096), T not a multiple of 16
+    # T <= 16, one-workgroup front: fp32-MFMA scores with E < 8 pad columns and a half
+    # K block (d % 16 == 8), capacity drops
+    MoEConfig("front_small_e5", T=13, d=200, m=64, E=5, k=2, dtype="bf16", gate_mode=1, cf=(1, 2), cfg_id=44),
+    # the largest one-workgroup front: E = 256, k = 32, heavy drops
+    MoEConfig("front_small_max", T=16, d=520, m=64, E=256, k=32, dtype="bf16", gate_mode=0, cf=(1, 1), bias="zipf",
+              cfg_id=45),
+    MoEConfig("front_small_e128", T=7, d=1024, m=64, E=128, k=6, dtype="bf16", gate_mode=0, cf=(5, 4), cfg_id=46),
+    # router with E < 8 experts over two K chunks of 4096 (d > 4096), T not a multiple of 16
     MoEConfig("router_two_k_ranges", T=101, d=4160, m=64, E=6, k=2, dtype="bf16", gate_mode=1, cf=None,
               cfg_id=24),
 ], ids=lambda c: c.name)
