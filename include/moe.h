@@ -151,12 +151,13 @@ const char* moe_status_str(int32_t status);
  *                   score is NaN/Inf; such a token gets ids 0..k-1 and weights 0
  *                   so that later calls stay in bounds.  Read it after the
  *                   stream synchronises.
- *   ws              >= moe_workspace_bytes(shape, MOE_WS_ROUTE) bytes: none for bf16
- *                   activations with E <= 8 (may then be NULL with ws_bytes 0); for
- *                   bf16 with T <= 16 and E > 8 the fp32 partial scores of each
- *                   2048-wide K range; else the bf16 split of w_r (bf16, E <= 64),
- *                   plus fp32 partial scores when E > 64 (fp32 activations: only the
- *                   [T,E] scores, E > 64) */
+ *   ws              >= moe_workspace_bytes(shape, MOE_WS_ROUTE) bytes.  bf16
+ *                   activations: with T <= 16, none for E <= 8 (may then be NULL
+ *                   with ws_bytes 0) and the fp32 partial scores of each 2048-wide
+ *                   K range for E > 8; with T > 16, the bf16 split of w_r (E <= 8:
+ *                   laid out as MFMA operands, 2 KB per 32 elements of d), plus
+ *                   fp32 partial scores when E > 64.  fp32 activations: only the
+ *                   [T,E] scores, E > 64. */
 moe_status moe_route(const moe_shape* shape, const void* x, const float* w_r, const float* b_r,
                      int32_t* topk_ids, float* topk_w, int32_t* status, void* ws, size_t ws_bytes,
                      void* stream);
