@@ -109,6 +109,7 @@ hipError_t launch_route(const moe_dims& s, const void* x, const float* w_r, cons
 // dispatch and row gather of the whole layer front in one workgroup (after a
 // split-K dot kernel for E > 8); the same outputs as launch_route followed by
 // launch_dispatch, and the GEMMs' tile prefix in tprefix.  ws: route_ws_bytes.
+// x_perm == nullptr: no row copy.
 bool front_fused_ok(const moe_dims& s);
 hipError_t launch_front(const moe_dims& s, const void* x, const float* w_r, const float* b_r, int32_t* topk_ids,
                         float* topk_w, int32_t* status, void* ws, hipStream_t st, int32_t* load, int32_t* offsets,
@@ -129,7 +130,8 @@ bool dispatch_uses_hist(const moe_dims& s);
 // tile_rows rows (gemm_tile_rows), so the GEMM launches can skip computing it.
 // topk_w: the routing weights (read only when s.accept_by_gate).
 // ws starts with the per-block expert counts (dispatch_hist); hist_ready: the
-// router has already written them, so the counting kernel is skipped.
+// router has already written them, so the counting kernel is skipped.  x_perm
+// == nullptr: no row copy (the caller reads x through src_token).
 hipError_t launch_dispatch(const moe_dims& s, const void* x, const int32_t* ids, const float* topk_w,
                            int32_t* load, int32_t* offsets, int32_t* slot, int32_t* row_of, int32_t* src_token,
                            void* x_perm, int32_t* stats, void* ws, hipStream_t st,
@@ -147,9 +149,14 @@ int gemm_tile_rows(int dtype);
 // sums.  With part == nullptr it never splits.
 int gemm1_splits(int dtype, int64_t max_rows, int G, int N, int K);
 size_t gemm1_part_bytes(int dtype, int64_t max_rows, int G, int N, int K);
+// gather (nullable, only where gemm1_gather_ok): A is the token-ordered [a_rows, K]
+// activations and grouped row r reads A row gather[r] (the dispatch's src_token,
+// readable up to 256 entries past the last row), so no grouped copy is needed.
+bool gemm1_gather_ok(int dtype, int N, int K, int64_t a_rows);
 hipError_t launch_gemm1(int dtype, const void* A, const int32_t* offsets, int G, int64_t max_rows,
                         const void* w_gate, const void* w_up, void* h, int N, int K,
-                        void* ws, hipStream_t st, bool prefix_ready = false, float* part = nullptr);
+                        void* ws, hipStream_t st, bool prefix_ready = false, float* part = nullptr,
+                        const int32_t* gather = nullptr);
 // GEMM2 may split K over S = gemm2_splits(...) (decided from the shape alone):
 // then H receives the partial sum over the first K range and H1 + (s - 1) max_rows N
 // the sum over range s = 1..S-1; with H1 == nullptr it never splits.

@@ -513,6 +513,7 @@ hipError_t launch_dispatch(const moe_dims& s, const void* x, const int32_t* ids,
         hipLaunchKernelGGL(dispatch_place_kernel, dim3(NB), dim3(DB_TOK), mask_lds, st, ids, s.T, s.k, s.E, s.C,
                            hist, offsets, slot, row_of, src_token, stats);
     }
+    if (!x_perm) return hipGetLastError();
     const int elem = s.dtype == MOE_BF16 ? 2 : 4;
     const int64_t row_bytes = (int64_t)s.d * elem;
     const unsigned grid = (unsigned)((s.T + 3) / 4);

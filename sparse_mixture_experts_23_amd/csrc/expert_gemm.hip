@@ -608,7 +608,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* _
                                                                const int32_t* __restrict__ offsets,
                                                                const int32_t* __restrict__ tprefix, int G,
                                                                int64_t nrows, int N, int K, int S, int nsup,
-                                                               int thin_all) {
+                                                               int thin_all, const int32_t* __restrict__ gather) {
     constexpr int BM = 256, BK = 64, WGN = 2, WAVES = 8;
     constexpr int NOPS = SWIGLU ? 2 : 1;
     constexpr int WM = 64, WN = BN / WGN;       // wave tile: 64 rows x WN columns of each operand
@@ -653,20 +653,40 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* _
     const int64_t k0 = (int64_t)kt_begin * BK;
     const uint16_t* Bg = B0 + (int64_t)tc.g * wstride + (int64_t)n0 * K + k0;
     const uint16_t* Bu = SWIGLU ? B1 + (int64_t)tc.g * wstride + (int64_t)n0 * K + k0 : Bg;
-    const uint16_t* At = A + tc.row_start * K + k0;
+    const uint16_t* At = A + (gather ? 0 : tc.row_start * K) + k0;
 
     // Load plan: load i of wave w fills tile rows (8 i + w) * 8 + lane / 8 at
     // physical chunk lane % 8, i.e. logical chunk (lane % 8) ^ swz(row).  A rows
     // past the group end and weight rows past N read tile row 0 instead (their
     // outputs are never stored).  Offsets are bytes from At / the weight base.
+    // gather (nullable): tile row r is row gather[row_start + r] of A (the grouped
+    // rows are read in place from the token-ordered activations); the indices of a
+    // wave's 8 consecutive rows are one scalar load, so no vector-memory wait
+    // stands before the first tile loads.
     uint32_t vo[8];
     const uint16_t* bbase[4];
+    int32_t gv[4][8] = {}, g0 = 0;
+    if (gather) {   // all index loads first (uniform addresses), then one wait
+        g0 = __builtin_amdgcn_readfirstlane(gather[tc.row_start]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                gv[i][j] = __builtin_amdgcn_readfirstlane(gather[tc.row_start + (WAVES * i + wave) * 8 + j]);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int row = (WAVES * i + wave) * 8 + lane / 8;
         const int ch = (lane % 8) ^ lds_swz(row);
-        const int r = tc.row_start + row < tc.row_end ? row : 0;
-        vo[i] = (uint32_t)(((int64_t)r * K + ch * 8) * 2);
+        const bool ok = tc.row_start + row < tc.row_end;
+        int64_t src = ok ? row : 0;
+        if (gather) {
+            int32_t mine = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) mine = lane / 8 == j ? gv[i][j] : mine;
+            src = ok ? mine : g0;
+        }
+        vo[i] = (uint32_t)((src * K + ch * 8) * 2);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1069,9 +1089,13 @@ size_t gemm1_part_bytes(int dtype, int64_t max_rows, int G, int N, int K) {
     return S > 1 ? (size_t)2 * S * max_rows * N * sizeof(float) : 0;
 }
 
+bool gemm1_gather_ok(int dtype, int N, int K, int64_t a_rows) {
+    return dtype == MOE_BF16 && asm_path_ok(N, K) && a_rows * K * 2 < ((int64_t)1 << 32);
+}
+
 hipError_t launch_gemm1(int dtype, const void* A, const int32_t* offsets, int G, int64_t max_rows, const void* w_gate,
                         const void* w_up, void* h, int N, int K, void* ws, hipStream_t st, bool prefix_ready,
-                        float* part) {
+                        float* part, const int32_t* gather) {
     const int BM = dtype == MOE_BF16 ? BF16_BM : F32_BM;
     const int BN = dtype == MOE_BF16 ? BF16_BN1 : F32_BN;
     hipError_t e = prefix_ready ? hipSuccess : prep_tiles(offsets, G, BM, ws, st);
@@ -1087,7 +1111,7 @@ hipError_t launch_gemm1(int dtype, const void* A, const int32_t* offsets, int G,
         hipLaunchKernelGGL((gemm_bf16_asm_kernel<BF16_BN1, true, true>), dim3(grid), dim3(512), 0, st,
                            static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(w_gate),
                            static_cast<const uint16_t*>(w_up), h, part, stride, offsets, tp, G, max_rows, N, K, S,
-                           NSUPER, one_round(max_rows, G, N, BF16_BN1, S));
+                           NSUPER, one_round(max_rows, G, N, BF16_BN1, S), gather);
         const int64_t n4 = max_rows * (N / 4);
         hipLaunchKernelGGL(swiglu_reduce_kernel, dim3((unsigned)std::min<int64_t>((n4 + 255) / 256, 8192)),
                            dim3(256), 0, st, part, S, stride, offsets, G, max_rows, N, static_cast<uint16_t*>(h));
@@ -1095,7 +1119,7 @@ hipError_t launch_gemm1(int dtype, const void* A, const int32_t* offsets, int G,
         hipLaunchKernelGGL((gemm_bf16_asm_kernel<BF16_BN1, true>), dim3(grid), dim3(512), 0, st,
                            static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(w_gate),
                            static_cast<const uint16_t*>(w_up), h, nullptr, (int64_t)0, offsets, tp, G, max_rows, N, K, 1,
-                           NSUPER, one_round(max_rows, G, N, BF16_BN1, 1));
+                           NSUPER, one_round(max_rows, G, N, BF16_BN1, 1), gather);
     else if (dtype == MOE_BF16)
         hipLaunchKernelGGL((gemm_bf16_kernel<BF16_BM, BF16_BN1, true>), dim3(grid), dim3(256), 0, st,
                            static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(w_gate),
@@ -1138,7 +1162,8 @@ hipError_t launch_gemm2(int dtype, const void* h, const int32_t* offsets, int G,
         hipLaunchKernelGGL((gemm_bf16_asm_kernel<BF16_BN2, false>), dim3(grid), dim3(512), 0, st,
                            static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w_down), nullptr, H, H1,
                            max_rows * N, offsets, tp, G, max_rows, N, K, S,
-                           super_width(max_rows, G, (N + BN - 1) / BN), one_round(max_rows, G, N, BF16_BN2, S));
+                           super_width(max_rows, G, (N + BN - 1) / BN), one_round(max_rows, G, N, BF16_BN2, S),
+                           (const int32_t*)nullptr);
     } else if (dtype == MOE_BF16) {
         hipLaunchKernelGGL((gemm_bf16_kernel<BF16_BM, BF16_BN2, false>), dim3(grid), dim3(256), 0, st,
                            static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w_down), nullptr, H,
@@ -1166,7 +1191,7 @@ hipError_t launch_scores_gemm(const void* x, const void* w, int64_t T, int N, in
         const unsigned grid = (tiles + XCDS - 1) / XCDS * XCDS * S;
         hipLaunchKernelGGL((gemm_bf16_asm_kernel<BF16_BN2, false>), dim3(grid), dim3(512), 0, st,
                            static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), nullptr, part,
-                           part + T * N, T * N, nullptr, nullptr, 1, T, N, K, S, NSUPER, 0);
+                           part + T * N, T * N, nullptr, nullptr, 1, T, N, K, S, NSUPER, 0, (const int32_t*)nullptr);
     } else {
         hipLaunchKernelGGL((gemm_bf16_kernel<BF16_BM, BF16_BN2, false>), dim3(tiles), dim3(256), 0, st,
                            static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), nullptr, part, nullptr,

@@ -92,6 +92,8 @@ struct ForwardWs {
     size_t total;
 };
 
+bool gather_rows(const moe_dims& d) { return gemm1_gather_ok(d.dtype, d.m, d.d, d.T); }
+
 ForwardWs carve_forward(const moe_dims& d, void* base) {
     ForwardWs w{};
     char* p = static_cast<char*>(base);
@@ -102,10 +104,13 @@ ForwardWs carve_forward(const moe_dims& d, void* base) {
         return r;
     };
     const int64_t R = max_rows(d);
+    // GEMM1 reads the grouped rows in place through src_token where it can (then
+    // src_token is padded by one row tile and there is no x_perm)
+    const bool gather = gather_rows(d);
     w.offsets = static_cast<int32_t*>(take(sizeof(int32_t) * (d.E + 1)));
     w.row_of = static_cast<int32_t*>(take(sizeof(int32_t) * d.T * d.k));
-    w.src_token = static_cast<int32_t*>(take(sizeof(int32_t) * R));
-    w.x_perm = take((size_t)R * d.d * elem(d));
+    w.src_token = static_cast<int32_t*>(take(sizeof(int32_t) * (R + (gather ? 256 : 0))));
+    w.x_perm = gather ? nullptr : take((size_t)R * d.d * elem(d));
     w.H = static_cast<float*>(take(sizeof(float) * R * d.d));
     w.s = d.m_shared ? static_cast<float*>(take(sizeof(float) * d.T * d.d)) : nullptr;
     w.route = take(route_ws_bytes(d));
@@ -151,16 +156,17 @@ moe_status gemm2_impl(const moe_dims& d, const void* h, const int32_t* offsets, 
 }
 
 // prefix_ready: the tile prefix at the start of ws was written by the dispatch scan.
+// gather (nullable): x_perm is then the token-ordered x, read through it (gather_rows)
 moe_status ffn_impl(const moe_dims& d, const void* x_perm, const int32_t* offsets, const void* w_gate,
                     const void* w_up, const void* w_down, float* H, void* ws, Partials* out, hipStream_t st,
-                    bool prefix_ready = false) {
+                    bool prefix_ready = false, const int32_t* gather = nullptr) {
     void* tp = ws;
     char* h = static_cast<char*>(ws) + align_up(gemm_ws_bytes(d.E));
     float* g1part = reinterpret_cast<float*>(h + align_up((size_t)max_rows(d) * d.m * elem(d)));
     float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(g1part) + g1_part_bytes(d));
     const int64_t R = max_rows(d);
     MOE_CHECK_HIP(launch_gemm1(d.dtype, x_perm, offsets, d.E, R, w_gate, w_up, h, d.m, d.d, tp, st, prefix_ready,
-                               g1_part_bytes(d) ? g1part : nullptr));
+                               g1_part_bytes(d) ? g1part : nullptr, gather));
     // GEMM2 uses the same row tiles: the prefix GEMM1 found (or was given) stays valid
     return gemm2_impl(d, h, offsets, w_down, H, tp, part, out, st, true);
 }
@@ -361,7 +367,8 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_r, 
                                       w.x_perm, stats, w.dispatch, st, tprefix, gemm_tile_rows(d.dtype), counted));
     }
     Partials parts;   // K-split partials of H beyond the first, added by the combine
-    rc = ffn_impl(d, w.x_perm, w.offsets, w_gate, w_up, w_down, w.H, w.ffn, &parts, st, true);
+    rc = w.x_perm ? ffn_impl(d, w.x_perm, w.offsets, w_gate, w_up, w_down, w.H, w.ffn, &parts, st, true)
+                  : ffn_impl(d, x, w.offsets, w_gate, w_up, w_down, w.H, w.ffn, &parts, st, true, w.src_token);
     if (rc != MOE_OK) return rc;
     if (d.m_shared) {
         rc = shared_impl(d, x, s_gate, s_up, s_down, w.s, w.shared, st);

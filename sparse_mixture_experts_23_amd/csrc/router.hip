@@ -704,6 +704,7 @@ __global__ __launch_bounds__(FS_THREADS) void front_small_kernel(
         topk_w[p] = s_w[p];
     }
     // copy every accepted row x[t] -> x_perm[row]: one wave per path, 4 x 16 B per lane in flight
+    if (!x_perm) return;
     const int64_t vpr = d / 8;   // 16-byte vectors per bf16 row (d % 8 == 0)
     const uint4* xv4 = reinterpret_cast<const uint4*>(x);
     for (int p = wave; p < T * k; p += FS_WAVES) {

@@ -71,7 +71,11 @@ def test_max_rows_and_workspace():
     ffn = L.moe_workspace_bytes(_shape(), L.MOE_WS_FFN)
     assert ffn >= 8192 * 14336 * 2                       # holds h
     fwd = L.moe_workspace_bytes(_shape(), L.MOE_WS_FORWARD)
-    assert fwd >= ffn + 8192 * 4096 * (2 + 4)            # + x_perm + H
+    assert fwd >= ffn + 8192 * 4096 * 4                  # + H (bf16: GEMM1 reads x in place)
+    assert fwd < ffn + 8192 * 4096 * (2 + 4)             # no grouped copy of x
+    ffn32 = L.moe_workspace_bytes(_shape(dtype=0), L.MOE_WS_FFN)
+    fwd32 = L.moe_workspace_bytes(_shape(dtype=0), L.MOE_WS_FORWARD)
+    assert fwd32 >= ffn32 + 8192 * 4096 * (4 + 4)        # fp32: + x_perm + H
     assert L.moe_workspace_bytes(_shape(k=0), L.MOE_WS_FORWARD) == 0
 
 
