@@ -260,7 +260,12 @@ moe_status moe_combine(const moe_shape* shape, const float* H, const int32_t* ro
 /* The whole layer: route -> dispatch -> expert FFN (+ shared) -> combine,
  * queued on `stream` with no host synchronisation.  s_gate/s_up/s_down may be
  * NULL only when shape->m_shared == 0.  Outputs as in the calls above;
- * every intermediate lives in ws (>= moe_workspace_bytes(shape, MOE_WS_FORWARD)). */
+ * every intermediate lives in ws (>= moe_workspace_bytes(shape, MOE_WS_FORWARD)).
+ * The results equal those of the staged calls bit for bit, but the path may
+ * differ: with bf16 activations the expert GEMMs read each grouped row in place
+ * from x through the dispatch's row map (no x_perm copy; the E <= 8 router also
+ * makes the dispatch's per-block counts), and with T <= 16 (bf16, E <= 256,
+ * acceptance in token order) route and dispatch run as one workgroup. */
 moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_r, const float* b_r,
                        const void* w_gate, const void* w_up, const void* w_down,
                        const void* s_gate, const void* s_up, const void* s_down,
