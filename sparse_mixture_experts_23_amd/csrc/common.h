@@ -100,11 +100,13 @@ namespace moe_kernels {
 // probs (nullable): also write every token's full softmax, probs[t E + e].
 // hist (nullable): the dispatch's per-block expert counts ([ceil(T / 256)][E]
 // int32).  Where the router path can count them while it selects (E <= 8, bf16),
-// it zeroes and fills them and sets *hist_done; otherwise it leaves them alone.
+// it zeroes and fills them, clears the two counters at acc_stats (nullable) and
+// sets *hist_done; otherwise it leaves them alone.
 size_t route_ws_bytes(const moe_dims& s);
 hipError_t launch_route(const moe_dims& s, const void* x, const float* w_r, const float* b_r,
                         int32_t* topk_ids, float* topk_w, int32_t* status, void* ws, hipStream_t st,
-                        float* probs = nullptr, int32_t* hist = nullptr, bool* hist_done = nullptr);
+                        float* probs = nullptr, int32_t* hist = nullptr, bool* hist_done = nullptr,
+                        int32_t* acc_stats = nullptr);
 // Small batches (bf16, 0 < T <= 16, E <= 256, acceptance in token order): route,
 // dispatch and row gather of the whole layer front in one workgroup (after a
 // split-K dot kernel for E > 8); the same outputs as launch_route followed by
@@ -126,6 +128,10 @@ size_t dispatch_ws_bytes(const moe_dims& s);
 // Whether launch_dispatch reads the per-block expert counts (more than one token
 // block, or acceptance by gate weight); a single block is counted in place.
 bool dispatch_uses_hist(const moe_dims& s);
+// Whether launch_dispatch derives the scan inside the placement kernel (a small
+// count table); the placement then accumulates the token statistics into
+// stats[MOE_STAT_TOKENS_DROPPED..AFFECTED], which whoever fills the table clears.
+bool dispatch_inline_scan(const moe_dims& s);
 // tprefix (nullable): also write the grouped GEMMs' tile prefix for tiles of
 // tile_rows rows (gemm_tile_rows), so the GEMM launches can skip computing it.
 // topk_w: the routing weights (read only when s.accept_by_gate).

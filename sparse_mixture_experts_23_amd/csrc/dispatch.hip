@@ -38,9 +38,13 @@ __device__ __forceinline__ void build_masks(unsigned long long* masks, const int
     __syncthreads();
 }
 
+// acc_stats (nullable): the two statistics the placement accumulates with atomics,
+// cleared here (block 0) for dispatch_place_scan_kernel.
 __global__ __launch_bounds__(DB_TOK) void dispatch_count_kernel(const int32_t* __restrict__ ids, int64_t T, int k,
-                                                                int E, int32_t* __restrict__ hist) {
+                                                                int E, int32_t* __restrict__ hist,
+                                                                int32_t* __restrict__ acc_stats) {
     extern __shared__ unsigned long long masks[];
+    if (acc_stats && blockIdx.x == 0 && threadIdx.x < 2) acc_stats[threadIdx.x] = 0;
     build_masks(masks, ids, T, k, E);
     for (int e = threadIdx.x; e < E; e += DB_TOK) {
         int c = 0;
@@ -172,6 +176,150 @@ __global__ __launch_bounds__(DB_TOK) void dispatch_place_kernel(const int32_t* _
     if (lane == 0) {
         s_drop[wave] = dropped;
         s_aff[wave] = affected;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        const int dsum = s_drop[0] + s_drop[1] + s_drop[2] + s_drop[3];
+        const int asum = s_aff[0] + s_aff[1] + s_aff[2] + s_aff[3];
+        if (dsum) atomicAdd(&stats[MOE_STAT_TOKENS_DROPPED], dsum);
+        if (asum) atomicAdd(&stats[MOE_STAT_TOKENS_AFFECTED], asum);
+    }
+}
+
+// Scan + place for small count tables (NB * E <= 4096, E <= 256): every block's
+// workgroup loads the whole per-block count table into LDS and derives from it
+// the totals L_e, its own base slots and the grouped-row offsets (the same integer
+// results as dispatch_scan_kernel), then places its tokens as dispatch_place_kernel
+// does -- one launch instead of two.  Block 0 also writes load, offsets, the tile
+// prefix and the statistics; the token statistics are accumulated with atomics
+// into counters the kernel that filled the table has cleared.  Dynamic LDS: masks
+// (4 E uint64), then s_base[E], s_off[E], s_hist[NB E] int32.
+constexpr int SCAN_INLINE_MAX = 4096;
+__global__ __launch_bounds__(DB_TOK) void dispatch_place_scan_kernel(
+    const int32_t* __restrict__ ids, int64_t T, int k, int E, int C, const int32_t* __restrict__ hist, int NB,
+    int32_t* __restrict__ load, int32_t* __restrict__ offsets, int32_t* __restrict__ slot,
+    int32_t* __restrict__ row_of, int32_t* __restrict__ src_token, int32_t* __restrict__ stats,
+    int32_t* __restrict__ tprefix, int tile_rows) {
+    extern __shared__ unsigned long long masks[];
+    int* s_base = reinterpret_cast<int*>(masks + 4 * E);
+    int* s_off = s_base + E;
+    int* s_hist = s_off + E;
+    __shared__ int s_sum[4], s_tiles[4], s_over[4], s_max[4], s_drop[4], s_aff[4];
+    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+    const int n = NB * E;
+    {   // the table: up to 16 loads per thread, all in flight together
+        int v[SCAN_INLINE_MAX / DB_TOK];
+#pragma unroll
+        for (int u = 0; u < SCAN_INLINE_MAX / DB_TOK; ++u) v[u] = hist[min(tid + DB_TOK * u, n - 1)];
+#pragma unroll
+        for (int u = 0; u < SCAN_INLINE_MAX / DB_TOK; ++u)
+            if (tid + DB_TOK * u < n) s_hist[tid + DB_TOK * u] = v[u];
+    }
+    build_masks(masks, ids, T, k, E);   // its barriers also publish s_hist
+    // thread e < E <= 256: L_e, this block's base, accepted, tiles; scans over e
+    const int e = tid;
+    int L = 0, base = 0;
+    if (e < E) {
+        for (int b = 0; b < NB; ++b) {
+            const int h = s_hist[b * E + e];
+            base += b < (int)blockIdx.x ? h : 0;
+            L += h;
+        }
+    }
+    const int acc = e < E ? min(L, C) : 0;
+    const int over = e < E ? max(L - C, 0) : 0;
+    const int tiles = tprefix ? (acc + tile_rows - 1) / tile_rows : 0;
+    int incl = acc, tincl = tiles;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int sv = __shfl_up(incl, o, MOE_WAVE);
+        const int tv = __shfl_up(tincl, o, MOE_WAVE);
+        if (lane >= o) {
+            incl += sv;
+            tincl += tv;
+        }
+    }
+    int ov = over, mx = L;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        ov += __shfl_xor(ov, o, MOE_WAVE);
+        mx = max(mx, __shfl_xor(mx, o, MOE_WAVE));
+    }
+    if (lane == 63) {
+        s_sum[wave] = incl;
+        s_tiles[wave] = tincl;
+    }
+    if (lane == 0) {
+        s_over[wave] = ov;
+        s_max[wave] = mx;
+    }
+    __syncthreads();
+    int before = 0, total = 0, otot = 0, mtot = 0, tbefore = 0, ttotal = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        if (w < wave) {
+            before += s_sum[w];
+            tbefore += s_tiles[w];
+        }
+        total += s_sum[w];
+        ttotal += s_tiles[w];
+        otot += s_over[w];
+        mtot = max(mtot, s_max[w]);
+    }
+    const int off = before + incl - acc;
+    if (e < E) {
+        s_off[e] = off;
+        s_base[e] = base;
+    }
+    __syncthreads();
+    // place: as dispatch_place_kernel, with this block's bases from LDS
+    const int64_t t = (int64_t)blockIdx.x * DB_TOK + tid;
+    int dropped = 0, affected = 0;
+    if (t < T) {
+        const unsigned long long below = (1ull << lane) - 1ull;
+        int nrej = 0;
+        for (int r = 0; r < k; ++r) {
+            const int ee = ids[t * k + r];
+            int c = -1, row = -1;
+            if ((unsigned)ee < (unsigned)E) {
+                int rank = __popcll(masks[wave * E + ee] & below);
+                for (int w = 0; w < wave; ++w) rank += __popcll(masks[w * E + ee]);
+                const int cand = s_base[ee] + rank;
+                if (cand < C) {
+                    c = cand;
+                    row = s_off[ee] + cand;
+                    src_token[row] = (int32_t)t;
+                }
+            }
+            slot[t * k + r] = c;
+            row_of[t * k + r] = row;
+            nrej += c < 0;
+        }
+        dropped = nrej == k;
+        affected = nrej > 0;
+    }
+    for (int o = 32; o >= 1; o >>= 1) {
+        dropped += __shfl_xor(dropped, o, MOE_WAVE);
+        affected += __shfl_xor(affected, o, MOE_WAVE);
+    }
+    if (lane == 0) {
+        s_drop[wave] = dropped;
+        s_aff[wave] = affected;
+    }
+    if (blockIdx.x == 0) {
+        if (e < E) {
+            load[e] = L;
+            offsets[e] = off;
+            if (tprefix) tprefix[e] = tbefore + tincl - tiles;
+        }
+        if (e == 0) {
+            offsets[E] = total;
+            if (tprefix) tprefix[E] = ttotal;
+            stats[MOE_STAT_OVERFLOW] = otot;
+            stats[MOE_STAT_ACCEPTED] = total;
+            stats[MOE_STAT_MAX_LOAD] = mtot;
+            for (int i = MOE_STAT_TOKENS_AFFECTED + 1; i < MOE_STAT_COUNT; ++i) stats[i] = 0;
+        }
     }
     __syncthreads();
     if (tid == 0) {
@@ -459,6 +607,11 @@ inline size_t al8(size_t v) { return (v + 7) / 8 * 8; }
 
 bool dispatch_uses_hist(const moe_dims& s) { return s.accept_by_gate || s.T > DB_TOK; }
 
+bool dispatch_inline_scan(const moe_dims& s) {
+    const int64_t NB = (s.T + DB_TOK - 1) / DB_TOK;
+    return !s.accept_by_gate && NB > 1 && s.E <= DB_TOK && NB * s.E <= SCAN_INLINE_MAX;
+}
+
 size_t dispatch_ws_bytes(const moe_dims& s) {
     const int64_t NB = (s.T + DB_TOK - 1) / DB_TOK;
     size_t b = al8((size_t)NB * (size_t)s.E * sizeof(int32_t));   // per-block counts / base slots
@@ -488,7 +641,7 @@ hipError_t launch_dispatch(const moe_dims& s, const void* x, const int32_t* ids,
         int32_t* req_path = reinterpret_cast<int32_t*>(p);
         if (NB > 0 && !hist_ready)
             hipLaunchKernelGGL(dispatch_count_kernel, dim3(NB), dim3(DB_TOK), mask_lds, st, ids, s.T, s.k, s.E,
-                               hist);
+                               hist, (int32_t*)nullptr);
         hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, st, hist, NB, s.E, s.C, load, offsets,
                            stats, tprefix, tile_rows, roff);
         if (NB == 0) return hipGetLastError();
@@ -502,10 +655,19 @@ hipError_t launch_dispatch(const moe_dims& s, const void* x, const int32_t* ids,
     } else if (NB == 1) {
         hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(1024), mask_lds + sizeof(int) * s.E, st, ids, s.T,
                            s.k, s.E, s.C, load, offsets, stats, tprefix, tile_rows, slot, row_of, src_token);
+    } else if (NB > 0 && dispatch_inline_scan(s)) {
+        // the token statistics are accumulated by the placement into counters the
+        // table's writer clears (here the count kernel, else the router)
+        if (!hist_ready)
+            hipLaunchKernelGGL(dispatch_count_kernel, dim3(NB), dim3(DB_TOK), mask_lds, st, ids, s.T, s.k, s.E,
+                               hist, stats + MOE_STAT_TOKENS_DROPPED);
+        const size_t lds = mask_lds + sizeof(int32_t) * (2 * s.E + (size_t)NB * s.E);
+        hipLaunchKernelGGL(dispatch_place_scan_kernel, dim3(NB), dim3(DB_TOK), lds, st, ids, s.T, s.k, s.E, s.C,
+                           hist, NB, load, offsets, slot, row_of, src_token, stats, tprefix, tile_rows);
     } else {
         if (NB > 0 && !hist_ready) {
             hipLaunchKernelGGL(dispatch_count_kernel, dim3(NB), dim3(DB_TOK), mask_lds, st, ids, s.T, s.k, s.E,
-                               hist);
+                               hist, (int32_t*)nullptr);
         }
         hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, st, hist, NB, s.E, s.C, load, offsets,
                            stats, tprefix, tile_rows, (int32_t*)nullptr);

@@ -362,7 +362,8 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_r, 
         // where it can, the router also counts the dispatch's per-block expert loads
         bool counted = false;
         MOE_CHECK_HIP(launch_route(d, x, w_r, b_r, topk_ids, topk_w, status, w.route, st, nullptr,
-                                   dispatch_uses_hist(d) ? static_cast<int32_t*>(w.dispatch) : nullptr, &counted));
+                                   dispatch_uses_hist(d) ? static_cast<int32_t*>(w.dispatch) : nullptr, &counted,
+                                   stats + MOE_STAT_TOKENS_DROPPED));
         MOE_CHECK_HIP(launch_dispatch(d, x, topk_ids, topk_w, load, w.offsets, slot, w.row_of, w.src_token,
                                       w.x_perm, stats, w.dispatch, st, tprefix, gemm_tile_rows(d.dtype), counted));
     }

@@ -211,9 +211,10 @@ __host__ __device__ inline int m8_steps(int d) { return (d + 31) / 32; }
 __global__ __launch_bounds__(256) void route_prep_kernel(const float* __restrict__ w_r, int d, int E,
                                                          uint4* __restrict__ bop, int NS,
                                                          int32_t* __restrict__ status, int32_t* __restrict__ hist,
-                                                         int64_t nhist) {
+                                                         int64_t nhist, int32_t* __restrict__ acc_stats) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i == 0) *status = MOE_OK;
+    if (acc_stats && i < 2) acc_stats[i] = 0;
     if (hist)
         for (int64_t h = i; h < nhist; h += (int64_t)gridDim.x * blockDim.x) hist[h] = 0;
     if (i >= (int64_t)NS * 128) return;
@@ -828,7 +829,7 @@ hipError_t launch_front(const moe_dims& s, const void* x, const float* w_r, cons
 
 hipError_t launch_route(const moe_dims& s, const void* x, const float* w_r, const float* b_r, int32_t* topk_ids,
                         float* topk_w, int32_t* status, void* ws, hipStream_t st, float* probs, int32_t* hist,
-                        bool* hist_done) {
+                        bool* hist_done, int32_t* acc_stats) {
     if (s.T == 0) {
         hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(64), 0, st, status, 1);
         return hipGetLastError();
@@ -841,7 +842,8 @@ hipError_t launch_route(const moe_dims& s, const void* x, const float* w_r, cons
         const bool count = hist != nullptr;
         const int64_t nhist = count ? (s.T + MOE_DISPATCH_BLOCK - 1) / MOE_DISPATCH_BLOCK * s.E : 0;
         hipLaunchKernelGGL(route_prep_kernel, dim3((unsigned)((NS * 128 + 255) / 256)), dim3(256), 0, st, w_r, s.d,
-                           s.E, static_cast<uint4*>(ws), NS, status, count ? hist : nullptr, nhist);
+                           s.E, static_cast<uint4*>(ws), NS, status, count ? hist : nullptr, nhist,
+                           count ? acc_stats : nullptr);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(route_mfma8_kernel, dim3((unsigned)((s.T + M8_TOK - 1) / M8_TOK)), dim3(M8_THREADS), 0,
