@@ -63,10 +63,13 @@ __device__ __forceinline__ void split3(const float4 w0, const float4 w1, uint4& 
 
 // w3[p][e][i] = plane p (hi, mid, lo) of w_r[e][i]; 8 weights per thread.  The
 // pad8 chunks after the three planes are zeroed (rows that round 3E up to a
-// multiple of 8 for the score GEMM).
+// multiple of 8 for the score GEMM).  status (nullable): cleared here, ahead of
+// the kernels that select.
 __global__ __launch_bounds__(256) void split_router_kernel(const float* __restrict__ w_r, int64_t n8,
-                                                           uint4* __restrict__ w3, int64_t pad8) {
+                                                           uint4* __restrict__ w3, int64_t pad8,
+                                                           int32_t* __restrict__ status) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (status && i == 0) *status = MOE_OK;
     if (i < pad8) w3[3 * n8 + i] = uint4{0u, 0u, 0u, 0u};
     if (i >= n8) return;
     const float4* src = reinterpret_cast<const float4*>(w_r) + 2 * i;
@@ -853,13 +856,15 @@ hipError_t launch_route(const moe_dims& s, const void* x, const float* w_r, cons
         if (e == hipSuccess && count && hist_done) *hist_done = true;
         return e;
     }
-    // The status word is cleared before any selection may set it: by the selecting
-    // kernel itself when that is a single workgroup, else by a kernel of its own.
+    // The status word is cleared before any selection may set it: by the plane split
+    // (bf16), by the selecting kernel itself when that is a single workgroup, else by
+    // a kernel of its own.
     const bool dot = s.dtype == MOE_BF16 && s.T <= DOT_TMAX;   // here E > 256
     // tokens per selecting workgroup
     const int64_t sel_tokens = dot || s.E > 64 ? 4 : RT_TOK;
     const bool self_zero = s.T <= sel_tokens;
-    if (!self_zero) hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(64), 0, st, status, 1);
+    const bool split = s.dtype == MOE_BF16 && !dot;   // the plane split runs first and clears it
+    if (!self_zero && !split) hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(64), 0, st, status, 1);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (dot) {
@@ -878,7 +883,7 @@ hipError_t launch_route(const moe_dims& s, const void* x, const float* w_r, cons
         const int64_t n8 = (int64_t)s.E * s.d / 8;
         const int64_t pad8 = s.E > 64 ? (int64_t)(score_cols(s.E) - 3 * s.E) * s.d / 8 : 0;
         hipLaunchKernelGGL(split_router_kernel, dim3((unsigned)((std::max(n8, pad8) + 255) / 256)), dim3(256), 0, st,
-                           w_r, n8, reinterpret_cast<uint4*>(w3), pad8);
+                           w_r, n8, reinterpret_cast<uint4*>(w3), pad8, status);
     }
     if (s.E <= 64) {
         const unsigned grid = (unsigned)((s.T + RT_TOK - 1) / RT_TOK);
