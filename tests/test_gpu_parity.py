@@ -260,6 +260,9 @@ RAGGED = MoEConfig("ragged_bf16", T=2000, d=328, m=200, E=4, k=2, dtype="bf16", 
     MoEConfig("front_small_max", T=16, d=520, m=64, E=256, k=32, dtype="bf16", gate_mode=0, cf=(1, 1), bias="zipf",
               cfg_id=45),
     MoEConfig("front_small_e128", T=7, d=1024, m=64, E=128, k=6, dtype="bf16", gate_mode=0, cf=(5, 4), cfg_id=46),
+    # router bias on the one-workgroup front, E = 8, capacity drops, d past one 4096-wide K range
+    MoEConfig("front_small_bias", T=11, d=4136, m=64, E=8, k=2, dtype="bf16", gate_mode=0, cf=(1, 2),
+              bias="first_two_plus2", cfg_id=48),
     # router with E < 8 experts over two K chunks of 4096 (d > 4096), T not a multiple of 16
     MoEConfig("router_two_k_ranges", T=101, d=4160, m=64, E=6, k=2, dtype="bf16", gate_mode=1, cf=None,
               cfg_id=24),
@@ -458,6 +461,9 @@ BALANCE_CASES = [
     MoEConfig("bal_f32_select", T=300, d=96, m=64, E=130, k=3, dtype="f32", gate_mode=0, cf=(1, 1), cfg_id=32),
     MoEConfig("bal_dot", T=13, d=256, m=64, E=70, k=4, dtype="bf16", gate_mode=0, cf=(1, 1), bias="zipf",
               cfg_id=37),
+    # one-workgroup front (route only) with fp32-FMA scores, E <= 8
+    MoEConfig("bal_front", T=9, d=1032, m=64, E=6, k=2, dtype="bf16", gate_mode=1, cf=(1, 1), bias="zipf",
+              cfg_id=47),
 ]
 
 
