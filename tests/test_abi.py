@@ -79,6 +79,19 @@ def test_max_rows_and_workspace():
     assert L.moe_workspace_bytes(_shape(k=0), L.MOE_WS_FORWARD) == 0
 
 
+def test_route_workspace_by_path():
+    """The router's workspace follows its path: none for the one-workgroup front
+    of small batches with E <= 8, the MFMA operand planes (2 KB per 32 elements of
+    d) above 16 tokens, the split-K partial scores for small batches with E > 8."""
+    route = lambda **kw: L.moe_workspace_bytes(_shape(**kw), L.MOE_WS_ROUTE)
+    align = 256
+    assert route(T=16, E=8) == align                          # no workspace (+ alignment slack)
+    assert route(T=17, E=8) >= 4096 // 32 * 2048
+    assert route(T=17, d=4104, E=8) >= (4104 + 31) // 32 * 2048
+    assert route(T=16, E=64, k=8) >= 2 * 16 * 64 * 4          # two 2048-wide K ranges of fp32 partials
+    assert route(T=16, E=8, dtype=0) == align                 # fp32 with E <= 64: scores in registers
+
+
 def test_argument_errors_return_before_any_launch():
     s = _shape(T=16, d=64, m=64)
     fake = 4096  # never dereferenced: every call below fails its host-side checks
