@@ -271,6 +271,37 @@ def test_parity_small(cfg):
     run_layer(cfg)
 
 
+def _random_configs(n: int = 64, seed: int = 20231203):
+    """Seeded layer shapes across the paths' thresholds: T on both sides of 16
+    (the one-workgroup front) and of 256 (one dispatch block), E from 1 to 256
+    (every router path below the large-E select), d with and without the
+    multiple of 64 the in-place GEMM1 rows need, both dtypes and gate modes, the
+    overflow variants and the shared expert."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dtype = "bf16" if rng.random() < 0.8 else "f32"
+        T = int(rng.choice([1, 2, 5, 9, 16, 17, 40, 130, 255, 256, 257, 300, 520]))
+        E = int(rng.choice([1, 2, 3, 5, 8, 12, 33, 64, 70, 130, 256]))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        d = int(rng.choice([64, 128, 200, 256, 328, 512, 520]))
+        m = int(rng.choice([32, 64, 96, 136, 192]))
+        cf = [None, (1, 1), (5, 4), (1, 2), (3, 2)][int(rng.integers(0, 5))]
+        bias = ["none", "zipf", "first_two_plus2"][int(rng.integers(0, 3))]
+        shared = int(rng.choice([0, 0, 0, 64]))
+        by_gate = bool(rng.random() < 0.15) and cf is not None
+        survivors = bool(rng.random() < 0.15) and cf is not None
+        out.append(MoEConfig(f"rand{i}_T{T}_E{E}_k{k}_d{d}_{dtype}", T=T, d=d, m=m, E=E, k=k, dtype=dtype,
+                             gate_mode=int(rng.integers(0, 2)), cf=cf, bias=bias, m_shared=shared, cfg_id=100 + i,
+                             accept_by_gate=by_gate, renorm_survivors=survivors))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_configs(), ids=lambda c: c.name)
+def test_parity_random_shapes(cfg):
+    run_layer(cfg)
+
+
 def test_dense_k_equal_E_matches_dense_brute_force():
     """k = E, no capacity: the layer is the dense mixture; compare the GPU with the
     oracle's separately written dense loop."""
