@@ -265,7 +265,11 @@ moe_status moe_combine(const moe_shape* shape, const float* H, const int32_t* ro
  * differ: with bf16 activations the expert GEMMs read each grouped row in place
  * from x through the dispatch's row map (no x_perm copy; the E <= 8 router also
  * makes the dispatch's per-block counts), and with T <= 16 (bf16, E <= 256,
- * acceptance in token order) route and dispatch run as one workgroup. */
+ * acceptance in token order) route and dispatch run as one workgroup.  The
+ * shared expert runs on a second, default-priority stream of the device that the
+ * call forks from `stream` with an event and joins before the combine, so it
+ * overlaps the routed path; the call stays ordered on `stream` (and capturable).
+ * The library creates that stream and its two events once per device. */
 moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_r, const float* b_r,
                        const void* w_gate, const void* w_up, const void* w_down,
                        const void* s_gate, const void* s_up, const void* s_down,

@@ -2,6 +2,7 @@
 // Every call only queues kernels on the caller's stream; nothing here
 // allocates, frees or synchronises.
 #include <climits>
+#include <mutex>
 
 #include "common.h"
 
@@ -122,6 +123,34 @@ ForwardWs carve_forward(const moe_dims& d, void* base) {
 }
 
 inline moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// The shared expert depends on x alone, so moe_forward runs it on a second stream
+// of the caller's device, concurrently with routing, dispatch and the routed
+// experts: an event on the caller's stream forks it, another joins it before the
+// combine.  One default-priority, non-blocking stream and two events per device,
+// created on first use and kept for the process (they hold no device memory);
+// the mutex keeps each call's record / wait sequence together when several host
+// threads launch layers on one device.
+struct SideStream {
+    hipStream_t stream = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int MAX_DEVICES = 64;
+std::mutex g_side_mu;
+SideStream g_side[MAX_DEVICES];
+
+hipError_t side_stream(SideStream** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    SideStream& s = g_side[dev];
+    if (!s.fork && (e = hipEventCreateWithFlags(&s.fork, hipEventDisableTiming)) != hipSuccess) return e;
+    if (!s.join && (e = hipEventCreateWithFlags(&s.join, hipEventDisableTiming)) != hipSuccess) return e;
+    if (!s.stream && (e = hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking)) != hipSuccess) return e;
+    *out = &s;
+    return hipSuccess;
+}
 
 #define MOE_CHECK_HIP(expr)                        \
     do {                                           \
@@ -352,6 +381,18 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_r, 
     ForwardWs w = carve_forward(d, ws);
     if (ws_bytes < w.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    // the shared expert on the side stream, forked before anything else
+    std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
+    SideStream* side = nullptr;
+    if (d.m_shared && d.T > 0) {
+        side_lock.lock();
+        MOE_CHECK_HIP(side_stream(&side));
+        MOE_CHECK_HIP(hipEventRecord(side->fork, st));
+        MOE_CHECK_HIP(hipStreamWaitEvent(side->stream, side->fork, 0));
+        rc = shared_impl(d, x, s_gate, s_up, s_down, w.s, w.shared, side->stream);
+        if (rc != MOE_OK) return rc;
+        MOE_CHECK_HIP(hipEventRecord(side->join, side->stream));
+    }
     // the dispatch (or the one-workgroup front of small batches) also writes the
     // GEMMs' tile prefix at the start of the FFN workspace
     int32_t* tprefix = static_cast<int32_t*>(w.ffn);
@@ -371,10 +412,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_r, 
     rc = w.x_perm ? ffn_impl(d, w.x_perm, w.offsets, w_gate, w_up, w_down, w.H, w.ffn, &parts, st, true)
                   : ffn_impl(d, x, w.offsets, w_gate, w_up, w_down, w.H, w.ffn, &parts, st, true, w.src_token);
     if (rc != MOE_OK) return rc;
-    if (d.m_shared) {
-        rc = shared_impl(d, x, s_gate, s_up, s_down, w.s, w.shared, st);
-        if (rc != MOE_OK) return rc;
-    }
+    if (side) MOE_CHECK_HIP(hipStreamWaitEvent(st, side->join, 0));
     return hip_status(launch_combine(d, w.H, parts.H1, parts.np, parts.stride, w.row_of, topk_w, w.s, y, st));
 }
 

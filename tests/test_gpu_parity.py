@@ -531,17 +531,22 @@ def test_gpu_balance_matches_oracle(cfg):
         f"rho_max {bal[L.MOE_BAL_RHO_MAX]:.4f}, path rejection {bal[L.MOE_BAL_PATH_REJECTION]:.4f}")
 
 
-def test_forward_captures_into_a_graph():
+@pytest.mark.parametrize("cfg", [
+    RAGGED.scaled(name="graph", cfg_id=43),
+    # shared expert: moe_forward forks it onto a second stream and joins it before the combine
+    MoEConfig("graph_shared", T=300, d=256, m=128, E=16, k=4, dtype="bf16", gate_mode=0, cf=(5, 4), m_shared=192,
+              cfg_id=49),
+], ids=lambda c: c.name)
+def test_forward_captures_into_a_graph(cfg):
     """moe_forward queues no host synchronisation and no memset, so it can be
     captured into a HIP graph: every replay, with eager forwards and a cleared
     output between them, equals the eager result bit for bit."""
-    cfg = RAGGED.scaled(name="graph", cfg_id=43)
     inp = make_inputs(cfg, 0, DEV)
     shape = shape_of(cfg)
     layer = api.MoELayer(shape, DEV)
 
     def fwd():
-        layer.forward(inp.x, inp.w_r, inp.b_r, inp.w_gate, inp.w_up, inp.w_down)
+        layer.forward(inp.x, inp.w_r, inp.b_r, inp.w_gate, inp.w_up, inp.w_down, inp.s_gate, inp.s_up, inp.s_down)
 
     fwd()
     torch.cuda.synchronize()
