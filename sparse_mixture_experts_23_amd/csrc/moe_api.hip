@@ -125,7 +125,7 @@ ForwardWs carve_forward(const moe_dims& d, void* base) {
 inline moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 // The shared expert depends on x alone, so moe_forward runs it on a second stream
-// of the caller's device, concurrently with routing, dispatch and the routed
+// of the device of the caller's stream, concurrently with routing, dispatch and the routed
 // experts: an event on the caller's stream forks it, another joins it before the
 // combine.  One default-priority, non-blocking stream and two events per device,
 // created on first use and kept for the process (they hold no device memory);
@@ -139,15 +139,25 @@ constexpr int MAX_DEVICES = 64;
 std::mutex g_side_mu;
 SideStream g_side[MAX_DEVICES];
 
-hipError_t side_stream(SideStream** out) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
+// The side stream of the device that `st` belongs to (made current only while
+// the stream and events are created).
+hipError_t side_stream(hipStream_t st, SideStream** out) {
+    hipDevice_t dev = 0;
+    hipError_t e = hipStreamGetDevice(st, &dev);
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
     SideStream& s = g_side[dev];
-    if (!s.fork && (e = hipEventCreateWithFlags(&s.fork, hipEventDisableTiming)) != hipSuccess) return e;
-    if (!s.join && (e = hipEventCreateWithFlags(&s.join, hipEventDisableTiming)) != hipSuccess) return e;
-    if (!s.stream && (e = hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking)) != hipSuccess) return e;
+    if (!s.fork || !s.join || !s.stream) {
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        if (!s.fork) e = hipEventCreateWithFlags(&s.fork, hipEventDisableTiming);
+        if (e == hipSuccess && !s.join) e = hipEventCreateWithFlags(&s.join, hipEventDisableTiming);
+        if (e == hipSuccess && !s.stream) e = hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking);
+        const hipError_t r = cur != dev ? hipSetDevice(cur) : hipSuccess;
+        if (e != hipSuccess) return e;
+        if (r != hipSuccess) return r;
+    }
     *out = &s;
     return hipSuccess;
 }
@@ -386,7 +396,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_r, 
     SideStream* side = nullptr;
     if (d.m_shared && d.T > 0) {
         side_lock.lock();
-        MOE_CHECK_HIP(side_stream(&side));
+        MOE_CHECK_HIP(side_stream(st, &side));
         MOE_CHECK_HIP(hipEventRecord(side->fork, st));
         MOE_CHECK_HIP(hipStreamWaitEvent(side->stream, side->fork, 0));
         rc = shared_impl(d, x, s_gate, s_up, s_down, w.s, w.shared, side->stream);
