@@ -400,29 +400,41 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_r, 
         MOE_CHECK_HIP(hipEventRecord(side->fork, st));
         MOE_CHECK_HIP(hipStreamWaitEvent(side->stream, side->fork, 0));
         rc = shared_impl(d, x, s_gate, s_up, s_down, w.s, w.shared, side->stream);
-        if (rc != MOE_OK) return rc;
-        MOE_CHECK_HIP(hipEventRecord(side->join, side->stream));
+        const hipError_t e = hipEventRecord(side->join, side->stream);
+        if (e != hipSuccess) return MOE_ERR_HIP;
+        if (rc != MOE_OK) {
+            // whatever the side stream queued still finishes before later work on st
+            return hipStreamWaitEvent(st, side->join, 0) == hipSuccess ? rc : MOE_ERR_HIP;
+        }
     }
+    // every return below first joins the side stream, also on an error
+    auto joined = [&](moe_status r) -> moe_status {
+        if (side && hipStreamWaitEvent(st, side->join, 0) != hipSuccess) return MOE_ERR_HIP;
+        return r;
+    };
     // the dispatch (or the one-workgroup front of small batches) also writes the
     // GEMMs' tile prefix at the start of the FFN workspace
     int32_t* tprefix = static_cast<int32_t*>(w.ffn);
     if (front_fused_ok(d)) {
-        MOE_CHECK_HIP(launch_front(d, x, w_r, b_r, topk_ids, topk_w, status, w.route, st, load, w.offsets, slot,
-                                   w.row_of, w.src_token, w.x_perm, stats, tprefix, gemm_tile_rows(d.dtype)));
+        if (launch_front(d, x, w_r, b_r, topk_ids, topk_w, status, w.route, st, load, w.offsets, slot, w.row_of,
+                         w.src_token, w.x_perm, stats, tprefix, gemm_tile_rows(d.dtype)) != hipSuccess)
+            return joined(MOE_ERR_HIP);
     } else {
         // where it can, the router also counts the dispatch's per-block expert loads
         bool counted = false;
-        MOE_CHECK_HIP(launch_route(d, x, w_r, b_r, topk_ids, topk_w, status, w.route, st, nullptr,
-                                   dispatch_uses_hist(d) ? static_cast<int32_t*>(w.dispatch) : nullptr, &counted,
-                                   stats + MOE_STAT_TOKENS_DROPPED));
-        MOE_CHECK_HIP(launch_dispatch(d, x, topk_ids, topk_w, load, w.offsets, slot, w.row_of, w.src_token,
-                                      w.x_perm, stats, w.dispatch, st, tprefix, gemm_tile_rows(d.dtype), counted));
+        if (launch_route(d, x, w_r, b_r, topk_ids, topk_w, status, w.route, st, nullptr,
+                         dispatch_uses_hist(d) ? static_cast<int32_t*>(w.dispatch) : nullptr, &counted,
+                         stats + MOE_STAT_TOKENS_DROPPED) != hipSuccess)
+            return joined(MOE_ERR_HIP);
+        if (launch_dispatch(d, x, topk_ids, topk_w, load, w.offsets, slot, w.row_of, w.src_token, w.x_perm, stats,
+                            w.dispatch, st, tprefix, gemm_tile_rows(d.dtype), counted) != hipSuccess)
+            return joined(MOE_ERR_HIP);
     }
     Partials parts;   // K-split partials of H beyond the first, added by the combine
     rc = w.x_perm ? ffn_impl(d, w.x_perm, w.offsets, w_gate, w_up, w_down, w.H, w.ffn, &parts, st, true)
                   : ffn_impl(d, x, w.offsets, w_gate, w_up, w_down, w.H, w.ffn, &parts, st, true, w.src_token);
+    rc = joined(rc);
     if (rc != MOE_OK) return rc;
-    if (side) MOE_CHECK_HIP(hipStreamWaitEvent(st, side->join, 0));
     return hip_status(launch_combine(d, w.H, parts.H1, parts.np, parts.stride, w.row_of, topk_w, w.s, y, st));
 }
 
