@@ -63,6 +63,12 @@ def copy_calibration(nbytes: int, reps: int):
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
 
 
+def _spread(v):
+    """Median, 10th and 90th percentile (nearest rank) of sorted step times in ms."""
+    pick = lambda q: v[min(len(v) - 1, int(round(q * (len(v) - 1))))]  # noqa: E731
+    return {"median": round(pick(0.5), 4), "p10": round(pick(0.1), 4), "p90": round(pick(0.9), 4), "n": len(v)}
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -141,11 +147,21 @@ def cpu_baseline(cfg, inp, budget_tokens):
     if cfg.m_shared:
         shared = (inp.s_gate.float().cpu().numpy(), inp.s_up.float().cpu().numpy(), inp.s_down.float().cpu().numpy())
     C = None if cfg.cf is None else O.capacity(Ts, cfg.k, cfg.E, *cfg.cf)
+    # the routing and slot-assignment steps on their own, for the phase split
     t0 = time.perf_counter()
+    rt = O.route(x, wr, b, cfg.k, cfg.gate_mode, cfg.renorm_form)
+    t1 = time.perf_counter()
+    cap = Ts if C is None else C
+    if cfg.accept_by_gate:
+        O.assign_slots_by_gate(rt.ids, O.round_to_f32(rt.w), cfg.E, cap)
+    else:
+        O.assign_slots(rt.ids, cfg.E, cap)
+    t2 = time.perf_counter()
     O.forward(x, wr, b, experts, cfg.k, cfg.gate_mode, C=C, shared=shared, round_h_bf16=cfg.dtype == "bf16",
               renorm_form=cfg.renorm_form, accept_by_gate=cfg.accept_by_gate,
               renorm_survivors=cfg.renorm_survivors)
-    dt = time.perf_counter() - t0
+    dt = time.perf_counter() - t2
+    t_route, t_disp = t1 - t0, t2 - t1
     threads = 1
     if threadpool_info is not None:
         info = [p for p in threadpool_info() if p.get("user_api") == "blas"]
@@ -153,7 +169,22 @@ def cpu_baseline(cfg, inp, budget_tokens):
             threads = max(p.get("num_threads", 1) for p in info)
     return {"value": Ts / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{Ts}-token routing group of the {cfg.name} layer (d={cfg.d}, m={cfg.m}, E={cfg.E}, "
-                      f"k={cfg.k}), fp64 numpy oracle, {dt:.1f} s"}
+                      f"k={cfg.k}), fp64 numpy oracle, {dt:.1f} s",
+            "phase_s": {"route": round(t_route, 3), "dispatch": round(t_disp, 3),
+                        "experts_and_combine": round(max(dt - t_route - t_disp, 0.0), 3)},
+            "cpu": _cpu_model()}
+
+
+def _cpu_model():
+    """Host CPU model and socket count from /proc/cpuinfo (Linux)."""
+    try:
+        txt = open("/proc/cpuinfo").read()
+    except OSError:
+        return None
+    models = {ln.split(":", 1)[1].strip() for ln in txt.splitlines() if ln.startswith("model name")}
+    sockets = {ln.split(":", 1)[1].strip() for ln in txt.splitlines() if ln.startswith("physical id")}
+    return {"model": sorted(models)[0] if models else None, "sockets": len(sockets) or None,
+            "threads_visible": len(os.sched_getaffinity(0))}
 
 
 def main():
@@ -170,6 +201,8 @@ def main():
                     help="override the workload's token count T (e.g. 1..64 for decode-sized batches)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="extra forwards each timed after a 512 MiB cache-flushing write (0: none)")
     ap.add_argument("--phases", default="1", help="0 disables the per-phase timing loop")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration) and exit")
@@ -204,17 +237,40 @@ def main():
     torch.cuda.synchronize()
     layer.check_status()
     log(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps")
+    # per-step HIP events on the launch stream (for the spread of step times)
+    st_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.steps)]
+    launch_stream = torch.cuda.current_stream()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for a, b in st_ev:
+        a.record(launch_stream)
         fwd()
+        b.record(launch_stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    step_ms = sorted(a.elapsed_time(b) for a, b in st_ev)
     ms = elapsed * 1e3 / max(args.steps, 1)
     tokens_per_s = cfg.T / (ms / 1e3)
     stats = layer.stats.cpu().tolist()
     load = layer.load.cpu().tolist()
     A = stats[L.MOE_STAT_ACCEPTED]
     log(f"[bench] {ms:.3f} ms/step, {tokens_per_s:,.0f} tokens/s, accepted paths {A}")
+
+    # cold caches: before each step, a 512 MiB write evicts the 256 MB last-level
+    # cache and the L2s, so the step reads its inputs from HBM
+    cold_ms = []
+    if args.cold_steps > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        cold_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.cold_steps)]
+        for i, (a, b) in enumerate(cold_ev):
+            flush.fill_(i & 0xFF)
+            a.record(launch_stream)
+            fwd()
+            b.record(launch_stream)
+        torch.cuda.synchronize()
+        cold_ms = sorted(a.elapsed_time(b) for a, b in cold_ev)
+        del flush
 
     # per-phase split with HIP events on the launch stream
     phases = {}
@@ -302,6 +358,8 @@ def main():
                   "max_load": stats[L.MOE_STAT_MAX_LOAD], "rho_max": round(stats[L.MOE_STAT_MAX_LOAD] / (T * k / cfg.E), 4),
                   "tokens_dropped": stats[L.MOE_STAT_TOKENS_DROPPED], "active_experts": active},
         "roofline": roofline,
+        "step_ms": _spread(step_ms),
+        "cold_step_ms": _spread(cold_ms) if cold_ms else None,
         **extra,
     }
     if not args.no_cpu_baseline:
