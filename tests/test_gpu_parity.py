@@ -567,3 +567,46 @@ def test_forward_captures_into_a_graph(cfg):
         fwd()
         torch.cuda.synchronize()
         assert torch.equal(layer.y, ref_y)
+
+
+def test_concurrent_host_threads_on_separate_streams():
+    """Two host threads launch shared-expert layers on their own streams at the
+    same time (the C calls release the GIL): the shared expert's side stream is
+    common to both, so each call's fork / join must stay paired.  Every forward
+    equals that input's single-threaded result bit for bit."""
+    import threading
+    cfg = MoEConfig("threads_shared", T=300, d=256, m=128, E=16, k=4, dtype="bf16", gate_mode=0, cf=(5, 4),
+                    m_shared=192, cfg_id=50)
+    shape = shape_of(cfg)
+    inps = [make_inputs(cfg, seed, DEV) for seed in (0, 1)]
+    refs = []
+    for inp in inps:
+        lay = api.forward(shape, inp.x, inp.w_r, inp.b_r, inp.w_gate, inp.w_up, inp.w_down, inp.s_gate, inp.s_up,
+                          inp.s_down)
+        refs.append(lay.y.clone())
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(i):
+        try:
+            inp, st = inps[i], torch.cuda.Stream()
+            layer = api.MoELayer(shape, DEV)
+            with torch.cuda.stream(st):
+                for _ in range(8):
+                    layer.y.fill_(-1.0)
+                    layer.forward(inp.x, inp.w_r, inp.b_r, inp.w_gate, inp.w_up, inp.w_down, inp.s_gate, inp.s_up,
+                                  inp.s_down)
+                    st.synchronize()
+                    if not torch.equal(layer.y, refs[i]):
+                        errors.append(f"thread {i}: output differs")
+                        return
+        except Exception as e:   # surfaced below
+            errors.append(f"thread {i}: {e!r}")
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads), "a worker thread did not finish"
+    assert not errors, errors
