@@ -93,6 +93,15 @@ struct moe_dims {
 // of tokens in [256 b, 256 b + 256) that selected expert e.
 constexpr int MOE_DISPATCH_BLOCK = 256;
 
+// Work-claim counters of the grouped bf16 GEMMs, kept after the tile prefix
+// (tprefix[0..G]) in the same workspace: MOE_SCHED_WORDS 64-bit words, one per
+// XCD for GEMM1, then one per XCD for GEMM2.  Every kernel that writes a tile
+// prefix also clears them, so each GEMM launch starts from zero.
+constexpr int MOE_SCHED_WORDS = 16;
+__host__ __device__ inline unsigned long long* moe_sched_words(int32_t* tprefix, int G) {
+    return reinterpret_cast<unsigned long long*>(tprefix + ((G + 2) & ~1));
+}
+
 namespace moe_kernels {
 
 // Router: scores, softmax, top-k, weights.  ws holds the weight planes or the

@@ -122,6 +122,7 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict
     if (e < E) offsets[e] = before + incl - acc;
     if (tprefix && e < E) tprefix[e] = tbefore + tincl - tiles;
     if (tprefix && e == 0) tprefix[E] = ttotal;
+    if (tprefix && e < MOE_SCHED_WORDS) moe_sched_words(tprefix, E)[e] = 0ull;
     if (roff && e < E) roff[e] = rbefore + rincl - (e < E ? L : 0);
     if (roff && e == 0) roff[E] = rtotal;
     if (e == 0) {
@@ -312,6 +313,7 @@ __global__ __launch_bounds__(DB_TOK) void dispatch_place_scan_kernel(
             offsets[e] = off;
             if (tprefix) tprefix[e] = tbefore + tincl - tiles;
         }
+        if (tprefix && e < MOE_SCHED_WORDS) moe_sched_words(tprefix, E)[e] = 0ull;
         if (e == 0) {
             offsets[E] = total;
             if (tprefix) tprefix[E] = ttotal;

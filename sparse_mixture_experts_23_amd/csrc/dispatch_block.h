@@ -123,6 +123,7 @@ __device__ void dispatch_one_block(const int32_t* __restrict__ ids, int64_t T, i
         offsets[e] = off;
         if (tprefix) tprefix[e] = tbefore + tincl - tiles;
     }
+    if (tprefix && e < MOE_SCHED_WORDS) moe_sched_words(tprefix, E)[e] = 0ull;
     if (e == 0) {
         offsets[E] = total;
         if (tprefix) tprefix[E] = ttotal;

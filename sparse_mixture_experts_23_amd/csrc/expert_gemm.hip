@@ -46,15 +46,10 @@ struct TileCoord {
     int64_t row_start, row_end;
 };
 
-__device__ __forceinline__ bool tile_coords(int b, const int32_t* __restrict__ offsets,
-                                            const int32_t* __restrict__ tprefix, int G, int64_t nrows, int BM, int NT,
-                                            TileCoord& tc, int nsup = NSUPER) {
-    const int MT = offsets ? tprefix[G] : (int)((nrows + BM - 1) / BM);
-    const int total = MT * NT;
-    if (b >= total) return false;
-    const int x = b % XCDS, j = b / XCDS;
-    const int q = total / XCDS, rmd = total % XCDS;
-    const int w = x * q + min(x, rmd) + j;
+// Work item w of the list (n super-tile, m tile, n tile) -> tile.
+__device__ __forceinline__ void tile_of_item(int w, const int32_t* __restrict__ offsets,
+                                             const int32_t* __restrict__ tprefix, int G, int64_t nrows, int BM,
+                                             int NT, int MT, TileCoord& tc, int nsup) {
     const int per_super = MT * nsup;
     const int ns = w / per_super;
     const int rem = w - ns * per_super;
@@ -76,7 +71,83 @@ __device__ __forceinline__ bool tile_coords(int b, const int32_t* __restrict__ o
         tc.row_start = (int64_t)mtg * BM;
         tc.row_end = nrows;
     }
+}
+
+__device__ __forceinline__ int tile_count(const int32_t* __restrict__ offsets, const int32_t* __restrict__ tprefix,
+                                          int G, int64_t nrows, int BM) {
+    return offsets ? tprefix[G] : (int)((nrows + BM - 1) / BM);
+}
+
+// Static schedule: workgroup b takes item w of XCD x = b % 8's contiguous run.
+__device__ __forceinline__ bool tile_coords(int b, const int32_t* __restrict__ offsets,
+                                            const int32_t* __restrict__ tprefix, int G, int64_t nrows, int BM, int NT,
+                                            TileCoord& tc, int nsup = NSUPER) {
+    const int MT = tile_count(offsets, tprefix, G, nrows, BM);
+    const int total = MT * NT;
+    if (b >= total) return false;
+    const int x = b % XCDS, j = b / XCDS;
+    const int q = total / XCDS, rmd = total % XCDS;
+    tile_of_item(x * q + min(x, rmd) + j, offsets, tprefix, G, nrows, BM, NT, MT, tc, nsup);
     return true;
+}
+
+// Balanced schedule.  The XCDs of one launch run at different shader clocks
+// (measured per XCD with s_memtime: up to ~10 % apart under the GEMMs' load), so
+// equal static runs leave the fast XCDs idle at the end.  Each XCD's run keeps
+// its first 7/8 static (taken by workgroup index, as in tile_coords); the last
+// eighth is claimed at run time.  Per XCD one 64-bit counter q[x] holds (low
+// half) the items its own workgroups took from the front of that eighth and
+// (high half) the items other XCDs' workgroups took from its back.  A claim is
+// one atomic add that returns both counts: it is valid iff their sum was below
+// the eighth's length D, which makes front and back claims disjoint and the
+// first D claims cover the eighth exactly.  A workgroup past its own eighth
+// steals from the back of the XCD with the most items left; a failed steal
+// leaves that XCD with none left for good, so at most 8 attempts are made.
+// The grid's workgroups past the item count (the host sizes the grid for the
+// largest possible tile count) are extra claimers, so a fast XCD can take more
+// than its own eighth.  Returns the item, or -1 when every item is taken.
+// Executed by all threads of the workgroup (the branch is uniform); `bcast` is
+// LDS the workgroup may use.
+__device__ __forceinline__ int claim_item(int b, int total, unsigned long long* __restrict__ q, int* bcast) {
+    const int x = b % XCDS, j = b / XCDS;
+    const int qq = total / XCDS, rmd = total % XCDS;
+    const int Lx = qq + (x < rmd ? 1 : 0), start = x * qq + min(x, rmd);
+    const int Sx = Lx - (Lx >> 3);
+    if (j < Sx) return start + j;
+    if (total == 0) return -1;
+    if (threadIdx.x == 0) {
+        int w = -1;
+        if (j < Lx) {   // one of the run's own workgroups: the front of its eighth first
+            const unsigned long long o =
+                __hip_atomic_fetch_add(q + x, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int h = (int)(o & 0xffffffffull), t = (int)(o >> 32);
+            if (h + t < (Lx >> 3)) w = start + Sx + h;
+        }
+        // workgroups past the run (the grid's slack) go straight to stealing
+        for (int attempt = 0; attempt <= XCDS && w < 0; ++attempt) {
+            int best = -1, left = 0;
+            for (int y = 0; y < XCDS; ++y) {
+                const unsigned long long v = __hip_atomic_load(q + y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const int Dy = (qq + (y < rmd ? 1 : 0)) >> 3;
+                const int r = Dy - (int)(v & 0xffffffffull) - (int)(v >> 32);
+                if (r > left) {
+                    left = r;
+                    best = y;
+                }
+            }
+            if (best < 0) break;
+            const unsigned long long v =
+                __hip_atomic_fetch_add(q + best, 1ull << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int Ly = qq + (best < rmd ? 1 : 0), Dy = Ly >> 3;
+            const int hy = (int)(v & 0xffffffffull), ty = (int)(v >> 32);
+            if (hy + ty < Dy) w = best * qq + min(best, rmd) + (Ly - Dy) + (Dy - 1 - ty);
+        }
+        *bcast = w;
+    }
+    __syncthreads();
+    const int w = *bcast;
+    __syncthreads();   // the word is overwritten by the first tile loads
+    return w;
 }
 
 // tprefix[g] = sum_{g' < g} ceil(rows(g') / BM); one workgroup, G <= 1024.
@@ -104,6 +175,7 @@ __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __rest
     }
     if (g < G) tprefix[g] = before + incl - cnt;
     if (g == 0) tprefix[G] = total;
+    if (g < MOE_SCHED_WORDS) moe_sched_words(tprefix, G)[g] = 0ull;
 }
 
 // ---------------------------------------------------------------------------
@@ -608,7 +680,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* _
                                                                const int32_t* __restrict__ offsets,
                                                                const int32_t* __restrict__ tprefix, int G,
                                                                int64_t nrows, int N, int K, int S, int nsup,
-                                                               int thin_all, const int32_t* __restrict__ gather) {
+                                                               int thin_all, const int32_t* __restrict__ gather,
+                                                               unsigned long long* __restrict__ sched) {
     constexpr int BM = 256, BK = 64, WGN = 2, WAVES = 8;
     constexpr int NOPS = SWIGLU ? 2 : 1;
     constexpr int WM = 64, WN = BN / WGN;       // wave tile: 64 rows x WN columns of each operand
@@ -630,7 +703,19 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_asm_kernel(const uint16_t* _
     const int NT = (N + BN - 1) / BN;
     const int tiles_grid = gridDim.x / S;
     const int split = blockIdx.x / tiles_grid;
-    if (!tile_coords(blockIdx.x - split * tiles_grid, offsets, tprefix, G, nrows, BM, NT, tc, nsup)) return;
+    if (sched && split == S - 1) {
+        // balanced schedule for the last K-split copy, whose end is the launch's
+        // end (earlier copies are followed by the next copy's work, and their grid
+        // slack is dispatched mid-launch, too early to balance anything); the LDS
+        // word is free until the first tile loads
+        const int MT = tile_count(offsets, tprefix, G, nrows, BM);
+        const int b = blockIdx.x - split * tiles_grid;
+        const int w = claim_item(b, MT * NT, sched, reinterpret_cast<int*>(lds));
+        if (w < 0) return;
+        tile_of_item(w, offsets, tprefix, G, nrows, BM, NT, MT, tc, nsup);
+    } else if (!tile_coords(blockIdx.x - split * tiles_grid, offsets, tprefix, G, nrows, BM, NT, tc, nsup)) {
+        return;
+    }
     const int KTall = K / BK;
     const int kt_begin = split * KTall / S, kt_end = (split + 1) * KTall / S;
     // SPLIT_GU (SwiGLU, S > 1): fp32 gate / up partials, gate of split s at Cpart + s
@@ -1044,6 +1129,14 @@ hipError_t prep_tiles(const int32_t* offsets, int G, int BM, void* ws, hipStream
     return hipGetLastError();
 }
 
+// Counter set `set` of the balanced schedule (grouped launches only): set 0 for
+// GEMM1, set 1 for GEMM2.  Launches whose whole grid fits in one round of
+// workgroups (small batches) keep the static schedule: every workgroup starts at
+// once, so there is no tail to balance and a claim would only add its latency.
+unsigned long long* sched_set(const int32_t* offsets, void* ws, int G, int set) {
+    return offsets ? moe_sched_words(static_cast<int32_t*>(ws), G) + set * XCDS : nullptr;
+}
+
 unsigned grid_size(const int32_t* offsets, int G, int64_t max_rows, int BM, int N, int BN) {
     const int64_t mt = (max_rows + BM - 1) / BM + (offsets ? G : 0);
     const int64_t nt = (N + BN - 1) / BN;
@@ -1054,7 +1147,11 @@ unsigned grid_size(const int32_t* offsets, int G, int64_t max_rows, int BM, int 
 
 namespace moe_kernels {
 
-size_t gemm_ws_bytes(int G) { return (((size_t)(G + 1) * sizeof(int32_t)) + 255) & ~(size_t)255; }
+// tile prefix (G + 1 int32, padded to 8 bytes) and the balanced schedule's counters
+size_t gemm_ws_bytes(int G) {
+    return ((size_t)((G + 2) & ~1) * sizeof(int32_t) + MOE_SCHED_WORDS * sizeof(unsigned long long) + 255) &
+           ~(size_t)255;
+}
 
 int gemm_tile_rows(int dtype) { return dtype == MOE_BF16 ? BF16_BM : F32_BM; }
 
@@ -1111,7 +1208,7 @@ hipError_t launch_gemm1(int dtype, const void* A, const int32_t* offsets, int G,
         hipLaunchKernelGGL((gemm_bf16_asm_kernel<BF16_BN1, true, true>), dim3(grid), dim3(512), 0, st,
                            static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(w_gate),
                            static_cast<const uint16_t*>(w_up), h, part, stride, offsets, tp, G, max_rows, N, K, S,
-                           NSUPER, one_round(max_rows, G, N, BF16_BN1, S), gather);
+                           NSUPER, one_round(max_rows, G, N, BF16_BN1, S), gather, (unsigned long long*)nullptr);
         const int64_t n4 = max_rows * (N / 4);
         hipLaunchKernelGGL(swiglu_reduce_kernel, dim3((unsigned)std::min<int64_t>((n4 + 255) / 256, 8192)),
                            dim3(256), 0, st, part, S, stride, offsets, G, max_rows, N, static_cast<uint16_t*>(h));
@@ -1119,7 +1216,8 @@ hipError_t launch_gemm1(int dtype, const void* A, const int32_t* offsets, int G,
         hipLaunchKernelGGL((gemm_bf16_asm_kernel<BF16_BN1, true>), dim3(grid), dim3(512), 0, st,
                            static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(w_gate),
                            static_cast<const uint16_t*>(w_up), h, nullptr, (int64_t)0, offsets, tp, G, max_rows, N, K, 1,
-                           NSUPER, one_round(max_rows, G, N, BF16_BN1, 1), gather);
+                           NSUPER, one_round(max_rows, G, N, BF16_BN1, 1), gather,
+                           one_round(max_rows, G, N, BF16_BN1, 1) ? nullptr : sched_set(offsets, ws, G, 0));
     else if (dtype == MOE_BF16)
         hipLaunchKernelGGL((gemm_bf16_kernel<BF16_BM, BF16_BN1, true>), dim3(grid), dim3(256), 0, st,
                            static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(w_gate),
@@ -1163,7 +1261,8 @@ hipError_t launch_gemm2(int dtype, const void* h, const int32_t* offsets, int G,
                            static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w_down), nullptr, H, H1,
                            max_rows * N, offsets, tp, G, max_rows, N, K, S,
                            super_width(max_rows, G, (N + BN - 1) / BN), one_round(max_rows, G, N, BF16_BN2, S),
-                           (const int32_t*)nullptr);
+                           (const int32_t*)nullptr,
+                           one_round(max_rows, G, N, BF16_BN2, S) ? nullptr : sched_set(offsets, ws, G, 1));
     } else if (dtype == MOE_BF16) {
         hipLaunchKernelGGL((gemm_bf16_kernel<BF16_BM, BF16_BN2, false>), dim3(grid), dim3(256), 0, st,
                            static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w_down), nullptr, H,
@@ -1191,7 +1290,8 @@ hipError_t launch_scores_gemm(const void* x, const void* w, int64_t T, int N, in
         const unsigned grid = (tiles + XCDS - 1) / XCDS * XCDS * S;
         hipLaunchKernelGGL((gemm_bf16_asm_kernel<BF16_BN2, false>), dim3(grid), dim3(512), 0, st,
                            static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), nullptr, part,
-                           part + T * N, T * N, nullptr, nullptr, 1, T, N, K, S, NSUPER, 0, (const int32_t*)nullptr);
+                           part + T * N, T * N, nullptr, nullptr, 1, T, N, K, S, NSUPER, 0, (const int32_t*)nullptr,
+                           (unsigned long long*)nullptr);
     } else {
         hipLaunchKernelGGL((gemm_bf16_kernel<BF16_BM, BF16_BN2, false>), dim3(tiles), dim3(256), 0, st,
                            static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), nullptr, part, nullptr,
