@@ -610,3 +610,25 @@ def test_concurrent_host_threads_on_separate_streams():
         t.join(timeout=120)
     assert not any(t.is_alive() for t in threads), "a worker thread did not finish"
     assert not errors, errors
+
+
+def test_balanced_schedule_multi_round_skewed_is_exact_and_deterministic():
+    """Grouped GEMMs of several rounds of workgroups with skewed expert loads:
+    the last eighth of each XCD's run is claimed at run time (and stolen across
+    XCDs), so which workgroup computes a tile varies from run to run.  Every
+    tile must still be computed exactly once: the layer matches the oracle on
+    sampled tokens, and twelve repeated forwards are identical bit for bit."""
+    cfg = MoEConfig("balanced_sched", T=2048, d=2048, m=1024, E=64, k=8, dtype="bf16", gate_mode=0, cf=(5, 4),
+                    bias="zipf", cfg_id=51)
+    r = run_layer(cfg, sample=96)
+    shape, inp = r["shape"], r["inp"]
+    # more row x column tiles than the 256 CUs in both GEMMs (several rounds)
+    rows = np.diff(r["disp"].offsets.cpu().numpy())
+    mt = int(sum((int(v) + 255) // 256 for v in rows))
+    assert mt * (cfg.m // 128) > 256 and mt * (cfg.d // 256) > 256
+    layer = api.MoELayer(shape, DEV)
+    for i in range(12):
+        layer.y.fill_(float("nan"))
+        layer.forward(inp.x, inp.w_r, inp.b_r, inp.w_gate, inp.w_up, inp.w_down)
+        torch.cuda.synchronize()
+        assert torch.equal(layer.y, r["y"]), f"repeat {i} differs"
