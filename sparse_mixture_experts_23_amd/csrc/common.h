@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <climits>
 
 #include "../../include/moe.h"
 
@@ -162,8 +163,15 @@ int gemm_tile_rows(int dtype);
 // tiles exist (decided from the shape alone); it then needs `part`, fp32 scratch
 // of gemm1_part_bytes(...) (S gate and S up partials), and forms h from their
 // sums.  With part == nullptr it never splits.
-int gemm1_splits(int dtype, int64_t max_rows, int G, int N, int K);
-size_t gemm1_part_bytes(int dtype, int64_t max_rows, int G, int N, int K);
+// group_rows: an upper bound on the rows of any one group (the routed experts:
+// min(T, C), a token adding at most one row per expert; the shared expert: T).
+// With at most MOE_GEMV_ROWS rows per group (decode batches) both GEMMs run as
+// grouped GEMVs that stream the active groups' weights, and never split K.
+constexpr int64_t MOE_GEMV_ROWS = 8;
+constexpr int64_t MOE_ROWS_UNKNOWN = INT64_MAX;
+bool gemv_path(int dtype, int64_t group_rows);
+int gemm1_splits(int dtype, int64_t max_rows, int G, int N, int K, int64_t group_rows = MOE_ROWS_UNKNOWN);
+size_t gemm1_part_bytes(int dtype, int64_t max_rows, int G, int N, int K, int64_t group_rows = MOE_ROWS_UNKNOWN);
 // gather (nullable, only where gemm1_gather_ok): A is the token-ordered [a_rows, K]
 // activations and grouped row r reads A row gather[r] (the dispatch's src_token,
 // readable up to 256 entries past the last row), so no grouped copy is needed.
@@ -171,14 +179,14 @@ bool gemm1_gather_ok(int dtype, int N, int K, int64_t a_rows);
 hipError_t launch_gemm1(int dtype, const void* A, const int32_t* offsets, int G, int64_t max_rows,
                         const void* w_gate, const void* w_up, void* h, int N, int K,
                         void* ws, hipStream_t st, bool prefix_ready = false, float* part = nullptr,
-                        const int32_t* gather = nullptr);
+                        const int32_t* gather = nullptr, int64_t group_rows = MOE_ROWS_UNKNOWN);
 // GEMM2 may split K over S = gemm2_splits(...) (decided from the shape alone):
 // then H receives the partial sum over the first K range and H1 + (s - 1) max_rows N
 // the sum over range s = 1..S-1; with H1 == nullptr it never splits.
-int gemm2_splits(int dtype, int64_t max_rows, int G, int N, int K);
+int gemm2_splits(int dtype, int64_t max_rows, int G, int N, int K, int64_t group_rows = MOE_ROWS_UNKNOWN);
 hipError_t launch_gemm2(int dtype, const void* h, const int32_t* offsets, int G, int64_t max_rows,
                         const void* w_down, float* H, float* H1, int N, int K, void* ws, hipStream_t st,
-                        bool prefix_ready = false);
+                        bool prefix_ready = false, int64_t group_rows = MOE_ROWS_UNKNOWN);
 // H += H1[0] + ... + H1[np - 1] (blocks of max_rows N floats, added in order) over the
 // rows [0, offsets[G]) (or [0, max_rows) without offsets); N % 4 == 0.
 hipError_t launch_add_partial(float* H, const float* H1, int np, const int32_t* offsets, int G, int64_t max_rows,

@@ -1053,6 +1053,128 @@ __global__ __launch_bounds__(256) void swiglu_reduce_kernel(const float* __restr
 // fp32 grouped GEMM (plain FMA)
 // ---------------------------------------------------------------------------
 
+// ---------------------------------------------------------------------------
+// Grouped GEMV for a handful of rows per group (decode batches)
+// ---------------------------------------------------------------------------
+//
+// With at most MOE_GEMV_ROWS rows in every group the expert GEMMs are weight
+// streams (a few flops per weight byte): no LDS staging, no MFMA.  Each wave owns
+// 4 weight rows over the whole K (SwiGLU: the gate and up rows of 2 output
+// columns; otherwise 4 output columns); per step a lane loads 16 bytes (8 bf16)
+// of each weight row and of each of the group's activation rows at K offset
+// 8 lane + 512 step and accumulates exact bf16 products in fp32; the 64 lanes'
+// partial sums are then added by a butterfly.  Small register and no LDS
+// footprint, so many waves per CU keep enough weight loads in flight.
+// Workgroup b: the (b / nchunk)-th group with rows (the active groups, found
+// with a ballot over offsets), output columns from (b % nchunk) * 4 waves.
+__device__ __forceinline__ float dot8_bf16(uint4 a, uint4 b, float acc) {
+    const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        acc = fmaf(__uint_as_float(av[i] << 16), __uint_as_float(bv[i] << 16), acc);
+        acc = fmaf(__uint_as_float(av[i] & 0xffff0000u), __uint_as_float(bv[i] & 0xffff0000u), acc);
+    }
+    return acc;
+}
+
+template <bool SWIGLU, int RMAX>
+__global__ __launch_bounds__(256) void gemv_bf16_kernel(const uint16_t* __restrict__ A,
+                                                        const uint16_t* __restrict__ B0,
+                                                        const uint16_t* __restrict__ B1, void* __restrict__ Cout,
+                                                        const int32_t* __restrict__ offsets, int G, int64_t nrows,
+                                                        int N, int K, int nchunk,
+                                                        const int32_t* __restrict__ gather) {
+    constexpr int UNROLL = RMAX == 1 ? 4 : (RMAX <= 4 ? 2 : 1);   // K steps in flight per wave
+    constexpr int COLS_W = SWIGLU ? 2 : 4;   // output columns per wave
+    const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+    const int a = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
+    int g = 0;
+    int64_t r0 = 0, r1 = nrows;
+    if (offsets) {
+        // the a-th group with rows (uniform loop: a, seen and the ballots are)
+        g = -1;
+        int seen = 0;
+        for (int g0 = 0; g0 < G; g0 += 64) {
+            const int gg = g0 + lane;
+            const bool ne = gg < G && offsets[gg + 1] > offsets[gg];
+            unsigned long long m = __ballot(ne);
+            const int cnt = __popcll(m);
+            if (a < seen + cnt) {
+                for (int i = a - seen; i > 0; --i) m &= m - 1;
+                g = g0 + __builtin_ctzll(m);
+                break;
+            }
+            seen += cnt;
+        }
+        if (g < 0) return;
+        r0 = offsets[g];
+        r1 = offsets[g + 1];
+    } else if (a > 0) {
+        return;
+    }
+    const int R = (int)min<int64_t>(r1 - r0, RMAX);   // the host guarantees r1 - r0 <= RMAX (rows bound)
+    const int c0 = (chunk * 4 + wave) * COLS_W;
+    if (R <= 0 || c0 >= N) return;
+    const int64_t wstride = (int64_t)N * K;
+    const uint16_t* wrow[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int col = c0 + (SWIGLU ? q % 2 : q);
+        const uint16_t* base = (SWIGLU && q >= 2 ? B1 : B0) + (int64_t)g * wstride;
+        wrow[q] = base + (int64_t)(col < N ? col : 0) * K;   // columns past N read column 0, never stored
+    }
+    const uint16_t* xrow[RMAX];
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) {
+        const int64_t row = r0 + (r < R ? r : 0);
+        xrow[r] = A + (gather ? (int64_t)gather[row] : row) * K;
+    }
+    float acc[RMAX][4];
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[r][q] = 0.f;
+#pragma unroll UNROLL
+    for (int k = lane * 8; k < K; k += 512) {
+        uint4 w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[q] = gload16(wrow[q] + k);
+#pragma unroll
+        for (int r = 0; r < RMAX; ++r) {
+            if (r < R) {
+                const uint4 xv = gload16(xrow[r] + k);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[r][q] = dot8_bf16(xv, w[q], acc[r][q]);
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) {
+        if (r < R) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[r][q] = wave_sum(acc[r][q]);
+        }
+    }
+    if (lane != 0) return;
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) {
+        if (r >= R) break;
+        const int64_t row = r0 + r;
+        if (SWIGLU) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                if (c0 + c < N)
+                    static_cast<uint16_t*>(Cout)[row * N + c0 + c] =
+                        (uint16_t)f32_to_bf16_bits(silu_f32(acc[r][c]) * acc[r][c + 2]);
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (c0 + q < N) static_cast<float*>(Cout)[row * N + c0 + q] = acc[r][q];
+        }
+    }
+}
+
 template <bool SWIGLU>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ A, const float* __restrict__ B0,
                                                        const float* __restrict__ B1, float* __restrict__ Cout,
@@ -1176,13 +1298,15 @@ int one_round(int64_t max_rows, int G, int N, int BN, int S) {
     return est_tiles(max_rows, G, N, BN) * S <= MOE_GEMM_CUS ? 1 : 0;
 }
 
-int gemm1_splits(int dtype, int64_t max_rows, int G, int N, int K) {
-    if (dtype != MOE_BF16 || !asm_path_ok(N, K)) return 1;
+bool gemv_path(int dtype, int64_t group_rows) { return dtype == MOE_BF16 && group_rows <= MOE_GEMV_ROWS; }
+
+int gemm1_splits(int dtype, int64_t max_rows, int G, int N, int K, int64_t group_rows) {
+    if (dtype != MOE_BF16 || !asm_path_ok(N, K) || gemv_path(dtype, group_rows)) return 1;
     return small_splits(max_rows, G, N, BF16_BN1, K);
 }
 
-size_t gemm1_part_bytes(int dtype, int64_t max_rows, int G, int N, int K) {
-    const int S = gemm1_splits(dtype, max_rows, G, N, K);
+size_t gemm1_part_bytes(int dtype, int64_t max_rows, int G, int N, int K, int64_t group_rows) {
+    const int S = gemm1_splits(dtype, max_rows, G, N, K, group_rows);
     return S > 1 ? (size_t)2 * S * max_rows * N * sizeof(float) : 0;
 }
 
@@ -1190,9 +1314,40 @@ bool gemm1_gather_ok(int dtype, int N, int K, int64_t a_rows) {
     return dtype == MOE_BF16 && asm_path_ok(N, K) && a_rows * K * 2 < ((int64_t)1 << 32);
 }
 
+// Grouped GEMV launch: one workgroup per (group with rows, chunk of 4 waves'
+// output columns); at most min(G, max_rows) groups have rows.
+template <bool SWIGLU>
+hipError_t launch_gemv(const void* A, const int32_t* offsets, int G, int64_t max_rows, int64_t group_rows,
+                       const void* B0, const void* B1, void* C, int N, int K, const int32_t* gather,
+                       hipStream_t st) {
+    const int cols_wg = 4 * (SWIGLU ? 2 : 4);
+    const int nchunk = (N + cols_wg - 1) / cols_wg;
+    const int64_t groups = offsets ? std::min<int64_t>(G, max_rows) : 1;
+    if (max_rows <= 0 || group_rows <= 0 || nchunk == 0) return hipSuccess;
+    const dim3 grid((unsigned)(groups * nchunk));
+    const uint16_t *a = static_cast<const uint16_t*>(A), *b0 = static_cast<const uint16_t*>(B0),
+                   *b1 = static_cast<const uint16_t*>(B1);
+    // the row bound picks the instance (registers for that many activation rows)
+    if (group_rows <= 1)
+        hipLaunchKernelGGL((gemv_bf16_kernel<SWIGLU, 1>), grid, dim3(256), 0, st, a, b0, b1, C, offsets, G,
+                           max_rows, N, K, nchunk, gather);
+    else if (group_rows <= 2)
+        hipLaunchKernelGGL((gemv_bf16_kernel<SWIGLU, 2>), grid, dim3(256), 0, st, a, b0, b1, C, offsets, G,
+                           max_rows, N, K, nchunk, gather);
+    else if (group_rows <= 4)
+        hipLaunchKernelGGL((gemv_bf16_kernel<SWIGLU, 4>), grid, dim3(256), 0, st, a, b0, b1, C, offsets, G,
+                           max_rows, N, K, nchunk, gather);
+    else
+        hipLaunchKernelGGL((gemv_bf16_kernel<SWIGLU, (int)MOE_GEMV_ROWS>), grid, dim3(256), 0, st, a, b0, b1, C,
+                           offsets, G, max_rows, N, K, nchunk, gather);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm1(int dtype, const void* A, const int32_t* offsets, int G, int64_t max_rows, const void* w_gate,
                         const void* w_up, void* h, int N, int K, void* ws, hipStream_t st, bool prefix_ready,
-                        float* part, const int32_t* gather) {
+                        float* part, const int32_t* gather, int64_t group_rows) {
+    if (gemv_path(dtype, group_rows))
+        return launch_gemv<true>(A, offsets, G, max_rows, group_rows, w_gate, w_up, h, N, K, gather, st);
     const int BM = dtype == MOE_BF16 ? BF16_BM : F32_BM;
     const int BN = dtype == MOE_BF16 ? BF16_BN1 : F32_BN;
     hipError_t e = prefix_ready ? hipSuccess : prep_tiles(offsets, G, BM, ws, st);
@@ -1200,7 +1355,7 @@ hipError_t launch_gemm1(int dtype, const void* A, const int32_t* offsets, int G,
     unsigned grid = grid_size(offsets, G, max_rows, BM, N, BN);
     if (grid == 0) return hipSuccess;
     const int32_t* tp = static_cast<const int32_t*>(ws);
-    const int S = part ? gemm1_splits(dtype, max_rows, G, N, K) : 1;
+    const int S = part ? gemm1_splits(dtype, max_rows, G, N, K, group_rows) : 1;
     if (dtype == MOE_BF16 && asm_path_ok(N, K) && S > 1) {
         // fp32 gate / up partials per K split, then SiLU(g) * u from their sums
         grid = (grid + XCDS - 1) / XCDS * XCDS * S;
@@ -1229,8 +1384,8 @@ hipError_t launch_gemm1(int dtype, const void* A, const int32_t* offsets, int G,
     return hipGetLastError();
 }
 
-int gemm2_splits(int dtype, int64_t max_rows, int G, int N, int K) {
-    if (dtype != MOE_BF16 || !asm_path_ok(N, K)) return 1;
+int gemm2_splits(int dtype, int64_t max_rows, int G, int N, int K, int64_t group_rows) {
+    if (dtype != MOE_BF16 || !asm_path_ok(N, K) || gemv_path(dtype, group_rows)) return 1;
     const int s_small = small_splits(max_rows, G, N, BF16_BN2, K);
     if (s_small > 1) return s_small;
     if (K % 128 != 0 || K < 2048) return 1;
@@ -1246,7 +1401,9 @@ int gemm2_splits(int dtype, int64_t max_rows, int G, int N, int K) {
 
 hipError_t launch_gemm2(int dtype, const void* h, const int32_t* offsets, int G, int64_t max_rows,
                         const void* w_down, float* H, float* H1, int N, int K, void* ws, hipStream_t st,
-                        bool prefix_ready) {
+                        bool prefix_ready, int64_t group_rows) {
+    if (gemv_path(dtype, group_rows))
+        return launch_gemv<false>(h, offsets, G, max_rows, group_rows, w_down, nullptr, H, N, K, nullptr, st);
     const int BM = dtype == MOE_BF16 ? BF16_BM : F32_BM;
     const int BN = dtype == MOE_BF16 ? BF16_BN2 : F32_BN;
     hipError_t e = prefix_ready ? hipSuccess : prep_tiles(offsets, G, BM, ws, st);
@@ -1254,7 +1411,7 @@ hipError_t launch_gemm2(int dtype, const void* h, const int32_t* offsets, int G,
     unsigned grid = grid_size(offsets, G, max_rows, BM, N, BN);
     if (grid == 0) return hipSuccess;
     const int32_t* tp = static_cast<const int32_t*>(ws);
-    const int S = H1 ? gemm2_splits(dtype, max_rows, G, N, K) : 1;
+    const int S = H1 ? gemm2_splits(dtype, max_rows, G, N, K, group_rows) : 1;
     if (dtype == MOE_BF16 && asm_path_ok(N, K)) {
         if (S > 1) grid = (grid + XCDS - 1) / XCDS * XCDS * S;
         hipLaunchKernelGGL((gemm_bf16_asm_kernel<BF16_BN2, false>), dim3(grid), dim3(512), 0, st,

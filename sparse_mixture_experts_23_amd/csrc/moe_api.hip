@@ -47,14 +47,19 @@ int64_t max_rows(const moe_dims& d) {
 
 size_t elem(const moe_dims& d) { return d.dtype == MOE_BF16 ? 2 : 4; }
 
+// At most one row per token and expert, and at most C per expert.
+int64_t group_rows(const moe_dims& d) { return d.T < d.C ? d.T : d.C; }
+
 // Bytes of the K-split partials of H beyond the first (S - 1 blocks of R d fp32)
 // when GEMM2 splits K for this shape; of GEMM1's gate / up partials.
 size_t partial_bytes(const moe_dims& d) {
     const int64_t R = max_rows(d);
-    const int S = gemm2_splits(d.dtype, R, d.E, d.d, d.m);
+    const int S = gemm2_splits(d.dtype, R, d.E, d.d, d.m, group_rows(d));
     return S > 1 ? align_up(sizeof(float) * (S - 1) * R * d.d) : 0;
 }
-size_t g1_part_bytes(const moe_dims& d) { return align_up(gemm1_part_bytes(d.dtype, max_rows(d), d.E, d.m, d.d)); }
+size_t g1_part_bytes(const moe_dims& d) {
+    return align_up(gemm1_part_bytes(d.dtype, max_rows(d), d.E, d.m, d.d, group_rows(d)));
+}
 // [tile prefix | h | GEMM1 partials | H partials]
 size_t ffn_ws(const moe_dims& d) {
     return align_up(gemm_ws_bytes(d.E)) + align_up((size_t)max_rows(d) * d.m * elem(d)) + g1_part_bytes(d) +
@@ -69,9 +74,11 @@ size_t route_stats_ws(const moe_dims& d) {
     return align_up(route_ws_bytes(d)) + align_up((size_t)d.T * d.E * sizeof(float));
 }
 // shared expert: [tile prefix | h | GEMM1 partials | s partials] (one group of T rows)
-size_t shared_g1_bytes(const moe_dims& d) { return align_up(gemm1_part_bytes(d.dtype, d.T, 1, d.m_shared, d.d)); }
+size_t shared_g1_bytes(const moe_dims& d) {
+    return align_up(gemm1_part_bytes(d.dtype, d.T, 1, d.m_shared, d.d, d.T));
+}
 size_t shared_g2_bytes(const moe_dims& d) {
-    const int S = gemm2_splits(d.dtype, d.T, 1, d.d, d.m_shared);
+    const int S = gemm2_splits(d.dtype, d.T, 1, d.d, d.m_shared, d.T);
     return S > 1 ? align_up(sizeof(float) * (S - 1) * d.T * d.d) : 0;
 }
 size_t shared_ws(const moe_dims& d) {
@@ -182,8 +189,9 @@ moe_status gemm2_impl(const moe_dims& d, const void* h, const int32_t* offsets, 
                       void* tp, float* part, Partials* out, hipStream_t st, bool prefix_ready = false) {
     const int64_t R = max_rows(d);
     float* H1 = partial_bytes(d) ? part : nullptr;
-    MOE_CHECK_HIP(launch_gemm2(d.dtype, h, offsets, d.E, R, w_down, H, H1, d.d, d.m, tp, st, prefix_ready));
-    const int np = H1 ? gemm2_splits(d.dtype, R, d.E, d.d, d.m) - 1 : 0;
+    MOE_CHECK_HIP(launch_gemm2(d.dtype, h, offsets, d.E, R, w_down, H, H1, d.d, d.m, tp, st, prefix_ready,
+                               group_rows(d)));
+    const int np = H1 ? gemm2_splits(d.dtype, R, d.E, d.d, d.m, group_rows(d)) - 1 : 0;
     if (out) {
         out->H1 = H1;
         out->np = np;
@@ -205,7 +213,7 @@ moe_status ffn_impl(const moe_dims& d, const void* x_perm, const int32_t* offset
     float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(g1part) + g1_part_bytes(d));
     const int64_t R = max_rows(d);
     MOE_CHECK_HIP(launch_gemm1(d.dtype, x_perm, offsets, d.E, R, w_gate, w_up, h, d.m, d.d, tp, st, prefix_ready,
-                               g1_part_bytes(d) ? g1part : nullptr, gather));
+                               g1_part_bytes(d) ? g1part : nullptr, gather, group_rows(d)));
     // GEMM2 uses the same row tiles: the prefix GEMM1 found (or was given) stays valid
     return gemm2_impl(d, h, offsets, w_down, H, tp, part, out, st, true);
 }
@@ -217,11 +225,11 @@ moe_status shared_impl(const moe_dims& d, const void* x, const void* s_gate, con
     float* g1part = reinterpret_cast<float*>(h + align_up((size_t)d.T * d.m_shared * elem(d)));
     float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(g1part) + shared_g1_bytes(d));
     MOE_CHECK_HIP(launch_gemm1(d.dtype, x, nullptr, 1, d.T, s_gate, s_up, h, d.m_shared, d.d, tp, st, false,
-                               shared_g1_bytes(d) ? g1part : nullptr));
+                               shared_g1_bytes(d) ? g1part : nullptr, nullptr, d.T));
     float* H1 = shared_g2_bytes(d) ? part : nullptr;
-    MOE_CHECK_HIP(launch_gemm2(d.dtype, h, nullptr, 1, d.T, s_down, s, H1, d.d, d.m_shared, tp, st));
+    MOE_CHECK_HIP(launch_gemm2(d.dtype, h, nullptr, 1, d.T, s_down, s, H1, d.d, d.m_shared, tp, st, false, d.T));
     if (H1) {
-        const int np = gemm2_splits(d.dtype, d.T, 1, d.d, d.m_shared) - 1;
+        const int np = gemm2_splits(d.dtype, d.T, 1, d.d, d.m_shared, d.T) - 1;
         MOE_CHECK_HIP(launch_add_partial(s, H1, np, nullptr, 1, d.T, d.d, st));
     }
     return MOE_OK;
@@ -331,7 +339,8 @@ moe_status moe_expert_gemm1(const moe_shape* shape, const void* x_perm, const in
     if (ws_bytes < gemm1_ws(d)) return MOE_ERR_WORKSPACE_TOO_SMALL;
     float* g1part = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(gemm_ws_bytes(d.E)));
     return hip_status(launch_gemm1(d.dtype, x_perm, offsets, d.E, max_rows(d), w_gate, w_up, h, d.m, d.d, ws,
-                                   static_cast<hipStream_t>(stream), false, g1_part_bytes(d) ? g1part : nullptr));
+                                   static_cast<hipStream_t>(stream), false, g1_part_bytes(d) ? g1part : nullptr,
+                                   nullptr, group_rows(d)));
 }
 
 moe_status moe_expert_gemm2(const moe_shape* shape, const void* h, const int32_t* offsets, const void* w_down,
