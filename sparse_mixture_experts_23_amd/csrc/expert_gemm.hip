@@ -1059,14 +1059,17 @@ __global__ __launch_bounds__(256) void swiglu_reduce_kernel(const float* __restr
 //
 // With at most MOE_GEMV_ROWS rows in every group the expert GEMMs are weight
 // streams (a few flops per weight byte): no LDS staging, no MFMA.  Each wave owns
-// 4 weight rows over the whole K (SwiGLU: the gate and up rows of 2 output
-// columns; otherwise 4 output columns); per step a lane loads 16 bytes (8 bf16)
+// 4 weight rows over the whole K, 8 when the groups have one row (SwiGLU: the
+// gate and up rows of half as many output columns); per step a lane loads 16 bytes (8 bf16)
 // of each weight row and of each of the group's activation rows at K offset
 // 8 lane + 512 step and accumulates exact bf16 products in fp32; the 64 lanes'
 // partial sums are then added by a butterfly.  Small register and no LDS
 // footprint, so many waves per CU keep enough weight loads in flight.
 // Workgroup b: the (b / nchunk)-th group with rows (the active groups, found
 // with a ballot over offsets), output columns from (b % nchunk) * 4 waves.
+// Weight rows per wave for an instance with at most `rmax` activation rows: with
+// one row the accumulators are few, so 8 rows (twice the loads per step) fit.
+__host__ __device__ constexpr int gemv_rows_per_wave(int rmax) { return rmax == 1 ? 8 : 4; }
 __device__ __forceinline__ float dot8_bf16(uint4 a, uint4 b, float acc) {
     const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
@@ -1084,8 +1087,9 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(const uint16_t* __restri
                                                         const int32_t* __restrict__ offsets, int G, int64_t nrows,
                                                         int N, int K, int nchunk,
                                                         const int32_t* __restrict__ gather) {
-    constexpr int UNROLL = RMAX == 1 ? 4 : (RMAX <= 4 ? 2 : 1);   // K steps in flight per wave
-    constexpr int COLS_W = SWIGLU ? 2 : 4;   // output columns per wave
+    constexpr int UNROLL = RMAX <= 4 ? 2 : 1;   // K steps in flight per wave
+    constexpr int RW = gemv_rows_per_wave(RMAX);
+    constexpr int COLS_W = SWIGLU ? RW / 2 : RW;   // output columns per wave
     const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
     const int a = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
     int g = 0;
@@ -1116,11 +1120,11 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(const uint16_t* __restri
     const int c0 = (chunk * 4 + wave) * COLS_W;
     if (R <= 0 || c0 >= N) return;
     const int64_t wstride = (int64_t)N * K;
-    const uint16_t* wrow[4];
+    const uint16_t* wrow[RW];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int col = c0 + (SWIGLU ? q % 2 : q);
-        const uint16_t* base = (SWIGLU && q >= 2 ? B1 : B0) + (int64_t)g * wstride;
+    for (int q = 0; q < RW; ++q) {
+        const int col = c0 + (SWIGLU ? q % COLS_W : q);
+        const uint16_t* base = (SWIGLU && q >= COLS_W ? B1 : B0) + (int64_t)g * wstride;
         wrow[q] = base + (int64_t)(col < N ? col : 0) * K;   // columns past N read column 0, never stored
     }
     const uint16_t* xrow[RMAX];
@@ -1129,22 +1133,22 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(const uint16_t* __restri
         const int64_t row = r0 + (r < R ? r : 0);
         xrow[r] = A + (gather ? (int64_t)gather[row] : row) * K;
     }
-    float acc[RMAX][4];
+    float acc[RMAX][RW];
 #pragma unroll
     for (int r = 0; r < RMAX; ++r)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[r][q] = 0.f;
+        for (int q = 0; q < RW; ++q) acc[r][q] = 0.f;
 #pragma unroll UNROLL
     for (int k = lane * 8; k < K; k += 512) {
-        uint4 w[4];
+        uint4 w[RW];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) w[q] = gload16(wrow[q] + k);
+        for (int q = 0; q < RW; ++q) w[q] = gload16(wrow[q] + k);
 #pragma unroll
         for (int r = 0; r < RMAX; ++r) {
             if (r < R) {
                 const uint4 xv = gload16(xrow[r] + k);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) acc[r][q] = dot8_bf16(xv, w[q], acc[r][q]);
+                for (int q = 0; q < RW; ++q) acc[r][q] = dot8_bf16(xv, w[q], acc[r][q]);
             }
         }
     }
@@ -1152,7 +1156,7 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(const uint16_t* __restri
     for (int r = 0; r < RMAX; ++r) {
         if (r < R) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[r][q] = wave_sum(acc[r][q]);
+            for (int q = 0; q < RW; ++q) acc[r][q] = wave_sum(acc[r][q]);
         }
     }
     if (lane != 0) return;
@@ -1162,14 +1166,14 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(const uint16_t* __restri
         const int64_t row = r0 + r;
         if (SWIGLU) {
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
+            for (int c = 0; c < COLS_W; ++c) {
                 if (c0 + c < N)
                     static_cast<uint16_t*>(Cout)[row * N + c0 + c] =
-                        (uint16_t)f32_to_bf16_bits(silu_f32(acc[r][c]) * acc[r][c + 2]);
+                        (uint16_t)f32_to_bf16_bits(silu_f32(acc[r][c]) * acc[r][c + COLS_W]);
             }
         } else {
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
+            for (int q = 0; q < RW; ++q)
                 if (c0 + q < N) static_cast<float*>(Cout)[row * N + c0 + q] = acc[r][q];
         }
     }
@@ -1316,31 +1320,29 @@ bool gemm1_gather_ok(int dtype, int N, int K, int64_t a_rows) {
 
 // Grouped GEMV launch: one workgroup per (group with rows, chunk of 4 waves'
 // output columns); at most min(G, max_rows) groups have rows.
+template <bool SWIGLU, int RMAX>
+hipError_t launch_gemv_rows(const void* A, const int32_t* offsets, int G, int64_t max_rows, const void* B0,
+                            const void* B1, void* C, int N, int K, const int32_t* gather, hipStream_t st) {
+    constexpr int RW = gemv_rows_per_wave(RMAX);
+    const int cols_wg = 4 * (SWIGLU ? RW / 2 : RW);   // 4 waves per workgroup
+    const int nchunk = (N + cols_wg - 1) / cols_wg;
+    const int64_t groups = offsets ? std::min<int64_t>(G, max_rows) : 1;
+    hipLaunchKernelGGL((gemv_bf16_kernel<SWIGLU, RMAX>), dim3((unsigned)(groups * nchunk)), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B0),
+                       static_cast<const uint16_t*>(B1), C, offsets, G, max_rows, N, K, nchunk, gather);
+    return hipGetLastError();
+}
+
+// the row bound picks the instance (registers for that many activation rows)
 template <bool SWIGLU>
 hipError_t launch_gemv(const void* A, const int32_t* offsets, int G, int64_t max_rows, int64_t group_rows,
                        const void* B0, const void* B1, void* C, int N, int K, const int32_t* gather,
                        hipStream_t st) {
-    const int cols_wg = 4 * (SWIGLU ? 2 : 4);
-    const int nchunk = (N + cols_wg - 1) / cols_wg;
-    const int64_t groups = offsets ? std::min<int64_t>(G, max_rows) : 1;
-    if (max_rows <= 0 || group_rows <= 0 || nchunk == 0) return hipSuccess;
-    const dim3 grid((unsigned)(groups * nchunk));
-    const uint16_t *a = static_cast<const uint16_t*>(A), *b0 = static_cast<const uint16_t*>(B0),
-                   *b1 = static_cast<const uint16_t*>(B1);
-    // the row bound picks the instance (registers for that many activation rows)
-    if (group_rows <= 1)
-        hipLaunchKernelGGL((gemv_bf16_kernel<SWIGLU, 1>), grid, dim3(256), 0, st, a, b0, b1, C, offsets, G,
-                           max_rows, N, K, nchunk, gather);
-    else if (group_rows <= 2)
-        hipLaunchKernelGGL((gemv_bf16_kernel<SWIGLU, 2>), grid, dim3(256), 0, st, a, b0, b1, C, offsets, G,
-                           max_rows, N, K, nchunk, gather);
-    else if (group_rows <= 4)
-        hipLaunchKernelGGL((gemv_bf16_kernel<SWIGLU, 4>), grid, dim3(256), 0, st, a, b0, b1, C, offsets, G,
-                           max_rows, N, K, nchunk, gather);
-    else
-        hipLaunchKernelGGL((gemv_bf16_kernel<SWIGLU, (int)MOE_GEMV_ROWS>), grid, dim3(256), 0, st, a, b0, b1, C,
-                           offsets, G, max_rows, N, K, nchunk, gather);
-    return hipGetLastError();
+    if (max_rows <= 0 || group_rows <= 0 || N <= 0) return hipSuccess;
+    if (group_rows <= 1) return launch_gemv_rows<SWIGLU, 1>(A, offsets, G, max_rows, B0, B1, C, N, K, gather, st);
+    if (group_rows <= 2) return launch_gemv_rows<SWIGLU, 2>(A, offsets, G, max_rows, B0, B1, C, N, K, gather, st);
+    if (group_rows <= 4) return launch_gemv_rows<SWIGLU, 4>(A, offsets, G, max_rows, B0, B1, C, N, K, gather, st);
+    return launch_gemv_rows<SWIGLU, (int)MOE_GEMV_ROWS>(A, offsets, G, max_rows, B0, B1, C, N, K, gather, st);
 }
 
 hipError_t launch_gemm1(int dtype, const void* A, const int32_t* offsets, int G, int64_t max_rows, const void* w_gate,
