@@ -266,6 +266,12 @@ RAGGED = MoEConfig("ragged_bf16", T=2000, d=328, m=200, E=4, k=2, dtype="bf16", 
     # router with E < 8 experts over two K chunks of 4096 (d > 4096), T not a multiple of 16
     MoEConfig("router_two_k_ranges", T=101, d=4160, m=64, E=6, k=2, dtype="bf16", gate_mode=1, cf=None,
               cfg_id=24),
+    # grouped GEMVs: at most 4 rows per expert from T (the 4-row instance), and from a
+    # capacity of 3 with T = 40 (drops; the row bound is min(T, C)); N and K tails
+    MoEConfig("gemv_rows4", T=4, d=1032, m=200, E=8, k=2, dtype="bf16", gate_mode=0, cf=None, m_shared=72,
+              cfg_id=52),
+    MoEConfig("gemv_capacity_bound", T=40, d=520, m=136, E=16, k=2, dtype="bf16", gate_mode=1, cf=(1, 2),
+              bias="zipf", cfg_id=53),
 ], ids=lambda c: c.name)
 def test_parity_small(cfg):
     run_layer(cfg)
