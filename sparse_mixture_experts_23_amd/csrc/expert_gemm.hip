@@ -1070,12 +1070,22 @@ __global__ __launch_bounds__(256) void swiglu_reduce_kernel(const float* __restr
 // Weight rows per wave for an instance with at most `rmax` activation rows: with
 // one row the accumulators are few, so 8 rows (twice the loads per step) fit.
 __host__ __device__ constexpr int gemv_rows_per_wave(int rmax) { return rmax == 1 ? 8 : 4; }
+// 8 bf16 products added to acc in fp32.  DOT2: four v_dot2c_f32_bf16 on the
+// packed operands (a pair of exact products per instruction: a third of the
+// VALU work, which matters from 4 activation rows on); otherwise eight FMAs on
+// the upcast values (measured faster with one or two rows).
+template <bool DOT2>
 __device__ __forceinline__ float dot8_bf16(uint4 a, uint4 b, float acc) {
     const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        acc = fmaf(__uint_as_float(av[i] << 16), __uint_as_float(bv[i] << 16), acc);
-        acc = fmaf(__uint_as_float(av[i] & 0xffff0000u), __uint_as_float(bv[i] & 0xffff0000u), acc);
+        if (DOT2) {
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, av[i]),
+                                                  __builtin_bit_cast(bf16x2_t, bv[i]), acc, false);
+        } else {
+            acc = fmaf(__uint_as_float(av[i] << 16), __uint_as_float(bv[i] << 16), acc);
+            acc = fmaf(__uint_as_float(av[i] & 0xffff0000u), __uint_as_float(bv[i] & 0xffff0000u), acc);
+        }
     }
     return acc;
 }
@@ -1148,7 +1158,7 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(const uint16_t* __restri
             if (r < R) {
                 const uint4 xv = gload16(xrow[r] + k);
 #pragma unroll
-                for (int q = 0; q < RW; ++q) acc[r][q] = dot8_bf16(xv, w[q], acc[r][q]);
+                for (int q = 0; q < RW; ++q) acc[r][q] = dot8_bf16<(RMAX >= 4)>(xv, w[q], acc[r][q]);
             }
         }
     }
