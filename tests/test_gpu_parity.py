@@ -542,6 +542,10 @@ def test_gpu_balance_matches_oracle(cfg):
     # shared expert: moe_forward forks it onto a second stream and joins it before the combine
     MoEConfig("graph_shared", T=300, d=256, m=128, E=16, k=4, dtype="bf16", gate_mode=0, cf=(5, 4), m_shared=192,
               cfg_id=49),
+    # several rounds of GEMM workgroups: the run-time tile claims use counters that
+    # the dispatch kernel clears inside the graph on every replay
+    MoEConfig("graph_multi_round", T=2048, d=2048, m=1024, E=64, k=8, dtype="bf16", gate_mode=0, cf=(5, 4),
+              bias="zipf", cfg_id=54),
 ], ids=lambda c: c.name)
 def test_forward_captures_into_a_graph(cfg):
     """moe_forward queues no host synchronisation and no memset, so it can be
