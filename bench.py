@@ -38,7 +38,7 @@ METRIC = "MoE-layer tokens/sec on 1 MI355X (Mixtral shape); expert-GEMM % of MFM
 # the bytes-per-KiB that the same counter reports for a plain device copy of known
 # size (`bench.py --copy-calibration`).  Valid only for the GEMM source it was
 # taken on: reported as null once expert_gemm.hip differs from that hash.
-GEMM1_TRAFFIC = {"bytes": 6422427363, "source_sha256": "cb482b79c5de673d0ca1fbcf0093d89a3e28c63fb53ebddbd70e74b49ad65d7e"}
+GEMM1_TRAFFIC = {"bytes": 6458101661, "source_sha256": "c76b687c0157b1b53b5b8dc3f7e2496aad83aa0e0d555786d4a10e4c57ec372d"}
 GEMM_SOURCE = os.path.join(ROOT, "sparse_mixture_experts_23_amd", "csrc", "expert_gemm.hip")
 
 
