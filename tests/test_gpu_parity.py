@@ -308,6 +308,31 @@ def test_parity_random_shapes(cfg):
     run_layer(cfg)
 
 
+def _random_large_configs(n: int = 8, seed: int = 5):
+    """Seeded layer shapes large enough that both grouped GEMMs take several
+    rounds of workgroups (so the run-time tile claims and cross-XCD steals are
+    exercised), with and without skew, capacity and a shared expert."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        T = int(rng.choice([1024, 1536, 2048, 3000, 4096]))
+        E = int(rng.choice([4, 8, 16, 32, 64]))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        d = int(rng.choice([512, 1024, 1536, 2048]))
+        m = int(rng.choice([256, 512, 768, 1024, 1536]))
+        cf = [None, (1, 1), (5, 4), (3, 2)][int(rng.integers(0, 4))]
+        bias = ["none", "zipf"][int(rng.integers(0, 2))]
+        shared = int(rng.choice([0, 0, 256]))
+        out.append(MoEConfig(f"big{i}_T{T}_E{E}_k{k}_d{d}_m{m}", T=T, d=d, m=m, E=E, k=k, dtype="bf16",
+                             gate_mode=int(rng.integers(0, 2)), cf=cf, bias=bias, m_shared=shared, cfg_id=500 + i))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_large_configs(), ids=lambda c: c.name)
+def test_parity_random_large_shapes(cfg):
+    run_layer(cfg, sample=48)
+
+
 def test_dense_k_equal_E_matches_dense_brute_force():
     """k = E, no capacity: the layer is the dense mixture; compare the GPU with the
     oracle's separately written dense loop."""
