@@ -92,6 +92,23 @@ def test_route_workspace_by_path():
     assert route(T=16, E=8, dtype=0) == align                 # fp32 with E <= 64: scores in registers
 
 
+def test_ffn_workspace_by_path():
+    """The expert-FFN workspace is the tile prefix (with the GEMMs' claim counters)
+    plus h; K-split partials are added only where the tiled GEMMs split K.  With at
+    most 8 rows per expert (min(T, C) <= 8, bf16) the grouped GEMVs never split."""
+    ffn = lambda **kw: L.moe_workspace_bytes(_shape(**kw), L.MOE_WS_FFN)
+    al = lambda v: (v + 255) // 256 * 256
+    m, E = 14336, 8
+    prefix = al(((E + 2) & ~1) * 4 + 16 * 8)
+    for T in (1, 4, 8):
+        R = min(T * 2, E * T)
+        assert ffn(T=T) == prefix + al(R * m * 2), T            # bf16 GEMVs: no partials
+    assert ffn(T=40, capacity=3) == prefix + al(min(40 * 2, E * 3) * m * 2)   # row bound min(T, C) = 3
+    R = 9 * 2
+    assert ffn(T=9) > prefix + al(R * m * 2)                      # tiled GEMMs split K for 9 rows
+    assert ffn(T=1, dtype=0) == prefix + al(2 * m * 4)            # fp32 layers never split
+
+
 def test_argument_errors_return_before_any_launch():
     s = _shape(T=16, d=64, m=64)
     fake = 4096  # never dereferenced: every call below fails its host-side checks
