@@ -129,9 +129,15 @@ class Stages:
         L.check(rc, phase)
 
 
-def cpu_baseline(cfg, inp, budget_tokens):
+def cpu_baseline(cfg, inp, budget_tokens, layer=None):
     """Time the oracle, as it stands, on a bounded sample of the same workload:
-    the first `budget_tokens` tokens form the routing group (same d, m, E, k)."""
+    the first `budget_tokens` tokens form the routing group (same d, m, E, k).
+    With `layer` (the timed GPU forward's outputs) and a sample that is the whole
+    routing group, the oracle's result also checks this run: the largest
+    |y_gpu - y_ref| / (1 + |y_ref|) over every element, the tokens whose score
+    margin at the top-k boundary is below 1e-5 (fp64 scores), and the tokens
+    whose selected set differs from the GPU's (their rows are left out of the
+    error, which then compares two different routings)."""
     import numpy as np
     from oracle import moe_oracle as O
     try:
@@ -157,10 +163,22 @@ def cpu_baseline(cfg, inp, budget_tokens):
     else:
         O.assign_slots(rt.ids, cfg.E, cap)
     t2 = time.perf_counter()
-    O.forward(x, wr, b, experts, cfg.k, cfg.gate_mode, C=C, shared=shared, round_h_bf16=cfg.dtype == "bf16",
-              renorm_form=cfg.renorm_form, accept_by_gate=cfg.accept_by_gate,
-              renorm_survivors=cfg.renorm_survivors)
+    res = O.forward(x, wr, b, experts, cfg.k, cfg.gate_mode, C=C, shared=shared, round_h_bf16=cfg.dtype == "bf16",
+                    renorm_form=cfg.renorm_form, accept_by_gate=cfg.accept_by_gate,
+                    renorm_survivors=cfg.renorm_survivors)
     dt = time.perf_counter() - t2
+    parity = None
+    if layer is not None and Ts == cfg.T:
+        boundary, _ = O.route_margins(res.route.g64, cfg.k)
+        ids_gpu = layer.topk_ids.cpu().numpy()
+        same = (np.sort(ids_gpu, axis=1) == np.sort(res.route.ids, axis=1)).all(axis=1)
+        y_gpu = layer.y.cpu().numpy().astype(np.float64)
+        err = (np.abs(y_gpu - res.y) / (1.0 + np.abs(res.y)))[same]
+        tol = 2e-2 if cfg.dtype == "bf16" else 1e-5
+        parity = {"tokens": int(Ts), "elements": int(err.size), "max_rel_err": float(err.max()) if err.size else 0.0,
+                  "tol": tol, "within_tol": bool(err.size == 0 or err.max() <= tol),
+                  "near_ties": int((boundary < 1e-5).sum()), "set_flips": int((~same).sum()),
+                  "slots_equal": bool((layer.slot.cpu().numpy() == res.dispatch.slot).all()) if same.all() else None}
     t_route, t_disp = t1 - t0, t2 - t1
     threads = 1
     if threadpool_info is not None:
@@ -172,7 +190,7 @@ def cpu_baseline(cfg, inp, budget_tokens):
                       f"k={cfg.k}), fp64 numpy oracle, {dt:.1f} s",
             "phase_s": {"route": round(t_route, 3), "dispatch": round(t_disp, 3),
                         "experts_and_combine": round(max(dt - t_route - t_disp, 0.0), 3)},
-            "cpu": _cpu_model()}
+            "cpu": _cpu_model(), "parity_vs_gpu": parity}
 
 
 def _cpu_model():
@@ -181,9 +199,14 @@ def _cpu_model():
         txt = open("/proc/cpuinfo").read()
     except OSError:
         return None
-    models = {ln.split(":", 1)[1].strip() for ln in txt.splitlines() if ln.startswith("model name")}
+    def field(name):
+        vals = {ln.split(":", 1)[1].strip() for ln in txt.splitlines() if ln.split(":", 1)[0].strip() == name}
+        return sorted(vals)[0] if vals else None
+
     sockets = {ln.split(":", 1)[1].strip() for ln in txt.splitlines() if ln.startswith("physical id")}
-    return {"model": sorted(models)[0] if models else None, "sockets": len(sockets) or None,
+    return {"model": field("model name"), "family": field("cpu family"), "model_id": field("model"),
+            "stepping": field("stepping"), "sockets": len(sockets) or None,
+            "logical_cpus": txt.count("\nprocessor") + txt.startswith("processor"),
             "threads_visible": len(os.sched_getaffinity(0))}
 
 
@@ -334,6 +357,10 @@ def main():
             "gemm2_tflops": round(gemm2_flop / t2 / 1e12, 2),
             "hbm_gbs": {"route": hbm(route_bytes, phases["route"]), "dispatch": hbm(disp_bytes, phases["dispatch"]),
                         "combine": hbm(comb_bytes, phases["combine"])},
+            "hbm_frac": {"route": round(route_bytes / (phases["route"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                         "dispatch": round(disp_bytes / (phases["dispatch"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                         "combine": round(comb_bytes / (phases["combine"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+            "hbm_algorithmic_bytes": {"route": route_bytes, "dispatch": disp_bytes, "combine": comb_bytes},
             "hbm_peak_gbs": PEAK_HBM_GBS,
         }
     out = {
@@ -364,7 +391,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log(f"[bench] timing the CPU oracle on a {args.cpu_sample_tokens}-token sample")
-        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens)
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens, layer)
     print(json.dumps(out), flush=True)
 
 

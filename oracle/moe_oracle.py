@@ -81,11 +81,6 @@ def router_params(d: int, E: int) -> int:
     return d * E
 
 
-def expert_flops(d: int, m: int, accepted_paths: int) -> int:
-    """Expert forward cost ~ 2 * (accepted paths) * P_e ([CH36] §36.5)."""
-    return 2 * accepted_paths * expert_params(d, m)
-
-
 # --------------------------------------------------------------------------
 # rounding helpers (definitions written out)
 # --------------------------------------------------------------------------

@@ -121,18 +121,3 @@ def check_output(y_gpu: np.ndarray, y_ref: np.ndarray, tol: float, what: str) ->
     worst = float(err.max()) if err.size else 0.0
     assert worst <= tol, f"{what}: max |y_gpu - y_ref| / (1 + |y_ref|) = {worst:.3e} > {tol}"
     return worst
-
-
-def pick_tokens(T: int, n: int, disp: O.Dispatch, seed: int = 0) -> np.ndarray:
-    """Sampled output rows: both ends, tokens with rejected paths, and random ones."""
-    rng = np.random.default_rng(seed)
-    pick = {0, T - 1}
-    rej = np.where((disp.slot < 0).any(axis=1))[0]
-    full = np.where((disp.slot < 0).all(axis=1))[0]
-    if len(full):
-        pick.add(int(full[0]))
-    if len(rej):
-        pick.update(int(t) for t in rng.choice(rej, size=min(2, len(rej)), replace=False))
-    while len(pick) < min(n, T):
-        pick.add(int(rng.integers(0, T)))
-    return np.array(sorted(pick))

@@ -228,6 +228,40 @@ def test_negative_zero_ties_with_positive_zero():
     assert rt.ids[0, 0] == 0           # equal scores: the lower id wins
 
 
+def test_route_margins_hand_computed():
+    """The score gaps that decide the selection, worked by hand on a small table.
+    Row 0 scores (3.0 at id 1, 2.0 at id 3, 0.5 at id 0, -1.0 at id 2) are listed
+    out of rank order, so a margin taken over ids instead of ranks, a sort in the
+    wrong direction or a flipped sign fails.  Row 1 holds an exact tie at the
+    boundary (margin 0), row 2 a tie inside the set."""
+    g = np.array([[0.5, 3.0, -1.0, 2.0],
+                  [1.0, 1.0, -2.0, 1.0],
+                  [-4.0, -0.25, -0.25, -3.0]])
+    # k < E: boundary = k-th minus (k+1)-th largest; adjacent gaps between ranks 0..k-1
+    b, a = O.route_margins(g, 2)
+    np.testing.assert_array_equal(b, [2.0 - 0.5, 1.0 - 1.0, -0.25 - (-3.0)])
+    np.testing.assert_array_equal(a, [[3.0 - 2.0], [0.0], [0.0]])
+    b, a = O.route_margins(g, 3)
+    np.testing.assert_array_equal(b, [0.5 - (-1.0), 1.0 - (-2.0), -3.0 - (-4.0)])
+    np.testing.assert_array_equal(a, [[1.0, 1.5], [0.0, 0.0], [0.0, 2.75]])
+    # k = 1: no adjacent in-set gap
+    b, a = O.route_margins(g, 1)
+    np.testing.assert_array_equal(b, [1.0, 0.0, 0.0])
+    assert a.shape == (3, 0)
+    # k = E: every expert is selected, the set cannot change (boundary = inf)
+    b, a = O.route_margins(g, 4)
+    assert np.isinf(b).all() and (b > 0).all()
+    np.testing.assert_array_equal(a, [[1.0, 1.5, 1.5], [0.0, 0.0, 3.0], [0.0, 2.75, 1.0]])
+    # the margins are never negative and do not depend on the order of the ids
+    perm = [2, 0, 3, 1]
+    for k in (1, 2, 3, 4):
+        b0, a0 = O.route_margins(g, k)
+        b1, a1 = O.route_margins(g[:, perm], k)
+        np.testing.assert_array_equal(b0, b1)
+        np.testing.assert_array_equal(a0, a1)
+        assert (b0 >= 0).all() and (a0 >= 0).all()
+
+
 def test_selection_by_probability_equals_selection_by_score():
     rng = np.random.default_rng(3)
     x = rng.standard_normal((64, 16))
