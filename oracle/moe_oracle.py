@@ -292,14 +292,102 @@ def assign_slots_by_gate(ids: np.ndarray, w: np.ndarray, E: int, C: int) -> Disp
     return _dispatch_from_slots(ids, slot, load, E, C)
 
 
+@dataclass
+class Reroute:
+    dispatch: Dispatch          # over the 2k columns: k candidates, then k spares
+    rerouted: int               # spare paths accepted
+    tokens_affected: int        # tokens with at least one candidate rejected in the first pass
+    tokens_dropped: int         # tokens left with no accepted path
+
+
+def assign_slots_reroute(ids2: np.ndarray, k: int, E: int, C: int) -> Reroute:
+    """Acceptance with rerouting to the next-choice expert.
+
+    [REVIEW] item 5 (capacity overflow as part of the quality record) names
+    rerouting to the next-choice expert as one treatment of a full expert;
+    [CH36] §36.3 (routing capacity and overflow) says a reroute calls another
+    set of parameters; [ROUTING] §6 lists it among the overflow treatments.
+    None of them fixes the rule, so this is a reading (stated where it is used):
+      * ids2 [T, 2k]: columns 0..k-1 are the token's selection S_t in rank
+        order, columns k..2k-1 its next experts in rank order (the spares;
+        -1 where the experts run out);
+      * first pass: Algorithm 36.1 ([CH36] §36.4) on the candidates, in token
+        order; c_e counts every request and ends as the requested load L_e;
+      * second pass, after every first-pass request: the j-th rejected
+        candidate of token t (rank order) asks for spare j of token t, in token
+        order; it is accepted iff its expert has accepted fewer than C paths,
+        and then takes the next slot; otherwise it is dropped (no third try).
+    The slots of column k + j are those of the spare requests.
+    """
+    ids2 = np.asarray(ids2, dtype=np.int64)
+    T = ids2.shape[0]
+    if C < 1:
+        raise OracleError("capacity must be >= 1")
+    counter = [0] * E
+    slot = np.full((T, 2 * k), -1, dtype=np.int64)
+    for t in range(T):                        # first pass: Algorithm 36.1
+        for r in range(k):
+            e = int(ids2[t, r])
+            if counter[e] < C:
+                slot[t, r] = counter[e]
+            counter[e] += 1
+    taken = [min(c, C) for c in counter]      # accepted paths per expert so far
+    rerouted = affected = dropped = 0
+    for t in range(T):                        # second pass: the rejected candidates, in token order
+        rejected = [r for r in range(k) if slot[t, r] < 0]
+        affected += bool(rejected)
+        for j in range(len(rejected)):
+            e = int(ids2[t, k + j])
+            if e < 0:                          # no next-choice expert left
+                continue
+            if taken[e] < C:
+                slot[t, k + j] = taken[e]
+                taken[e] += 1
+                rerouted += 1
+        dropped += not (slot[t] >= 0).any()
+    disp = _dispatch_from_slots(ids2, slot, np.array(counter, dtype=np.int64), E, C)
+    return Reroute(dispatch=disp, rerouted=rerouted, tokens_affected=affected, tokens_dropped=dropped)
+
+
+def spare_weights(g32: np.ndarray, ids: np.ndarray, spare: np.ndarray, mode: int,
+                  renorm_form: str = RENORM_FORM_SOFTMAX_THEN_RENORM) -> np.ndarray:
+    """Routing weight of a spare (next-choice) expert: the gate value of the
+    expert that would compute the path, with the token's selection normalizer
+    (a reading; no renormalisation, as in Algorithm 36.1):
+      RENORM  p_e' / sum_{j in S_t} p_j  (both forms of gate_weights);
+      SWITCH  p_e', the full-softmax probability.
+    Entries of `spare` equal to -1 (no expert left) get weight 0."""
+    rows = np.arange(g32.shape[0])[:, None]
+    sp = np.maximum(np.asarray(spare, dtype=np.int64), 0)
+    if mode == GATE_SWITCH:
+        w = softmax_rows(g32)[rows, sp]
+    elif mode != GATE_RENORM:
+        raise OracleError("unknown gate mode")
+    elif renorm_form == RENORM_FORM_SOFTMAX_THEN_RENORM:
+        p = softmax_rows(g32)
+        w = p[rows, sp] / p[rows, ids].sum(axis=1, keepdims=True)
+    elif renorm_form == RENORM_FORM_TOPK_THEN_SOFTMAX:
+        gsel = g32[rows, ids]
+        top = gsel.max(axis=1, keepdims=True)
+        w = np.exp(g32[rows, sp] - top) / np.exp(gsel - top).sum(axis=1, keepdims=True)
+    else:
+        raise OracleError("unknown renormalisation form")
+    return np.where(np.asarray(spare) >= 0, w, 0.0)
+
+
 def _dispatch_from_slots(ids: np.ndarray, slot: np.ndarray, load: np.ndarray, E: int, C: int) -> Dispatch:
     """Grouped-row offsets, row map and load statistics from per-path slots
-    ([REVIEW] equations for C_e, O and rho_max; rho_max on the requested load)."""
+    ([REVIEW] equations for C_e, O and rho_max; rho_max on the requested load).
+    The rows of expert e are its accepted paths, counted from the slots."""
     T, k = ids.shape
-    accepted = np.minimum(load, C)
+    accepted = np.zeros(E, dtype=np.int64)
+    for t in range(T):
+        for r in range(k):
+            if slot[t, r] >= 0:
+                accepted[ids[t, r]] += 1
     offsets = np.zeros(E + 1, dtype=np.int64)
     offsets[1:] = np.cumsum(accepted)
-    row_of = np.where(slot >= 0, offsets[ids] + slot, -1)
+    row_of = np.where(slot >= 0, offsets[np.maximum(ids, 0)] + slot, -1)
     src_token = np.empty(int(offsets[-1]), dtype=np.int64)
     for t in range(T):
         for r in range(k):
@@ -452,7 +540,7 @@ def forward(x, w_r, b_r, experts: WeightsArg, k: int, mode: int,
             tokens: Optional[Sequence[int]] = None,
             ids_override: Optional[np.ndarray] = None,
             accept_by_gate: bool = False, renorm_survivors: bool = False,
-            accept_weights: Optional[np.ndarray] = None) -> ForwardResult:
+            accept_weights: Optional[np.ndarray] = None, reroute: bool = False) -> ForwardResult:
     """One sparse MoE layer forward, Algorithm 36.1 ([CH36] §36.4) with the
     conventions above.  The output excludes the residual ([CH36] §36.3: a
     token whose every path is rejected keeps only its residual, which the
@@ -471,7 +559,10 @@ def forward(x, w_r, b_r, experts: WeightsArg, k: int, mode: int,
     `accept_weights` if given (the fp32 weights of the run being checked, so
     that both sides take the decision on the same values) else on the weights
     rounded to fp32; `renorm_survivors` renormalises each token's weights over
-    its accepted paths (survivor_weights).
+    its accepted paths (survivor_weights).  `reroute` sends every rejected path
+    to the token's next-choice expert (assign_slots_reroute); the routing
+    records then have 2k columns, the k selected experts and the k spares
+    (ids_override is then [T, 2k] as well), weighted by spare_weights.
     """
     x = np.asarray(x)
     T = x.shape[0]
@@ -487,23 +578,40 @@ def forward(x, w_r, b_r, experts: WeightsArg, k: int, mode: int,
         disp = assign_slots(empty, E, C if C is not None else 1)
         return ForwardResult(np.zeros((0, d)), np.zeros(0, dtype=np.int64), r, disp)
     rt = route(x, w_r, b_r, k, mode, renorm_form)
-    if ids_override is not None:
-        rt.ids = np.asarray(ids_override, dtype=np.int64)
-        rt.w = gate_weights(rt.g32, rt.ids, mode, renorm_form)
     cap = T if C is None else C
-    if accept_by_gate:
-        aw = round_to_f32(rt.w) if accept_weights is None else np.asarray(accept_weights)
-        disp = assign_slots_by_gate(rt.ids, aw, E, cap)
+    rr = None
+    if reroute:
+        if accept_by_gate:
+            raise OracleError("rerouting is read with acceptance in token order")
+        n = min(2 * k, E)
+        ids2 = np.full((T, 2 * k), -1, dtype=np.int64)
+        ids2[:, :n] = select_topk(rt.g32, n)
+        if ids_override is not None:
+            ids2 = np.asarray(ids_override, dtype=np.int64)
+        w2 = np.zeros((T, 2 * k))
+        w2[:, :k] = gate_weights(rt.g32, ids2[:, :k], mode, renorm_form)
+        w2[:, k:] = spare_weights(rt.g32, ids2[:, :k], ids2[:, k:], mode, renorm_form)
+        rt.ids, rt.w = ids2, w2
+        rr = assign_slots_reroute(ids2, k, E, cap)
+        disp = rr.dispatch
     else:
-        disp = assign_slots(rt.ids, E, cap)
+        if ids_override is not None:
+            rt.ids = np.asarray(ids_override, dtype=np.int64)
+            rt.w = gate_weights(rt.g32, rt.ids, mode, renorm_form)
+        if accept_by_gate:
+            aw = round_to_f32(rt.w) if accept_weights is None else np.asarray(accept_weights)
+            disp = assign_slots_by_gate(rt.ids, aw, E, cap)
+        else:
+            disp = assign_slots(rt.ids, E, cap)
     w_comb = survivor_weights(disp.row_of, rt.w) if renorm_survivors else rt.w
+    P = rt.ids.shape[1]   # routing records per token: k, or 2k with rerouting
     tok = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
 
     # Expert FFN per accepted path of the requested tokens, evaluated expert
     # by expert (rows are independent, so this is the row-wise definition).
     path_out = {}
     for e in range(E):
-        sel = [(int(t), r) for t in tok for r in range(k)
+        sel = [(int(t), r) for t in tok for r in range(P)
                if rt.ids[t, r] == e and disp.slot[t, r] >= 0]
         if not sel:
             continue
@@ -523,7 +631,7 @@ def forward(x, w_r, b_r, experts: WeightsArg, k: int, mode: int,
     if s is not None:
         y += s
     for i, t in enumerate(tok):
-        for r in range(k):
+        for r in range(P):
             row = int(disp.row_of[t, r])
             if row >= 0:
                 y[i] += float(w_comb[t, r]) * path_out[row]
@@ -531,6 +639,9 @@ def forward(x, w_r, b_r, experts: WeightsArg, k: int, mode: int,
                  max_load=disp.max_load, rho_max=disp.rho_max,
                  tokens_dropped=disp.tokens_dropped, tokens_affected=disp.tokens_affected,
                  rejected_paths=disp.rejected_paths)
+    if rr is not None:
+        stats.update(rerouted=rr.rerouted, tokens_dropped=rr.tokens_dropped, tokens_affected=rr.tokens_affected,
+                     rejected_paths=disp.overflow - rr.rerouted)
     return ForwardResult(y=y, tokens=tok, route=rt, dispatch=disp, stats=stats)
 
 

@@ -598,3 +598,126 @@ def test_gate_priority_invariants(seed):
     big = O.assign_slots_by_gate(ids, w, E, T)
     ref = O.assign_slots(ids, E, T)
     assert np.array_equal(big.slot, ref.slot) and np.array_equal(big.row_of, ref.row_of)
+
+
+# ---------------------------------------------------------------------------
+# Overflow variant: rerouting a rejected path to the next-choice expert
+# (hand-worked fixtures; the reading is stated in the fixture and the oracle)
+# ---------------------------------------------------------------------------
+
+def _reroute_case(c, mode):
+    P = np.array(c["probs"])
+    T, E = P.shape
+    k = c["k"]
+    x = np.eye(T)
+    w_r = np.log(P).T.astype(np.float32)        # [E, d = T]: the scores are ln p
+    rt = O.route(x, w_r, None, k, mode)
+    n = min(2 * k, E)
+    ids2 = np.full((T, 2 * k), -1, dtype=np.int64)
+    ids2[:, :n] = O.select_topk(rt.g32, n)
+    w2 = np.zeros((T, 2 * k))
+    w2[:, :k] = O.gate_weights(rt.g32, ids2[:, :k], mode)
+    w2[:, k:] = O.spare_weights(rt.g32, ids2[:, :k], ids2[:, k:], mode)
+    return x, w_r, ids2, w2
+
+
+@pytest.mark.parametrize("case", _golden("reroute_next_choice.json")["cases"], ids=lambda c: c["name"])
+def test_reroute_hand_worked_examples(case):
+    C = O.capacity(len(case["probs"]), case["k"], len(case["probs"][0]), *case["capacity_factor"])
+    assert C == case["capacity"]
+    for mode, key in ((O.GATE_RENORM, "y_diag_renorm"), (O.GATE_SWITCH, "y_diag_switch")):
+        if key not in case:
+            continue
+        x, w_r, ids2, w2 = _reroute_case(case, mode)
+        assert ids2.tolist() == case["ids_2k"]
+        rr = O.assign_slots_reroute(ids2, case["k"], len(case["expert_scale"]), C)
+        d = rr.dispatch
+        assert d.slot.tolist() == case["slot_2k"]
+        assert d.load.tolist() == case["requested_load"]
+        assert d.offsets.tolist() == case["offsets"]
+        assert d.src_token.tolist() == case["src_token"]
+        assert d.overflow == case["first_pass_overflow"]
+        assert (rr.rerouted, rr.tokens_affected, rr.tokens_dropped) == (
+            case["rerouted"], case["tokens_affected"], case["tokens_dropped"])
+        # linear experts on the grouped rows, combined over the 2k columns
+        out = np.zeros((int(d.offsets[-1]), x.shape[1]))
+        T = x.shape[0]
+        for t in range(T):
+            for c in range(ids2.shape[1]):
+                if d.row_of[t, c] >= 0:
+                    out[d.row_of[t, c]] = case["expert_scale"][ids2[t, c]] * x[t]
+        y = O.combine(T, x.shape[1], d.row_of, w2, out)
+        want = [float(Fraction(*v)) for v in case[key]]
+        np.testing.assert_allclose(np.diag(y), want, atol=1e-6)
+        assert np.count_nonzero(y - np.diag(np.diag(y))) == 0
+
+
+def _reroute_by_expert(ids2, k, E, C):
+    """The same acceptance written per expert instead of as one ordered sweep:
+    an expert keeps its first min(L_e, C) candidate requests in token order,
+    then, of the spare requests made to it (the j-th rejected candidate of a
+    token asks for its spare j), the first C - min(L_e, C) in token order."""
+    T = ids2.shape[0]
+    slot = np.full((T, 2 * k), -1, dtype=np.int64)
+    first = {e: [(t, r) for t in range(T) for r in range(k) if ids2[t, r] == e] for e in range(E)}
+    for e, reqs in first.items():
+        for c, (t, r) in enumerate(reqs[:C]):
+            slot[t, r] = c
+    spare_reqs = {e: [] for e in range(E)}
+    for t in range(T):
+        rejected = [r for r in range(k) if slot[t, r] < 0]
+        for j in range(len(rejected)):
+            if ids2[t, k + j] >= 0:
+                spare_reqs[int(ids2[t, k + j])].append((t, k + j))
+    for e, reqs in spare_reqs.items():
+        base = min(len(first[e]), C)
+        for c, (t, col) in enumerate(reqs[:max(C - base, 0)]):
+            slot[t, col] = base + c
+    return slot
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_reroute_invariants(seed):
+    rng = np.random.default_rng(100 + seed)
+    for _ in range(20):
+        E = int(rng.integers(2, 9))
+        k = int(rng.integers(1, E + 1))
+        T = int(rng.integers(1, 40))
+        C = int(rng.integers(1, max(2, T * k // E + 2)))
+        g = rng.integers(-3, 4, size=(T, E)).astype(np.float64)     # many exact ties
+        n = min(2 * k, E)
+        ids2 = np.full((T, 2 * k), -1, dtype=np.int64)
+        ids2[:, :n] = O.select_topk(g, n)
+        rr = O.assign_slots_reroute(ids2, k, E, C)
+        d = rr.dispatch
+        # the same slots from the per-expert formulation
+        np.testing.assert_array_equal(d.slot, _reroute_by_expert(ids2, k, E, C))
+        # the candidates' acceptance is Algorithm 36.1's, unchanged by the reroutes
+        np.testing.assert_array_equal(d.slot[:, :k], O.assign_slots(ids2[:, :k], E, C).slot)
+        # capacity holds, every row is used once, served experts are distinct per token
+        acc = np.bincount(ids2[d.slot >= 0], minlength=E)
+        assert (acc <= C).all() and int(d.offsets[-1]) == int((d.slot >= 0).sum())
+        assert sorted(d.row_of[d.row_of >= 0].tolist()) == list(range(int(d.offsets[-1])))
+        for t in range(T):
+            served = ids2[t][d.slot[t] >= 0].tolist()
+            assert len(served) == len(set(served)) and len(served) <= k
+            # spare j is used only when at least j + 1 candidates were rejected
+            nrej = int((d.slot[t, :k] < 0).sum())
+            assert all(d.slot[t, k + j] < 0 for j in range(nrej, k))
+        assert d.load.tolist() == np.bincount(ids2[:, :k].ravel(), minlength=E).tolist()
+        assert rr.rerouted == int((d.slot[:, k:] >= 0).sum()) <= d.overflow
+        assert rr.tokens_dropped == int((~(d.slot >= 0).any(axis=1)).sum())
+        if d.overflow == 0:
+            assert rr.rerouted == 0 and (d.slot[:, k:] < 0).all()
+
+
+def test_reroute_without_overflow_is_the_plain_layer():
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((40, 16))
+    w_r = rng.standard_normal((6, 16)).astype(np.float32)
+    ex = tuple(rng.standard_normal((6, 8, 16)) * 0.2 for _ in range(2)) + (rng.standard_normal((6, 16, 8)) * 0.2,)
+    plain = O.forward(x, w_r, None, ex, 2, O.GATE_RENORM, C=None)
+    rer = O.forward(x, w_r, None, ex, 2, O.GATE_RENORM, C=None, reroute=True)
+    np.testing.assert_array_equal(rer.route.ids[:, :2], plain.route.ids)
+    np.testing.assert_allclose(rer.y, plain.y, rtol=0, atol=1e-12)
+    assert rer.stats["rerouted"] == 0
