@@ -87,6 +87,18 @@ typedef struct {
      *                    accepted path still adds nothing) */
     int32_t accept_by_gate;
     int32_t renorm_survivors;
+    /* reroute 1: a path its expert rejects asks for the token's next-choice
+     * expert instead ("The real cost of sparse expert models" item 5; ch. 36
+     * §36.3 overflow treatments; read here as: the j-th rejected candidate of a
+     * token, in rank order, asks for its j-th next expert in rank order; these
+     * requests are accepted in token order, after every first-pass request, into
+     * the capacity left; a path rejected again is dropped).  The routing records
+     * (topk_ids, topk_w, slot, row_of) then have P = 2k columns per token: the
+     * k selected experts, then the next k in rank order (id -1, weight 0 where
+     * the experts run out).  A next-choice path's weight is its expert's gate
+     * value with the selection's normalizer (RENORM p_e' / sum_{j in S_t} p_j,
+     * SWITCH p_e').  Requires accept_by_gate == 0. */
+    int32_t reroute;
 } moe_shape;
 
 /* Indices of the int32 statistics vector written by moe_dispatch. */
@@ -96,6 +108,8 @@ enum {
     MOE_STAT_MAX_LOAD = 2,        /* max_e L_e (requested, before capacity)      */
     MOE_STAT_TOKENS_DROPPED = 3,  /* tokens with every path rejected             */
     MOE_STAT_TOKENS_AFFECTED = 4, /* tokens with at least one path rejected      */
+    MOE_STAT_REROUTED = 5,        /* with reroute: rejected paths served by a
+                                     next-choice expert (O counts the first pass) */
     MOE_STAT_COUNT = 8
 };
 
@@ -109,6 +123,12 @@ enum {
     MOE_BAL_RHO_MAX = 4,          /* max_e L_e / (T k / E)                            */
     MOE_BAL_COUNT = 5
 };
+
+/* Bytes at the start of every route, route-stats and forward workspace that
+ * hold the router's completion counters.  They must be zero before the first
+ * call that uses the workspace (clear them once when the buffer is allocated)
+ * and must not be used for anything else; every call leaves them at zero. */
+#define MOE_SYNC_BYTES 256
 
 /* Which call a workspace is sized for. */
 typedef enum {

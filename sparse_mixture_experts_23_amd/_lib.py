@@ -32,7 +32,10 @@ MOE_STAT_ACCEPTED = 1
 MOE_STAT_MAX_LOAD = 2
 MOE_STAT_TOKENS_DROPPED = 3
 MOE_STAT_TOKENS_AFFECTED = 4
+MOE_STAT_REROUTED = 5
 MOE_STAT_COUNT = 8
+
+MOE_SYNC_BYTES = 256   # zeroed once at the start of route / route-stats / forward workspaces
 
 MOE_WS_DISPATCH = 0
 MOE_WS_FFN = 1
@@ -52,7 +55,7 @@ MOE_BAL_COUNT = 5
 class MoeShape(ctypes.Structure):
     _fields_ = [("T", c_int64), ("d", c_int32), ("m", c_int32), ("E", c_int32), ("k", c_int32),
                 ("capacity", c_int32), ("gate_mode", c_int32), ("dtype", c_int32), ("m_shared", c_int32),
-                ("accept_by_gate", c_int32), ("renorm_survivors", c_int32)]
+                ("accept_by_gate", c_int32), ("renorm_survivors", c_int32), ("reroute", c_int32)]
 
 
 class MoeError(RuntimeError):

@@ -58,8 +58,14 @@ def _torch_dtype(shape: L.MoeShape):
 
 
 def workspace(shape: L.MoeShape, kind: int, device="cuda") -> torch.Tensor:
+    """Workspace for the named call; the router's sync words at the start of a
+    route, route-stats or forward workspace are zeroed once here (the library
+    leaves them at zero after every call)."""
     n = L.moe_workspace_bytes(shape, kind)
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    if kind in (L.MOE_WS_ROUTE, L.MOE_WS_ROUTE_STATS, L.MOE_WS_FORWARD):
+        ws[:L.MOE_SYNC_BYTES].zero_()
+    return ws
 
 
 def route(shape: L.MoeShape, x, w_r, b_r=None):

@@ -88,11 +88,22 @@ struct moe_dims {
     int m_shared;
     int accept_by_gate;     // overflow variant: acceptance by routing weight
     int renorm_survivors;   // overflow variant: weights renormalised over accepted paths
+    int reroute;            // overflow variant: rejected paths go to the next-choice expert
 };
+
+// Routing records per token: the k selected experts, and with rerouting the next
+// k in rank order as well.
+inline int moe_paths(const moe_dims& s) { return s.reroute ? 2 * s.k : s.k; }
 
 // Tokens per block of the dispatch's per-block expert counts, hist[b][e] = number
 // of tokens in [256 b, 256 b + 256) that selected expert e.
 constexpr int MOE_DISPATCH_BLOCK = 256;
+
+// Tokens per workgroup of the E <= 8 router, and so per row of the expert counts
+// it makes for the dispatch.  Its sync words, MOE_SYNC_BYTES at the start of every
+// route, route-stats and forward workspace: [0] workgroups finished, [1]
+// non-finite flag.
+constexpr int MOE_ROUTE_TOK = 16;
 
 // Work-claim counters of the grouped bf16 GEMMs, kept after the tile prefix
 // (tprefix[0..G]) in the same workspace: MOE_SCHED_WORDS 64-bit words, one per
@@ -106,15 +117,16 @@ __host__ __device__ inline unsigned long long* moe_sched_words(int32_t* tprefix,
 namespace moe_kernels {
 
 // Router: scores, softmax, top-k, weights.  ws holds the weight planes or the
-// fp32 scores (route_ws_bytes).
+// fp32 scores (route_ws_bytes).  sync: the MOE_SYNC_BYTES of sync words (zero on
+// entry, zero again when the launch ends), used by the E <= 8 path.
 // probs (nullable): also write every token's full softmax, probs[t E + e].
-// hist (nullable): the dispatch's per-block expert counts ([ceil(T / 256)][E]
-// int32).  Where the router path can count them while it selects (E <= 8, bf16),
-// it zeroes and fills them, clears the two counters at acc_stats (nullable) and
-// sets *hist_done; otherwise it leaves them alone.
+// hist (nullable): the dispatch's expert counts per MOE_ROUTE_TOK tokens
+// ([ceil(T / MOE_ROUTE_TOK)][E] int32, dispatch_router_counts_ok).  Where the
+// router path counts them while it selects (E <= 8), it fills them, clears the
+// two counters at acc_stats and sets *hist_done; otherwise it leaves them alone.
 size_t route_ws_bytes(const moe_dims& s);
 hipError_t launch_route(const moe_dims& s, const void* x, const float* w_r, const float* b_r,
-                        int32_t* topk_ids, float* topk_w, int32_t* status, void* ws, hipStream_t st,
+                        int32_t* topk_ids, float* topk_w, int32_t* status, void* ws, int32_t* sync, hipStream_t st,
                         float* probs = nullptr, int32_t* hist = nullptr, bool* hist_done = nullptr,
                         int32_t* acc_stats = nullptr);
 // Small batches (bf16, 0 < T <= 16, E <= 256, acceptance in token order): route,
@@ -138,6 +150,9 @@ size_t dispatch_ws_bytes(const moe_dims& s);
 // Whether launch_dispatch reads the per-block expert counts (more than one token
 // block, or acceptance by gate weight); a single block is counted in place.
 bool dispatch_uses_hist(const moe_dims& s);
+// Whether launch_dispatch can take the counts per MOE_ROUTE_TOK tokens from the
+// router (the inline scan, with a table of at most SCAN_INLINE_MAX entries).
+bool dispatch_router_counts_ok(const moe_dims& s);
 // Whether launch_dispatch derives the scan inside the placement kernel (a small
 // count table); the placement then accumulates the token statistics into
 // stats[MOE_STAT_TOKENS_DROPPED..AFFECTED], which whoever fills the table clears.
@@ -146,7 +161,8 @@ bool dispatch_inline_scan(const moe_dims& s);
 // tile_rows rows (gemm_tile_rows), so the GEMM launches can skip computing it.
 // topk_w: the routing weights (read only when s.accept_by_gate).
 // ws starts with the per-block expert counts (dispatch_hist); hist_ready: the
-// router has already written them, so the counting kernel is skipped.  x_perm
+// router has already written them per MOE_ROUTE_TOK tokens
+// (dispatch_router_counts_ok), so the counting kernel is skipped.  x_perm
 // == nullptr: no row copy (the caller reads x through src_token).
 hipError_t launch_dispatch(const moe_dims& s, const void* x, const int32_t* ids, const float* topk_w,
                            int32_t* load, int32_t* offsets, int32_t* slot, int32_t* row_of, int32_t* src_token,

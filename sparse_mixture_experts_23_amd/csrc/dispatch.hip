@@ -187,17 +187,20 @@ __global__ __launch_bounds__(DB_TOK) void dispatch_place_kernel(const int32_t* _
     }
 }
 
-// Scan + place for small count tables (NB * E <= 4096, E <= 256): every block's
-// workgroup loads the whole per-block count table into LDS and derives from it
-// the totals L_e, its own base slots and the grouped-row offsets (the same integer
-// results as dispatch_scan_kernel), then places its tokens as dispatch_place_kernel
-// does -- one launch instead of two.  Block 0 also writes load, offsets, the tile
-// prefix and the statistics; the token statistics are accumulated with atomics
-// into counters the kernel that filled the table has cleared.  Dynamic LDS: masks
-// (4 E uint64), then s_base[E], s_off[E], s_hist[NB E] int32.
+// Scan + place for small count tables (NR * E <= 4096, E <= 256): every block's
+// workgroup loads the whole count table into LDS and derives from it the totals
+// L_e, its own base slots and the grouped-row offsets (the same integer results
+// as dispatch_scan_kernel), then places its tokens as dispatch_place_kernel does
+// -- one launch instead of two.  The table has NR rows, `sub` per 256-token
+// block: one row per block (the count kernel) or one per router workgroup of
+// MOE_ROUTE_TOK tokens; a block's base is the sum of the rows before its first.  Block 0 also
+// writes load, offsets, the tile prefix and the statistics; the token statistics
+// are accumulated with atomics into counters the kernel that filled the table has
+// cleared.  Dynamic LDS: masks (4 E uint64), then s_base[E], s_off[E],
+// s_hist[NR E] int32.
 constexpr int SCAN_INLINE_MAX = 4096;
 __global__ __launch_bounds__(DB_TOK) void dispatch_place_scan_kernel(
-    const int32_t* __restrict__ ids, int64_t T, int k, int E, int C, const int32_t* __restrict__ hist, int NB,
+    const int32_t* __restrict__ ids, int64_t T, int k, int E, int C, const int32_t* __restrict__ hist, int NR, int sub,
     int32_t* __restrict__ load, int32_t* __restrict__ offsets, int32_t* __restrict__ slot,
     int32_t* __restrict__ row_of, int32_t* __restrict__ src_token, int32_t* __restrict__ stats,
     int32_t* __restrict__ tprefix, int tile_rows) {
@@ -207,7 +210,7 @@ __global__ __launch_bounds__(DB_TOK) void dispatch_place_scan_kernel(
     int* s_hist = s_off + E;
     __shared__ int s_sum[4], s_tiles[4], s_over[4], s_max[4], s_drop[4], s_aff[4];
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
-    const int n = NB * E;
+    const int n = NR * E;
     {   // the table: up to 16 loads per thread, all in flight together
         int v[SCAN_INLINE_MAX / DB_TOK];
 #pragma unroll
@@ -221,9 +224,10 @@ __global__ __launch_bounds__(DB_TOK) void dispatch_place_scan_kernel(
     const int e = tid;
     int L = 0, base = 0;
     if (e < E) {
-        for (int b = 0; b < NB; ++b) {
+        const int first = (int)blockIdx.x * sub;   // this block's first row
+        for (int b = 0; b < NR; ++b) {
             const int h = s_hist[b * E + e];
-            base += b < (int)blockIdx.x ? h : 0;
+            base += b < first ? h : 0;
             L += h;
         }
     }
@@ -614,9 +618,14 @@ bool dispatch_inline_scan(const moe_dims& s) {
     return !s.accept_by_gate && NB > 1 && s.E <= DB_TOK && NB * s.E <= SCAN_INLINE_MAX;
 }
 
+bool dispatch_router_counts_ok(const moe_dims& s) {
+    return dispatch_inline_scan(s) && (s.T + MOE_ROUTE_TOK - 1) / MOE_ROUTE_TOK * s.E <= SCAN_INLINE_MAX;
+}
+
 size_t dispatch_ws_bytes(const moe_dims& s) {
     const int64_t NB = (s.T + DB_TOK - 1) / DB_TOK;
-    size_t b = al8((size_t)NB * (size_t)s.E * sizeof(int32_t));   // per-block counts / base slots
+    const int64_t rows = dispatch_router_counts_ok(s) ? (s.T + MOE_ROUTE_TOK - 1) / MOE_ROUTE_TOK : NB;
+    size_t b = al8((size_t)rows * (size_t)s.E * sizeof(int32_t));   // per-block (or router-group) counts / bases
     if (s.accept_by_gate) {
         // request offsets, thresholds, request keys and path ids
         b += al8(sizeof(int32_t) * (s.E + 1)) + sizeof(unsigned long long) * s.E +
@@ -641,7 +650,7 @@ hipError_t launch_dispatch(const moe_dims& s, const void* x, const int32_t* ids,
         unsigned long long* req_key = reinterpret_cast<unsigned long long*>(p);
         p += sizeof(unsigned long long) * (size_t)s.T * s.k;
         int32_t* req_path = reinterpret_cast<int32_t*>(p);
-        if (NB > 0 && !hist_ready)
+        if (NB > 0)
             hipLaunchKernelGGL(dispatch_count_kernel, dim3(NB), dim3(DB_TOK), mask_lds, st, ids, s.T, s.k, s.E,
                                hist, (int32_t*)nullptr);
         hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, st, hist, NB, s.E, s.C, load, offsets,
@@ -659,15 +668,18 @@ hipError_t launch_dispatch(const moe_dims& s, const void* x, const int32_t* ids,
                            s.k, s.E, s.C, load, offsets, stats, tprefix, tile_rows, slot, row_of, src_token);
     } else if (NB > 0 && dispatch_inline_scan(s)) {
         // the token statistics are accumulated by the placement into counters the
-        // table's writer clears (here the count kernel, else the router)
+        // table's writer clears (here the count kernel, else the router, whose
+        // table has one row per 64 tokens)
         if (!hist_ready)
             hipLaunchKernelGGL(dispatch_count_kernel, dim3(NB), dim3(DB_TOK), mask_lds, st, ids, s.T, s.k, s.E,
                                hist, stats + MOE_STAT_TOKENS_DROPPED);
-        const size_t lds = mask_lds + sizeof(int32_t) * (2 * s.E + (size_t)NB * s.E);
+        const int sub = hist_ready ? DB_TOK / MOE_ROUTE_TOK : 1;
+        const int NR = hist_ready ? (int)((s.T + MOE_ROUTE_TOK - 1) / MOE_ROUTE_TOK) : NB;
+        const size_t lds = mask_lds + sizeof(int32_t) * (2 * s.E + (size_t)NR * s.E);
         hipLaunchKernelGGL(dispatch_place_scan_kernel, dim3(NB), dim3(DB_TOK), lds, st, ids, s.T, s.k, s.E, s.C,
-                           hist, NB, load, offsets, slot, row_of, src_token, stats, tprefix, tile_rows);
+                           hist, NR, sub, load, offsets, slot, row_of, src_token, stats, tprefix, tile_rows);
     } else {
-        if (NB > 0 && !hist_ready) {
+        if (NB > 0) {
             hipLaunchKernelGGL(dispatch_count_kernel, dim3(NB), dim3(DB_TOK), mask_lds, st, ids, s.T, s.k, s.E,
                                hist, (int32_t*)nullptr);
         }

@@ -2,7 +2,10 @@
 // Every call only queues kernels on the caller's stream; nothing here
 // allocates, frees or synchronises.
 #include <climits>
+#include <map>
+#include <memory>
 #include <mutex>
+#include <utility>
 
 #include "common.h"
 
@@ -22,8 +25,10 @@ moe_status check_shape(const moe_shape* s, moe_dims* out) {
     if (s->E > 1024 || s->k > 32) return MOE_ERR_UNSUPPORTED;
     if (s->T * (int64_t)s->k > (int64_t)INT_MAX) return MOE_ERR_UNSUPPORTED;
     if (s->dtype == MOE_BF16 && (s->d % 8 || s->m % 8 || s->m_shared % 8)) return MOE_ERR_UNSUPPORTED;
-    if ((s->accept_by_gate != 0 && s->accept_by_gate != 1) || (s->renorm_survivors != 0 && s->renorm_survivors != 1))
+    if ((s->accept_by_gate != 0 && s->accept_by_gate != 1) || (s->renorm_survivors != 0 && s->renorm_survivors != 1) ||
+        (s->reroute != 0 && s->reroute != 1))
         return MOE_ERR_INVALID_ARGUMENT;
+    if (s->reroute) return MOE_ERR_UNSUPPORTED;   // rerouting: the dispatch and combine come next
     if (out) {
         out->T = s->T;
         out->d = s->d;
@@ -36,6 +41,7 @@ moe_status check_shape(const moe_shape* s, moe_dims* out) {
         out->m_shared = s->m_shared;
         out->accept_by_gate = s->accept_by_gate;
         out->renorm_survivors = s->renorm_survivors;
+        out->reroute = s->reroute;
     }
     return MOE_OK;
 }
@@ -69,10 +75,10 @@ size_t ffn_ws(const moe_dims& d) {
 size_t gemm1_ws(const moe_dims& d) { return align_up(gemm_ws_bytes(d.E)) + g1_part_bytes(d); }
 // moe_expert_gemm2 alone: [tile prefix | H partials]
 size_t gemm2_ws(const moe_dims& d) { return align_up(gemm_ws_bytes(d.E)) + partial_bytes(d); }
+// moe_route's workspace: the sync words, then the router's own part
+size_t route_ws(const moe_dims& d) { return MOE_SYNC_BYTES + align_up(route_ws_bytes(d)); }
 // moe_route's workspace, then the [T, E] fp32 probabilities
-size_t route_stats_ws(const moe_dims& d) {
-    return align_up(route_ws_bytes(d)) + align_up((size_t)d.T * d.E * sizeof(float));
-}
+size_t route_stats_ws(const moe_dims& d) { return route_ws(d) + align_up((size_t)d.T * d.E * sizeof(float)); }
 // shared expert: [tile prefix | h | GEMM1 partials | s partials] (one group of T rows)
 size_t shared_g1_bytes(const moe_dims& d) {
     return align_up(gemm1_part_bytes(d.dtype, d.T, 1, d.m_shared, d.d, d.T));
@@ -87,6 +93,7 @@ size_t shared_ws(const moe_dims& d) {
 }
 
 struct ForwardWs {
+    int32_t* sync;
     int32_t* offsets;
     int32_t* row_of;
     int32_t* src_token;
@@ -115,8 +122,9 @@ ForwardWs carve_forward(const moe_dims& d, void* base) {
     // GEMM1 reads the grouped rows in place through src_token where it can (then
     // src_token is padded by one row tile and there is no x_perm)
     const bool gather = gather_rows(d);
+    w.sync = static_cast<int32_t*>(take(MOE_SYNC_BYTES));   // fixed place: the same for every shape
     w.offsets = static_cast<int32_t*>(take(sizeof(int32_t) * (d.E + 1)));
-    w.row_of = static_cast<int32_t*>(take(sizeof(int32_t) * d.T * d.k));
+    w.row_of = static_cast<int32_t*>(take(sizeof(int32_t) * d.T * moe_paths(d)));
     w.src_token = static_cast<int32_t*>(take(sizeof(int32_t) * (R + (gather ? 256 : 0))));
     w.x_perm = gather ? nullptr : take((size_t)R * d.d * elem(d));
     w.H = static_cast<float*>(take(sizeof(float) * R * d.d));
@@ -132,40 +140,50 @@ ForwardWs carve_forward(const moe_dims& d, void* base) {
 inline moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 // The shared expert depends on x alone, so moe_forward runs it on a second stream
-// of the device of the caller's stream, concurrently with routing, dispatch and the routed
-// experts: an event on the caller's stream forks it, another joins it before the
-// combine.  One default-priority, non-blocking stream and two events per device,
-// created on first use and kept for the process (they hold no device memory);
-// the mutex keeps each call's record / wait sequence together when several host
-// threads launch layers on one device.
+// concurrently with the routed path: an event on the caller's stream forks it,
+// another joins it before the combine.  Each caller stream gets a side stream of
+// its own (default priority, non-blocking, on the caller stream's device) and
+// its own two events, created on first use and kept for the process (they hold
+// no device memory), so calls on different caller streams share no state: one
+// stream's graph capture never reaches another stream's eager calls.  The
+// entry's mutex keeps one call's record / wait sequence together when several
+// host threads launch on the same caller stream.
 struct SideStream {
     hipStream_t stream = nullptr;
     hipEvent_t fork = nullptr, join = nullptr;
+    std::mutex mu;
 };
 constexpr int MAX_DEVICES = 64;
-std::mutex g_side_mu;
-SideStream g_side[MAX_DEVICES];
+std::mutex g_side_mu;   // guards the map only
+std::map<std::pair<int, hipStream_t>, std::unique_ptr<SideStream>> g_side;
 
-// The side stream of the device that `st` belongs to (made current only while
-// the stream and events are created).
+// The side stream paired with caller stream `st` (its device made current only
+// while the stream and events are created).
 hipError_t side_stream(hipStream_t st, SideStream** out) {
     hipDevice_t dev = 0;
     hipError_t e = hipStreamGetDevice(st, &dev);
     if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
-    SideStream& s = g_side[dev];
-    if (!s.fork || !s.join || !s.stream) {
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    std::unique_ptr<SideStream>& slot = g_side[{(int)dev, st}];
+    if (!slot) {
+        std::unique_ptr<SideStream> s(new SideStream);
         int cur = 0;
         if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
         if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
-        if (!s.fork) e = hipEventCreateWithFlags(&s.fork, hipEventDisableTiming);
-        if (e == hipSuccess && !s.join) e = hipEventCreateWithFlags(&s.join, hipEventDisableTiming);
-        if (e == hipSuccess && !s.stream) e = hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking);
+        e = hipEventCreateWithFlags(&s->fork, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&s->join, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipStreamCreateWithFlags(&s->stream, hipStreamNonBlocking);
         const hipError_t r = cur != dev ? hipSetDevice(cur) : hipSuccess;
-        if (e != hipSuccess) return e;
-        if (r != hipSuccess) return r;
+        if (e != hipSuccess || r != hipSuccess) {   // leave no half-made entry behind
+            if (s->fork) (void)hipEventDestroy(s->fork);
+            if (s->join) (void)hipEventDestroy(s->join);
+            if (s->stream) (void)hipStreamDestroy(s->stream);
+            g_side.erase({(int)dev, st});
+            return e != hipSuccess ? e : r;
+        }
+        slot = std::move(s);
     }
-    *out = &s;
+    *out = slot.get();
     return hipSuccess;
 }
 
@@ -237,6 +255,77 @@ moe_status shared_impl(const moe_dims& d, const void* x, const void* s_gate, con
 
 }  // namespace
 
+namespace {
+
+// The whole layer; side_ok: the shared expert may run on a side stream (else on
+// the caller's stream, after the dispatch).
+moe_status forward_impl(const moe_shape* shape, const void* x, const float* w_r, const float* b_r, const void* w_gate,
+                        const void* w_up, const void* w_down, const void* s_gate, const void* s_up,
+                        const void* s_down, float* y, int32_t* topk_ids, float* topk_w, int32_t* load, int32_t* slot,
+                        int32_t* stats, int32_t* status, void* ws, size_t ws_bytes, void* stream, bool side_ok) {
+    moe_dims d;
+    moe_status rc = check_shape(shape, &d);
+    if (rc != MOE_OK) return rc;
+    if (!status || !load || !stats || !ws || !w_gate || !w_up || !w_down) return MOE_ERR_INVALID_ARGUMENT;
+    if (d.T > 0 && (!x || !w_r || !y || !topk_ids || !topk_w || !slot)) return MOE_ERR_INVALID_ARGUMENT;
+    if (d.m_shared && (!s_gate || !s_up || !s_down)) return MOE_ERR_INVALID_ARGUMENT;
+    ForwardWs w = carve_forward(d, ws);
+    if (ws_bytes < w.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    // The shared expert runs on the caller stream's side stream.  With the
+    // one-workgroup front of small batches it is forked before the front, whose
+    // latency it then overlaps; otherwise after the dispatch, so that its GEMMs,
+    // which fill the GPU, do not hold the CUs the router and the dispatch need.
+    SideStream* side = nullptr;
+    std::unique_lock<std::mutex> side_lock;
+    bool side_forked = false;
+    auto fork_shared = [&]() -> moe_status {
+        if (!side_ok) return shared_impl(d, x, s_gate, s_up, s_down, w.s, w.shared, st);
+        MOE_CHECK_HIP(side_stream(st, &side));
+        side_lock = std::unique_lock<std::mutex>(side->mu);
+        MOE_CHECK_HIP(hipEventRecord(side->fork, st));
+        MOE_CHECK_HIP(hipStreamWaitEvent(side->stream, side->fork, 0));
+        side_forked = true;
+        const moe_status r = shared_impl(d, x, s_gate, s_up, s_down, w.s, w.shared, side->stream);
+        if (hipEventRecord(side->join, side->stream) != hipSuccess) return MOE_ERR_HIP;
+        return r;
+    };
+    // every return below first joins the side stream, also on an error
+    auto joined = [&](moe_status r) -> moe_status {
+        if (side_forked && hipStreamWaitEvent(st, side->join, 0) != hipSuccess) return MOE_ERR_HIP;
+        return r;
+    };
+    const bool shared = d.m_shared && d.T > 0;
+    // the dispatch (or the one-workgroup front of small batches) also writes the
+    // GEMMs' tile prefix at the start of the FFN workspace
+    int32_t* tprefix = static_cast<int32_t*>(w.ffn);
+    if (front_fused_ok(d)) {
+        if (shared && side_ok && (rc = fork_shared()) != MOE_OK) return joined(rc);
+        if (launch_front(d, x, w_r, b_r, topk_ids, topk_w, status, w.route, st, load, w.offsets, slot, w.row_of,
+                         w.src_token, w.x_perm, stats, tprefix, gemm_tile_rows(d.dtype)) != hipSuccess)
+            return joined(MOE_ERR_HIP);
+    } else {
+        // where it can, the router also counts the dispatch's expert loads
+        bool counted = false;
+        if (launch_route(d, x, w_r, b_r, topk_ids, topk_w, status, w.route, w.sync, st, nullptr,
+                         dispatch_router_counts_ok(d) ? static_cast<int32_t*>(w.dispatch) : nullptr, &counted,
+                         stats + MOE_STAT_TOKENS_DROPPED) != hipSuccess)
+            return joined(MOE_ERR_HIP);
+        if (launch_dispatch(d, x, topk_ids, topk_w, load, w.offsets, slot, w.row_of, w.src_token, w.x_perm, stats,
+                            w.dispatch, st, tprefix, gemm_tile_rows(d.dtype), counted) != hipSuccess)
+            return joined(MOE_ERR_HIP);
+    }
+    if (shared && (!side_ok || !front_fused_ok(d)) && (rc = fork_shared()) != MOE_OK) return joined(rc);
+    Partials parts;   // K-split partials of H beyond the first, added by the combine
+    rc = w.x_perm ? ffn_impl(d, w.x_perm, w.offsets, w_gate, w_up, w_down, w.H, w.ffn, &parts, st, true)
+                  : ffn_impl(d, x, w.offsets, w_gate, w_up, w_down, w.H, w.ffn, &parts, st, true, w.src_token);
+    rc = joined(rc);
+    if (rc != MOE_OK) return rc;
+    return hip_status(launch_combine(d, w.H, parts.H1, parts.np, parts.stride, w.row_of, topk_w, w.s, y, st));
+}
+
+}  // namespace
+
 extern "C" {
 
 int32_t moe_capacity(int64_t T, int32_t k, int32_t E, int32_t cf_num, int32_t cf_den) {
@@ -261,7 +350,7 @@ size_t moe_workspace_bytes(const moe_shape* shape, int32_t kind) {
     moe_dims d;
     if (check_shape(shape, &d) != MOE_OK) return 0;
     switch (kind) {
-        case MOE_WS_ROUTE: return align_up(route_ws_bytes(d)) + ALIGN;
+        case MOE_WS_ROUTE: return route_ws(d) + ALIGN;
         case MOE_WS_ROUTE_STATS: return route_stats_ws(d) + ALIGN;
         case MOE_WS_DISPATCH: return align_up(dispatch_ws_bytes(d)) + ALIGN;
         case MOE_WS_FFN: return ffn_ws(d);
@@ -292,8 +381,10 @@ moe_status moe_route_stats(const moe_shape* shape, const void* x, const float* w
     if (!status || !prob_sum || (d.T > 0 && (!x || !w_r || !topk_ids || !topk_w))) return MOE_ERR_INVALID_ARGUMENT;
     if (!ws || ws_bytes < route_stats_ws(d)) return MOE_ERR_WORKSPACE_TOO_SMALL;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    float* probs = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(route_ws_bytes(d)));
-    MOE_CHECK_HIP(launch_route(d, x, w_r, b_r, topk_ids, topk_w, status, ws, st, probs));
+    char* base = static_cast<char*>(ws);
+    float* probs = reinterpret_cast<float*>(base + route_ws(d));
+    MOE_CHECK_HIP(launch_route(d, x, w_r, b_r, topk_ids, topk_w, status, base + MOE_SYNC_BYTES,
+                               reinterpret_cast<int32_t*>(base), st, probs));
     return hip_status(launch_prob_sum(d, probs, prob_sum, st));
 }
 
@@ -312,8 +403,10 @@ moe_status moe_route(const moe_shape* shape, const void* x, const float* w_r, co
     moe_status rc = check_shape(shape, &d);
     if (rc != MOE_OK) return rc;
     if (!status || (d.T > 0 && (!x || !w_r || !topk_ids || !topk_w))) return MOE_ERR_INVALID_ARGUMENT;
-    if (route_ws_bytes(d) > 0 && (!ws || ws_bytes < route_ws_bytes(d))) return MOE_ERR_WORKSPACE_TOO_SMALL;
-    return hip_status(launch_route(d, x, w_r, b_r, topk_ids, topk_w, status, ws, static_cast<hipStream_t>(stream)));
+    if (!ws || ws_bytes < route_ws(d)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    char* base = static_cast<char*>(ws);
+    return hip_status(launch_route(d, x, w_r, b_r, topk_ids, topk_w, status, base + MOE_SYNC_BYTES,
+                                   reinterpret_cast<int32_t*>(base), static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_dispatch(const moe_shape* shape, const void* x, const int32_t* topk_ids, const float* topk_w,
@@ -391,60 +484,8 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_r, 
                        const void* s_up, const void* s_down, float* y, int32_t* topk_ids, float* topk_w,
                        int32_t* load, int32_t* slot, int32_t* stats, int32_t* status, void* ws, size_t ws_bytes,
                        void* stream) {
-    moe_dims d;
-    moe_status rc = check_shape(shape, &d);
-    if (rc != MOE_OK) return rc;
-    if (!status || !load || !stats || !ws || !w_gate || !w_up || !w_down) return MOE_ERR_INVALID_ARGUMENT;
-    if (d.T > 0 && (!x || !w_r || !y || !topk_ids || !topk_w || !slot)) return MOE_ERR_INVALID_ARGUMENT;
-    if (d.m_shared && (!s_gate || !s_up || !s_down)) return MOE_ERR_INVALID_ARGUMENT;
-    ForwardWs w = carve_forward(d, ws);
-    if (ws_bytes < w.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    // the shared expert on the side stream, forked before anything else
-    std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
-    SideStream* side = nullptr;
-    if (d.m_shared && d.T > 0) {
-        side_lock.lock();
-        MOE_CHECK_HIP(side_stream(st, &side));
-        MOE_CHECK_HIP(hipEventRecord(side->fork, st));
-        MOE_CHECK_HIP(hipStreamWaitEvent(side->stream, side->fork, 0));
-        rc = shared_impl(d, x, s_gate, s_up, s_down, w.s, w.shared, side->stream);
-        const hipError_t e = hipEventRecord(side->join, side->stream);
-        if (e != hipSuccess) return MOE_ERR_HIP;
-        if (rc != MOE_OK) {
-            // whatever the side stream queued still finishes before later work on st
-            return hipStreamWaitEvent(st, side->join, 0) == hipSuccess ? rc : MOE_ERR_HIP;
-        }
-    }
-    // every return below first joins the side stream, also on an error
-    auto joined = [&](moe_status r) -> moe_status {
-        if (side && hipStreamWaitEvent(st, side->join, 0) != hipSuccess) return MOE_ERR_HIP;
-        return r;
-    };
-    // the dispatch (or the one-workgroup front of small batches) also writes the
-    // GEMMs' tile prefix at the start of the FFN workspace
-    int32_t* tprefix = static_cast<int32_t*>(w.ffn);
-    if (front_fused_ok(d)) {
-        if (launch_front(d, x, w_r, b_r, topk_ids, topk_w, status, w.route, st, load, w.offsets, slot, w.row_of,
-                         w.src_token, w.x_perm, stats, tprefix, gemm_tile_rows(d.dtype)) != hipSuccess)
-            return joined(MOE_ERR_HIP);
-    } else {
-        // where it can, the router also counts the dispatch's per-block expert loads
-        bool counted = false;
-        if (launch_route(d, x, w_r, b_r, topk_ids, topk_w, status, w.route, st, nullptr,
-                         dispatch_uses_hist(d) ? static_cast<int32_t*>(w.dispatch) : nullptr, &counted,
-                         stats + MOE_STAT_TOKENS_DROPPED) != hipSuccess)
-            return joined(MOE_ERR_HIP);
-        if (launch_dispatch(d, x, topk_ids, topk_w, load, w.offsets, slot, w.row_of, w.src_token, w.x_perm, stats,
-                            w.dispatch, st, tprefix, gemm_tile_rows(d.dtype), counted) != hipSuccess)
-            return joined(MOE_ERR_HIP);
-    }
-    Partials parts;   // K-split partials of H beyond the first, added by the combine
-    rc = w.x_perm ? ffn_impl(d, w.x_perm, w.offsets, w_gate, w_up, w_down, w.H, w.ffn, &parts, st, true)
-                  : ffn_impl(d, x, w.offsets, w_gate, w_up, w_down, w.H, w.ffn, &parts, st, true, w.src_token);
-    rc = joined(rc);
-    if (rc != MOE_OK) return rc;
-    return hip_status(launch_combine(d, w.H, parts.H1, parts.np, parts.stride, w.row_of, topk_w, w.s, y, st));
+    return forward_impl(shape, x, w_r, b_r, w_gate, w_up, w_down, s_gate, s_up, s_down, y, topk_ids, topk_w, load,
+                        slot, stats, status, ws, ws_bytes, stream, true);
 }
 
 }  // extern "C"

@@ -13,9 +13,10 @@
 // x * w_r is formed as three exact bf16 x bf16 products accumulated in fp32 on the
 // MFMA units -- an fp32 dot product up to summation order.
 //
-// E <= 8 (bf16 activations): a small kernel writes the planes as ready-made MFMA
-//   operands (two 16-column tiles: hi | mid and lo | 0), then one fused kernel
-//   computes the scores of 16 tokens on 8 waves and selects (route_mfma8_kernel).
+// E <= 8 (bf16 activations, T > 16): one kernel; each workgroup splits w_r into
+//   the planes itself, chunk by chunk, as ready-made MFMA operands (two 16-column
+//   tiles: hi | mid and lo | 0) while it stages 16 tokens' activations through
+//   LDS with coalesced loads, then selects (route_lds8_kernel).
 // E <= 64: one fused kernel; 8 waves share 16 tokens, each wave takes one K
 //   slice with all its loads in flight at once, the slices are summed in LDS in a
 //   fixed order and the waves select.
@@ -25,8 +26,8 @@
 //   GPU); a selection kernel with one wave per token adds, per expert, the three
 //   plane columns of every split in a fixed order.
 // Selection: k rounds of a 64-bit (order-preserving score key, ~id) wave arg-max.
-// Everything is deterministic: fixed summation orders; the only atomics are the
-// integer expert counts the E <= 8 path adds for the dispatch.
+// Everything is deterministic: fixed summation orders; the only atomics are
+// integer counts (the E <= 8 path's completion count and non-finite flag).
 #include <algorithm>
 
 #include "common.h"
@@ -187,121 +188,277 @@ __device__ void select_token(const float* __restrict__ row, const float* __restr
 }
 
 // ---------------------------------------------------------------------------
-// E <= 8, bf16 activations: fused scores + selection on MFMA, 16 tokens per workgroup
+// E <= 8, bf16 activations, T > 16: 16 tokens per workgroup, K staged through LDS
 // ---------------------------------------------------------------------------
 //
-// route_prep_kernel lays the three bf16 planes of w_r out as the B operands of
-// v_mfma_f32_16x16x32_bf16 for two 16-column tiles, tile 0 = [hi e0..7 | mid e0..7]
-// and tile 1 = [lo e0..7 | 0]: entry (s, tile, lane) is the 8 bf16 that lane
-// `lane` (column lane % 16, K group lane / 16) supplies for the K step of 32 that
-// starts at 32 s, so each operand load of a wave is one contiguous 1 KB read.  The
-// same launch clears the status word and the dispatch's per-block counts.
+// Each workgroup takes 16 tokens over the whole K, in chunks of 512.  Per chunk,
+// the activations are read with coalesced 16-byte loads (a wave instruction
+// reads 1 KB of one token row) and written to LDS, and the chunk of w_r (fp32)
+// is split into three exact bf16 planes (hi + mid + lo carries all 24
+// significand bits; the hardware round-to-nearest-even conversion), stored as
+// the B operands of v_mfma_f32_16x16x32_bf16 for two 16-column tiles, [hi
+// e0..7 | mid e0..7] and [lo e0..7 | 0].  Wave w of 8 then runs K steps 2w, 2w+1 of
+// the chunk: A fragments from the staged rows, 2 MFMAs per step, fp32
+// accumulation (three exact products per element: an fp32 dot product up to
+// summation order).  The loads of the next RL_DEPTH chunks (activations and
+// weights, in chunk order, so the in-order completion of loads never makes a
+// chunk wait for a later one) are in flight while a chunk is computed; the LDS
+// is double-buffered, so one barrier per chunk suffices.  At the end a lane adds
+// its hi column, the mid column one lane over and its lo column, the waves'
+// sums are added in wave order, and one thread per token selects.
 //
-// route_mfma8_kernel: 8 waves; wave w takes K steps [16 w, 16 w + 16) of every
-// chunk of 128 steps and issues all activation and operand loads of the chunk
-// before its first MFMA.  Per (token, expert) a lane adds its hi column, the mid
-// column one lane over and its lo column; the waves' partials are summed in wave
-// order in LDS, then each wave selects two tokens and counts the chosen experts
-// into the block's dispatch counts (integer adds: order-independent).
-constexpr int M8_TOK = 16;                        // tokens per workgroup
-constexpr int M8_WAVES = 8;
-constexpr int M8_THREADS = 64 * M8_WAVES;
-constexpr int M8_STEPS = 16;                      // K steps of 32 per wave per chunk
-constexpr int M8_CHUNK = M8_WAVES * M8_STEPS;     // K steps per chunk (4096 elements)
+// The status word needs no clearing launch: a workgroup that finds a
+// non-finite score raises a flag in the sync words, every workgroup then counts
+// itself done, and the last one writes the status from the flag and puts both
+// words back to zero (relaxed device-scope atomics; the flag's atomic completes
+// before the count's is issued).
+constexpr int RL_TOK = MOE_ROUTE_TOK;               // tokens per workgroup
+constexpr int RL_KC = 512;                          // K elements per chunk
+constexpr int RL_STEPS = RL_KC / 32;                // MFMA K steps per chunk
+constexpr int RL_ROW = RL_KC * 2 + 16;              // LDS bytes per staged row (padded: conflict-free A reads)
+constexpr int RL_DEPTH = 4;                         // chunks of loads in flight
+constexpr int RL_WAVES = 8;                         // K steps of a chunk split over the waves
+constexpr int RL_THREADS = 64 * RL_WAVES;
+constexpr int RL_XU = RL_TOK * (RL_KC / 8) / RL_THREADS;   // 16-byte activation units per thread and chunk
+constexpr int RL_WI = 8 * RL_STEPS * 4 / RL_THREADS;       // 8-weight items per thread and chunk
+constexpr int RL_SPW = RL_STEPS / RL_WAVES;                 // K steps per wave and chunk
 
-__host__ __device__ inline int m8_steps(int d) { return (d + 31) / 32; }
+// LDS slot of B-operand entry (step s, lane' l) inside its 64-entry tile: l with
+// its low three bits XORed by ((l >> 4) & 3) | ((s & 1) << 2).  A wave reading a
+// tile (lane' = lane) still covers 8 distinct bank groups per 8 lanes (the XOR is
+// constant over them), and a wave writing the planes of one expert (8 lanes = 4
+// groups of 8 x 2 steps) does too: no bank conflicts either way.
+__device__ __forceinline__ int rl_slot(int s, int l) { return l ^ (((l >> 4) & 3) | ((s & 1) << 2)); }
 
-__global__ __launch_bounds__(256) void route_prep_kernel(const float* __restrict__ w_r, int d, int E,
-                                                         uint4* __restrict__ bop, int NS,
-                                                         int32_t* __restrict__ status, int32_t* __restrict__ hist,
-                                                         int64_t nhist, int32_t* __restrict__ acc_stats) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i == 0) *status = MOE_OK;
-    if (acc_stats && i < 2) acc_stats[i] = 0;
-    if (hist)
-        for (int64_t h = i; h < nhist; h += (int64_t)gridDim.x * blockDim.x) hist[h] = 0;
-    if (i >= (int64_t)NS * 128) return;
-    const int s = (int)(i / 128), tile = (int)(i / 64) % 2, lane = (int)(i % 64);
-    const int c = lane % 16, e = c % 8, kk = 32 * s + 8 * (lane / 16);
-    uint4 out = {0u, 0u, 0u, 0u};
-    if (e < E && kk < d && (tile == 0 || c < 8)) {   // d % 8 == 0: a group of 8 is wholly in or out
-        const float4* src = reinterpret_cast<const float4*>(w_r + (int64_t)e * d + kk);
-        uint4 H, M, L;
-        split3(src[0], src[1], H, M, L);
-        out = tile == 1 ? L : (c < 8 ? H : M);
+// Split 8 fp32 weights into three bf16 vectors whose sum reproduces them exactly
+// (round to nearest even at each level).
+__device__ __forceinline__ void split3_rne(const float4 w0, const float4 w1, uint4& H, uint4& M, uint4& L) {
+    const float v[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    uint32_t h[4], m[4], l[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        h[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
+        const float r0 = v[2 * j] - __uint_as_float(h[j] << 16);
+        const float r1 = v[2 * j + 1] - __uint_as_float(h[j] & 0xffff0000u);
+        m[j] = pack_bf16x2(r0, r1);
+        const float s0 = r0 - __uint_as_float(m[j] << 16);
+        const float s1 = r1 - __uint_as_float(m[j] & 0xffff0000u);
+        l[j] = pack_bf16x2(s0, s1);
     }
-    bop[i] = out;
+    H = {h[0], h[1], h[2], h[3]};
+    M = {m[0], m[1], m[2], m[3]};
+    L = {l[0], l[1], l[2], l[3]};
 }
 
-__global__ __launch_bounds__(M8_THREADS) void route_mfma8_kernel(const uint16_t* __restrict__ x,
-                                                                 const uint4* __restrict__ bop,
-                                                                 const float* __restrict__ b_r, int64_t T, int d,
-                                                                 int E, int k, int mode,
-                                                                 int32_t* __restrict__ topk_ids,
-                                                                 float* __restrict__ topk_w,
-                                                                 int32_t* __restrict__ status,
-                                                                 float* __restrict__ probs,
-                                                                 int32_t* __restrict__ hist) {
-    __shared__ float part[M8_WAVES * M8_TOK * 8];
-    __shared__ float lg[M8_TOK * 8];
-    __shared__ int cnt[8];
+// Selection for one token whose (at most 8) scores one thread holds, bias
+// included: min(kout, E) rounds of an arg-max in ascending id order with a
+// strict comparison (equal scores keep the lower id); the first k are the
+// selection, the rest the next choices (reroute).  Weights: RENORM the softmax
+// over the selected k (a next choice: its exponential over the same sum),
+// SWITCH the full softmax.  A non-finite token gets ids 0..k-1 (then -1) and
+// weights 0.  Returns the selected experts as a bit mask.
+__device__ uint32_t select8_thread(const float (&v)[8], bool bad, int E, int k, int kout, int mode, int64_t t,
+                                   int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
+                                   float* __restrict__ probs) {
+    const int rounds = min(kout, E);
+    uint32_t taken = 0, sel = 0;
+    int ids[8];
+    float gs[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        ids[r] = -1;
+        gs[r] = 0.f;
+        if (r < rounds) {
+            int best = 0;
+            uint32_t bkey = 0;
+            float bval = 0.f;
+            bool have = false;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if (e < E && !((taken >> e) & 1u)) {
+                    const uint32_t key = float_order_key(v[e]);
+                    if (!have || key > bkey) {
+                        have = true;
+                        best = e;
+                        bkey = key;
+                        bval = v[e];
+                    }
+                }
+            }
+            taken |= 1u << best;
+            if (r < k) sel = taken;
+            ids[r] = best;
+            gs[r] = bval;
+        }
+    }
+    const float g_top = gs[0];
+    float zall = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        if (e < E) zall += expf(v[e] - g_top);
+    float zs = 0.f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+        if (r < k) zs += expf(gs[r] - g_top);
+    const float z = mode == MOE_GATE_SWITCH ? zall : zs;
+    for (int r = 0; r < kout; ++r) {
+        int id = -1;
+        float wt = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            if (q == r && q < rounds) {
+                id = ids[q];
+                wt = expf(gs[q] - g_top) / z;
+            }
+        if (bad) {
+            id = r < k ? r : -1;
+            wt = 0.f;
+        }
+        topk_ids[t * kout + r] = id;
+        topk_w[t * kout + r] = wt;
+    }
+    if (probs) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (e < E) probs[t * E + e] = bad ? 0.f : expf(v[e] - g_top) / zall;
+    }
+    return bad ? (1u << k) - 1u : sel;
+}
+
+template <int NCT>   // chunks, fully unrolled (chunks past d are zero chunks)
+__global__ __launch_bounds__(RL_THREADS) void route_lds8_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ w_r, const float* __restrict__ b_r, int64_t T, int d,
+    int E, int k, int kout, int mode, int32_t* __restrict__ sync, int32_t* __restrict__ topk_ids,
+    float* __restrict__ topk_w, int32_t* __restrict__ status, float* __restrict__ probs, int32_t* __restrict__ hist,
+    int32_t* __restrict__ acc_stats) {
+    __shared__ __align__(16) unsigned char xs[2][RL_TOK * RL_ROW];
+    __shared__ uint4 bs[2][RL_STEPS * 128];
+    __shared__ float red[RL_WAVES][RL_TOK * 8];
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
-    const int lr = lane % 16, grp = lane / 16;   // A: token row lr; B and D: column lr
-    if (tid < 8) cnt[tid] = 0;
-    const int64_t t0 = (int64_t)blockIdx.x * M8_TOK;
-    // rows past T repeat row T - 1 (never selected)
-    const uint16_t* xrow = x + min(t0 + lr, T - 1) * (int64_t)d;
-    const int NS = m8_steps(d);
-    floatx4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = wave * M8_STEPS; s0 < NS; s0 += M8_CHUNK) {
-        // Every load is unconditional from a clamped, valid address, so all of them
-        // are in flight together; activation groups past d (or past the last step)
-        // are zeroed afterwards, and the operands there are 0 (the prep wrote
-        // zeros) or a repeat of the last step (multiplied by the zeroed activations).
-        uint4 xv[M8_STEPS], b0[M8_STEPS], b1[M8_STEPS];
+    const int64_t t0 = (int64_t)blockIdx.x * RL_TOK;
+    const int NC = (d + RL_KC - 1) / RL_KC;   // <= NCT
+    if (acc_stats && blockIdx.x == 0 && tid < 2) acc_stats[tid] = 0;
+    // the zero quarter of the second column tile (lanes 16 q + 8..15) never changes
+    for (int i = tid; i < 2 * RL_STEPS * 32; i += RL_THREADS) {
+        const int b = i / (RL_STEPS * 32), r = i % (RL_STEPS * 32), s = r / 32, z = r % 32;
+        bs[b][s * 128 + 64 + rl_slot(s, 16 * (z / 8) + 8 + z % 8)] = uint4{0u, 0u, 0u, 0u};
+    }
+    // Loads of chunk c, every one unconditional from a clamped, valid address (a
+    // chunk past the last repeats it, a unit past d reads the row's last 16 bytes
+    // and is zeroed when stored).  Activations: unit u = tid + 256 i of the chunk's
+    // 16 rows x 64 units of 16 bytes (row u / 64).  Weights: item it = tid + 256 j
+    // of 8 experts x 16 steps x 4 groups of 8 (expert it / 64, step (it / 4) % 16,
+    // group it % 4), 32 bytes each.
+    uint4 xr[RL_DEPTH][RL_XU];
+    float4 wr[RL_DEPTH][RL_WI][2];
+    auto issue = [&](int slot, int c) {
+        const int cc = min(c, NC - 1);
 #pragma unroll
-        for (int j = 0; j < M8_STEPS; ++j) {
-            const int kk = min(32 * min(s0 + j, NS - 1) + 8 * grp, d - 8);
-            xv[j] = *reinterpret_cast<const uint4*>(xrow + kk);
+        for (int i = 0; i < RL_XU; ++i) {
+            const int u = tid + RL_THREADS * i;
+            const int64_t row = min(t0 + u / 64, T - 1);
+            const int kk = min(cc * RL_KC + 8 * (u % 64), d - 8);
+            xr[slot][i] = *reinterpret_cast<const uint4*>(x + row * d + kk);
         }
 #pragma unroll
-        for (int j = 0; j < M8_STEPS; ++j) {
-            const int64_t s = min(s0 + j, NS - 1);
-            b0[j] = bop[s * 128 + lane];
-            b1[j] = bop[s * 128 + 64 + lane];
+        for (int j = 0; j < RL_WI; ++j) {
+            const int it = tid + RL_THREADS * j;
+            const int e = min(it / 64, E - 1);
+            const int kk = min(cc * RL_KC + 32 * ((it / 4) % RL_STEPS) + 8 * (it % 4), d - 8);
+            const float4* src = reinterpret_cast<const float4*>(w_r + (int64_t)e * d + kk);
+            wr[slot][j][0] = src[0];
+            wr[slot][j][1] = src[1];
         }
+        // keep the loads in chunk order: the in-order completion count then waits
+        // for exactly the chunk in hand
+        __builtin_amdgcn_sched_barrier(0);
+    };
 #pragma unroll
-        for (int j = 0; j < M8_STEPS; ++j) {
-            if (!(s0 + j < NS && 32 * (s0 + j) + 8 * grp < d)) xv[j] = uint4{0u, 0u, 0u, 0u};
+    for (int u = 0; u < RL_DEPTH; ++u) issue(u, u);
+    floatx4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    const int lr = lane % 16, grp = lane / 16;
+    // Straight-line code over the chunks (no loop back-edge, no branch on loaded
+    // data), so the compiler's load counting waits for exactly the chunk in hand.
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) {
+        const int u = c % RL_DEPTH, buf = c & 1;
+        // activations of chunk c -> LDS rows (units past d zeroed by a mask, which
+        // the compiler cannot turn into a conditional load)
+#pragma unroll
+        for (int i = 0; i < RL_XU; ++i) {
+            const int uu = tid + RL_THREADS * i;
+            const uint32_t keep = c * RL_KC + 8 * (uu % 64) < d ? 0xffffffffu : 0u;
+            const uint4 v = xr[u][i];
+            *reinterpret_cast<uint4*>(&xs[buf][(uu / 64) * RL_ROW + (uu % 64) * 16]) =
+                uint4{v.x & keep, v.y & keep, v.z & keep, v.w & keep};
         }
+        // weights of chunk c -> planes (zero for experts >= E and K past d)
 #pragma unroll
-        for (int j = 0; j < M8_STEPS; ++j) {
-            a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xv[j]), as_bf16x8(b0[j]), a0, 0, 0, 0);
-            a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xv[j]), as_bf16x8(b1[j]), a1, 0, 0, 0);
+        for (int j = 0; j < RL_WI; ++j) {
+            const int it = tid + RL_THREADS * j;
+            const int e = it / 64, s = (it / 4) % RL_STEPS, q = it % 4;
+            uint4 H, M, Lo;   // split unconditionally, zeroed by a mask
+            split3_rne(wr[u][j][0], wr[u][j][1], H, M, Lo);
+            const uint32_t keep = e < E && c * RL_KC + 32 * s + 8 * q < d ? 0xffffffffu : 0u;
+            uint4* b = &bs[buf][s * 128];
+            b[rl_slot(s, 16 * q + e)] = uint4{H.x & keep, H.y & keep, H.z & keep, H.w & keep};
+            b[rl_slot(s, 16 * q + e + 8)] = uint4{M.x & keep, M.y & keep, M.z & keep, M.w & keep};
+            b[64 + rl_slot(s, 16 * q + e)] = uint4{Lo.x & keep, Lo.y & keep, Lo.z & keep, Lo.w & keep};
+        }
+        if (c + RL_DEPTH < NCT) issue(u, c + RL_DEPTH);   // the ring slot just emptied
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < RL_SPW; ++j) {
+            const int s = RL_SPW * wave + j;
+            const uint4 a = *reinterpret_cast<const uint4*>(&xs[buf][lr * RL_ROW + (32 * s + 8 * grp) * 2]);
+            const uint4 b0 = bs[buf][s * 128 + rl_slot(s, lane)], b1 = bs[buf][s * 128 + 64 + rl_slot(s, lane)];
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b0), acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b1), acc1, 0, 0, 0);
         }
     }
     // lane (lr, grp) holds column lr of both tiles for tokens 4 grp + i
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const float mid = __shfl_xor(a0[i], 8, MOE_WAVE);
-        if (lr < 8) part[(wave * M8_TOK + 4 * grp + i) * 8 + lr] = (a0[i] + mid) + a1[i];
+        const float mid = __shfl_xor(acc0[i], 8, MOE_WAVE);
+        if (lr < 8) red[wave][(4 * grp + i) * 8 + lr] = (acc0[i] + mid) + acc1[i];
     }
     __syncthreads();
-    if (tid < M8_TOK * 8) {
-        float sc = 0.f;
-#pragma unroll
-        for (int w = 0; w < M8_WAVES; ++w) sc += part[w * M8_TOK * 8 + tid];
-        lg[tid] = sc;
-    }
-    __syncthreads();
-    for (int r = wave; r < M8_TOK; r += M8_WAVES) {
+    if (wave == 0) {
+        // one thread per token: the waves' sums in wave order, bias, selection
+        const int r = lane;
         const int64_t t = t0 + r;
-        if (t >= T) break;
-        select_token<1>(lg + r * 8, b_r, E, k, mode, t, topk_ids, topk_w, status, probs, hist ? cnt : nullptr);
-    }
-    if (hist) {   // uniform: every thread reaches the barrier
-        __syncthreads();
-        if (tid < E && cnt[tid]) atomicAdd(&hist[(t0 / MOE_DISPATCH_BLOCK) * E + tid], cnt[tid]);
+        const bool valid = r < RL_TOK && t < T;
+        float v[8];
+        bool bad = false;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            v[e] = -INFINITY;
+            if (e < E && valid) {
+                const int p = r * 8 + e;
+                float sum = red[0][p];
+#pragma unroll
+                for (int w = 1; w < RL_WAVES; ++w) sum += red[w][p];
+                v[e] = sum + (b_r ? b_r[e] : 0.f);
+                bad |= !isfinite(v[e]);
+            }
+        }
+        uint32_t sel = 0;
+        if (valid) sel = select8_thread(v, bad, E, k, kout, mode, t, topk_ids, topk_w, probs);
+        if (hist) {   // this workgroup's selection count per expert, for the dispatch
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int cnt = __popcll(__ballot((sel >> e) & 1u));
+                if (e < E && lane == e) hist[(int64_t)blockIdx.x * E + e] = cnt;
+            }
+        }
+        if (__any(bad) && lane == 0) {
+            atomicOr(&sync[1], 1);
+            __builtin_amdgcn_s_waitcnt(0);   // the flag is in before this workgroup counts itself done
+        }
+        if (lane == 0 && atomicAdd(&sync[0], 1) == (int)gridDim.x - 1) {   // the last workgroup
+            *status = atomicExch(&sync[1], 0) ? MOE_ERR_NONFINITE_LOGIT : MOE_OK;
+            atomicExch(&sync[0], 0);
+        }
     }
 }
 
@@ -777,11 +934,16 @@ __global__ __launch_bounds__(1024) void prob_column_sum_kernel(const float* __re
 
 namespace moe_kernels {
 
+// route_lds8_kernel serves bf16 layers with E <= 8 and T > 16.
+bool route_lds8_ok(const moe_dims& s) {
+    return s.dtype == MOE_BF16 && s.E <= 8 && s.T > DOT_TMAX && s.d <= 32 * RL_KC;
+}
+
 size_t route_ws_bytes(const moe_dims& s) {
     if (s.dtype != MOE_BF16) return s.E > 64 ? (size_t)s.T * s.E * sizeof(float) : 0;
     if (s.T <= DOT_TMAX)   // front_small_kernel (E <= 8), else route_dot_kernel's partials
         return s.E <= 8 ? 0 : (size_t)((s.d + 2047) / 2048) * s.T * s.E * sizeof(float);
-    if (s.E <= 8) return (size_t)m8_steps(s.d) * 128 * sizeof(uint4);   // route_mfma8_kernel operands
+    if (route_lds8_ok(s)) return 0;   // the sync words only
     const int N3 = score_cols(s.E);
     size_t planes = ((size_t)N3 * s.d * 2 + 255) & ~(size_t)255;
     if (s.E <= 64) return planes;
@@ -831,8 +993,8 @@ hipError_t launch_front(const moe_dims& s, const void* x, const float* w_r, cons
 }
 
 hipError_t launch_route(const moe_dims& s, const void* x, const float* w_r, const float* b_r, int32_t* topk_ids,
-                        float* topk_w, int32_t* status, void* ws, hipStream_t st, float* probs, int32_t* hist,
-                        bool* hist_done, int32_t* acc_stats) {
+                        float* topk_w, int32_t* status, void* ws, int32_t* sync, hipStream_t st, float* probs,
+                        int32_t* hist, bool* hist_done, int32_t* acc_stats) {
     if (s.T == 0) {
         hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(64), 0, st, status, 1);
         return hipGetLastError();
@@ -840,20 +1002,22 @@ hipError_t launch_route(const moe_dims& s, const void* x, const float* w_r, cons
     if (s.dtype == MOE_BF16 && s.T <= FS_TOK && s.E <= FS_EMAX)
         return launch_front_small<false>(s, x, w_r, b_r, topk_ids, topk_w, status, probs, ws, st, nullptr, nullptr,
                                          nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0);
-    if (s.dtype == MOE_BF16 && s.E <= 8) {
-        const int NS = m8_steps(s.d);
-        const bool count = hist != nullptr;
-        const int64_t nhist = count ? (s.T + MOE_DISPATCH_BLOCK - 1) / MOE_DISPATCH_BLOCK * s.E : 0;
-        hipLaunchKernelGGL(route_prep_kernel, dim3((unsigned)((NS * 128 + 255) / 256)), dim3(256), 0, st, w_r, s.d,
-                           s.E, static_cast<uint4*>(ws), NS, status, count ? hist : nullptr, nhist,
-                           count ? acc_stats : nullptr);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(route_mfma8_kernel, dim3((unsigned)((s.T + M8_TOK - 1) / M8_TOK)), dim3(M8_THREADS), 0,
-                           st, static_cast<const uint16_t*>(x), static_cast<const uint4*>(ws), b_r, s.T, s.d, s.E,
-                           s.k, s.gate_mode, topk_ids, topk_w, status, probs, count ? hist : nullptr);
-        e = hipGetLastError();
-        if (e == hipSuccess && count && hist_done) *hist_done = true;
+    if (route_lds8_ok(s)) {
+        const unsigned grid = (unsigned)((s.T + RL_TOK - 1) / RL_TOK);
+        const int NC = (s.d + RL_KC - 1) / RL_KC;
+#define MOE_LDS8(NCV)                                                                                           \
+    hipLaunchKernelGGL((route_lds8_kernel<NCV>), dim3(grid), dim3(RL_THREADS), 0, st,                            \
+                       static_cast<const uint16_t*>(x), w_r, b_r, s.T, s.d, s.E, s.k, moe_paths(s), s.gate_mode, \
+                       sync, topk_ids, topk_w, status, probs, hist, hist ? acc_stats : nullptr)
+        if (NC <= 1) MOE_LDS8(1);
+        else if (NC <= 2) MOE_LDS8(2);
+        else if (NC <= 4) MOE_LDS8(4);
+        else if (NC <= 8) MOE_LDS8(8);
+        else if (NC <= 16) MOE_LDS8(16);
+        else MOE_LDS8(32);
+#undef MOE_LDS8
+        const hipError_t e = hipGetLastError();
+        if (e == hipSuccess && hist && hist_done) *hist_done = true;
         return e;
     }
     // The status word is cleared before any selection may set it: by the plane split

@@ -35,7 +35,7 @@ def test_capacity_helper_exact_ceiling():
 
 def _shape(**kw):
     base = dict(T=4096, d=4096, m=14336, E=8, k=2, capacity=0, gate_mode=0, dtype=1, m_shared=0,
-                accept_by_gate=0, renorm_survivors=0)
+                accept_by_gate=0, renorm_survivors=0, reroute=0)
     base.update(kw)
     return L.MoeShape(*[base[f] for f, _ in L.MoeShape._fields_])
 
@@ -56,6 +56,8 @@ def test_shape_checks():
     assert L.moe_check_shape(_shape(accept_by_gate=1, renorm_survivors=1)) == L.MOE_OK
     assert L.moe_check_shape(_shape(accept_by_gate=2)) == L.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_check_shape(_shape(renorm_survivors=-1)) == L.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_check_shape(_shape(reroute=2)) == L.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_check_shape(_shape(reroute=1)) == L.MOE_ERR_UNSUPPORTED
 
 
 def test_max_rows_and_workspace():
@@ -80,16 +82,20 @@ def test_max_rows_and_workspace():
 
 
 def test_route_workspace_by_path():
-    """The router's workspace follows its path: none for the one-workgroup front
-    of small batches with E <= 8, the MFMA operand planes (2 KB per 32 elements of
-    d) above 16 tokens, the split-K partial scores for small batches with E > 8."""
+    """The router's workspace is the sync words (MOE_SYNC_BYTES) plus what its path
+    needs: nothing for E <= 8 with bf16 activations (the one-workgroup front of
+    small batches, and above 16 tokens the kernel that splits w_r itself), the
+    split-K partial scores for small batches with E > 8, the three bf16 planes of
+    w_r for 8 < E <= 64 above 16 tokens."""
     route = lambda **kw: L.moe_workspace_bytes(_shape(**kw), L.MOE_WS_ROUTE)
-    align = 256
-    assert route(T=16, E=8) == align                          # no workspace (+ alignment slack)
-    assert route(T=17, E=8) >= 4096 // 32 * 2048
-    assert route(T=17, d=4104, E=8) >= (4104 + 31) // 32 * 2048
-    assert route(T=16, E=64, k=8) >= 2 * 16 * 64 * 4          # two 2048-wide K ranges of fp32 partials
-    assert route(T=16, E=8, dtype=0) == align                 # fp32 with E <= 64: scores in registers
+    align, sync = 256, L.MOE_SYNC_BYTES
+    assert route(T=16, E=8) == sync + align
+    assert route(T=17, E=8) == sync + align
+    assert route(T=4096, E=8) == sync + align
+    assert route(T=1024, d=1024, E=8, k=1) == sync + align
+    assert route(T=16, E=64, k=8) >= sync + 2 * 16 * 64 * 4   # two 2048-wide K ranges of fp32 partials
+    assert route(T=100, E=40, k=4) >= sync + 3 * 40 * 4096 * 2  # hi, mid, lo planes
+    assert route(T=16, E=8, dtype=0) == sync + align           # fp32 with E <= 64: scores in registers
 
 
 def test_ffn_workspace_by_path():

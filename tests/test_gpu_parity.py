@@ -4,8 +4,11 @@ same seeded inputs, with the staged protocol:
   2. dispatch: the GPU's ids through the oracle's serial slot loop give the GPU's
      slots, row map, loads, offsets, grouped rows and statistics bit for bit;
   3. FFN + combine: y within 1e-5 (fp32 layers) or 2e-2 (bf16 layers) of the
-     oracle's, relative to 1 + |y_ref|, on every element (or on sampled tokens
-     at the full Mixtral / Qwen3 / DeepSeek-V3 sizes).
+     oracle's, relative to 1 + |y_ref|, on every element of every layer,
+     including the full Mixtral / Qwen3 / DeepSeek-V3 sizes;
+  4. end to end: where the GPU's ids equal the oracle's on every token, the
+     oracle evaluates the layer on its own routing; only where a near-tie
+     flipped a selection does it take the GPU's ids (reported).
 """
 import json
 import os
@@ -18,10 +21,10 @@ import torch
 from conftest import GOLDEN
 from oracle import moe_oracle as O
 from parity_helpers import (BF16_TOL, F32_TOL, check_output, compare_dispatch, compare_route, expert_provider, log,
-                            np64, oracle_capacity, pick_tokens, shape_of)
+                            np64, oracle_capacity, shape_of)
 from sparse_mixture_experts_23_amd import _lib as L
 from sparse_mixture_experts_23_amd import api
-from sparse_mixture_experts_23_amd.workloads import CONFIGS, MoEConfig, make_inputs
+from sparse_mixture_experts_23_amd.workloads import CONFIGS, MoEConfig, MoEInputs, make_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -35,9 +38,10 @@ def _free_memory():
     torch.cuda.empty_cache()
 
 
-def run_layer(cfg: MoEConfig, seed: int = 0, sample: int = 0):
+def run_layer(cfg: MoEConfig, seed: int = 0, inp=None):
     log(f"[parity] {cfg.name} T={cfg.T} d={cfg.d} m={cfg.m} E={cfg.E} k={cfg.k} dtype={cfg.dtype} seed={seed}")
-    inp = make_inputs(cfg, seed, device=DEV)
+    if inp is None:
+        inp = make_inputs(cfg, seed, device=DEV)
     shape = shape_of(cfg)
     # staged calls through the C-ABI
     ids, w, status = api.route(shape, inp.x, inp.w_r, inp.b_r)
@@ -63,22 +67,22 @@ def run_layer(cfg: MoEConfig, seed: int = 0, sample: int = 0):
     rep = compare_route(cfg, rt, ids_np, w_np)
     C = oracle_capacity(cfg) or cfg.T
     dref = compare_dispatch(cfg, ids_np, C, disp, inp.x, w_np.astype(np.float32))
-    tokens = pick_tokens(cfg.T, sample, dref) if sample else None
     shared = None
     if cfg.m_shared:
         shared = (inp.s_gate.float().cpu().numpy(), inp.s_up.float().cpu().numpy(), inp.s_down.float().cpu().numpy())
+    # end to end on the oracle's own routing unless a near-tie changed an id
+    e2e = bool((ids_np == rt.ids).all())
     res = O.forward(x64, wr, b, expert_provider(inp), cfg.k, cfg.gate_mode, C=oracle_capacity(cfg), shared=shared,
-                    round_h_bf16=cfg.dtype == "bf16", renorm_form=cfg.renorm_form, tokens=tokens,
-                    ids_override=ids_np, accept_by_gate=cfg.accept_by_gate,
+                    round_h_bf16=cfg.dtype == "bf16", renorm_form=cfg.renorm_form,
+                    ids_override=None if e2e else ids_np, accept_by_gate=cfg.accept_by_gate,
                     renorm_survivors=cfg.renorm_survivors, accept_weights=w_np.astype(np.float32))
-    y_gpu = np64(y)
-    if tokens is not None:
-        y_gpu = y_gpu[tokens]
+    if e2e:
+        np.testing.assert_array_equal(disp.slot.cpu().numpy(), res.dispatch.slot)
     tol = F32_TOL if cfg.dtype == "f32" else BF16_TOL
-    worst = check_output(y_gpu, res.y, tol, cfg.name)
-    log(f"[parity] {cfg.name}: ok  max rel err {worst:.2e}  near-ties {rep.near_ties}  flips "
-        f"{len(rep.flipped_tokens)}  O={dref.overflow} A={int(dref.offsets[-1])} rho_max={dref.rho_max:.3f} "
-        f"dropped={dref.tokens_dropped}")
+    worst = check_output(np64(y), res.y, tol, cfg.name)
+    log(f"[parity] {cfg.name}: ok  all {cfg.T}x{cfg.d} outputs, max rel err {worst:.2e}  near-ties {rep.near_ties}  "
+        f"flips {len(rep.flipped_tokens)}  ({'oracle route' if e2e else 'GPU ids'})  O={dref.overflow} "
+        f"A={int(dref.offsets[-1])} rho_max={dref.rho_max:.3f} dropped={dref.tokens_dropped}")
     return dict(inp=inp, shape=shape, y=y, ids=ids, disp=disp, dref=dref)
 
 
@@ -330,7 +334,7 @@ def _random_large_configs(n: int = 8, seed: int = 5):
 
 @pytest.mark.parametrize("cfg", _random_large_configs(), ids=lambda c: c.name)
 def test_parity_random_large_shapes(cfg):
-    run_layer(cfg, sample=48)
+    run_layer(cfg)
 
 
 def test_dense_k_equal_E_matches_dense_brute_force():
@@ -346,12 +350,12 @@ def test_dense_k_equal_E_matches_dense_brute_force():
 
 
 # ---------------------------------------------------------------------------
-# the pages' model shapes at full size (sampled output rows)
+# the pages' model shapes at full size (every output element)
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name,sample", [("mixtral", 12), ("qwen3_like", 12), ("dsv3_like", 5)])
-def test_parity_full_size(name, sample):
-    out = run_layer(CONFIGS[name], sample=sample)
+@pytest.mark.parametrize("name", ["mixtral", "qwen3_like", "dsv3_like"])
+def test_parity_full_size(name):
+    out = run_layer(CONFIGS[name])
     st = out["disp"].stats.cpu().numpy()
     load = out["disp"].load.cpu().numpy()
     assert int(load.sum()) == CONFIGS[name].T * CONFIGS[name].k        # sum of requests = T k
@@ -365,10 +369,104 @@ DSV3_SMALL = MoEConfig("dsv3_small_decode", T=2, d=1024, m=512, E=64, k=8, dtype
 
 
 @pytest.mark.parametrize("cfg", [CONFIGS["mixtral"].with_tokens(1), CONFIGS["mixtral"].with_tokens(8),
-                                 DSV3_SMALL, DSV3_SMALL.with_tokens(16)],
-                         ids=["mixtral_T1", "mixtral_T8", "dsv3_small_T2", "dsv3_small_T16"])
+                                 CONFIGS["mixtral"].with_tokens(64), DSV3_SMALL, DSV3_SMALL.with_tokens(16)],
+                         ids=["mixtral_T1", "mixtral_T8", "mixtral_T64", "dsv3_small_T2", "dsv3_small_T16"])
 def test_parity_decode(cfg):
     run_layer(cfg)
+
+
+def test_parity_decode_dsv3_full_shape():
+    """The DeepSeek-V3-like layer (d=7168, E=256, k=8, m=2048, shared expert
+    m=2048) at decode batch sizes T = 1, 8 and 16: grouped GEMVs (T <= 8) and
+    the K-split tiled path (T = 16), every output element against the oracle.
+    One draw of the 22.5 GB of expert weights serves the three batch sizes; x is
+    the first T rows of a 16-token draw."""
+    cfg16 = CONFIGS["dsv3_like"].with_tokens(16)
+    inp = make_inputs(cfg16, 0, device=DEV)
+    for T in (1, 8, 16):
+        sub = MoEInputs(**{**inp.__dict__, "cfg": cfg16.with_tokens(T), "x": inp.x[:T].contiguous()})
+        run_layer(cfg16.with_tokens(T), inp=sub)
+
+
+# ---------------------------------------------------------------------------
+# exact score ties: the lower expert id wins, on every router path
+# ---------------------------------------------------------------------------
+
+# (name, T, d, E, k, dtype, bias): one case per router path of moe_route / moe_forward
+TIE_CASES = [
+    ("mfma_e8", 300, 512, 8, 2, "bf16", "none"),          # E <= 8, T > 16: plane-split MFMA scores
+    ("mfma_e6_signed_zero_bias", 200, 256, 6, 3, "bf16", "signed_zero"),
+    ("small_e40", 200, 256, 40, 4, "bf16", "group"),       # 8 < E <= 64: fused MFMA kernel
+    ("gemm_e100", 200, 256, 100, 8, "bf16", "none"),       # E > 64: score GEMM + selection
+    ("gemm_e300", 150, 256, 300, 8, "bf16", "signed_zero"),
+    ("front_e8", 12, 512, 8, 2, "bf16", "none"),           # T <= 16, E <= 8: one-workgroup front
+    ("front_e40", 10, 520, 40, 4, "bf16", "group"),        # T <= 16, E > 8: dot kernel + front
+    ("dot_select_e300", 9, 256, 300, 8, "bf16", "none"),   # T <= 16, E > 256: dot kernel + selection
+    ("f32_small_e16", 100, 128, 16, 3, "f32", "signed_zero"),   # fp32 activations, E <= 64
+    ("f32_select_e100", 100, 128, 100, 5, "f32", "group"),       # fp32 activations, E > 64
+]
+
+
+def _tie_inputs(name, T, d, E, k, dtype, bias, seed=0):
+    """Integer-valued activations and router weights (|x|, |w| <= 2), so every
+    score is an integer below 2^24 and exact in fp32 whatever the summation
+    order, on both sides.  Router rows are duplicated across scattered expert
+    ids (equal scores for every token), some tokens are all zero (all E scores
+    tie) and the signed-zero bias mixes -0.0 and +0.0."""
+    rng = np.random.default_rng(1000 + seed)
+    cfg = MoEConfig("ties_" + name, T=T, d=d, m=64, E=E, k=k, dtype=dtype, gate_mode=0, cf=None, cfg_id=60)
+    inp = make_inputs(cfg, seed, DEV)
+    n_base = max(1, (E + 2) // 3)
+    base = rng.integers(-2, 3, size=(n_base, d)).astype(np.float32)
+    grp = rng.integers(0, n_base, size=E)
+    w_r = base[grp]
+    x = rng.integers(-2, 3, size=(T, d)).astype(np.float32)
+    x[rng.choice(T, size=max(1, T // 10), replace=False)] = 0.0
+    if bias == "signed_zero":
+        b = np.where(rng.random(E) < 0.5, -0.0, 0.0).astype(np.float32)
+    elif bias == "group":
+        b = (grp % 3 - 1).astype(np.float32)       # equal within a group of duplicated rows
+    else:
+        b = None
+    inp.x = torch.from_numpy(x).to(DEV).to(cfg.torch_dtype)
+    inp.w_r = torch.from_numpy(np.ascontiguousarray(w_r)).to(DEV)
+    inp.b_r = None if b is None else torch.from_numpy(b).to(DEV)
+    return cfg, inp
+
+
+@pytest.mark.parametrize("case", TIE_CASES, ids=[c[0] for c in TIE_CASES])
+def test_exact_ties_lower_id_wins(case):
+    """Algorithm 36.1's selection step orders equal scores by ascending expert
+    id.  With exact integer scores there is no rounding to excuse a mismatch, so
+    the ids of moe_route and of moe_forward must equal the oracle's bit for bit
+    on every token (no near-tie exemption), and the layer must match the oracle
+    end to end on the oracle's own routing."""
+    cfg, inp = _tie_inputs(*case)
+    log(f"[ties] {cfg.name} T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} dtype={cfg.dtype}")
+    shape = shape_of(cfg)
+    x64 = np64(inp.x)
+    wr = inp.w_r.cpu().numpy()
+    b = None if inp.b_r is None else inp.b_r.cpu().numpy()
+    rt = O.route(x64, wr, b, cfg.k, cfg.gate_mode, cfg.renorm_form)
+    # the inputs really tie: at the set boundary and inside the selected set
+    srt = -np.sort(-rt.g32, axis=1)
+    at_boundary = int((srt[:, cfg.k - 1] == srt[:, cfg.k]).sum()) if cfg.k < cfg.E else 0
+    in_set = int((srt[:, : cfg.k - 1] == srt[:, 1: cfg.k]).any(axis=1).sum()) if cfg.k > 1 else 0
+    assert at_boundary > 0 and in_set > 0
+    assert (rt.g64 == rt.g32).all(), "integer scores must be exact in fp32"
+    ids, w, status = api.route(shape, inp.x, inp.w_r, inp.b_r)
+    torch.cuda.synchronize()
+    assert int(status.item()) == L.MOE_OK
+    np.testing.assert_array_equal(ids.cpu().numpy(), rt.ids)
+    np.testing.assert_allclose(w.cpu().numpy(), rt.w, rtol=0, atol=1e-6)
+    layer = api.forward(shape, inp.x, inp.w_r, inp.b_r, inp.w_gate, inp.w_up, inp.w_down)
+    np.testing.assert_array_equal(layer.topk_ids.cpu().numpy(), rt.ids)
+    res = O.forward(x64, wr, b, expert_provider(inp), cfg.k, cfg.gate_mode, C=None,
+                    round_h_bf16=cfg.dtype == "bf16", renorm_form=cfg.renorm_form)
+    np.testing.assert_array_equal(layer.slot.cpu().numpy(), res.dispatch.slot)
+    worst = check_output(np64(layer.y), res.y, F32_TOL if cfg.dtype == "f32" else BF16_TOL, cfg.name)
+    log(f"[ties] {cfg.name}: ok  ties at the boundary {at_boundary}, inside the set {in_set}, "
+        f"max rel err {worst:.2e}")
 
 
 # ---------------------------------------------------------------------------
@@ -400,11 +498,13 @@ def test_nonfinite_score_sets_status_and_keeps_ids_in_range():
         layer.check_status()
 
 
-@pytest.mark.parametrize("T,E", [(4, 8), (10, 40), (3, 100), (40, 100)])
+@pytest.mark.parametrize("T,E", [(4, 8), (10, 40), (3, 100), (40, 100), (40, 8), (700, 6)])
 def test_status_word_set_then_cleared(T, E):
     """The router's status word: set by a non-finite score, back to MOE_OK on the
     next clean call — also where the selecting kernel is a single workgroup that
-    clears the word itself (T <= 8 with E <= 8, T <= 16 with E <= 64, T <= 4 above)."""
+    clears the word itself (T <= 8 with E <= 8, T <= 16 with E <= 64, T <= 4 above),
+    and on the split-K path for E <= 8, where the last token group to finish
+    writes it (one group with T = 40, eleven with T = 700)."""
     cfg = MoEConfig("status", T=T, d=128, m=64, E=E, k=2, dtype="bf16", gate_mode=0, cf=None, cfg_id=34)
     inp = make_inputs(cfg, 0, DEV)
     shape = shape_of(cfg)
@@ -428,6 +528,61 @@ def test_status_word_set_then_cleared(T, E):
         torch.cuda.synchronize()
         assert int(st.item()) == want
     assert torch.equal(ids_b, ids)
+
+
+def test_router_many_workgroups():
+    """E <= 8 router over 100003 tokens (6251 workgroups counting themselves done
+    in the sync words, the last one partial) with a dispatch table too large for
+    the router-made counts: the whole layer against the oracle, every element."""
+    cfg = MoEConfig("router_many_wg", T=100003, d=64, m=64, E=8, k=2, dtype="bf16", gate_mode=0, cf=(5, 4),
+                    bias="zipf", cfg_id=56)
+    run_layer(cfg)
+
+
+@pytest.mark.parametrize("cfg", [
+    MoEConfig("sync_route", T=1000, d=512, m=64, E=8, k=2, dtype="bf16", gate_mode=0, cf=(5, 4), cfg_id=57),
+    MoEConfig("sync_switch", T=1024, d=1024, m=64, E=8, k=1, dtype="bf16", gate_mode=1, cf=(5, 4),
+              bias="first_two_plus2", cfg_id=58),
+], ids=lambda c: c.name)
+def test_router_sync_words_return_to_zero(cfg):
+    """The E <= 8 router's counters live in the first MOE_SYNC_BYTES of the route,
+    route-stats and forward workspaces: zero before the first call, and every
+    call must leave them zero (the next call counts from there).  Repeated calls
+    on one workspace, with a non-finite score in between, give identical ids."""
+    inp = make_inputs(cfg, 0, DEV)
+    shape = shape_of(cfg)
+    st = torch.cuda.current_stream().cuda_stream
+    T, k, E = cfg.T, cfg.k, cfg.E
+    ids = [torch.empty((T, k), dtype=torch.int32, device=DEV) for _ in range(3)]
+    w = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    status = torch.empty(1, dtype=torch.int32, device=DEV)
+    ws = api.workspace(shape, L.MOE_WS_ROUTE, DEV)
+    bad = inp.x.clone()
+    bad[T // 2, 3] = float("nan")
+    for i, (x, want) in enumerate(((inp.x, L.MOE_OK), (bad, L.MOE_ERR_NONFINITE_LOGIT), (inp.x, L.MOE_OK))):
+        L.check(L.moe_route(shape, x.data_ptr(), inp.w_r.data_ptr(), 0 if inp.b_r is None else inp.b_r.data_ptr(),
+                            ids[i].data_ptr(), w.data_ptr(), status.data_ptr(), ws.data_ptr(), ws.numel(), st),
+                "moe_route")
+        torch.cuda.synchronize()
+        assert int(status.item()) == want
+        assert int(ws[:L.MOE_SYNC_BYTES].count_nonzero()) == 0, f"sync words left non-zero after call {i}"
+    assert torch.equal(ids[0], ids[2])
+    rs = api.workspace(shape, L.MOE_WS_ROUTE_STATS, DEV)
+    prob_sum = torch.empty(E, dtype=torch.float32, device=DEV)
+    for _ in range(2):
+        L.check(L.moe_route_stats(shape, inp.x.data_ptr(), inp.w_r.data_ptr(),
+                                  0 if inp.b_r is None else inp.b_r.data_ptr(), ids[1].data_ptr(), w.data_ptr(),
+                                  status.data_ptr(), prob_sum.data_ptr(), rs.data_ptr(), rs.numel(), st),
+                "moe_route_stats")
+        torch.cuda.synchronize()
+        assert int(rs[:L.MOE_SYNC_BYTES].count_nonzero()) == 0
+        assert torch.equal(ids[1], ids[0])
+    layer = api.MoELayer(shape, DEV)
+    for _ in range(2):
+        layer.forward(inp.x, inp.w_r, inp.b_r, inp.w_gate, inp.w_up, inp.w_down)
+        torch.cuda.synchronize()
+        assert int(layer.ws[:L.MOE_SYNC_BYTES].count_nonzero()) == 0
+        assert torch.equal(layer.topk_ids, ids[0])
 
 
 def test_run_twice_bitwise_and_causal_prefix():
@@ -647,15 +802,93 @@ def test_concurrent_host_threads_on_separate_streams():
     assert not errors, errors
 
 
+def test_capture_on_one_stream_while_another_thread_runs_eagerly():
+    """One host thread captures shared-expert forwards into a graph on its stream
+    while another thread runs eager forwards on a second stream inside that
+    capture window.  Each caller stream has a side stream of its own, so the eager
+    calls never reach the capture: they run, and equal the single-stream result bit
+    for bit, and every replay of the graph does too."""
+    import threading
+    cfg = MoEConfig("capture_vs_eager", T=300, d=256, m=128, E=16, k=4, dtype="bf16", gate_mode=0, cf=(5, 4),
+                    m_shared=192, cfg_id=55)
+    shape = shape_of(cfg)
+    inps = [make_inputs(cfg, seed, DEV) for seed in (0, 1)]
+
+    def run(layer, inp):
+        layer.forward(inp.x, inp.w_r, inp.b_r, inp.w_gate, inp.w_up, inp.w_down, inp.s_gate, inp.s_up, inp.s_down)
+
+    refs = []
+    for inp in inps:
+        lay = api.MoELayer(shape, DEV)
+        run(lay, inp)
+        torch.cuda.synchronize()
+        refs.append(lay.y.clone())
+    layers = [api.MoELayer(shape, DEV) for _ in range(2)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for i in range(2):   # one call per caller stream first: its side stream is made outside any capture
+        with torch.cuda.stream(streams[i]):
+            run(layers[i], inps[i])
+    torch.cuda.synchronize()
+    errors, opened, eager_ran = [], threading.Event(), threading.Event()
+    graph = torch.cuda.CUDAGraph()
+
+    def capturer():
+        try:
+            with torch.cuda.graph(graph, stream=streams[0], capture_error_mode="thread_local"):
+                run(layers[0], inps[0])
+                opened.set()
+                if not eager_ran.wait(60):
+                    errors.append("the eager thread did not finish a forward inside the capture window")
+                run(layers[0], inps[0])
+        except Exception as e:   # surfaced below
+            errors.append(f"capture: {e!r}")
+        finally:
+            opened.set()
+
+    def eager():
+        try:
+            if not opened.wait(60):
+                errors.append("the capture did not start")
+                return
+            with torch.cuda.stream(streams[1]):
+                for i in range(4):
+                    layers[1].y.fill_(-1.0)
+                    run(layers[1], inps[1])
+                    streams[1].synchronize()
+                    if not torch.equal(layers[1].y, refs[1]):
+                        errors.append(f"eager forward {i} differs")
+                    eager_ran.set()
+        except Exception as e:
+            errors.append(f"eager: {e!r}")
+        finally:
+            eager_ran.set()
+
+    threads = [threading.Thread(target=capturer), threading.Thread(target=eager)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads), "a worker thread did not finish"
+    assert not errors, errors
+    for _ in range(3):
+        layers[0].y.fill_(-1.0)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(layers[0].y, refs[0])
+        run(layers[1], inps[1])
+        torch.cuda.synchronize()
+        assert torch.equal(layers[1].y, refs[1])
+
+
 def test_balanced_schedule_multi_round_skewed_is_exact_and_deterministic():
     """Grouped GEMMs of several rounds of workgroups with skewed expert loads:
     the last eighth of each XCD's run is claimed at run time (and stolen across
     XCDs), so which workgroup computes a tile varies from run to run.  Every
     tile must still be computed exactly once: the layer matches the oracle on
-    sampled tokens, and twelve repeated forwards are identical bit for bit."""
+    every output element, and twelve repeated forwards are identical bit for bit."""
     cfg = MoEConfig("balanced_sched", T=2048, d=2048, m=1024, E=64, k=8, dtype="bf16", gate_mode=0, cf=(5, 4),
                     bias="zipf", cfg_id=51)
-    r = run_layer(cfg, sample=96)
+    r = run_layer(cfg)
     shape, inp = r["shape"], r["inp"]
     # more row x column tiles than the 256 CUs in both GEMMs (several rounds)
     rows = np.diff(r["disp"].offsets.cpu().numpy())
