@@ -301,6 +301,28 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_r, 
                        int32_t* slot, int32_t* stats, int32_t* status,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* moe_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same kernels and results as moe_forward (bit for bit), but the workspace is a
+ * file-scope device array of MOE_NOALLOC_SCRATCH_BYTES that the library holds on
+ * every device it runs on until the process ends, and the shared expert runs on
+ * `stream` itself (no side stream or event is created).  No call allocates or
+ * frees memory.  The first call on a device resolves the array's address on
+ * that device (make it outside graph capture); later calls only launch.
+ * Returns MOE_ERR_WORKSPACE_TOO_SMALL, launching nothing, when
+ * moe_workspace_bytes(shape, MOE_WS_FORWARD) exceeds the array (64 MiB covers,
+ * e.g., the Mixtral-shaped layer up to T = 512, the DeepSeek-V3-like layer up
+ * to T = 64 and the Switch-shaped layer at T = 1024).  Every call on a device
+ * shares that device's array, whose contents persist between calls: calls that
+ * overlap on one GPU (other streams, other host threads) race and must be
+ * serialised by the caller.  Other arguments and outputs as moe_forward. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status moe_forward_noalloc(const moe_shape* shape, const void* x, const float* w_r, const float* b_r,
+                               const void* w_gate, const void* w_up, const void* w_down,
+                               const void* s_gate, const void* s_up, const void* s_down,
+                               float* y, int32_t* topk_ids, float* topk_w, int32_t* load,
+                               int32_t* slot, int32_t* stats, int32_t* status, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -36,6 +36,7 @@ MOE_STAT_REROUTED = 5
 MOE_STAT_COUNT = 8
 
 MOE_SYNC_BYTES = 256   # zeroed once at the start of route / route-stats / forward workspaces
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 MOE_WS_DISPATCH = 0
 MOE_WS_FFN = 1
@@ -87,6 +88,7 @@ _SIGS = {
                                  c_size_t, c_void_p]),
     "moe_combine": (c_int32, [POINTER(MoeShape), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "moe_forward": (c_int32, [POINTER(MoeShape)] + [c_void_p] * 16 + [c_void_p, c_size_t, c_void_p]),
+    "moe_forward_noalloc": (c_int32, [POINTER(MoeShape)] + [c_void_p] * 16 + [c_void_p]),
 }
 
 _lib = None
@@ -184,3 +186,9 @@ def moe_forward(shape, x, w_r, b_r, w_gate, w_up, w_down, s_gate, s_up, s_down, 
                 stats, status, ws, ws_bytes, stream) -> int:
     return lib().moe_forward(ctypes.byref(shape), x, w_r, b_r, w_gate, w_up, w_down, s_gate, s_up, s_down, y,
                              topk_ids, topk_w, load, slot, stats, status, ws, ws_bytes, stream)
+
+
+def moe_forward_noalloc(shape, x, w_r, b_r, w_gate, w_up, w_down, s_gate, s_up, s_down, y, topk_ids, topk_w, load,
+                        slot, stats, status, stream) -> int:
+    return lib().moe_forward_noalloc(ctypes.byref(shape), x, w_r, b_r, w_gate, w_up, w_down, s_gate, s_up, s_down,
+                                     y, topk_ids, topk_w, load, slot, stats, status, stream)

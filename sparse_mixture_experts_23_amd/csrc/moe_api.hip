@@ -257,6 +257,38 @@ moe_status shared_impl(const moe_dims& d, const void* x, const void* s_gate, con
 
 namespace {
 
+// ---- the allocation-free forward's scratch -----------------------------------
+// One workspace per device in a file-scope device array, zero when the module is
+// loaded (the router's sync words at its start need that; every call leaves them
+// at zero).  In host code `scratch` only names the symbol: its device address is
+// looked up once per device, with that device current, and only that address is
+// ever passed to kernels.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+hipError_t scratch_address(hipStream_t st, void** out) {
+    hipDevice_t dev = 0;
+    hipError_t e = hipStreamGetDevice(st, &dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        const hipError_t r = cur != dev ? hipSetDevice(cur) : hipSuccess;
+        if (e != hipSuccess) return e;
+        if (r != hipSuccess) return r;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
 // The whole layer; side_ok: the shared expert may run on a side stream (else on
 // the caller's stream, after the dispatch).
 moe_status forward_impl(const moe_shape* shape, const void* x, const float* w_r, const float* b_r, const void* w_gate,
@@ -486,6 +518,21 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_r, 
                        void* stream) {
     return forward_impl(shape, x, w_r, b_r, w_gate, w_up, w_down, s_gate, s_up, s_down, y, topk_ids, topk_w, load,
                         slot, stats, status, ws, ws_bytes, stream, true);
+}
+
+moe_status moe_forward_noalloc(const moe_shape* shape, const void* x, const float* w_r, const float* b_r,
+                               const void* w_gate, const void* w_up, const void* w_down, const void* s_gate,
+                               const void* s_up, const void* s_down, float* y, int32_t* topk_ids, float* topk_w,
+                               int32_t* load, int32_t* slot, int32_t* stats, int32_t* status, void* stream) {
+    moe_dims d;
+    moe_status rc = check_shape(shape, &d);
+    if (rc != MOE_OK) return rc;
+    if (carve_forward(d, nullptr).total > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    void* ws = nullptr;
+    if (scratch_address(static_cast<hipStream_t>(stream), &ws) != hipSuccess) return MOE_ERR_HIP;
+    // the shared expert on the caller's stream: no side stream or event is made
+    return forward_impl(shape, x, w_r, b_r, w_gate, w_up, w_down, s_gate, s_up, s_down, y, topk_ids, topk_w, load,
+                        slot, stats, status, ws, MOE_NOALLOC_SCRATCH_BYTES, stream, false);
 }
 
 }  // extern "C"
