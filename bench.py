@@ -85,7 +85,7 @@ class Stages:
 
     def __init__(self, shape, inp):
         dev = inp.x.device
-        T, k, E, d, m = shape.T, shape.k, shape.E, shape.d, shape.m
+        T, k, E, d, m = shape.T, api.paths(shape), shape.E, shape.d, shape.m
         R = L.moe_max_rows(shape)
         self.shape, self.inp, self.R = shape, inp, R
         z = lambda *s, dt=torch.int32: torch.empty(s, dtype=dt, device=dev)  # noqa: E731
@@ -167,18 +167,23 @@ def cpu_baseline(cfg, inp, budget_tokens, layer=None):
     cap = Ts if C is None else C
     if cfg.accept_by_gate:
         O.assign_slots_by_gate(rt.ids, O.round_to_f32(rt.w), cfg.E, cap)
+    elif cfg.reroute:
+        n = min(2 * cfg.k, cfg.E)
+        ids2 = np.full((Ts, 2 * cfg.k), -1, dtype=np.int64)
+        ids2[:, :n] = O.select_topk(rt.g32, n)
+        O.assign_slots_reroute(ids2, cfg.k, cfg.E, cap)
     else:
         O.assign_slots(rt.ids, cfg.E, cap)
     t2 = time.perf_counter()
     res = O.forward(x, wr, b, experts, cfg.k, cfg.gate_mode, C=C, shared=shared, round_h_bf16=cfg.dtype == "bf16",
                     renorm_form=cfg.renorm_form, accept_by_gate=cfg.accept_by_gate,
-                    renorm_survivors=cfg.renorm_survivors)
+                    renorm_survivors=cfg.renorm_survivors, reroute=cfg.reroute)
     dt = time.perf_counter() - t2
     parity = None
     if layer is not None and Ts == cfg.T:
         boundary, _ = O.route_margins(res.route.g64, cfg.k)
         ids_gpu = layer.topk_ids.cpu().numpy()
-        same = (np.sort(ids_gpu, axis=1) == np.sort(res.route.ids, axis=1)).all(axis=1)
+        same = (np.sort(ids_gpu, axis=1) == np.sort(res.route.ids, axis=1)).all(axis=1)   # every record
         y_gpu = layer.y.cpu().numpy().astype(np.float64)
         err = (np.abs(y_gpu - res.y) / (1.0 + np.abs(res.y)))[same]
         tol = 2e-2 if cfg.dtype == "bf16" else 1e-5
@@ -227,6 +232,8 @@ def main():
                     help="overflow variant: experts over capacity keep their highest-weight requests")
     ap.add_argument("--renorm-survivors", action="store_true",
                     help="overflow variant: weights renormalised over each token's accepted paths")
+    ap.add_argument("--reroute", action="store_true",
+                    help="overflow variant: a rejected path goes to the token's next-choice expert")
     ap.add_argument("--tokens", type=int, default=0,
                     help="override the workload's token count T (e.g. 1..64 for decode-sized batches)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
@@ -250,13 +257,15 @@ def main():
     cfg = CONFIGS[args.workload]
     if args.tokens:
         cfg = cfg.with_tokens(args.tokens)
-    if args.accept_by_gate or args.renorm_survivors:
-        cfg = cfg.scaled(accept_by_gate=args.accept_by_gate, renorm_survivors=args.renorm_survivors)
+    if args.accept_by_gate or args.renorm_survivors or args.reroute:
+        cfg = cfg.scaled(accept_by_gate=args.accept_by_gate, renorm_survivors=args.renorm_survivors,
+                         reroute=args.reroute)
     log(f"[bench] workload {cfg.name}: generating inputs on the GPU")
     inp = make_inputs(cfg, seed=0, device="cuda")
     C = 0 if cfg.cf is None else api.capacity(cfg.T, cfg.k, cfg.E, *cfg.cf)
     shape = api.make_shape(cfg.T, cfg.d, cfg.m, cfg.E, cfg.k, C, cfg.gate_mode, cfg.torch_dtype, cfg.m_shared,
-                           accept_by_gate=cfg.accept_by_gate, renorm_survivors=cfg.renorm_survivors)
+                           accept_by_gate=cfg.accept_by_gate, renorm_survivors=cfg.renorm_survivors,
+                           reroute=cfg.reroute)
     layer = api.MoELayer(shape, "cuda")
     fwd = lambda: layer.forward(inp.x, inp.w_r, inp.b_r, inp.w_gate, inp.w_up, inp.w_down,  # noqa: E731
                                 inp.s_gate, inp.s_up, inp.s_down)
@@ -392,10 +401,12 @@ def main():
                    "capacity": C or "unlimited", "gate": "switch" if cfg.gate_mode else "renorm",
                    "shared_expert_m": cfg.m_shared, "router": "fp32", "accumulate": "fp32",
                    "acceptance": "gate weight" if cfg.accept_by_gate else "token order",
-                   "rejected_paths": "renormalise survivors" if cfg.renorm_survivors else "drop"},
+                   "rejected_paths": ("reroute to the next choice" if cfg.reroute else "drop")
+                   + (", renormalise survivors" if cfg.renorm_survivors else "")},
         "stats": {"accepted_paths": A, "overflow": stats[L.MOE_STAT_OVERFLOW],
                   "max_load": stats[L.MOE_STAT_MAX_LOAD], "rho_max": round(stats[L.MOE_STAT_MAX_LOAD] / (T * k / cfg.E), 4),
-                  "tokens_dropped": stats[L.MOE_STAT_TOKENS_DROPPED], "active_experts": active},
+                  "tokens_dropped": stats[L.MOE_STAT_TOKENS_DROPPED], "rerouted": stats[L.MOE_STAT_REROUTED],
+                  "active_experts": active},
         "roofline": roofline,
         "step_ms": _spread(step_ms),
         "cold_step_ms": _spread(cold_ms) if cold_ms else None,

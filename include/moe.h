@@ -164,8 +164,9 @@ const char* moe_status_str(int32_t status);
  * Algorithm 36.1 selection step; "MoE token routing" §2).
  *   x        [T,d]  dtype
  *   w_r      [E,d]  fp32;  b_r [E] fp32 or NULL
- *   topk_ids [T,k]  int32 out: rank order (descending fp32 score, lower id first on ties)
- *   topk_w   [T,k]  fp32 out: RENORM a = p_e / sum_{j in S} p_j (sums to 1);
+ *   topk_ids [T,P]  int32 out: rank order (descending fp32 score, lower id first on ties);
+ *                   P = k, or 2k with shape->reroute (then the k next choices follow)
+ *   topk_w   [T,P]  fp32 out: RENORM a = p_e / sum_{j in S} p_j (sums to 1);
  *                   SWITCH a = p_e (full softmax)
  *   status   [1]    int32 out: set to MOE_OK, or MOE_ERR_NONFINITE_LOGIT if any
  *                   score is NaN/Inf; such a token gets ids 0..k-1 and weights 0
@@ -211,15 +212,18 @@ moe_status moe_balance(const moe_shape* shape, const int32_t* load, const int32_
  * 36.1 acceptance step and its invariants; "The real cost of sparse expert
  * models" equations for C_e, O and rho_max).
  *   x         [T,d]      dtype
- *   topk_ids  [T,k]      int32 in (values must lie in [0,E); each row distinct)
- *   topk_w    [T,k]      fp32 in: the routing weights; read only with
+ *   topk_ids  [T,P]      int32 in (values must lie in [0,E); each row distinct; with
+ *                        reroute, next-choice records may be -1); P as in moe_route
+ *   topk_w    [T,P]      fp32 in: the routing weights; read only with
  *                        shape->accept_by_gate (then required; else may be NULL)
  *   load      [E]        int32 out: requested load L_e
  *   offsets   [E+1]      int32 out: exclusive prefix sum of min(L_e, C)
- *   slot      [T,k]      int32 out: slot c within the expert (number of earlier
+ *   slot      [T,P]      int32 out: slot c within the expert (number of earlier
  *                        tokens that requested the same expert; with
  *                        accept_by_gate, of earlier accepted tokens), or -1 if rejected
- *   row_of    [T,k]      int32 out: offsets[e] + slot, or -1
+ *   row_of    [T,P]      int32 out: offsets[e] + slot, or -1.  With reroute, the
+ *                        slot and row of next choice j (column k + j) are set when
+ *                        the j-th rejected selection of the token was served there
  *   src_token [max_rows] int32 out: token of each grouped row (rows >= A untouched)
  *   x_perm    [max_rows,d] dtype out: x_perm[row] = x[src_token[row]]; rows are
  *                        grouped by expert, token order inside each expert
@@ -276,7 +280,8 @@ moe_status moe_shared_ffn(const moe_shape* shape, const void* x, const void* s_g
  * summed in rank order r = 0..k-1, in fp32.  With shape->renorm_survivors each
  * topk_w[t,r] is first divided by the sum (rank order) of the token's accepted
  * weights.
- *   H [max_rows,d] fp32;  row_of, topk_w [T,k];  shared_out [T,d] fp32 or NULL;
+ *   H [max_rows,d] fp32;  row_of, topk_w [T,P] (P = k, or 2k with reroute: every
+ *   record with a row is added, in column order);  shared_out [T,d] fp32 or NULL;
  *   y [T,d] fp32 out (fully overwritten). */
 moe_status moe_combine(const moe_shape* shape, const float* H, const int32_t* row_of,
                        const float* topk_w, const float* shared_out, float* y, void* stream);
@@ -285,6 +290,7 @@ moe_status moe_combine(const moe_shape* shape, const float* H, const int32_t* ro
  * queued on `stream` with no host synchronisation.  s_gate/s_up/s_down may be
  * NULL only when shape->m_shared == 0.  Outputs as in the calls above;
  * every intermediate lives in ws (>= moe_workspace_bytes(shape, MOE_WS_FORWARD)).
+ * topk_ids, topk_w and slot have P columns as in moe_route (2k with reroute).
  * The results equal those of the staged calls bit for bit, but the path may
  * differ: with bf16 activations the expert GEMMs read each grouped row in place
  * from x through the dispatch's row map (no x_perm copy; the E <= 8 router also

@@ -38,10 +38,10 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape: tuple):
 
 def make_shape(T: int, d: int, m: int, E: int, k: int, capacity: int = 0, gate_mode: int = L.MOE_GATE_RENORM,
                dtype=torch.bfloat16, m_shared: int = 0, accept_by_gate: bool = False,
-               renorm_survivors: bool = False) -> L.MoeShape:
+               renorm_survivors: bool = False, reroute: bool = False) -> L.MoeShape:
     s = L.MoeShape(T, d, m, E, k, capacity, gate_mode,
                    _dtype_code(dtype) if isinstance(dtype, torch.dtype) else int(dtype), m_shared,
-                   int(accept_by_gate), int(renorm_survivors))
+                   int(accept_by_gate), int(renorm_survivors), int(reroute))
     L.check(L.moe_check_shape(s), "moe_check_shape")
     return s
 
@@ -57,6 +57,12 @@ def _torch_dtype(shape: L.MoeShape):
     return torch.bfloat16 if shape.dtype == L.MOE_BF16 else torch.float32
 
 
+def paths(shape: L.MoeShape) -> int:
+    """Routing records per token: k, or 2k with rerouting (the k selected
+    experts, then the next k in rank order)."""
+    return 2 * shape.k if shape.reroute else shape.k
+
+
 def workspace(shape: L.MoeShape, kind: int, device="cuda") -> torch.Tensor:
     """Workspace for the named call; the router's sync words at the start of a
     route, route-stats or forward workspace are zeroed once here (the library
@@ -69,9 +75,9 @@ def workspace(shape: L.MoeShape, kind: int, device="cuda") -> torch.Tensor:
 
 
 def route(shape: L.MoeShape, x, w_r, b_r=None):
-    """Returns (topk_ids [T,k] int32, topk_w [T,k] fp32, status [1] int32)."""
+    """Returns (topk_ids [T,P] int32, topk_w [T,P] fp32, status [1] int32), P = paths(shape)."""
     dev = x.device
-    T, k = shape.T, shape.k
+    T, k = shape.T, paths(shape)
     _need(x, "x", _torch_dtype(shape), (T, shape.d))
     _need(w_r, "w_r", torch.float32, (shape.E, shape.d))
     if b_r is not None:
@@ -88,7 +94,7 @@ def route(shape: L.MoeShape, x, w_r, b_r=None):
 def route_stats(shape: L.MoeShape, x, w_r, b_r=None):
     """moe_route_stats: (topk_ids, topk_w, status, prob_sum [E] fp32)."""
     dev = x.device
-    T, k = shape.T, shape.k
+    T, k = shape.T, paths(shape)
     _need(x, "x", _torch_dtype(shape), (T, shape.d))
     _need(w_r, "w_r", torch.float32, (shape.E, shape.d))
     if b_r is not None:
@@ -126,9 +132,10 @@ class DispatchOut:
 
 
 def dispatch(shape: L.MoeShape, x, topk_ids, topk_w=None) -> DispatchOut:
-    """topk_w (the routing weights) is needed only with shape.accept_by_gate."""
+    """topk_w (the routing weights) is needed only with shape.accept_by_gate.
+    topk_ids and the slot / row_of outputs have P = paths(shape) columns."""
     dev = x.device
-    T, k, E = shape.T, shape.k, shape.E
+    T, k, E = shape.T, paths(shape), shape.E
     R = L.moe_max_rows(shape)
     _need(x, "x", _torch_dtype(shape), (T, shape.d))
     _need(topk_ids, "topk_ids", torch.int32, (T, k))
@@ -207,7 +214,7 @@ class MoELayer:
 
     def __init__(self, shape: L.MoeShape, device="cuda"):
         self.shape = shape
-        T, k, E, d = shape.T, shape.k, shape.E, shape.d
+        T, k, E, d = shape.T, paths(shape), shape.E, shape.d
         self.y = torch.empty((T, d), dtype=torch.float32, device=device)
         self.topk_ids = torch.empty((T, k), dtype=torch.int32, device=device)
         self.topk_w = torch.empty((T, k), dtype=torch.float32, device=device)

@@ -10,7 +10,8 @@
 // its paths in rank order with fp32 fused multiply-adds, so the result is
 // deterministic without atomics.  Overflow variant (ch. 36 §36.4 worked
 // example): with renorm_survivors each accepted weight is first divided by the
-// sum of the token's accepted weights.
+// sum of the token's accepted weights.  With rerouting a token has 2k records
+// (its selection, then its next choices), summed the same way.
 #include "common.h"
 
 namespace {
@@ -140,10 +141,10 @@ hipError_t launch_combine(const moe_dims& s, const float* H, const float* H1, in
     const unsigned grid = (unsigned)((s.T * nchunk + 3) / 4);
     if (vec4)
         hipLaunchKernelGGL(combine_kernel<true>, dim3(grid), dim3(256), 0, st, H, H1, np, part_stride, row_of, topk_w,
-                           shared_out, y, s.T, s.d, s.k, nchunk, s.renorm_survivors);
+                           shared_out, y, s.T, s.d, moe_paths(s), nchunk, s.renorm_survivors);
     else
         hipLaunchKernelGGL(combine_kernel<false>, dim3(grid), dim3(256), 0, st, H, H1, np, part_stride, row_of,
-                           topk_w, shared_out, y, s.T, s.d, s.k, nchunk, s.renorm_survivors);
+                           topk_w, shared_out, y, s.T, s.d, moe_paths(s), nchunk, s.renorm_survivors);
     return hipGetLastError();
 }
 

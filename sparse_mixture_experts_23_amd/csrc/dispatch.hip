@@ -556,6 +556,96 @@ __global__ __launch_bounds__(256) void dispatch_gather_kernel(const V* __restric
     }
 }
 
+// ---------------------------------------------------------------------------
+// Overflow variant: rerouting a rejected path to the next-choice expert
+// ("The real cost of sparse expert models" item 5; ch. 36 §36.3 overflow
+// treatments).  Read as: the candidates are accepted first, in token order
+// (Algorithm 36.1); then the j-th rejected candidate of each token, in rank
+// order, asks for the token's j-th next expert, in token order, into the
+// capacity left; rejected again, it is dropped.  Every second-pass request comes
+// after every first-pass one, so running the ordinary dispatch over 2T "tokens"
+// -- the candidates, then each token's spare requests -- gives exactly these
+// slots: an expert with L_e < C accepts the spare requests while L_e + (earlier
+// spare requests) < C, one with L_e >= C none, as the definition says.
+// ---------------------------------------------------------------------------
+
+// v[t][r] = ids[t][r] (r < k): the candidates of the P = 2k routing records.
+__global__ __launch_bounds__(256) void reroute_candidates_kernel(const int32_t* __restrict__ ids, int64_t T, int k,
+                                                                 int32_t* __restrict__ v) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= T * k) return;
+    v[i] = ids[(i / k) * 2 * k + i % k];
+}
+
+// v[T + t][j] = ids[t][k + j] for the first (number of rejected candidates) j,
+// else -1 (no request); slot1: the first pass's slots [T][k].
+__global__ __launch_bounds__(256) void reroute_requests_kernel(const int32_t* __restrict__ ids, int64_t T, int k,
+                                                               const int32_t* __restrict__ slot1,
+                                                               int32_t* __restrict__ v) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= T) return;
+    int nrej = 0;
+    for (int r = 0; r < k; ++r) nrej += slot1[t * k + r] < 0;
+    for (int j = 0; j < k; ++j) v[(T + t) * k + j] = j < nrej ? ids[t * 2 * k + k + j] : -1;
+}
+
+// One workgroup: the 2T-token run's slots and rows folded back to [T][2k]
+// (candidate r at column r, spare j at column k + j), the spare rows' source
+// token, and the statistics (O and max load from the first pass, accepted rows
+// from the second, rerouted paths, tokens affected / left with no path).
+__global__ __launch_bounds__(1024) void reroute_finish_kernel(int64_t T, int k, const int32_t* __restrict__ slot2,
+                                                              const int32_t* __restrict__ row2,
+                                                              const int32_t* __restrict__ stats1,
+                                                              const int32_t* __restrict__ stats2,
+                                                              int32_t* __restrict__ slot, int32_t* __restrict__ row_of,
+                                                              int32_t* __restrict__ src_token,
+                                                              int32_t* __restrict__ stats) {
+    __shared__ int s_sum[3][16];
+    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+    int rerouted = 0, affected = 0, dropped = 0;
+    for (int64_t t = tid; t < T; t += 1024) {
+        int served = 0, nrej = 0;
+        for (int r = 0; r < k; ++r) {
+            const int c = slot2[t * k + r], rw = row2[t * k + r];
+            slot[t * 2 * k + r] = c;
+            row_of[t * 2 * k + r] = rw;
+            served += c >= 0;
+            nrej += c < 0;
+        }
+        for (int j = 0; j < k; ++j) {
+            const int c = slot2[(T + t) * k + j], rw = row2[(T + t) * k + j];
+            slot[t * 2 * k + k + j] = c;
+            row_of[t * 2 * k + k + j] = rw;
+            if (rw >= 0) {
+                src_token[rw] = (int32_t)t;
+                ++rerouted;
+                ++served;
+            }
+        }
+        affected += nrej > 0;
+        dropped += served == 0;
+    }
+    int v[3] = {rerouted, affected, dropped};
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+        for (int o = 32; o >= 1; o >>= 1) v[q] += __shfl_xor(v[q], o, MOE_WAVE);
+        if (lane == 0) s_sum[q][wave] = v[q];
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int tot[3] = {0, 0, 0};
+        for (int q = 0; q < 3; ++q)
+            for (int w = 0; w < 16; ++w) tot[q] += s_sum[q][w];
+        for (int i = 0; i < MOE_STAT_COUNT; ++i) stats[i] = 0;
+        stats[MOE_STAT_OVERFLOW] = stats1[MOE_STAT_OVERFLOW];
+        stats[MOE_STAT_ACCEPTED] = stats2[MOE_STAT_ACCEPTED];
+        stats[MOE_STAT_MAX_LOAD] = stats1[MOE_STAT_MAX_LOAD];
+        stats[MOE_STAT_REROUTED] = tot[0];
+        stats[MOE_STAT_TOKENS_AFFECTED] = tot[1];
+        stats[MOE_STAT_TOKENS_DROPPED] = tot[2];
+    }
+}
+
 // Load-balance statistics ("LLM from scratch" ch. 36 §36.4 and its worked
 // example): f_e = L_e / (T k), the pre-capacity share of routing records;
 // p_bar_e = prob_sum_e / T, the mean full-softmax probability; the balance value
@@ -619,10 +709,55 @@ bool dispatch_inline_scan(const moe_dims& s) {
 }
 
 bool dispatch_router_counts_ok(const moe_dims& s) {
-    return dispatch_inline_scan(s) && (s.T + MOE_ROUTE_TOK - 1) / MOE_ROUTE_TOK * s.E <= SCAN_INLINE_MAX;
+    return !s.reroute && dispatch_inline_scan(s) && (s.T + MOE_ROUTE_TOK - 1) / MOE_ROUTE_TOK * s.E <= SCAN_INLINE_MAX;
 }
 
+namespace {
+// The rerouting dispatch's two ordinary runs: over the T candidates' tokens, and
+// over 2T tokens (candidates, then spare requests).
+moe_dims reroute_pass(const moe_dims& s, int64_t T) {
+    moe_dims r = s;
+    r.T = T;
+    r.reroute = 0;
+    return r;
+}
+// [v 2Tk | slot1, row1 Tk | src1 | offsets1 E+1 | stats1, stats2 | load2 E | slot2, row2 2Tk | run workspace]
+struct RerouteWs {
+    int32_t *v, *slot1, *row1, *src1, *off1, *stats1, *stats2, *load2, *slot2, *row2;
+    void* run;
+    size_t total;
+};
+RerouteWs carve_reroute(const moe_dims& s, void* base) {
+    RerouteWs w{};
+    char* p = static_cast<char*>(base);
+    size_t off = 0;
+    auto take = [&](size_t n) -> int32_t* {
+        int32_t* r = p ? reinterpret_cast<int32_t*>(p + off) : nullptr;
+        off += al8(n * sizeof(int32_t));
+        return r;
+    };
+    const int64_t Tk = s.T * s.k;
+    const moe_dims s1 = reroute_pass(s, s.T), s2 = reroute_pass(s, 2 * s.T);
+    w.v = take(2 * Tk);
+    w.slot1 = take(Tk);
+    w.row1 = take(Tk);
+    w.src1 = take(Tk < (int64_t)s.E * s.C ? Tk : (int64_t)s.E * s.C);
+    w.off1 = take(s.E + 1);
+    w.stats1 = take(MOE_STAT_COUNT);
+    w.stats2 = take(MOE_STAT_COUNT);
+    w.load2 = take(s.E);
+    w.slot2 = take(2 * Tk);
+    w.row2 = take(2 * Tk);
+    off = (off + 255) & ~(size_t)255;
+    w.run = p ? p + off : nullptr;
+    const size_t a = dispatch_ws_bytes(s1), b = dispatch_ws_bytes(s2);
+    w.total = off + (a > b ? a : b);
+    return w;
+}
+}  // namespace
+
 size_t dispatch_ws_bytes(const moe_dims& s) {
+    if (s.reroute) return carve_reroute(s, nullptr).total;
     const int64_t NB = (s.T + DB_TOK - 1) / DB_TOK;
     const int64_t rows = dispatch_router_counts_ok(s) ? (s.T + MOE_ROUTE_TOK - 1) / MOE_ROUTE_TOK : NB;
     size_t b = al8((size_t)rows * (size_t)s.E * sizeof(int32_t));   // per-block (or router-group) counts / bases
@@ -641,7 +776,26 @@ hipError_t launch_dispatch(const moe_dims& s, const void* x, const int32_t* ids,
     const int NB = (int)((s.T + DB_TOK - 1) / DB_TOK);
     int32_t* hist = static_cast<int32_t*>(ws);
     const size_t mask_lds = sizeof(unsigned long long) * 4 * s.E;
-    if (s.accept_by_gate) {
+    if (s.reroute) {
+        if (s.T == 0) return launch_dispatch(reroute_pass(s, 0), x, ids, topk_w, load, offsets, slot, row_of,
+                                             src_token, nullptr, stats, ws, st, tprefix, tile_rows);
+        const RerouteWs w = carve_reroute(s, ws);
+        const int64_t Tk = s.T * s.k;
+        hipLaunchKernelGGL(reroute_candidates_kernel, dim3((unsigned)((Tk + 255) / 256)), dim3(256), 0, st, ids, s.T,
+                           s.k, w.v);
+        // first pass: the candidates alone give L_e (the requested load), O, the max load and the rejections
+        hipError_t e = launch_dispatch(reroute_pass(s, s.T), x, w.v, nullptr, load, w.off1, w.slot1, w.row1, w.src1,
+                                       nullptr, w.stats1, w.run, st);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(reroute_requests_kernel, dim3((unsigned)((s.T + 255) / 256)), dim3(256), 0, st, ids, s.T,
+                           s.k, w.slot1, w.v);
+        // second pass over 2T tokens: the final slots, rows, offsets and the GEMMs' tile prefix
+        e = launch_dispatch(reroute_pass(s, 2 * s.T), x, w.v, nullptr, w.load2, offsets, w.slot2, w.row2, src_token,
+                            nullptr, w.stats2, w.run, st, tprefix, tile_rows);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(reroute_finish_kernel, dim3(1), dim3(1024), 0, st, s.T, s.k, w.slot2, w.row2, w.stats1,
+                           w.stats2, slot, row_of, src_token, stats);
+    } else if (s.accept_by_gate) {
         char* p = static_cast<char*>(ws) + al8((size_t)NB * s.E * sizeof(int32_t));
         int32_t* roff = reinterpret_cast<int32_t*>(p);
         p += al8(sizeof(int32_t) * (s.E + 1));
@@ -693,16 +847,17 @@ hipError_t launch_dispatch(const moe_dims& s, const void* x, const int32_t* ids,
     const int elem = s.dtype == MOE_BF16 ? 2 : 4;
     const int64_t row_bytes = (int64_t)s.d * elem;
     const unsigned grid = (unsigned)((s.T + 3) / 4);
+    const int P = moe_paths(s);   // routing records per token
     if (row_bytes % 16 == 0)
         hipLaunchKernelGGL(dispatch_gather_kernel<uint4>, dim3(grid), dim3(256), 0, st, static_cast<const uint4*>(x),
-                           s.T, s.k, row_bytes / 16, row_of, static_cast<uint4*>(x_perm));
+                           s.T, P, row_bytes / 16, row_of, static_cast<uint4*>(x_perm));
     else if (row_bytes % 4 == 0)
         hipLaunchKernelGGL(dispatch_gather_kernel<uint32_t>, dim3(grid), dim3(256), 0, st,
-                           static_cast<const uint32_t*>(x), s.T, s.k, row_bytes / 4, row_of,
+                           static_cast<const uint32_t*>(x), s.T, P, row_bytes / 4, row_of,
                            static_cast<uint32_t*>(x_perm));
     else
         hipLaunchKernelGGL(dispatch_gather_kernel<uint16_t>, dim3(grid), dim3(256), 0, st,
-                           static_cast<const uint16_t*>(x), s.T, s.k, row_bytes / 2, row_of,
+                           static_cast<const uint16_t*>(x), s.T, P, row_bytes / 2, row_of,
                            static_cast<uint16_t*>(x_perm));
     return hipGetLastError();
 }

@@ -28,7 +28,7 @@ moe_status check_shape(const moe_shape* s, moe_dims* out) {
     if ((s->accept_by_gate != 0 && s->accept_by_gate != 1) || (s->renorm_survivors != 0 && s->renorm_survivors != 1) ||
         (s->reroute != 0 && s->reroute != 1))
         return MOE_ERR_INVALID_ARGUMENT;
-    if (s->reroute) return MOE_ERR_UNSUPPORTED;   // rerouting: the dispatch and combine come next
+    if (s->reroute && s->accept_by_gate) return MOE_ERR_UNSUPPORTED;   // rerouting is read with token order
     if (out) {
         out->T = s->T;
         out->d = s->d;

@@ -96,10 +96,13 @@ __device__ __forceinline__ floatx4_t mfma3(const bf16x8_t a, const uint4 H, cons
 // selection and weights for one token (called by a whole wave)
 // ---------------------------------------------------------------------------
 // b_r, topk_ids and topk_w may point to global memory or LDS.  cnt (nullable,
-// LDS): cnt[e] += 1 for every expert id written.
+// LDS): cnt[e] += 1 for every selected expert id.  kout: records written per
+// token, k or (rerouting) 2k: min(kout, E) rounds, the ones after the first k
+// being the next choices, weighted with the selection's normalizer; records past
+// E get id -1 and weight 0.
 template <int EPL>
-__device__ void select_token(const float* __restrict__ row, const float* __restrict__ b_r, int E, int k, int mode,
-                             int64_t t, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
+__device__ void select_token(const float* __restrict__ row, const float* __restrict__ b_r, int E, int k, int kout,
+                             int mode, int64_t t, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
                              int32_t* __restrict__ status, float* __restrict__ probs, int* cnt = nullptr) {
     const int lane = threadIdx.x % 64;
     float v[EPL];
@@ -115,10 +118,10 @@ __device__ void select_token(const float* __restrict__ row, const float* __restr
         v[j] = g;
     }
     if (__any(bad)) {
-        if (lane < k) {
-            topk_ids[t * k + lane] = lane;
-            topk_w[t * k + lane] = 0.f;
-            if (cnt) atomicAdd(&cnt[lane], 1);
+        if (lane < kout) {
+            topk_ids[t * kout + lane] = lane < k ? lane : -1;
+            topk_w[t * kout + lane] = 0.f;
+            if (cnt && lane < k) atomicAdd(&cnt[lane], 1);
         }
         if (lane == 0) *status = MOE_ERR_NONFINITE_LOGIT;
         if (probs) {
@@ -128,11 +131,12 @@ __device__ void select_token(const float* __restrict__ row, const float* __restr
         }
         return;
     }
-    // k rounds of a wave arg-max over (score key, lower id first).
+    // rounds of a wave arg-max over (score key, lower id first).
+    const int rounds = min(kout, E);
     uint32_t taken = 0;
-    int my_e = 0;
+    int my_e = -1;
     float my_g = 0.f;
-    for (int s = 0; s < k; ++s) {
+    for (int s = 0; s < rounds; ++s) {
         unsigned long long best = 0ull;
 #pragma unroll
         for (int j = 0; j < EPL; ++j) {
@@ -176,14 +180,14 @@ __device__ void select_token(const float* __restrict__ row, const float* __restr
         z = wave_sum(z);
         wgt = expf(my_g - g_top) / z;
     } else {
-        const float ez = lane < k ? expf(my_g - g_top) : 0.f;
-        const float z = wave_sum(ez);
+        const float ez = lane < rounds ? expf(my_g - g_top) : 0.f;
+        const float z = wave_sum(lane < k ? ez : 0.f);
         wgt = ez / z;
     }
-    if (lane < k) {
-        topk_ids[t * k + lane] = my_e;
-        topk_w[t * k + lane] = wgt;
-        if (cnt) atomicAdd(&cnt[my_e], 1);
+    if (lane < kout) {
+        topk_ids[t * kout + lane] = my_e;
+        topk_w[t * kout + lane] = lane < rounds ? wgt : 0.f;
+        if (cnt && lane < k) atomicAdd(&cnt[my_e], 1);
     }
 }
 
@@ -538,7 +542,8 @@ __global__ __launch_bounds__(RT_THREADS) void route_small_kernel(const void* __r
                                                                  const float* __restrict__ w_r,
                                                                  const uint16_t* __restrict__ w3,
                                                                  const float* __restrict__ b_r, int64_t T, int d,
-                                                                 int E, int k, int mode, int32_t* __restrict__ topk_ids,
+                                                                 int E, int k, int kout, int mode,
+                                                                 int32_t* __restrict__ topk_ids,
                                                                  float* __restrict__ topk_w,
                                                                  int32_t* __restrict__ status,
                                                                  float* __restrict__ probs, int zero_status) {
@@ -564,7 +569,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_small_kernel(const void* __r
     for (int r = wave; r < RT_TOK; r += RT_WAVES) {
         const int64_t t = t0 + r;
         if (t >= T) break;
-        select_token<1>(lg + r * E, b_r, E, k, mode, t, topk_ids, topk_w, status, probs);
+        select_token<1>(lg + r * E, b_r, E, k, kout, mode, t, topk_ids, topk_w, status, probs);
     }
 }
 
@@ -592,7 +597,7 @@ __global__ __launch_bounds__(256) void router_scores_f32_kernel(const float* __r
 template <int EPL>
 __global__ __launch_bounds__(256) void route_select_kernel(const float* __restrict__ part, int KS, int P, int NP,
                                                            const float* __restrict__ b_r, int64_t T, int E, int k,
-                                                           int mode, int32_t* __restrict__ topk_ids,
+                                                           int kout, int mode, int32_t* __restrict__ topk_ids,
                                                            float* __restrict__ topk_w, int32_t* __restrict__ status,
                                                            float* __restrict__ probs, int zero_status) {
     __shared__ float rows[4][EPL * 64];
@@ -638,7 +643,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    select_token<EPL>(rows[wave], b_r, E, k, mode, t, topk_ids, topk_w, status, probs);
+    select_token<EPL>(rows[wave], b_r, E, k, kout, mode, t, topk_ids, topk_w, status, probs);
 }
 
 // ---------------------------------------------------------------------------
@@ -762,7 +767,8 @@ constexpr int FS_KR = 4 * FS_THREADS;   // K elements per range
 template <int EPL, bool DISPATCH>
 __global__ __launch_bounds__(FS_THREADS) void front_small_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ w_r, const float* __restrict__ dpart, int KS,
-    const float* __restrict__ b_r, int64_t T, int d, int E, int k, int C, int mode, int32_t* __restrict__ topk_ids,
+    const float* __restrict__ b_r, int64_t T, int d, int E, int k, int kout, int C, int mode,
+    int32_t* __restrict__ topk_ids,
     float* __restrict__ topk_w, int32_t* __restrict__ status, float* __restrict__ probs, int32_t* __restrict__ load,
     int32_t* __restrict__ offsets, int32_t* __restrict__ slot, int32_t* __restrict__ row_of,
     int32_t* __restrict__ src_token, uint4* __restrict__ x_perm, int32_t* __restrict__ stats,
@@ -854,7 +860,7 @@ __global__ __launch_bounds__(FS_THREADS) void front_small_kernel(
     // with DISPATCH the ids and weights go to LDS first and to memory at the end, so
     // no barrier below waits for their stores
     if (wave < T)
-        select_token<EPL>(lg + wave * E, s_bias, E, k, mode, wave, DISPATCH ? s_ids : topk_ids,
+        select_token<EPL>(lg + wave * E, s_bias, E, k, DISPATCH ? k : kout, mode, wave, DISPATCH ? s_ids : topk_ids,
                           DISPATCH ? s_w : topk_w, status, probs);
     if (!DISPATCH) return;
     __syncthreads();
@@ -889,7 +895,7 @@ void launch_select(const moe_dims& s, const float* part, int KS, int P, int NP, 
                    float* w, int32_t* status, float* probs, hipStream_t st) {
     const unsigned grid = (unsigned)((s.T + 3) / 4);
     hipLaunchKernelGGL((route_select_kernel<EPL>), dim3(grid), dim3(256), 0, st, part, KS, P, NP, b_r, s.T, s.E, s.k,
-                       s.gate_mode, ids, w, status, probs, grid == 1 ? 1 : 0);
+                       moe_paths(s), s.gate_mode, ids, w, status, probs, grid == 1 ? 1 : 0);
 }
 
 // prob_sum[e] = sum over t of probs[t E + e]: 16 waves per 64 experts, wave w
@@ -951,7 +957,7 @@ size_t route_ws_bytes(const moe_dims& s) {
 }
 
 bool front_fused_ok(const moe_dims& s) {
-    return s.dtype == MOE_BF16 && s.T > 0 && s.T <= FS_TOK && s.E <= FS_EMAX && !s.accept_by_gate;
+    return s.dtype == MOE_BF16 && s.T > 0 && s.T <= FS_TOK && s.E <= FS_EMAX && !s.accept_by_gate && !s.reroute;
 }
 
 namespace {
@@ -972,7 +978,8 @@ hipError_t launch_front_small(const moe_dims& s, const void* x, const float* w_r
     }
 #define MOE_FRONT(EPLV)                                                                                         \
     hipLaunchKernelGGL((front_small_kernel<EPLV, DISPATCH>), dim3(1), dim3(FS_THREADS), 0, st,                 \
-                       static_cast<const uint16_t*>(x), w_r, dpart, KS, b_r, s.T, s.d, s.E, s.k, s.C, s.gate_mode, \
+                       static_cast<const uint16_t*>(x), w_r, dpart, KS, b_r, s.T, s.d, s.E, s.k, moe_paths(s), s.C, \
+                       s.gate_mode,                                                                           \
                        topk_ids, topk_w, status, probs, load, offsets, slot, row_of, src_token,                \
                        static_cast<uint4*>(x_perm), stats, tprefix, tile_rows)
     if (s.E <= 64) MOE_FRONT(1);
@@ -1056,12 +1063,12 @@ hipError_t launch_route(const moe_dims& s, const void* x, const float* w_r, cons
     do {                                                                                                       \
         if (s.dtype == MOE_BF16)                                                                               \
             hipLaunchKernelGGL((route_small_kernel<true, NTV>), dim3(grid), dim3(RT_THREADS), 0, st, x, w_r, w3, \
-                               b_r, s.T, s.d, s.E, s.k, s.gate_mode, topk_ids, topk_w, status, probs,          \
-                               self_zero ? 1 : 0);                                                     \
+                               b_r, s.T, s.d, s.E, s.k, moe_paths(s), s.gate_mode, topk_ids, topk_w, status,  \
+                               probs, self_zero ? 1 : 0);                                                     \
         else                                                                                                   \
             hipLaunchKernelGGL((route_small_kernel<false, NTV>), dim3(grid), dim3(RT_THREADS), 0, st, x, w_r, w3, \
-                               b_r, s.T, s.d, s.E, s.k, s.gate_mode, topk_ids, topk_w, status, probs,          \
-                               self_zero ? 1 : 0);                                                     \
+                               b_r, s.T, s.d, s.E, s.k, moe_paths(s), s.gate_mode, topk_ids, topk_w, status,  \
+                               probs, self_zero ? 1 : 0);                                                     \
     } while (0)
         if (NT == 1) MOE_SMALL(1);
         else if (NT == 2) MOE_SMALL(2);

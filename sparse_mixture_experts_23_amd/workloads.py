@@ -45,6 +45,7 @@ class MoEConfig:
     cfg_id: int = 0
     accept_by_gate: bool = False      # overflow variant: capacity competition by routing weight
     renorm_survivors: bool = False    # overflow variant: weights renormalised over accepted paths
+    reroute: bool = False             # overflow variant: rejected paths go to the next-choice expert
 
     @property
     def torch_dtype(self):

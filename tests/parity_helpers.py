@@ -39,7 +39,8 @@ def shape_of(cfg: MoEConfig) -> L.MoeShape:
         C = api.capacity(cfg.T, cfg.k, cfg.E, *cfg.cf)
         assert C == O.capacity(cfg.T, cfg.k, cfg.E, *cfg.cf)
     return api.make_shape(cfg.T, cfg.d, cfg.m, cfg.E, cfg.k, C, cfg.gate_mode, cfg.torch_dtype, cfg.m_shared,
-                          accept_by_gate=cfg.accept_by_gate, renorm_survivors=cfg.renorm_survivors)
+                          accept_by_gate=cfg.accept_by_gate, renorm_survivors=cfg.renorm_survivors,
+                          reroute=cfg.reroute)
 
 
 def oracle_capacity(cfg: MoEConfig):
@@ -87,13 +88,57 @@ def compare_route(cfg: MoEConfig, rt: O.Route, ids_gpu: np.ndarray, w_gpu: np.nd
     return RouteReport(near_ties=int(near.sum()), flipped_tokens=flipped)
 
 
+def reroute_ids(g32: np.ndarray, k: int) -> np.ndarray:
+    """The oracle's 2k routing records: the selection, then the next choices
+    (-1 where the experts run out), as the oracle's forward forms them."""
+    T, E = g32.shape
+    n = min(2 * k, E)
+    ids2 = np.full((T, 2 * k), -1, dtype=np.int64)
+    ids2[:, :n] = O.select_topk(g32, n)
+    return ids2
+
+
+def compare_route_reroute(cfg: MoEConfig, rt: O.Route, ids_gpu: np.ndarray, w_gpu: np.ndarray) -> RouteReport:
+    """Staged check 1 with rerouting: the selected set (first k records) and the
+    set of the first min(2k, E) records equal wherever their boundary margins
+    are >= 1e-5, rank order equal where every adjacent margin is clear, and the
+    weights (selection and next choices, with the selection's normalizer)
+    within the same tolerance as without rerouting."""
+    k, E = cfg.k, cfg.E
+    n = min(2 * k, E)
+    ref = reroute_ids(rt.g32, k)
+    b_k, _ = O.route_margins(rt.g64, k)
+    b_n, adj = O.route_margins(rt.g64, n)
+    near = (b_k < NEAR_TIE) | (b_n < NEAR_TIE)
+    same = (np.sort(ids_gpu[:, :k], axis=1) == np.sort(ref[:, :k], axis=1)).all(axis=1) & \
+        (np.sort(ids_gpu[:, :n], axis=1) == np.sort(ref[:, :n], axis=1)).all(axis=1)
+    bad = np.where(~same & ~near)[0]
+    assert len(bad) == 0, f"routing records differ at tokens {bad[:10].tolist()}"
+    assert (ids_gpu[:, n:] == -1).all(), "records past E must be -1"
+    clear = same & (adj >= NEAR_TIE).all(axis=1) if n > 1 else same
+    assert (ids_gpu[clear] == ref[clear]).all(), "rank order differs on a token without near-ties"
+    ids64 = ids_gpu.astype(np.int64)
+    w_ref = np.zeros_like(w_gpu, dtype=np.float64)
+    w_ref[:, :k] = O.gate_weights(rt.g32, ids64[:, :k], cfg.gate_mode, cfg.renorm_form)
+    w_ref[:, k:] = O.spare_weights(rt.g32, ids64[:, :k], ids64[:, k:], cfg.gate_mode, cfg.renorm_form)
+    tol = WEIGHT_TOL + WEIGHT_ULPS * np.abs(rt.g32).max(axis=1, keepdims=True)
+    excess = (np.abs(w_ref - w_gpu) - tol)[same]
+    assert excess.size == 0 or excess.max() <= 0, f"routing weight error exceeds tolerance by {excess.max():.3e}"
+    flipped = np.where(~same)[0].tolist()
+    return RouteReport(near_ties=int(near.sum()), flipped_tokens=flipped)
+
+
 def compare_dispatch(cfg: MoEConfig, ids_gpu: np.ndarray, C: int, out: api.DispatchOut, x: torch.Tensor,
                      w_gpu: np.ndarray = None):
     """Staged check 2: the GPU's ids through the oracle's serial slot loop must give
     the GPU's slots, row map, loads, offsets, rows and statistics bit for bit.
     With acceptance by gate weight the decision is taken on the GPU's fp32
     weights w_gpu on both sides (the same values decide the same integers)."""
-    if cfg.accept_by_gate:
+    rr = None
+    if cfg.reroute:
+        rr = O.assign_slots_reroute(ids_gpu.astype(np.int64), cfg.k, cfg.E, C)
+        ref = rr.dispatch
+    elif cfg.accept_by_gate:
         ref = O.assign_slots_by_gate(ids_gpu.astype(np.int64), np.asarray(w_gpu, dtype=np.float32), cfg.E, C)
     else:
         ref = O.assign_slots(ids_gpu.astype(np.int64), cfg.E, C)
@@ -107,8 +152,13 @@ def compare_dispatch(cfg: MoEConfig, ids_gpu: np.ndarray, C: int, out: api.Dispa
     assert st[L.MOE_STAT_OVERFLOW] == ref.overflow
     assert st[L.MOE_STAT_ACCEPTED] == A
     assert st[L.MOE_STAT_MAX_LOAD] == ref.max_load
-    assert st[L.MOE_STAT_TOKENS_DROPPED] == ref.tokens_dropped
-    assert st[L.MOE_STAT_TOKENS_AFFECTED] == ref.tokens_affected
+    if rr is not None:
+        assert st[L.MOE_STAT_REROUTED] == rr.rerouted
+        assert st[L.MOE_STAT_TOKENS_DROPPED] == rr.tokens_dropped
+        assert st[L.MOE_STAT_TOKENS_AFFECTED] == rr.tokens_affected
+    else:
+        assert st[L.MOE_STAT_TOKENS_DROPPED] == ref.tokens_dropped
+        assert st[L.MOE_STAT_TOKENS_AFFECTED] == ref.tokens_affected
     # the gathered rows are exact copies of their tokens' rows
     if A > 0:
         src = out.src_token[:A].long()

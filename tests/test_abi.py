@@ -56,8 +56,10 @@ def test_shape_checks():
     assert L.moe_check_shape(_shape(accept_by_gate=1, renorm_survivors=1)) == L.MOE_OK
     assert L.moe_check_shape(_shape(accept_by_gate=2)) == L.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_check_shape(_shape(renorm_survivors=-1)) == L.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_check_shape(_shape(reroute=1)) == L.MOE_OK
+    assert L.moe_check_shape(_shape(reroute=1, renorm_survivors=1)) == L.MOE_OK
     assert L.moe_check_shape(_shape(reroute=2)) == L.MOE_ERR_INVALID_ARGUMENT
-    assert L.moe_check_shape(_shape(reroute=1)) == L.MOE_ERR_UNSUPPORTED
+    assert L.moe_check_shape(_shape(reroute=1, accept_by_gate=1)) == L.MOE_ERR_UNSUPPORTED
 
 
 def test_max_rows_and_workspace():
