@@ -51,6 +51,9 @@ def gemm1_traffic_bytes():
     return GEMM1_TRAFFIC["bytes"] if sha == GEMM1_TRAFFIC["source_sha256"] else None
 
 
+SHORT_PHASE_BATCH = 10   # launches per timed batch of a short (memory-bound) phase
+
+
 def copy_calibration(nbytes: int, reps: int):
     """A plain device-to-device copy of nbytes, `reps` times: the reference whose
     FETCH_SIZE / WRITE_SIZE counters calibrate the GEMM's."""
@@ -71,13 +74,6 @@ def _spread(v):
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
-
-
-def gpu_sleep(stream, cycles: int = 20_000_000):
-    """Queue a spin kernel (~10 ms) on `stream`: the launches queued after it
-    start back to back once it ends."""
-    with torch.cuda.stream(stream):
-        torch.cuda._sleep(cycles)
 
 
 class Stages:
@@ -324,20 +320,28 @@ def main():
         reps = max(args.steps, 1)
         ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
               for n in names}
-        # The phases run interleaved, as in a forward (so the heavy GEMMs see the
-        # clock a forward gives them), and the whole batch is queued while the GPU
-        # runs a spin kernel, so that the short phases run back to back and their
-        # events time the GPU rather than the host's launch latency.
-        gpu_sleep(st)
+        # The phases run interleaved, as in a forward, and the whole batch is
+        # queued behind a few full forwards: the short phases then run back to back
+        # (their events time the GPU, not the host's launch latency), and the GPU
+        # never idles, so the heavy GEMMs run at the clock the timed forwards saw
+        # (an idle gap lets the power controller overshoot: after one, the first
+        # GEMMs run ~20 % slower for several milliseconds).
+        # A short phase is timed over a batch of back-to-back launches (per-launch
+        # time = the batch's time / its size): a pair of events around a single
+        # launch of a few microseconds adds several microseconds of its own.
+        batch = {n: (1 if n in ("gemm1", "gemm2", "shared") else SHORT_PHASE_BATCH) for n in names}
+        for _ in range(4):
+            fwd()
         for r in range(reps):
             for n in names:
                 a, b = ev[n][r]
                 a.record(st)
-                stg.run(n, st.cuda_stream)
+                for _ in range(batch[n]):
+                    stg.run(n, st.cuda_stream)
                 b.record(st)
         torch.cuda.synchronize()
         for n in names:
-            phases[n] = sum(a.elapsed_time(b) for a, b in ev[n]) / reps
+            phases[n] = sum(a.elapsed_time(b) for a, b in ev[n]) / reps / batch[n]
         log("[bench] phases (ms): " + ", ".join(f"{n}={v:.4f}" for n, v in phases.items()))
 
     d, m, k, T = cfg.d, cfg.m, cfg.k, cfg.T

@@ -244,8 +244,8 @@ moe_status moe_dispatch(const moe_shape* shape, const void* x, const int32_t* to
  *           offsets[E] <= moe_max_rows, and no expert holding more than min(T, C)
  *           rows — as moe_dispatch builds them, a token adding at most one row per
  *           expert and an expert accepting at most C; with min(T, C) <= 8 the calls
- *           run as grouped GEMVs sized by that bound, and rows of an expert past it
- *           are not computed)
+ *           run as grouped GEMVs sized by that bound, and an expert holding more
+ *           rows gets its first min(T, C) rows computed and the rest set to NaN)
  *   w_gate, w_up [E,m,d] dtype;  w_down [E,d,m] dtype
  *   H       [max_rows,d] fp32 out (rows >= offsets[E] untouched)
  *   ws      >= moe_workspace_bytes(shape, MOE_WS_FFN) (holds h) */

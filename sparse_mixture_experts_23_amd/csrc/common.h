@@ -124,6 +124,9 @@ namespace moe_kernels {
 // ([ceil(T / MOE_ROUTE_TOK)][E] int32, dispatch_router_counts_ok).  Where the
 // router path counts them while it selects (E <= 8), it fills them, clears the
 // two counters at acc_stats and sets *hist_done; otherwise it leaves them alone.
+// With *hist_done set, the status word is not written here: the router only
+// raises the flag in sync[1], and launch_dispatch (given status and that flag)
+// writes the status and clears the flag.
 size_t route_ws_bytes(const moe_dims& s);
 hipError_t launch_route(const moe_dims& s, const void* x, const float* w_r, const float* b_r,
                         int32_t* topk_ids, float* topk_w, int32_t* status, void* ws, int32_t* sync, hipStream_t st,
@@ -163,11 +166,14 @@ bool dispatch_inline_scan(const moe_dims& s);
 // ws starts with the per-block expert counts (dispatch_hist); hist_ready: the
 // router has already written them per MOE_ROUTE_TOK tokens
 // (dispatch_router_counts_ok), so the counting kernel is skipped.  x_perm
-// == nullptr: no row copy (the caller reads x through src_token).
+// == nullptr: no row copy (the caller reads x through src_token).  status /
+// route_flag (with hist_ready): the router left its non-finite flag at route_flag
+// instead of writing the status; the placement writes *status from it and clears it.
 hipError_t launch_dispatch(const moe_dims& s, const void* x, const int32_t* ids, const float* topk_w,
                            int32_t* load, int32_t* offsets, int32_t* slot, int32_t* row_of, int32_t* src_token,
                            void* x_perm, int32_t* stats, void* ws, hipStream_t st,
-                           int32_t* tprefix = nullptr, int tile_rows = 0, bool hist_ready = false);
+                           int32_t* tprefix = nullptr, int tile_rows = 0, bool hist_ready = false,
+                           int32_t* status = nullptr, int32_t* route_flag = nullptr);
 
 // Grouped expert GEMMs.  offsets == nullptr means one group covering rows [0, nrows).
 size_t gemm_ws_bytes(int G);

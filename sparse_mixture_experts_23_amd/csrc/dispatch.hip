@@ -203,9 +203,12 @@ __global__ __launch_bounds__(DB_TOK) void dispatch_place_scan_kernel(
     const int32_t* __restrict__ ids, int64_t T, int k, int E, int C, const int32_t* __restrict__ hist, int NR, int sub,
     int32_t* __restrict__ load, int32_t* __restrict__ offsets, int32_t* __restrict__ slot,
     int32_t* __restrict__ row_of, int32_t* __restrict__ src_token, int32_t* __restrict__ stats,
-    int32_t* __restrict__ tprefix, int tile_rows) {
+    int32_t* __restrict__ tprefix, int tile_rows, int32_t* __restrict__ status, int32_t* __restrict__ route_flag) {
     extern __shared__ unsigned long long masks[];
     int* s_base = reinterpret_cast<int*>(masks + 4 * E);
+    // the router's non-finite flag -> the status word (the router launch has ended)
+    if (status && blockIdx.x == 0 && threadIdx.x == 0)
+        *status = atomicExch(route_flag, 0) ? MOE_ERR_NONFINITE_LOGIT : MOE_OK;
     int* s_off = s_base + E;
     int* s_hist = s_off + E;
     __shared__ int s_sum[4], s_tiles[4], s_over[4], s_max[4], s_drop[4], s_aff[4];
@@ -772,7 +775,7 @@ size_t dispatch_ws_bytes(const moe_dims& s) {
 hipError_t launch_dispatch(const moe_dims& s, const void* x, const int32_t* ids, const float* topk_w, int32_t* load,
                            int32_t* offsets, int32_t* slot, int32_t* row_of, int32_t* src_token, void* x_perm,
                            int32_t* stats, void* ws, hipStream_t st, int32_t* tprefix, int tile_rows,
-                           bool hist_ready) {
+                           bool hist_ready, int32_t* status, int32_t* route_flag) {
     const int NB = (int)((s.T + DB_TOK - 1) / DB_TOK);
     int32_t* hist = static_cast<int32_t*>(ws);
     const size_t mask_lds = sizeof(unsigned long long) * 4 * s.E;
@@ -831,7 +834,8 @@ hipError_t launch_dispatch(const moe_dims& s, const void* x, const int32_t* ids,
         const int NR = hist_ready ? (int)((s.T + MOE_ROUTE_TOK - 1) / MOE_ROUTE_TOK) : NB;
         const size_t lds = mask_lds + sizeof(int32_t) * (2 * s.E + (size_t)NR * s.E);
         hipLaunchKernelGGL(dispatch_place_scan_kernel, dim3(NB), dim3(DB_TOK), lds, st, ids, s.T, s.k, s.E, s.C,
-                           hist, NR, sub, load, offsets, slot, row_of, src_token, stats, tprefix, tile_rows);
+                           hist, NR, sub, load, offsets, slot, row_of, src_token, stats, tprefix, tile_rows,
+                           hist_ready ? status : nullptr, route_flag);
     } else {
         if (NB > 0) {
             hipLaunchKernelGGL(dispatch_count_kernel, dim3(NB), dim3(DB_TOK), mask_lds, st, ids, s.T, s.k, s.E,

@@ -1126,9 +1126,21 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(const uint16_t* __restri
     } else if (a > 0) {
         return;
     }
-    const int R = (int)min<int64_t>(r1 - r0, RMAX);   // the host guarantees r1 - r0 <= RMAX (rows bound)
+    const int R = (int)min<int64_t>(r1 - r0, RMAX);
     const int c0 = (chunk * 4 + wave) * COLS_W;
     if (R <= 0 || c0 >= N) return;
+    if (r1 - r0 > RMAX) {
+        // more rows than the bound the host sized RMAX by (offsets a dispatch would
+        // not build): the rows past it are not computed, so they are set to NaN
+        // rather than left holding stale values
+        for (int64_t i = lane; i < (r1 - r0 - RMAX) * COLS_W; i += 64) {
+            const int64_t row = r0 + RMAX + i / COLS_W;
+            const int col = c0 + (int)(i % COLS_W);
+            if (col >= N) continue;
+            if (SWIGLU) static_cast<uint16_t*>(Cout)[row * N + col] = 0x7fc0;
+            else static_cast<float*>(Cout)[row * N + col] = __int_as_float(0x7fc00000);
+        }
+    }
     const int64_t wstride = (int64_t)N * K;
     const uint16_t* wrow[RW];
 #pragma unroll

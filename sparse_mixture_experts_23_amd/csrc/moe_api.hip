@@ -345,7 +345,8 @@ moe_status forward_impl(const moe_shape* shape, const void* x, const float* w_r,
                          stats + MOE_STAT_TOKENS_DROPPED) != hipSuccess)
             return joined(MOE_ERR_HIP);
         if (launch_dispatch(d, x, topk_ids, topk_w, load, w.offsets, slot, w.row_of, w.src_token, w.x_perm, stats,
-                            w.dispatch, st, tprefix, gemm_tile_rows(d.dtype), counted) != hipSuccess)
+                            w.dispatch, st, tprefix, gemm_tile_rows(d.dtype), counted, counted ? status : nullptr,
+                            w.sync + 1) != hipSuccess)
             return joined(MOE_ERR_HIP);
     }
     // without a side stream the shared expert runs on `stream`, after the dispatch

@@ -255,16 +255,21 @@ __device__ __forceinline__ void split3_rne(const float4 w0, const float4 w1, uin
 }
 
 // Selection for one token whose (at most 8) scores one thread holds, bias
-// included: min(kout, E) rounds of an arg-max in ascending id order with a
-// strict comparison (equal scores keep the lower id); the first k are the
-// selection, the rest the next choices (reroute).  Weights: RENORM the softmax
-// over the selected k (a next choice: its exponential over the same sum),
-// SWITCH the full softmax.  A non-finite token gets ids 0..k-1 (then -1) and
-// weights 0.  Returns the selected experts as a bit mask.
-__device__ uint32_t select8_thread(const float (&v)[8], bool bad, int E, int k, int kout, int mode, int64_t t,
-                                   int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
-                                   float* __restrict__ probs) {
+// included (experts past E hold -inf): min(kout, E) rounds of an arg-max in
+// ascending id order with a strict comparison (equal scores keep the lower id);
+// the first k are the selection, the rest the next choices (reroute).  Weights:
+// RENORM the softmax over the selected k (a next choice: its exponential over the
+// same sum), SWITCH the full softmax.  A non-finite token gets ids 0..k-1 (then
+// -1) and weights 0.  Branch-free over the experts (selects on order keys; an
+// unavailable expert has key 0, below every score's).  Returns the selected
+// experts as a bit mask.
+__device__ __forceinline__ uint32_t select8_thread(const float (&v)[8], bool bad, int E, int k, int kout, int mode,
+                                                   int64_t t, int32_t* __restrict__ topk_ids,
+                                                   float* __restrict__ topk_w, float* __restrict__ probs) {
     const int rounds = min(kout, E);
+    uint32_t key[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) key[e] = e < E ? float_order_key(v[e]) : 0u;
     uint32_t taken = 0, sel = 0;
     int ids[8];
     float gs[8];
@@ -274,20 +279,15 @@ __device__ uint32_t select8_thread(const float (&v)[8], bool bad, int E, int k, 
         gs[r] = 0.f;
         if (r < rounds) {
             int best = 0;
-            uint32_t bkey = 0;
-            float bval = 0.f;
-            bool have = false;
+            uint32_t bkey = 0u;
+            float bval = v[0];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                if (e < E && !((taken >> e) & 1u)) {
-                    const uint32_t key = float_order_key(v[e]);
-                    if (!have || key > bkey) {
-                        have = true;
-                        best = e;
-                        bkey = key;
-                        bval = v[e];
-                    }
-                }
+                const uint32_t ke = ((taken >> e) & 1u) ? 0u : key[e];
+                const bool better = ke > bkey;
+                best = better ? e : best;
+                bkey = better ? ke : bkey;
+                bval = better ? v[e] : bval;
             }
             taken |= 1u << best;
             if (r < k) sel = taken;
@@ -300,26 +300,25 @@ __device__ uint32_t select8_thread(const float (&v)[8], bool bad, int E, int k, 
 #pragma unroll
     for (int e = 0; e < 8; ++e)
         if (e < E) zall += expf(v[e] - g_top);
-    float zs = 0.f;
+    float ex[8], zs = 0.f;
 #pragma unroll
-    for (int r = 0; r < 8; ++r)
-        if (r < k) zs += expf(gs[r] - g_top);
+    for (int r = 0; r < 8; ++r) {
+        ex[r] = r < rounds ? expf(gs[r] - g_top) : 0.f;
+        if (r < k) zs += ex[r];
+    }
     const float z = mode == MOE_GATE_SWITCH ? zall : zs;
-    for (int r = 0; r < kout; ++r) {
-        int id = -1;
-        float wt = 0.f;
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-            if (q == r && q < rounds) {
-                id = ids[q];
-                wt = expf(gs[q] - g_top) / z;
+    for (int r = 0; r < 8; ++r) {
+        if (r < kout) {
+            int id = r < rounds ? ids[r] : -1;
+            float wt = r < rounds ? ex[r] / z : 0.f;
+            if (bad) {
+                id = r < k ? r : -1;
+                wt = 0.f;
             }
-        if (bad) {
-            id = r < k ? r : -1;
-            wt = 0.f;
+            topk_ids[t * kout + r] = id;
+            topk_w[t * kout + r] = wt;
         }
-        topk_ids[t * kout + r] = id;
-        topk_w[t * kout + r] = wt;
     }
     if (probs) {
 #pragma unroll
@@ -327,6 +326,80 @@ __device__ uint32_t select8_thread(const float (&v)[8], bool bad, int E, int k, 
             if (e < E) probs[t * E + e] = bad ? 0.f : expf(v[e] - g_top) / zall;
     }
     return bad ? (1u << k) - 1u : sel;
+}
+
+// Wave 0 of a 16-token router workgroup, after the waves' partial scores are in
+// red[wave][token * 8 + expert]: one lane per token adds them in wave order plus
+// the bias and selects; the workgroup's per-expert selection counts go to hist
+// (for the dispatch).  Non-finite scores raise the flag in the sync words.
+// Without hist the workgroup then counts itself done (its atomic in flight during
+// the selection), and the last workgroup to finish writes the status and puts the
+// sync words back to zero (relaxed device-scope atomics; the flag's atomic
+// completes before the count's is issued).  With hist the counting is skipped:
+// the dispatch kernel that consumes the counts runs after this launch and turns
+// the flag into the status (one atomic, off this kernel's critical path).
+__device__ __forceinline__ void route8_select(const float (*red)[RL_TOK * 8], int64_t t0, int64_t T, int E, int k,
+                                              int kout, int mode, const float* __restrict__ b_r,
+                                              int32_t* __restrict__ sync, int32_t* __restrict__ topk_ids,
+                                              float* __restrict__ topk_w, int32_t* __restrict__ status,
+                                              float* __restrict__ probs, int32_t* __restrict__ hist) {
+    const int lane = threadIdx.x % 64;
+    const int r = lane;
+    const int64_t t = t0 + r;
+    const bool valid = r < RL_TOK && t < T;
+    const int rr = min(r, RL_TOK - 1);
+    float s[8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const float4 a = reinterpret_cast<const float4*>(red[0] + rr * 8)[h];
+        s[4 * h] = a.x;
+        s[4 * h + 1] = a.y;
+        s[4 * h + 2] = a.z;
+        s[4 * h + 3] = a.w;
+    }
+#pragma unroll
+    for (int w = 1; w < RL_WAVES; ++w) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const float4 a = reinterpret_cast<const float4*>(red[w] + rr * 8)[h];
+            s[4 * h] += a.x;
+            s[4 * h + 1] += a.y;
+            s[4 * h + 2] += a.z;
+            s[4 * h + 3] += a.w;
+        }
+    }
+    float v[8];
+    bool bad = false;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        v[e] = -INFINITY;
+        if (e < E) {
+            v[e] = s[e] + (b_r ? b_r[e] : 0.f);
+            bad |= valid && !isfinite(v[e]);
+        }
+    }
+    // with hist (the forward), the dispatch's placement kernel that reads the
+    // counts writes the status from the flag: no workgroup here waits for an atomic
+    const bool defer = hist != nullptr;
+    if (__any(bad) && lane == 0) {
+        atomicOr(&sync[1], 1);
+        if (!defer) __builtin_amdgcn_s_waitcnt(0);   // the flag is in before this workgroup counts itself done
+    }
+    int done = 0;
+    if (lane == 0 && !defer) done = atomicAdd(&sync[0], 1);
+    uint32_t sel = 0;
+    if (valid) sel = select8_thread(v, bad, E, k, kout, mode, t, topk_ids, topk_w, probs);
+    if (hist) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int cnt = __popcll(__ballot((sel >> e) & 1u));
+            if (e < E && lane == e) hist[(int64_t)blockIdx.x * E + e] = cnt;
+        }
+    }
+    if (lane == 0 && !defer && done == (int)gridDim.x - 1) {   // the last workgroup
+        *status = atomicExch(&sync[1], 0) ? MOE_ERR_NONFINITE_LOGIT : MOE_OK;
+        atomicExch(&sync[0], 0);
+    }
 }
 
 template <int NCT>   // chunks, fully unrolled (chunks past d are zero chunks)
@@ -337,7 +410,7 @@ __global__ __launch_bounds__(RL_THREADS) void route_lds8_kernel(
     int32_t* __restrict__ acc_stats) {
     __shared__ __align__(16) unsigned char xs[2][RL_TOK * RL_ROW];
     __shared__ uint4 bs[2][RL_STEPS * 128];
-    __shared__ float red[RL_WAVES][RL_TOK * 8];
+    __shared__ __align__(16) float red[RL_WAVES][RL_TOK * 8];
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
     const int64_t t0 = (int64_t)blockIdx.x * RL_TOK;
     const int NC = (d + RL_KC - 1) / RL_KC;   // <= NCT
@@ -427,43 +500,7 @@ __global__ __launch_bounds__(RL_THREADS) void route_lds8_kernel(
         if (lr < 8) red[wave][(4 * grp + i) * 8 + lr] = (acc0[i] + mid) + acc1[i];
     }
     __syncthreads();
-    if (wave == 0) {
-        // one thread per token: the waves' sums in wave order, bias, selection
-        const int r = lane;
-        const int64_t t = t0 + r;
-        const bool valid = r < RL_TOK && t < T;
-        float v[8];
-        bool bad = false;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            v[e] = -INFINITY;
-            if (e < E && valid) {
-                const int p = r * 8 + e;
-                float sum = red[0][p];
-#pragma unroll
-                for (int w = 1; w < RL_WAVES; ++w) sum += red[w][p];
-                v[e] = sum + (b_r ? b_r[e] : 0.f);
-                bad |= !isfinite(v[e]);
-            }
-        }
-        uint32_t sel = 0;
-        if (valid) sel = select8_thread(v, bad, E, k, kout, mode, t, topk_ids, topk_w, probs);
-        if (hist) {   // this workgroup's selection count per expert, for the dispatch
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int cnt = __popcll(__ballot((sel >> e) & 1u));
-                if (e < E && lane == e) hist[(int64_t)blockIdx.x * E + e] = cnt;
-            }
-        }
-        if (__any(bad) && lane == 0) {
-            atomicOr(&sync[1], 1);
-            __builtin_amdgcn_s_waitcnt(0);   // the flag is in before this workgroup counts itself done
-        }
-        if (lane == 0 && atomicAdd(&sync[0], 1) == (int)gridDim.x - 1) {   // the last workgroup
-            *status = atomicExch(&sync[1], 0) ? MOE_ERR_NONFINITE_LOGIT : MOE_OK;
-            atomicExch(&sync[0], 0);
-        }
-    }
+    if (wave == 0) route8_select(red, t0, T, E, k, kout, mode, b_r, sync, topk_ids, topk_w, status, probs, hist);
 }
 
 // ---------------------------------------------------------------------------

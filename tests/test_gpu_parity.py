@@ -633,7 +633,8 @@ def test_router_sync_words_return_to_zero(cfg):
     """The E <= 8 router's counters live in the first MOE_SYNC_BYTES of the route,
     route-stats and forward workspaces: zero before the first call, and every
     call must leave them zero (the next call counts from there).  Repeated calls
-    on one workspace, with a non-finite score in between, give identical ids."""
+    on one workspace, with a non-finite score in between, give identical ids and
+    the right status word (in the forward written by the dispatch's placement)."""
     inp = make_inputs(cfg, 0, DEV)
     shape = shape_of(cfg)
     st = torch.cuda.current_stream().cuda_stream
@@ -662,12 +663,16 @@ def test_router_sync_words_return_to_zero(cfg):
         torch.cuda.synchronize()
         assert int(rs[:L.MOE_SYNC_BYTES].count_nonzero()) == 0
         assert torch.equal(ids[1], ids[0])
+    # the forward: the router leaves its non-finite flag to the dispatch's
+    # placement kernel, which writes the status and clears the flag
     layer = api.MoELayer(shape, DEV)
-    for _ in range(2):
-        layer.forward(inp.x, inp.w_r, inp.b_r, inp.w_gate, inp.w_up, inp.w_down)
+    for i, (x, want) in enumerate(((inp.x, L.MOE_OK), (bad, L.MOE_ERR_NONFINITE_LOGIT), (inp.x, L.MOE_OK))):
+        layer.forward(x, inp.w_r, inp.b_r, inp.w_gate, inp.w_up, inp.w_down)
         torch.cuda.synchronize()
-        assert int(layer.ws[:L.MOE_SYNC_BYTES].count_nonzero()) == 0
-        assert torch.equal(layer.topk_ids, ids[0])
+        assert int(layer.status.item()) == want, f"forward {i}"
+        assert int(layer.ws[:L.MOE_SYNC_BYTES].count_nonzero()) == 0, f"sync words left non-zero after forward {i}"
+        if want == L.MOE_OK:
+            assert torch.equal(layer.topk_ids, ids[0])
 
 
 def test_run_twice_bitwise_and_causal_prefix():
@@ -720,6 +725,45 @@ def test_expert_gemms_thin_tiles(d, m):
                            round_h_bf16=True)
         worst = max(worst, check_output(H64[lo:hi], ref, BF16_TOL, f"group {g} ({hi - lo} rows)"))
     log(f"[parity] expert GEMMs d={d} m={m}: ok  max rel err {worst:.2e}")
+
+
+@pytest.mark.parametrize("T,groups", [(1, [2, 0]), (2, [0, 4, 0]), (4, [7, 0, 1]), (8, [16, 0, 0, 0])])
+def test_expert_ffn_group_over_the_row_bound(T, groups):
+    """Decode-sized shapes run the expert GEMMs as grouped GEMVs sized by the
+    per-expert row bound min(T, C).  Offsets that give an expert more rows than
+    that (outside what moe_dispatch builds) must not leave stale values behind:
+    the first min(T, C) rows of such an expert are computed (checked against the
+    oracle's SwiGLU expert, as are the other groups), the rest read NaN in h and
+    in H, through moe_expert_ffn and the two halves alone."""
+    E, k, d, m = len(groups), 2, 192, 320
+    A = sum(groups)
+    assert A <= T * k
+    cfg = MoEConfig("gemv_over_bound", T=T, d=d, m=m, E=E, k=k, dtype="bf16", gate_mode=0, cf=None, cfg_id=26)
+    log(f"[parity] grouped GEMV with groups {groups} over the row bound {T}")
+    inp = make_inputs(cfg, 0, DEV)
+    shape = shape_of(cfg)
+    R = L.moe_max_rows(shape)
+    assert R >= A
+    x_perm = (torch.randn(R, d, generator=torch.Generator().manual_seed(7)) * 0.5).to(torch.bfloat16).to(DEV)
+    offs = np.concatenate([[0], np.cumsum(groups)]).astype(np.int32)
+    offsets = torch.from_numpy(offs).to(DEV)
+    H_ffn = api.expert_ffn(shape, x_perm, offsets, inp.w_gate, inp.w_up, inp.w_down)
+    h = api.expert_gemm1(shape, x_perm, offsets, inp.w_gate, inp.w_up)
+    H = api.expert_gemm2(shape, h, offsets, inp.w_down)
+    torch.cuda.synchronize()
+    assert torch.equal(H_ffn[:A].isnan(), H[:A].isnan())
+    x64, h64, H64 = np64(x_perm), np64(h), np64(H)
+    for g in range(E):
+        lo, hi = int(offs[g]), int(offs[g + 1])
+        if hi == lo:
+            continue
+        cut = min(hi, lo + T)
+        ref = O.swiglu_ffn(x64[lo:cut], np64(inp.w_gate[g]), np64(inp.w_up[g]), np64(inp.w_down[g]),
+                           round_h_bf16=True)
+        check_output(H64[lo:cut], ref, BF16_TOL, f"group {g} ({hi - lo} rows, bound {T})")
+        assert torch.equal(H_ffn[lo:cut], H[lo:cut])
+        assert np.isfinite(h64[lo:cut]).all()
+        assert np.isnan(h64[cut:hi]).all() and np.isnan(H64[cut:hi]).all(), f"group {g}: rows past the bound"
 
 
 # ---------------------------------------------------------------------------
