@@ -452,15 +452,12 @@ __global__ __launch_bounds__(RL_THREADS) void route_lds8_kernel(
     };
 #pragma unroll
     for (int u = 0; u < RL_DEPTH; ++u) issue(u, u);
-    floatx4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    const int lr = lane % 16, grp = lane / 16;
-    // Straight-line code over the chunks (no loop back-edge, no branch on loaded
-    // data), so the compiler's load counting waits for exactly the chunk in hand.
-#pragma unroll
-    for (int c = 0; c < NCT; ++c) {
+    // Chunk c's activations -> LDS rows of buffer c & 1 (units past d zeroed by a
+    // mask, which the compiler cannot turn into a conditional load), its weights ->
+    // the planes (zero for experts >= E and K past d); then the freed ring slot
+    // takes the loads of chunk c + RL_DEPTH.
+    auto stage = [&](int c) {
         const int u = c % RL_DEPTH, buf = c & 1;
-        // activations of chunk c -> LDS rows (units past d zeroed by a mask, which
-        // the compiler cannot turn into a conditional load)
 #pragma unroll
         for (int i = 0; i < RL_XU; ++i) {
             const int uu = tid + RL_THREADS * i;
@@ -469,7 +466,6 @@ __global__ __launch_bounds__(RL_THREADS) void route_lds8_kernel(
             *reinterpret_cast<uint4*>(&xs[buf][(uu / 64) * RL_ROW + (uu % 64) * 16]) =
                 uint4{v.x & keep, v.y & keep, v.z & keep, v.w & keep};
         }
-        // weights of chunk c -> planes (zero for experts >= E and K past d)
 #pragma unroll
         for (int j = 0; j < RL_WI; ++j) {
             const int it = tid + RL_THREADS * j;
@@ -482,16 +478,35 @@ __global__ __launch_bounds__(RL_THREADS) void route_lds8_kernel(
             b[rl_slot(s, 16 * q + e + 8)] = uint4{M.x & keep, M.y & keep, M.z & keep, M.w & keep};
             b[64 + rl_slot(s, 16 * q + e)] = uint4{Lo.x & keep, Lo.y & keep, Lo.z & keep, Lo.w & keep};
         }
-        if (c + RL_DEPTH < NCT) issue(u, c + RL_DEPTH);   // the ring slot just emptied
-        __syncthreads();
+        if (c + RL_DEPTH < NCT) issue(u, c + RL_DEPTH);
+    };
+    floatx4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    const int lr = lane % 16, grp = lane / 16;
+    // Software pipeline, one barrier per chunk: while chunk c's operands are read
+    // from LDS and multiplied, chunk c + 1 is split and staged into the other
+    // buffer (last read for chunk c - 1, before the previous barrier).
+    // Straight-line code over the chunks (no loop back-edge, no branch on loaded
+    // data), so the compiler's load counting waits for exactly the chunk in hand.
+    stage(0);
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) {
+        const int buf = c & 1;
+        uint4 a[RL_SPW], b0[RL_SPW], b1[RL_SPW];
 #pragma unroll
         for (int j = 0; j < RL_SPW; ++j) {
             const int s = RL_SPW * wave + j;
-            const uint4 a = *reinterpret_cast<const uint4*>(&xs[buf][lr * RL_ROW + (32 * s + 8 * grp) * 2]);
-            const uint4 b0 = bs[buf][s * 128 + rl_slot(s, lane)], b1 = bs[buf][s * 128 + 64 + rl_slot(s, lane)];
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b0), acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b1), acc1, 0, 0, 0);
+            a[j] = *reinterpret_cast<const uint4*>(&xs[buf][lr * RL_ROW + (32 * s + 8 * grp) * 2]);
+            b0[j] = bs[buf][s * 128 + rl_slot(s, lane)];
+            b1[j] = bs[buf][s * 128 + 64 + rl_slot(s, lane)];
         }
+        if (c + 1 < NCT) stage(c + 1);
+#pragma unroll
+        for (int j = 0; j < RL_SPW; ++j) {
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[j]), as_bf16x8(b0[j]), acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[j]), as_bf16x8(b1[j]), acc1, 0, 0, 0);
+        }
+        if (c + 1 < NCT) __syncthreads();
     }
     // lane (lr, grp) holds column lr of both tiles for tokens 4 grp + i
 #pragma unroll
