@@ -219,11 +219,9 @@ __device__ void select_token(const float* __restrict__ row, const float* __restr
 constexpr int RL_TOK = MOE_ROUTE_TOK;               // tokens per workgroup
 constexpr int RL_KC = 512;                          // K elements per chunk
 constexpr int RL_STEPS = RL_KC / 32;                // MFMA K steps per chunk
-constexpr int RL_ROW = RL_KC * 2 + 16;              // LDS bytes per staged row (padded: conflict-free A reads)
 constexpr int RL_DEPTH = 4;                         // chunks of loads in flight
 constexpr int RL_WAVES = 8;                         // K steps of a chunk split over the waves
 constexpr int RL_THREADS = 64 * RL_WAVES;
-constexpr int RL_XU = RL_TOK * (RL_KC / 8) / RL_THREADS;   // 16-byte activation units per thread and chunk
 constexpr int RL_WI = 8 * RL_STEPS * 4 / RL_THREADS;       // 8-weight items per thread and chunk
 constexpr int RL_SPW = RL_STEPS / RL_WAVES;                 // K steps per wave and chunk
 
@@ -408,7 +406,6 @@ __global__ __launch_bounds__(RL_THREADS) void route_lds8_kernel(
     int E, int k, int kout, int mode, int32_t* __restrict__ sync, int32_t* __restrict__ topk_ids,
     float* __restrict__ topk_w, int32_t* __restrict__ status, float* __restrict__ probs, int32_t* __restrict__ hist,
     int32_t* __restrict__ acc_stats) {
-    __shared__ __align__(16) unsigned char xs[2][RL_TOK * RL_ROW];
     __shared__ uint4 bs[2][RL_STEPS * 128];
     __shared__ __align__(16) float red[RL_WAVES][RL_TOK * 8];
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
@@ -420,23 +417,30 @@ __global__ __launch_bounds__(RL_THREADS) void route_lds8_kernel(
         const int b = i / (RL_STEPS * 32), r = i % (RL_STEPS * 32), s = r / 32, z = r % 32;
         bs[b][s * 128 + 64 + rl_slot(s, 16 * (z / 8) + 8 + z % 8)] = uint4{0u, 0u, 0u, 0u};
     }
+    const int lr = lane % 16, grp = lane / 16;
     // Loads of chunk c, every one unconditional from a clamped, valid address (a
-    // chunk past the last repeats it, a unit past d reads the row's last 16 bytes
-    // and is zeroed when stored).  Activations: unit u = tid + 256 i of the chunk's
-    // 16 rows x 64 units of 16 bytes (row u / 64).  Weights: item it = tid + 256 j
-    // of 8 experts x 16 steps x 4 groups of 8 (expert it / 64, step (it / 4) % 16,
-    // group it % 4), 32 bytes each.
-    uint4 xr[RL_DEPTH][RL_XU];
+    // chunk past the last repeats it, K past d reads the row's last 16 bytes and
+    // is zeroed before use).  Activations go straight to the MFMA A operand: lane
+    // (token lr, group grp) loads the 16 bytes at K offset 32 s + 8 grp of each of
+    // its wave's steps s.  Weights: item it = tid + 512 j of 8 experts x 16 steps x
+    // 4 groups of 8 (expert it / 64, step (it / 4) % 16, group it % 4), 32 bytes
+    // each, split into the LDS planes by the whole workgroup.
+    const uint16_t* xrow = x + min(t0 + lr, T - 1) * (int64_t)d;
+    uint4 xr[RL_DEPTH][RL_SPW];
     float4 wr[RL_DEPTH][RL_WI][2];
-    auto issue = [&](int slot, int c) {
+    auto issue_x = [&](int slot, int c) {
         const int cc = min(c, NC - 1);
 #pragma unroll
-        for (int i = 0; i < RL_XU; ++i) {
-            const int u = tid + RL_THREADS * i;
-            const int64_t row = min(t0 + u / 64, T - 1);
-            const int kk = min(cc * RL_KC + 8 * (u % 64), d - 8);
-            xr[slot][i] = *reinterpret_cast<const uint4*>(x + row * d + kk);
+        for (int j = 0; j < RL_SPW; ++j) {
+            const int kk = min(cc * RL_KC + 32 * (RL_SPW * wave + j) + 8 * grp, d - 8);
+            xr[slot][j] = *reinterpret_cast<const uint4*>(xrow + kk);
         }
+        // keep the loads in issue order: the in-order completion count then waits
+        // for exactly the chunk in hand
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto issue_w = [&](int slot, int c) {
+        const int cc = min(c, NC - 1);
 #pragma unroll
         for (int j = 0; j < RL_WI; ++j) {
             const int it = tid + RL_THREADS * j;
@@ -446,26 +450,17 @@ __global__ __launch_bounds__(RL_THREADS) void route_lds8_kernel(
             wr[slot][j][0] = src[0];
             wr[slot][j][1] = src[1];
         }
-        // keep the loads in chunk order: the in-order completion count then waits
-        // for exactly the chunk in hand
         __builtin_amdgcn_sched_barrier(0);
     };
 #pragma unroll
-    for (int u = 0; u < RL_DEPTH; ++u) issue(u, u);
-    // Chunk c's activations -> LDS rows of buffer c & 1 (units past d zeroed by a
-    // mask, which the compiler cannot turn into a conditional load), its weights ->
-    // the planes (zero for experts >= E and K past d); then the freed ring slot
-    // takes the loads of chunk c + RL_DEPTH.
+    for (int u = 0; u < RL_DEPTH; ++u) {
+        issue_w(u, u);
+        issue_x(u, u);
+    }
+    // Chunk c's weights -> the planes of LDS buffer c & 1 (zero for experts >= E
+    // and K past d); the freed ring slot takes the weights of chunk c + RL_DEPTH.
     auto stage = [&](int c) {
         const int u = c % RL_DEPTH, buf = c & 1;
-#pragma unroll
-        for (int i = 0; i < RL_XU; ++i) {
-            const int uu = tid + RL_THREADS * i;
-            const uint32_t keep = c * RL_KC + 8 * (uu % 64) < d ? 0xffffffffu : 0u;
-            const uint4 v = xr[u][i];
-            *reinterpret_cast<uint4*>(&xs[buf][(uu / 64) * RL_ROW + (uu % 64) * 16]) =
-                uint4{v.x & keep, v.y & keep, v.z & keep, v.w & keep};
-        }
 #pragma unroll
         for (int j = 0; j < RL_WI; ++j) {
             const int it = tid + RL_THREADS * j;
@@ -478,34 +473,36 @@ __global__ __launch_bounds__(RL_THREADS) void route_lds8_kernel(
             b[rl_slot(s, 16 * q + e + 8)] = uint4{M.x & keep, M.y & keep, M.z & keep, M.w & keep};
             b[64 + rl_slot(s, 16 * q + e)] = uint4{Lo.x & keep, Lo.y & keep, Lo.z & keep, Lo.w & keep};
         }
-        if (c + RL_DEPTH < NCT) issue(u, c + RL_DEPTH);
+        if (c + RL_DEPTH < NCT) issue_w(u, c + RL_DEPTH);
     };
     floatx4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    const int lr = lane % 16, grp = lane / 16;
-    // Software pipeline, one barrier per chunk: while chunk c's operands are read
-    // from LDS and multiplied, chunk c + 1 is split and staged into the other
-    // buffer (last read for chunk c - 1, before the previous barrier).
+    // Software pipeline, one barrier per chunk: while chunk c's weight planes are
+    // read from LDS and multiplied, chunk c + 1's are split and staged into the
+    // other buffer (last read for chunk c - 1, before the previous barrier).
     // Straight-line code over the chunks (no loop back-edge, no branch on loaded
     // data), so the compiler's load counting waits for exactly the chunk in hand.
     stage(0);
     __syncthreads();
 #pragma unroll
     for (int c = 0; c < NCT; ++c) {
-        const int buf = c & 1;
-        uint4 a[RL_SPW], b0[RL_SPW], b1[RL_SPW];
+        const int u = c % RL_DEPTH, buf = c & 1;
+        uint4 b0[RL_SPW], b1[RL_SPW];
 #pragma unroll
         for (int j = 0; j < RL_SPW; ++j) {
             const int s = RL_SPW * wave + j;
-            a[j] = *reinterpret_cast<const uint4*>(&xs[buf][lr * RL_ROW + (32 * s + 8 * grp) * 2]);
             b0[j] = bs[buf][s * 128 + rl_slot(s, lane)];
             b1[j] = bs[buf][s * 128 + 64 + rl_slot(s, lane)];
         }
         if (c + 1 < NCT) stage(c + 1);
 #pragma unroll
         for (int j = 0; j < RL_SPW; ++j) {
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[j]), as_bf16x8(b0[j]), acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[j]), as_bf16x8(b1[j]), acc1, 0, 0, 0);
+            const uint32_t keep = c * RL_KC + 32 * (RL_SPW * wave + j) + 8 * grp < d ? 0xffffffffu : 0u;
+            const uint4 v = xr[u][j];
+            const uint4 a = {v.x & keep, v.y & keep, v.z & keep, v.w & keep};
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b0[j]), acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b1[j]), acc1, 0, 0, 0);
         }
+        if (c + RL_DEPTH < NCT) issue_x(u, c + RL_DEPTH);
         if (c + 1 < NCT) __syncthreads();
     }
     // lane (lr, grp) holds column lr of both tiles for tokens 4 grp + i
