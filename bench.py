@@ -38,7 +38,7 @@ METRIC = "MoE-layer tokens/sec on 1 MI355X (Mixtral shape); expert-GEMM % of MFM
 # the bytes-per-KiB that the same counter reports for a plain device copy of known
 # size (`bench.py --copy-calibration`).  Valid only for the GEMM source it was
 # taken on: reported as null once expert_gemm.hip differs from that hash.
-GEMM1_TRAFFIC = {"bytes": 6458101661, "source_sha256": "c76b687c0157b1b53b5b8dc3f7e2496aad83aa0e0d555786d4a10e4c57ec372d"}
+GEMM1_TRAFFIC = {"bytes": 6352646976, "source_sha256": "45a1b2906a5d85cfd46fdcf4da9fb591aabf6280919d2fcfbcb731aaaf730681"}
 GEMM_SOURCE = os.path.join(ROOT, "sparse_mixture_experts_23_amd", "csrc", "expert_gemm.hip")
 
 
@@ -51,7 +51,8 @@ def gemm1_traffic_bytes():
     return GEMM1_TRAFFIC["bytes"] if sha == GEMM1_TRAFFIC["source_sha256"] else None
 
 
-SHORT_PHASE_BATCH = 10   # launches per timed batch of a short (memory-bound) phase
+SHORT_PHASE_BATCH = 10   # launches per timed batch of a short phase
+SHORT_PHASE_MS = 0.2     # phases whose single launch takes less are timed in batches
 
 
 def copy_calibration(nbytes: int, reps: int):
@@ -314,9 +315,15 @@ def main():
         st = torch.cuda.current_stream()
         names = (["route", "dispatch", "gemm1", "gemm2"] + (["shared"] if cfg.m_shared else []) + ["combine"]
                  + ["route_stats", "balance"])
-        for n in names:   # warm each stage once
+        single = {}
+        for n in names:   # warm each stage once, with a rough single-launch time
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(st)
             stg.run(n, st.cuda_stream)
+            b.record(st)
+            single[n] = (a, b)
         torch.cuda.synchronize()
+        single = {n: a.elapsed_time(b) for n, (a, b) in single.items()}
         reps = max(args.steps, 1)
         ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
               for n in names}
@@ -326,10 +333,11 @@ def main():
         # never idles, so the heavy GEMMs run at the clock the timed forwards saw
         # (an idle gap lets the power controller overshoot: after one, the first
         # GEMMs run ~20 % slower for several milliseconds).
-        # A short phase is timed over a batch of back-to-back launches (per-launch
-        # time = the batch's time / its size): a pair of events around a single
-        # launch of a few microseconds adds several microseconds of its own.
-        batch = {n: (1 if n in ("gemm1", "gemm2", "shared") else SHORT_PHASE_BATCH) for n in names}
+        # A short phase (under SHORT_PHASE_MS for one launch) is timed over a batch
+        # of back-to-back launches (per-launch time = the batch's time / its size):
+        # a pair of events around a single launch of a few microseconds adds
+        # several microseconds of its own.
+        batch = {n: (SHORT_PHASE_BATCH if single[n] < SHORT_PHASE_MS else 1) for n in names}
         for _ in range(4):
             fwd()
         for r in range(reps):
