@@ -738,7 +738,7 @@ def test_expert_ffn_group_over_the_row_bound(T, groups):
     E, k, d, m = len(groups), 2, 192, 320
     A = sum(groups)
     assert A <= T * k
-    cfg = MoEConfig("gemv_over_bound", T=T, d=d, m=m, E=E, k=k, dtype="bf16", gate_mode=0, cf=None, cfg_id=26)
+    cfg = MoEConfig("gemv_over_bound", T=T, d=d, m=m, E=E, k=k, dtype="bf16", gate_mode=0, cf=None, cfg_id=101)
     log(f"[parity] grouped GEMV with groups {groups} over the row bound {T}")
     inp = make_inputs(cfg, 0, DEV)
     shape = shape_of(cfg)
