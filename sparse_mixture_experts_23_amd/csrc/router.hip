@@ -14,9 +14,10 @@
 // MFMA units -- an fp32 dot product up to summation order.
 //
 // E <= 8 (bf16 activations, T > 16): one kernel; each workgroup splits w_r into
-//   the planes itself, chunk by chunk, as ready-made MFMA operands (two 16-column
-//   tiles: hi | mid and lo | 0) while it stages 16 tokens' activations through
-//   LDS with coalesced loads, then selects (route_lds8_kernel).
+//   the planes itself, chunk by chunk, as ready-made MFMA operands in LDS (two
+//   16-column tiles: hi | mid and lo | 0), its lanes load their 16 tokens'
+//   activations straight into the MFMA operands, then it selects
+//   (route_lds8_kernel).
 // E <= 64: one fused kernel; 8 waves share 16 tokens, each wave takes one K
 //   slice with all its loads in flight at once, the slices are summed in LDS in a
 //   fixed order and the waves select.
@@ -192,30 +193,32 @@ __device__ void select_token(const float* __restrict__ row, const float* __restr
 }
 
 // ---------------------------------------------------------------------------
-// E <= 8, bf16 activations, T > 16: 16 tokens per workgroup, K staged through LDS
+// E <= 8, bf16 activations, T > 16: 16 tokens per workgroup, weight planes in LDS
 // ---------------------------------------------------------------------------
 //
 // Each workgroup takes 16 tokens over the whole K, in chunks of 512.  Per chunk,
-// the activations are read with coalesced 16-byte loads (a wave instruction
-// reads 1 KB of one token row) and written to LDS, and the chunk of w_r (fp32)
-// is split into three exact bf16 planes (hi + mid + lo carries all 24
-// significand bits; the hardware round-to-nearest-even conversion), stored as
-// the B operands of v_mfma_f32_16x16x32_bf16 for two 16-column tiles, [hi
-// e0..7 | mid e0..7] and [lo e0..7 | 0].  Wave w of 8 then runs K steps 2w, 2w+1 of
-// the chunk: A fragments from the staged rows, 2 MFMAs per step, fp32
-// accumulation (three exact products per element: an fp32 dot product up to
-// summation order).  The loads of the next RL_DEPTH chunks (activations and
-// weights, in chunk order, so the in-order completion of loads never makes a
-// chunk wait for a later one) are in flight while a chunk is computed; the LDS
-// is double-buffered, so one barrier per chunk suffices.  At the end a lane adds
-// its hi column, the mid column one lane over and its lo column, the waves'
-// sums are added in wave order, and one thread per token selects.
+// the workgroup splits the chunk of w_r (fp32) into three exact bf16 planes
+// (hi + mid + lo carries all 24 significand bits; the hardware
+// round-to-nearest-even conversion) and stores them in LDS as the B operands of
+// v_mfma_f32_16x16x32_bf16 for two 16-column tiles, [hi e0..7 | mid e0..7] and
+// [lo e0..7 | 0].  Wave w of 8 runs K steps 2w, 2w+1 of every chunk; each lane
+// loads its own A fragment (16 bytes of its token row per step) straight from
+// memory; 2 MFMAs per step, fp32 accumulation (three exact products per
+// element: an fp32 dot product up to summation order).  The loads of the next
+// RL_DEPTH chunks are in flight while a chunk is computed, in chunk order, so
+// the in-order completion of loads never makes a chunk wait for a later one;
+// the planes are double-buffered and chunk c + 1 is staged while chunk c is
+// multiplied, so one barrier per chunk suffices.  At the end a lane adds its hi
+// column, the mid column one lane over and its lo column, the waves' sums are
+// added in wave order, and one thread per token selects.
 //
 // The status word needs no clearing launch: a workgroup that finds a
-// non-finite score raises a flag in the sync words, every workgroup then counts
-// itself done, and the last one writes the status from the flag and puts both
-// words back to zero (relaxed device-scope atomics; the flag's atomic completes
-// before the count's is issued).
+// non-finite score raises a flag in the sync words.  Standalone, every
+// workgroup then counts itself done, and the last one writes the status from
+// the flag and puts both words back to zero (relaxed device-scope atomics; the
+// flag's atomic completes before the count's is issued).  In the forward (the
+// router also writing the dispatch's counts) the dispatch's placement kernel
+// turns the flag into the status instead.
 constexpr int RL_TOK = MOE_ROUTE_TOK;               // tokens per workgroup
 constexpr int RL_KC = 512;                          // K elements per chunk
 constexpr int RL_STEPS = RL_KC / 32;                // MFMA K steps per chunk
