@@ -17,6 +17,7 @@
 namespace {
 
 constexpr int COMBINE_U = 4;   // 64-lane column blocks per wave (float4 each; scalar path: floats)
+constexpr int COMBINE_PR = 4;  // paths whose rows are loaded together (vector path)
 
 // H1 (nullable): np further K-split partials of H, block p at H1 + p ps; the row
 // used is ((H + P_0) + P_1) + ... (the value a caller that folded them into H in
@@ -58,46 +59,57 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                 const int c = c0 + u * 64 + lane;
                 acc[u] = (shared_out && c < nv) ? S4[t * nv + c] : float4{0.f, 0.f, 0.f, 0.f};
             }
-            for (int r = 0; r < k; ++r) {
-                const int row = lane_value(myrow, r);
-                const float a = lane_value(myw, r);
-                if (row < 0) continue;   // uniform across the wave
-                float4 h[U];
+            // COMBINE_PR paths per round: their rows' loads are issued together, then
+            // they are added in rank order (a rejected path loads nothing, adds nothing)
+            for (int r0 = 0; r0 < k; r0 += COMBINE_PR) {
+                int row[COMBINE_PR];
+                float a[COMBINE_PR];
+                float4 h[COMBINE_PR][U];
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int c = c0 + u * 64 + lane;
-                    h[u] = c < nv ? H4[(int64_t)row * nv + c] : float4{0.f, 0.f, 0.f, 0.f};
-                }
-                // the first partial's loads are issued with H's (no loop in between)
-                if (np > 0) {
-#pragma unroll
-                    for (int u = 0; u < U; ++u) {
-                        const int c = c0 + u * 64 + lane;
-                        const float4 h1 = c < nv ? H14[(int64_t)row * nv + c] : float4{0.f, 0.f, 0.f, 0.f};
-                        h[u].x += h1.x;
-                        h[u].y += h1.y;
-                        h[u].z += h1.z;
-                        h[u].w += h1.w;
-                    }
-                }
-                for (int p = 1; p < np; ++p) {
-                    const float4* P4 = H14 + p * (ps / 4);
+                for (int q = 0; q < COMBINE_PR; ++q) {
+                    row[q] = r0 + q < k ? lane_value(myrow, r0 + q) : -1;
+                    a[q] = r0 + q < k ? lane_value(myw, r0 + q) : 0.f;
+                    if (row[q] < 0) continue;   // uniform across the wave
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
                         const int c = c0 + u * 64 + lane;
-                        const float4 h1 = c < nv ? P4[(int64_t)row * nv + c] : float4{0.f, 0.f, 0.f, 0.f};
-                        h[u].x += h1.x;
-                        h[u].y += h1.y;
-                        h[u].z += h1.z;
-                        h[u].w += h1.w;
+                        h[q][u] = c < nv ? H4[(int64_t)row[q] * nv + c] : float4{0.f, 0.f, 0.f, 0.f};
+                    }
+                    // the first partial's loads are issued with H's (no loop in between)
+                    if (np > 0) {
+#pragma unroll
+                        for (int u = 0; u < U; ++u) {
+                            const int c = c0 + u * 64 + lane;
+                            const float4 h1 = c < nv ? H14[(int64_t)row[q] * nv + c] : float4{0.f, 0.f, 0.f, 0.f};
+                            h[q][u].x += h1.x;
+                            h[q][u].y += h1.y;
+                            h[q][u].z += h1.z;
+                            h[q][u].w += h1.w;
+                        }
+                    }
+                    for (int p = 1; p < np; ++p) {
+                        const float4* P4 = H14 + p * (ps / 4);
+#pragma unroll
+                        for (int u = 0; u < U; ++u) {
+                            const int c = c0 + u * 64 + lane;
+                            const float4 h1 = c < nv ? P4[(int64_t)row[q] * nv + c] : float4{0.f, 0.f, 0.f, 0.f};
+                            h[q][u].x += h1.x;
+                            h[q][u].y += h1.y;
+                            h[q][u].z += h1.z;
+                            h[q][u].w += h1.w;
+                        }
                     }
                 }
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    acc[u].x = fmaf(a, h[u].x, acc[u].x);
-                    acc[u].y = fmaf(a, h[u].y, acc[u].y);
-                    acc[u].z = fmaf(a, h[u].z, acc[u].z);
-                    acc[u].w = fmaf(a, h[u].w, acc[u].w);
+                for (int q = 0; q < COMBINE_PR; ++q) {
+                    if (row[q] < 0) continue;
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        acc[u].x = fmaf(a[q], h[q][u].x, acc[u].x);
+                        acc[u].y = fmaf(a[q], h[q][u].y, acc[u].y);
+                        acc[u].z = fmaf(a[q], h[q][u].z, acc[u].z);
+                        acc[u].w = fmaf(a[q], h[q][u].w, acc[u].w);
+                    }
                 }
             }
 #pragma unroll
