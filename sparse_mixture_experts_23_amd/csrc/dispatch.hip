@@ -16,6 +16,9 @@
 //           earlier lanes (built with order-independent LDS atomic ORs), so
 //           the result never depends on thread timing
 //   gather: x_perm[row] = x[token], one wave per token, 16-byte vector copies.
+// Where the rows are copied and no router table exists, scan and place run
+// inside the gather's workgroups (dispatch_place_gather_kernel), on ranks the
+// count kernel leaves in `slot`.
 #include "common.h"
 #include "dispatch_block.h"
 
@@ -39,10 +42,13 @@ __device__ __forceinline__ void build_masks(unsigned long long* masks, const int
 }
 
 // acc_stats (nullable): the two statistics the placement accumulates with atomics,
-// cleared here (block 0) for dispatch_place_scan_kernel.
+// cleared here (block 0) for the placement kernels.
+// rank (nullable): also each path's rank among the block's paths to its expert,
+// in token order (0 for an id out of range), rank[t k + r].
 __global__ __launch_bounds__(DB_TOK) void dispatch_count_kernel(const int32_t* __restrict__ ids, int64_t T, int k,
                                                                 int E, int32_t* __restrict__ hist,
-                                                                int32_t* __restrict__ acc_stats) {
+                                                                int32_t* __restrict__ acc_stats,
+                                                                int32_t* __restrict__ rank) {
     extern __shared__ unsigned long long masks[];
     if (acc_stats && blockIdx.x == 0 && threadIdx.x < 2) acc_stats[threadIdx.x] = 0;
     build_masks(masks, ids, T, k, E);
@@ -52,6 +58,97 @@ __global__ __launch_bounds__(DB_TOK) void dispatch_count_kernel(const int32_t* _
         for (int w = 0; w < 4; ++w) c += __popcll(masks[w * E + e]);
         hist[(int64_t)blockIdx.x * E + e] = c;
     }
+    const int64_t t = (int64_t)blockIdx.x * DB_TOK + threadIdx.x;
+    if (rank && t < T) {
+        const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+        const unsigned long long below = (1ull << lane) - 1ull;
+        for (int r = 0; r < k; ++r) {
+            const int ee = ids[t * k + r];
+            int n = 0;
+            if ((unsigned)ee < (unsigned)E) {
+                n = __popcll(masks[wave * E + ee] & below);
+                for (int w = 0; w < wave; ++w) n += __popcll(masks[w * E + ee]);
+            }
+            rank[t * k + r] = n;
+        }
+    }
+}
+
+// Scans over the experts for one 256-thread workgroup: thread e < E (E <= 256)
+// brings L (= L_e) and base (the paths to e in the token blocks before this
+// workgroup's); on return (after a barrier) s_off[e] holds expert e's first
+// grouped row and s_base[e] its base.  Workgroup 0 also writes load, offsets,
+// the tile prefix (tprefix nullable; tprefix[e] = tiles of the experts before e,
+// rows per tile tile_rows) and the load statistics, and clears the other
+// statistics but the two token counts.
+__device__ __forceinline__ void expert_scan(int L, int base, int E, int C, int* s_off, int* s_base,
+                                            int32_t* __restrict__ load, int32_t* __restrict__ offsets,
+                                            int32_t* __restrict__ stats, int32_t* __restrict__ tprefix,
+                                            int tile_rows) {
+    __shared__ int s_sum[4], s_tiles[4], s_over[4], s_max[4];
+    const int e = threadIdx.x, wave = e / 64, lane = e % 64;
+    const int acc = e < E ? min(L, C) : 0;
+    const int over = e < E ? max(L - C, 0) : 0;
+    const int tiles = tprefix ? (acc + tile_rows - 1) / tile_rows : 0;
+    int incl = acc, tincl = tiles;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int sv = __shfl_up(incl, o, MOE_WAVE);
+        const int tv = __shfl_up(tincl, o, MOE_WAVE);
+        if (lane >= o) {
+            incl += sv;
+            tincl += tv;
+        }
+    }
+    int ov = over, mx = e < E ? L : 0;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        ov += __shfl_xor(ov, o, MOE_WAVE);
+        mx = max(mx, __shfl_xor(mx, o, MOE_WAVE));
+    }
+    if (lane == 63) {
+        s_sum[wave] = incl;
+        s_tiles[wave] = tincl;
+    }
+    if (lane == 0) {
+        s_over[wave] = ov;
+        s_max[wave] = mx;
+    }
+    __syncthreads();
+    int before = 0, total = 0, otot = 0, mtot = 0, tbefore = 0, ttotal = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        if (w < wave) {
+            before += s_sum[w];
+            tbefore += s_tiles[w];
+        }
+        total += s_sum[w];
+        ttotal += s_tiles[w];
+        otot += s_over[w];
+        mtot = max(mtot, s_max[w]);
+    }
+    const int off = before + incl - acc;
+    if (e < E) {
+        s_off[e] = off;
+        s_base[e] = base;
+    }
+    if (blockIdx.x == 0) {
+        if (e < E) {
+            load[e] = L;
+            offsets[e] = off;
+            if (tprefix) tprefix[e] = tbefore + tincl - tiles;
+        }
+        if (tprefix && e < MOE_SCHED_WORDS) moe_sched_words(tprefix, E)[e] = 0ull;
+        if (e == 0) {
+            offsets[E] = total;
+            if (tprefix) tprefix[E] = ttotal;
+            stats[MOE_STAT_OVERFLOW] = otot;
+            stats[MOE_STAT_ACCEPTED] = total;
+            stats[MOE_STAT_MAX_LOAD] = mtot;
+            for (int i = MOE_STAT_TOKENS_AFFECTED + 1; i < MOE_STAT_COUNT; ++i) stats[i] = 0;
+        }
+    }
+    __syncthreads();
 }
 
 // One workgroup of 1024 threads (E <= 1024): thread e scans expert e over blocks.
@@ -211,7 +308,7 @@ __global__ __launch_bounds__(DB_TOK) void dispatch_place_scan_kernel(
         *status = atomicExch(route_flag, 0) ? MOE_ERR_NONFINITE_LOGIT : MOE_OK;
     int* s_off = s_base + E;
     int* s_hist = s_off + E;
-    __shared__ int s_sum[4], s_tiles[4], s_over[4], s_max[4], s_drop[4], s_aff[4];
+    __shared__ int s_drop[4], s_aff[4];
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
     const int n = NR * E;
     {   // the table: up to 16 loads per thread, all in flight together
@@ -223,7 +320,7 @@ __global__ __launch_bounds__(DB_TOK) void dispatch_place_scan_kernel(
             if (tid + DB_TOK * u < n) s_hist[tid + DB_TOK * u] = v[u];
     }
     build_masks(masks, ids, T, k, E);   // its barriers also publish s_hist
-    // thread e < E <= 256: L_e, this block's base, accepted, tiles; scans over e
+    // thread e < E <= 256: L_e and this block's base, then the scans over e
     const int e = tid;
     int L = 0, base = 0;
     if (e < E) {
@@ -234,52 +331,7 @@ __global__ __launch_bounds__(DB_TOK) void dispatch_place_scan_kernel(
             L += h;
         }
     }
-    const int acc = e < E ? min(L, C) : 0;
-    const int over = e < E ? max(L - C, 0) : 0;
-    const int tiles = tprefix ? (acc + tile_rows - 1) / tile_rows : 0;
-    int incl = acc, tincl = tiles;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int sv = __shfl_up(incl, o, MOE_WAVE);
-        const int tv = __shfl_up(tincl, o, MOE_WAVE);
-        if (lane >= o) {
-            incl += sv;
-            tincl += tv;
-        }
-    }
-    int ov = over, mx = L;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        ov += __shfl_xor(ov, o, MOE_WAVE);
-        mx = max(mx, __shfl_xor(mx, o, MOE_WAVE));
-    }
-    if (lane == 63) {
-        s_sum[wave] = incl;
-        s_tiles[wave] = tincl;
-    }
-    if (lane == 0) {
-        s_over[wave] = ov;
-        s_max[wave] = mx;
-    }
-    __syncthreads();
-    int before = 0, total = 0, otot = 0, mtot = 0, tbefore = 0, ttotal = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        if (w < wave) {
-            before += s_sum[w];
-            tbefore += s_tiles[w];
-        }
-        total += s_sum[w];
-        ttotal += s_tiles[w];
-        otot += s_over[w];
-        mtot = max(mtot, s_max[w]);
-    }
-    const int off = before + incl - acc;
-    if (e < E) {
-        s_off[e] = off;
-        s_base[e] = base;
-    }
-    __syncthreads();
+    expert_scan(L, base, E, C, s_off, s_base, load, offsets, stats, tprefix, tile_rows);
     // place: as dispatch_place_kernel, with this block's bases from LDS
     const int64_t t = (int64_t)blockIdx.x * DB_TOK + tid;
     int dropped = 0, affected = 0;
@@ -313,22 +365,6 @@ __global__ __launch_bounds__(DB_TOK) void dispatch_place_scan_kernel(
     if (lane == 0) {
         s_drop[wave] = dropped;
         s_aff[wave] = affected;
-    }
-    if (blockIdx.x == 0) {
-        if (e < E) {
-            load[e] = L;
-            offsets[e] = off;
-            if (tprefix) tprefix[e] = tbefore + tincl - tiles;
-        }
-        if (tprefix && e < MOE_SCHED_WORDS) moe_sched_words(tprefix, E)[e] = 0ull;
-        if (e == 0) {
-            offsets[E] = total;
-            if (tprefix) tprefix[E] = ttotal;
-            stats[MOE_STAT_OVERFLOW] = otot;
-            stats[MOE_STAT_ACCEPTED] = total;
-            stats[MOE_STAT_MAX_LOAD] = mtot;
-            for (int i = MOE_STAT_TOKENS_AFFECTED + 1; i < MOE_STAT_COUNT; ++i) stats[i] = 0;
-        }
     }
     __syncthreads();
     if (tid == 0) {
@@ -555,6 +591,100 @@ __global__ __launch_bounds__(256) void dispatch_gather_kernel(const V* __restric
         for (int r = 0; r < k; ++r) {
             const int row = lane_value(myrow, r);
             if (row >= 0 && ok) x_perm[(int64_t)row * vec_per_row + c] = v;
+        }
+    }
+}
+
+// The standalone dispatch's placement, fused into its row gather.  The count
+// kernel has written the per-block table hist[NB][E] and, into `slot`, each
+// path's rank inside its 256-token block.  Every workgroup (4 tokens, one wave
+// each) scans the table for its block's bases and the grouped offsets, places
+// its tokens' paths (slot, row_of, src_token, as the separate placement would)
+// and copies their rows, whose first NPF 64-lane chunks are already in flight
+// while the table is scanned: the placement rides on the copy instead of taking
+// a launch of its own.  Workgroup 0 writes load, offsets, the tile prefix and
+// the load statistics; the two token statistics are left to
+// dispatch_token_stats_kernel (one atomic add per 256 tokens instead of one per
+// workgroup here, which serialise on their two words).  Dynamic LDS: s_base[E],
+// s_off[E], s_hist[NB E] int32.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // 16-byte chunks (kept in registers)
+template <typename V, int NPF>
+__global__ __launch_bounds__(256) void dispatch_place_gather_kernel(
+    const V* __restrict__ x, const int32_t* __restrict__ ids, int64_t T, int k, int E, int C,
+    const int32_t* __restrict__ hist, int NB, int32_t* __restrict__ load, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ slot, int32_t* __restrict__ row_of, int32_t* __restrict__ src_token,
+    int32_t* __restrict__ stats, int32_t* __restrict__ tprefix, int tile_rows, int64_t vec_per_row,
+    V* __restrict__ x_perm) {
+    extern __shared__ int s_base[];
+    int* s_off = s_base + E;
+    int* s_hist = s_off + E;
+    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+    const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+    const bool live = t < T;
+    const V* src = x + (live ? t : 0) * vec_per_row;
+    V v[NPF];   // unconditional loads (clamped into the row), all in flight together
+#pragma unroll
+    for (int u = 0; u < NPF; ++u) v[u] = src[min((int64_t)u * 64 + lane, vec_per_row - 1)];
+    // lane r < k: path r's expert and rank (loaded with the row, used after the scan)
+    const int64_t pr = (live ? t : 0) * k + min(lane, k - 1);
+    const int my_e = ids[pr], my_rank = slot[pr];
+    {   // the table into LDS: up to 16 loads per thread, all in flight together
+        const int n = NB * E;
+        int h[SCAN_INLINE_MAX / 256];
+#pragma unroll
+        for (int u = 0; u < SCAN_INLINE_MAX / 256; ++u) h[u] = hist[min(tid + 256 * u, n - 1)];
+#pragma unroll
+        for (int u = 0; u < SCAN_INLINE_MAX / 256; ++u)
+            if (tid + 256 * u < n) s_hist[tid + 256 * u] = h[u];
+    }
+    __syncthreads();
+    // thread e < E: L_e over all blocks, base = paths to e in the blocks before this one
+    const int blk = (int)((int64_t)blockIdx.x * 4 / DB_TOK);
+    int L = 0, base = 0;
+    if (tid < E) {
+        for (int b = 0; b < NB; ++b) {
+            const int h = s_hist[b * E + tid];
+            base += b < blk ? h : 0;
+            L += h;
+        }
+    }
+    expert_scan(L, base, E, C, s_off, s_base, load, offsets, stats, tprefix, tile_rows);
+    // lane r < k places path r of this wave's token
+    int myrow = -1;
+    if (live && lane < k) {
+        int c = -1;
+        if ((unsigned)my_e < (unsigned)E) {
+            const int cand = s_base[my_e] + my_rank;
+            if (cand < C) {
+                c = cand;
+                myrow = s_off[my_e] + cand;
+                src_token[myrow] = (int32_t)t;
+            }
+        }
+        slot[t * k + lane] = c;
+        row_of[t * k + lane] = myrow;
+    }
+    if (live) {
+        for (int r = 0; r < k; ++r) {
+            const int row = lane_value(myrow, r);   // uniform over the wave
+            if (row < 0) continue;
+            V* dst = x_perm + (int64_t)row * vec_per_row;
+#pragma unroll
+            for (int u = 0; u < NPF; ++u) {
+                const int64_t c = (int64_t)u * 64 + lane;
+                if (c < vec_per_row) dst[c] = v[u];
+            }
+        }
+        // uniform trip count: every lane stays active around lane_value
+        for (int64_t c0 = (int64_t)NPF * 64; c0 < vec_per_row; c0 += 64) {
+            const int64_t c = c0 + lane;
+            const bool ok = c < vec_per_row;
+            V w;
+            if (ok) w = src[c];
+            for (int r = 0; r < k; ++r) {
+                const int row = lane_value(myrow, r);
+                if (row >= 0 && ok) x_perm[(int64_t)row * vec_per_row + c] = w;
+            }
         }
     }
 }
@@ -809,7 +939,7 @@ hipError_t launch_dispatch(const moe_dims& s, const void* x, const int32_t* ids,
         int32_t* req_path = reinterpret_cast<int32_t*>(p);
         if (NB > 0)
             hipLaunchKernelGGL(dispatch_count_kernel, dim3(NB), dim3(DB_TOK), mask_lds, st, ids, s.T, s.k, s.E,
-                               hist, (int32_t*)nullptr);
+                               hist, (int32_t*)nullptr, (int32_t*)nullptr);
         hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, st, hist, NB, s.E, s.C, load, offsets,
                            stats, tprefix, tile_rows, roff);
         if (NB == 0) return hipGetLastError();
@@ -823,13 +953,36 @@ hipError_t launch_dispatch(const moe_dims& s, const void* x, const int32_t* ids,
     } else if (NB == 1) {
         hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(1024), mask_lds + sizeof(int) * s.E, st, ids, s.T,
                            s.k, s.E, s.C, load, offsets, stats, tprefix, tile_rows, slot, row_of, src_token);
+    } else if (NB > 0 && dispatch_inline_scan(s) && !hist_ready && x_perm) {
+        // standalone, with the row copy: count (table and ranks), then placement + gather
+        hipLaunchKernelGGL(dispatch_count_kernel, dim3(NB), dim3(DB_TOK), mask_lds, st, ids, s.T, s.k, s.E, hist,
+                           stats + MOE_STAT_TOKENS_DROPPED, slot);
+        const int elem = s.dtype == MOE_BF16 ? 2 : 4;
+        const int64_t row_bytes = (int64_t)s.d * elem;
+        const unsigned grid = (unsigned)((s.T + 3) / 4);
+        const size_t lds = sizeof(int32_t) * (2 + (size_t)NB) * s.E;
+        if (row_bytes % 16 == 0)
+            hipLaunchKernelGGL((dispatch_place_gather_kernel<u32x4, 8>), dim3(grid), dim3(256), lds, st,
+                               static_cast<const u32x4*>(x), ids, s.T, s.k, s.E, s.C, hist, NB, load, offsets, slot,
+                               row_of, src_token, stats, tprefix, tile_rows, row_bytes / 16,
+                               static_cast<u32x4*>(x_perm));
+        else   // fp32 rows (bf16 rows are whole 16-byte chunks: d % 8 == 0)
+            hipLaunchKernelGGL((dispatch_place_gather_kernel<uint32_t, 8>), dim3(grid), dim3(256), lds, st,
+                               static_cast<const uint32_t*>(x), ids, s.T, s.k, s.E, s.C, hist, NB, load, offsets,
+                               slot, row_of, src_token, stats, tprefix, tile_rows, row_bytes / 4,
+                               static_cast<uint32_t*>(x_perm));
+        // with distinct ids per token no path is rejected unless C < T (the
+        // counters stay as the count kernel cleared them)
+        if (s.C < s.T)
+            hipLaunchKernelGGL(dispatch_token_stats_kernel, dim3(NB), dim3(DB_TOK), 0, st, row_of, s.T, s.k, stats);
+        return hipGetLastError();
     } else if (NB > 0 && dispatch_inline_scan(s)) {
         // the token statistics are accumulated by the placement into counters the
         // table's writer clears (here the count kernel, else the router, whose
         // table has one row per 64 tokens)
         if (!hist_ready)
             hipLaunchKernelGGL(dispatch_count_kernel, dim3(NB), dim3(DB_TOK), mask_lds, st, ids, s.T, s.k, s.E,
-                               hist, stats + MOE_STAT_TOKENS_DROPPED);
+                               hist, stats + MOE_STAT_TOKENS_DROPPED, (int32_t*)nullptr);
         const int sub = hist_ready ? DB_TOK / MOE_ROUTE_TOK : 1;
         const int NR = hist_ready ? (int)((s.T + MOE_ROUTE_TOK - 1) / MOE_ROUTE_TOK) : NB;
         const size_t lds = mask_lds + sizeof(int32_t) * (2 * s.E + (size_t)NR * s.E);
@@ -839,7 +992,7 @@ hipError_t launch_dispatch(const moe_dims& s, const void* x, const int32_t* ids,
     } else {
         if (NB > 0) {
             hipLaunchKernelGGL(dispatch_count_kernel, dim3(NB), dim3(DB_TOK), mask_lds, st, ids, s.T, s.k, s.E,
-                               hist, (int32_t*)nullptr);
+                               hist, (int32_t*)nullptr, (int32_t*)nullptr);
         }
         hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, st, hist, NB, s.E, s.C, load, offsets,
                            stats, tprefix, tile_rows, (int32_t*)nullptr);
@@ -855,14 +1008,10 @@ hipError_t launch_dispatch(const moe_dims& s, const void* x, const int32_t* ids,
     if (row_bytes % 16 == 0)
         hipLaunchKernelGGL(dispatch_gather_kernel<uint4>, dim3(grid), dim3(256), 0, st, static_cast<const uint4*>(x),
                            s.T, P, row_bytes / 16, row_of, static_cast<uint4*>(x_perm));
-    else if (row_bytes % 4 == 0)
+    else   // fp32 rows (bf16 rows are whole 16-byte chunks: d % 8 == 0)
         hipLaunchKernelGGL(dispatch_gather_kernel<uint32_t>, dim3(grid), dim3(256), 0, st,
                            static_cast<const uint32_t*>(x), s.T, P, row_bytes / 4, row_of,
                            static_cast<uint32_t*>(x_perm));
-    else
-        hipLaunchKernelGGL(dispatch_gather_kernel<uint16_t>, dim3(grid), dim3(256), 0, st,
-                           static_cast<const uint16_t*>(x), s.T, P, row_bytes / 2, row_of,
-                           static_cast<uint16_t*>(x_perm));
     return hipGetLastError();
 }
 

@@ -558,6 +558,36 @@ def test_exact_ties_lower_id_wins(case):
 # edge cases and properties
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("T,d,dtype,E,k,cf", [
+    (600, 64, torch.bfloat16, 12, 3, (1, 2)),    # 16-byte chunks, half the paths rejected
+    (600, 34, torch.float32, 12, 3, None),       # 4-byte chunks
+    (257, 40, torch.bfloat16, 5, 2, (1, 1)),     # one token in the last block
+    (600, 3, torch.float32, 8, 1, (1, 2)),       # fp32 rows of 12 bytes
+    (600, 64, torch.bfloat16, 1, 1, (1, 2)),     # one expert
+    (777, 4160, torch.bfloat16, 16, 2, (5, 4)),  # rows longer than the chunks loaded ahead (16-byte)
+    (300, 1025, torch.float32, 7, 4, (1, 2)),    # rows longer than the chunks loaded ahead (4-byte)
+])
+def test_dispatch_row_copy_widths(T, d, dtype, E, k, cf):
+    """The standalone dispatch over more than one 256-token block, on both row
+    widths the row copy distinguishes (16- and 4-byte chunks, rows shorter and
+    longer than the part loaded while the placement is computed), with and
+    without rejections: slots, row map, loads, offsets, statistics and rows equal
+    the oracle's serial slot loop bit for bit (ids drawn as random distinct
+    experts per token)."""
+    rng = np.random.default_rng(T * 7919 + d * 31 + E)
+    ids_np = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    C = api.capacity(T, k, E, *cf) if cf else T
+    shape = api.make_shape(T, d, 8, E, k, C if cf else 0, L.MOE_GATE_RENORM, dtype)
+    x = torch.randn((T, d), device=DEV).to(dtype)
+    disp = api.dispatch(shape, x, torch.tensor(ids_np, device=DEV))
+    torch.cuda.synchronize()
+    plain = MoEConfig("dispatch_only", T=T, d=d, m=8, E=E, k=k, dtype="bf16" if dtype == torch.bfloat16 else "f32",
+                      gate_mode=0, cf=cf, cfg_id=0)
+    ref = compare_dispatch(plain, ids_np, C, disp, x)
+    log(f"[dispatch] T={T} d={d} {dtype} E={E} k={k} C={C}: ok  accepted {int(ref.offsets[-1])} of {T * k}, "
+        f"tokens dropped {ref.tokens_dropped}")
+
+
 def test_empty_group():
     shape = api.make_shape(0, 64, 64, 8, 2, 0, L.MOE_GATE_RENORM, torch.bfloat16)
     x = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
