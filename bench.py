@@ -38,7 +38,7 @@ METRIC = "MoE-layer tokens/sec on 1 MI355X (Mixtral shape); expert-GEMM % of MFM
 # the bytes-per-KiB that the same counter reports for a plain device copy of known
 # size (`bench.py --copy-calibration`).  Valid only for the GEMM source it was
 # taken on: reported as null once expert_gemm.hip differs from that hash.
-GEMM1_TRAFFIC = {"bytes": 6295945328, "source_sha256": "45a1b2906a5d85cfd46fdcf4da9fb591aabf6280919d2fcfbcb731aaaf730681"}
+GEMM1_TRAFFIC = {"bytes": 6340091130, "source_sha256": "6c65a95c5971346d7e2a08453f9d4ed1eaa6ca5b244b15606034a24a01a5beab"}
 GEMM_SOURCE = os.path.join(ROOT, "sparse_mixture_experts_23_amd", "csrc", "expert_gemm.hip")
 
 

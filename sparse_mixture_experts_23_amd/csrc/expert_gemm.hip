@@ -417,7 +417,12 @@ __device__ __forceinline__ void lds_barrier_reads_done() {
 // activation loads of tile kt + 2 and the reads of the next tile's first
 // operands.  Splitting the 8 loads over two substeps instead of one burst saved
 // ~3 % of the layer.  Every LDS read the block issues is waited for inside the
-// block.
+// block.  Past the barrier a wave raises its issue priority (s_setprio 1) and
+// drops it again after the next tile's first substep, so the waves still in
+// that stretch -- the ones behind -- win the SIMD's issue over those already
+// past it and the workgroup reaches its next barrier closer together (GEMM1
+// of the Mixtral layer 2.5-3.5 % faster, GEMM2 ~2 %, same-box A/B; raising it
+// in steps over all four substeps measured the same).
 //
 // The MFMAs take the weight fragment as their first operand (C^T = B^T A^T), so a
 // lane's accumulator holds one output row and, per group of 4 registers, 4
@@ -469,6 +474,7 @@ __device__ __forceinline__ void lds_barrier_reads_done() {
     "s_waitcnt lgkmcnt(0)\n\t"                                                           \
     "s_waitcnt vmcnt(4)\n\t"                                                             \
     "s_barrier\n\t"                                                                      \
+    "s_setprio 1\n\t"                                                                     \
     MOE_M0(ldsA, "0") MOE_MF(c0, ya0, yb0) MOE_LD(vo0, sa)                                  \
     MOE_M0(ldsA, "8192") MOE_MF(c1, ya1, yb0) MOE_LD(vo1, sa) MOE_DSR(xa0, na0, "0")        \
     MOE_M0(ldsA, "16384") MOE_MF(c2, ya0, yb1) MOE_LD(vo2, sa) MOE_DSR(xb0, nb0, "0")       \
@@ -496,6 +502,7 @@ __device__ __forceinline__ void gemm_tile_asm(floatx16_t (&c)[8], bf16x8_t (&x)[
     uint32_t saved_m0;
     asm volatile("s_mov_b32 %[sv], m0\n\t"
                  MOE_SUBSTEP_B(x, y, ra1, rb1)
+                 "s_setprio 0\n\t"
                  MOE_SUBSTEP(y, x, ra2, rb2)
                  MOE_SUBSTEP(x, y, ra3, rb3)
                  MOE_LASTSUB
@@ -528,6 +535,7 @@ __device__ __forceinline__ void gemm_tile_asm(floatx16_t (&c)[8], bf16x8_t (&x)[
     "s_waitcnt lgkmcnt(0)\n\t"                                                           \
     "s_waitcnt vmcnt(4)\n\t"                                                             \
     "s_barrier\n\t"                                                                      \
+    "s_setprio 1\n\t"                                                                     \
     MOE_M0(ldsA, "0") MOE_MF(c0, ya0, yb0) MOE_LD(vo0, sa)                                  \
     MOE_M0(ldsA, "8192") MOE_DSR(xa0, na0, "0") MOE_LD(vo1, sa)                             \
     MOE_M0(ldsA, "16384") MOE_MF(c2, ya0, yb1) MOE_LD(vo2, sa)                              \
@@ -546,6 +554,7 @@ __device__ __forceinline__ void gemm_tile_asm_half(floatx16_t (&c)[8], bf16x8_t 
     uint32_t saved_m0;
     asm volatile("s_mov_b32 %[sv], m0\n\t"
                  MOE_SUBSTEP_HALF_B(x, y, ra1, rb1)
+                 "s_setprio 0\n\t"
                  MOE_SUBSTEP_HALF(y, x, ra2, rb2)
                  MOE_SUBSTEP_HALF(x, y, ra3, rb3)
                  MOE_LASTSUB_HALF
@@ -610,6 +619,7 @@ __device__ __forceinline__ void gemm_tile_asm_loads_only(floatx16_t (&c)[8], bf1
     "s_waitcnt lgkmcnt(0)\n\t"                                                           \
     "s_waitcnt vmcnt(10)\n\t"                                                            \
     "s_barrier\n\t"                                                                      \
+    "s_setprio 1\n\t"                                                                     \
     MOE_MF(c0, ya0, yb0) MOE_DSR(xa0, na0, "0")                                          \
     MOE_MF(c2, ya0, yb1) MOE_DSR(xb0, nb0, "0")                                          \
     MOE_MF(c4, ya0, yb2) MOE_DSRI(xb1, nb0, ob1) MOE_DSRI(xb2, nb0, ob2)                 \
@@ -626,6 +636,7 @@ __device__ __forceinline__ void gemm_tile_asm_thin(floatx16_t (&c)[8], bf16x8_t 
     uint32_t saved_m0;
     asm volatile("s_mov_b32 %[sv], m0\n\t"
                  MOE_SUBSTEP_HALF_B(x, y, ra1, rb1)
+                 "s_setprio 0\n\t"
                  MOE_SUBSTEP_HALF_A1(y, x, ra2, rb2)
                  MOE_SUBSTEP_HALF(x, y, ra3, rb3)
                  MOE_LASTSUB_HALF_THIN
