@@ -308,6 +308,26 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_r, 
                        int32_t* slot, int32_t* stats, int32_t* status,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* Weight repacking, once per weight set and outside the forward: a batched
+ * transpose dst[b][j][i] = src[b][i][j] (b < batch, i < rows, j < cols) of
+ * elements of elem_bytes (2: bf16, 4: fp32), the bits copied unchanged.  It
+ * turns weights kept in the pages' x W layout, in-features x out-features
+ * ("LLM from scratch" ch. 36 §36.1; §36.8 notes that libraries store the
+ * transpose), into this library's out x in layout:
+ *   router W_r [d,E] fp32           batch 1, rows d,   cols E     -> w_r [E,d]
+ *   W_gate, W_up [E,d,m] dtype      batch E, rows d,   cols m     -> [E,m,d]
+ *   W_down [E,m,d] dtype            batch E, rows m,   cols d     -> [E,d,m]
+ *   shared gate / up [d,m_shared]   batch 1, rows d,   cols m_shared
+ *   shared down [m_shared,d]        batch 1, rows m_shared, cols d
+ *   src, dst   device buffers of batch x rows x cols elements; they must not
+ *              overlap (no in-place transpose); the caller owns both
+ * Returns MOE_ERR_INVALID_ARGUMENT (launching nothing) for a null pointer with a
+ * non-empty matrix, negative sizes, elem_bytes other than 2 or 4, or
+ * overlapping buffers, and MOE_ERR_UNSUPPORTED for batch > 65535 or
+ * rows > 4194240.  Asynchronous on `stream`. */
+moe_status moe_pack_weights(const void* src, void* dst, int64_t batch, int64_t rows, int64_t cols,
+                            int32_t elem_bytes, void* stream);
+
 /* moe_forward for callers that cannot allocate device memory: code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
  * same kernels and results as moe_forward (bit for bit), but the workspace is a

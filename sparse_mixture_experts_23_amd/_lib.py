@@ -89,6 +89,7 @@ _SIGS = {
     "moe_combine": (c_int32, [POINTER(MoeShape), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "moe_forward": (c_int32, [POINTER(MoeShape)] + [c_void_p] * 16 + [c_void_p, c_size_t, c_void_p]),
     "moe_forward_noalloc": (c_int32, [POINTER(MoeShape)] + [c_void_p] * 16 + [c_void_p]),
+    "moe_pack_weights": (c_int32, [c_void_p, c_void_p, c_int64, c_int64, c_int64, c_int32, c_void_p]),
 }
 
 _lib = None
@@ -192,3 +193,7 @@ def moe_forward_noalloc(shape, x, w_r, b_r, w_gate, w_up, w_down, s_gate, s_up, 
                         slot, stats, status, stream) -> int:
     return lib().moe_forward_noalloc(ctypes.byref(shape), x, w_r, b_r, w_gate, w_up, w_down, s_gate, s_up, s_down,
                                      y, topk_ids, topk_w, load, slot, stats, status, stream)
+
+
+def moe_pack_weights(src, dst, batch, rows, cols, elem_bytes, stream) -> int:
+    return lib().moe_pack_weights(src, dst, batch, rows, cols, elem_bytes, stream)

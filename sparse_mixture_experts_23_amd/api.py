@@ -74,6 +74,21 @@ def workspace(shape: L.MoeShape, kind: int, device="cuda") -> torch.Tensor:
     return ws
 
 
+def pack_weights(w: torch.Tensor) -> torch.Tensor:
+    """A weight in the pages' in x out layout, [rows, cols] or [batch, rows, cols]
+    (bf16 or fp32), as the library's out x in layout [.., cols, rows]:
+    W_r [d,E] -> w_r [E,d]; W_gate, W_up [E,d,m] -> [E,m,d]; W_down [E,m,d] -> [E,d,m]."""
+    if w.dtype not in (torch.bfloat16, torch.float32) or w.dim() not in (2, 3) or not w.is_cuda \
+            or not w.is_contiguous():
+        raise ValueError(f"pack_weights: expected a contiguous 2-D or 3-D bf16/fp32 GPU tensor, got "
+                         f"{w.dtype} {tuple(w.shape)} on {w.device}")
+    batch, rows, cols = (1,) + tuple(w.shape) if w.dim() == 2 else tuple(w.shape)
+    out = torch.empty(w.shape[:-2] + (cols, rows), dtype=w.dtype, device=w.device)
+    L.check(L.moe_pack_weights(_ptr(w), _ptr(out), batch, rows, cols, w.element_size(), _stream()),
+            "moe_pack_weights")
+    return out
+
+
 def route(shape: L.MoeShape, x, w_r, b_r=None):
     """Returns (topk_ids [T,P] int32, topk_w [T,P] fp32, status [1] int32), P = paths(shape)."""
     dev = x.device

@@ -17,7 +17,7 @@ OBJ = os.path.join(PKG, "_build")
 LIB_NAME = "libmoe_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["router.hip", "dispatch.hip", "expert_gemm.hip", "combine.hip", "moe_api.hip"]
+SOURCES = ["router.hip", "dispatch.hip", "expert_gemm.hip", "combine.hip", "pack.hip", "moe_api.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

@@ -148,6 +148,11 @@ hipError_t launch_prob_sum(const moe_dims& s, const float* probs, float* prob_su
 hipError_t launch_balance(const moe_dims& s, const int32_t* load, const int32_t* stats, const float* prob_sum,
                           float* out, hipStream_t st);
 
+// dst[b][j][i] = src[b][i][j] over batch matrices of rows x cols elements of
+// elem_bytes (2 or 4); grid limits: batch <= 65535, rows <= 65535 x 64.
+hipError_t launch_transpose(const void* src, void* dst, int64_t batch, int64_t rows, int64_t cols, int elem_bytes,
+                            hipStream_t st);
+
 // Dispatch.
 size_t dispatch_ws_bytes(const moe_dims& s);
 // Whether launch_dispatch reads the per-block expert counts (more than one token

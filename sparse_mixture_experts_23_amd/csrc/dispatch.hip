@@ -979,7 +979,7 @@ hipError_t launch_dispatch(const moe_dims& s, const void* x, const int32_t* ids,
     } else if (NB > 0 && dispatch_inline_scan(s)) {
         // the token statistics are accumulated by the placement into counters the
         // table's writer clears (here the count kernel, else the router, whose
-        // table has one row per 64 tokens)
+        // table has one row per MOE_ROUTE_TOK tokens)
         if (!hist_ready)
             hipLaunchKernelGGL(dispatch_count_kernel, dim3(NB), dim3(DB_TOK), mask_lds, st, ids, s.T, s.k, s.E,
                                hist, stats + MOE_STAT_TOKENS_DROPPED, (int32_t*)nullptr);

@@ -423,6 +423,18 @@ moe_status moe_route_stats(const moe_shape* shape, const void* x, const float* w
     return hip_status(launch_prob_sum(d, probs, prob_sum, st));
 }
 
+moe_status moe_pack_weights(const void* src, void* dst, int64_t batch, int64_t rows, int64_t cols,
+                            int32_t elem_bytes, void* stream) {
+    if (batch < 0 || rows < 0 || cols < 0 || (elem_bytes != 2 && elem_bytes != 4)) return MOE_ERR_INVALID_ARGUMENT;
+    if (batch == 0 || rows == 0 || cols == 0) return MOE_OK;
+    if (batch > 65535 || rows > 65535 * 64) return MOE_ERR_UNSUPPORTED;
+    if (!src || !dst) return MOE_ERR_INVALID_ARGUMENT;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+    const uintptr_t n = static_cast<uintptr_t>(batch * rows * cols * elem_bytes);
+    if (a < b + n && b < a + n) return MOE_ERR_INVALID_ARGUMENT;   // overlapping buffers
+    return hip_status(launch_transpose(src, dst, batch, rows, cols, elem_bytes, static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_balance(const moe_shape* shape, const int32_t* load, const int32_t* stats, const float* prob_sum,
                        float* out, void* stream) {
     moe_dims d;

@@ -139,3 +139,20 @@ def test_argument_errors_return_before_any_launch():
     assert L.moe_forward(s, *args, fake, 16, None) == L.MOE_ERR_WORKSPACE_TOO_SMALL
     assert L.moe_status_str(L.MOE_ERR_NONFINITE_LOGIT).startswith("MOE_ERR_NONFINITE_LOGIT")
     assert L.moe_status_str(99) == "unknown moe_status"
+
+
+def test_pack_weights_argument_checks():
+    """moe_pack_weights refuses bad arguments on the host, before any launch (the
+    addresses below are never dereferenced)."""
+    a, b = 1 << 40, 1 << 41
+    assert L.moe_pack_weights(a, b, 1, 4, 4, 3, None) == L.MOE_ERR_INVALID_ARGUMENT     # element size
+    assert L.moe_pack_weights(a, b, -1, 4, 4, 2, None) == L.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_pack_weights(a, b, 1, -4, 4, 2, None) == L.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_pack_weights(None, b, 1, 4, 4, 2, None) == L.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_pack_weights(a, None, 1, 4, 4, 4, None) == L.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_pack_weights(a, a + 16, 1, 4, 4, 2, None) == L.MOE_ERR_INVALID_ARGUMENT  # overlap
+    assert L.moe_pack_weights(a + 16, a, 1, 4, 4, 2, None) == L.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_pack_weights(a, b, 65536, 4, 4, 2, None) == L.MOE_ERR_UNSUPPORTED
+    assert L.moe_pack_weights(a, b, 1, 65535 * 64 + 1, 4, 2, None) == L.MOE_ERR_UNSUPPORTED
+    assert L.moe_pack_weights(None, None, 0, 4, 4, 2, None) == L.MOE_OK                   # empty: nothing to do
+    assert L.moe_pack_weights(None, None, 3, 4, 0, 4, None) == L.MOE_OK

@@ -588,6 +588,45 @@ def test_dispatch_row_copy_widths(T, d, dtype, E, k, cf):
         f"tokens dropped {ref.tokens_dropped}")
 
 
+@pytest.mark.parametrize("shape,dtype", [((4096, 8), torch.float32), ((3, 130, 70), torch.bfloat16),
+                                         ((8, 64, 64), torch.bfloat16), ((2, 1, 65), torch.float32),
+                                         ((5, 200, 1), torch.bfloat16), ((1, 129, 4100), torch.bfloat16)],
+                         ids=["w_r", "ragged_bf16", "whole_tiles", "one_row", "one_col", "wide"])
+def test_pack_weights_is_the_transpose(shape, dtype):
+    """moe_pack_weights copies every element to its transposed place, bit for bit
+    (ragged 64 x 64 tiles, single rows and columns, fp32 and bf16)."""
+    g = torch.Generator().manual_seed(sum(shape))
+    w = torch.randn(shape, generator=g).to(dtype).to(DEV)
+    packed = api.pack_weights(w)
+    torch.cuda.synchronize()
+    want = w.transpose(-1, -2).contiguous()
+    assert packed.shape == want.shape
+    assert torch.equal(packed.view(torch.int16 if dtype == torch.bfloat16 else torch.int32),
+                       want.view(torch.int16 if dtype == torch.bfloat16 else torch.int32))
+
+
+def test_forward_on_weights_packed_from_the_pages_layout():
+    """Weights kept in the pages' x W layout (W_r [d,E], W_gate / W_up [E,d,m],
+    W_down [E,m,d], shared [d,m_s] / [m_s,d]) and repacked with
+    moe_pack_weights give the same layer, bit for bit, as the library's own
+    layout."""
+    cfg = MoEConfig("packed", T=300, d=256, m=192, E=8, k=2, dtype="bf16", gate_mode=0, cf=(5, 4), m_shared=64,
+                    cfg_id=31)
+    inp = make_inputs(cfg, 0, DEV)
+    shape = shape_of(cfg)
+    ref = api.forward(shape, inp.x, inp.w_r, inp.b_r, inp.w_gate, inp.w_up, inp.w_down, inp.s_gate, inp.s_up,
+                      inp.s_down)
+    pages = [t.transpose(-1, -2).contiguous() for t in (inp.w_r, inp.w_gate, inp.w_up, inp.w_down, inp.s_gate,
+                                                         inp.s_up, inp.s_down)]
+    assert pages[0].shape == (cfg.d, cfg.E) and pages[1].shape == (cfg.E, cfg.d, cfg.m)
+    assert pages[3].shape == (cfg.E, cfg.m, cfg.d) and pages[6].shape == (cfg.m_shared, cfg.d)
+    packed = [api.pack_weights(t) for t in pages]
+    out = api.forward(shape, inp.x, packed[0], inp.b_r, *packed[1:])
+    torch.cuda.synchronize()
+    assert torch.equal(out.y, ref.y) and torch.equal(out.topk_ids, ref.topk_ids)
+    assert torch.equal(out.slot, ref.slot) and torch.equal(out.stats, ref.stats)
+
+
 def test_empty_group():
     shape = api.make_shape(0, 64, 64, 8, 2, 0, L.MOE_GATE_RENORM, torch.bfloat16)
     x = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
