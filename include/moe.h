@@ -323,8 +323,9 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_r, 
  *              overlap (no in-place transpose); the caller owns both
  * Returns MOE_ERR_INVALID_ARGUMENT (launching nothing) for a null pointer with a
  * non-empty matrix, negative sizes, elem_bytes other than 2 or 4, or
- * overlapping buffers, and MOE_ERR_UNSUPPORTED for batch > 65535 or
- * rows > 4194240.  Asynchronous on `stream`. */
+ * overlapping buffers, and MOE_ERR_UNSUPPORTED for batch > 65535,
+ * rows > 4194240 or more than INT64_MAX / 4 bytes in all.  Asynchronous on
+ * `stream`. */
 moe_status moe_pack_weights(const void* src, void* dst, int64_t batch, int64_t rows, int64_t cols,
                             int32_t elem_bytes, void* stream);
 

@@ -428,6 +428,7 @@ moe_status moe_pack_weights(const void* src, void* dst, int64_t batch, int64_t r
     if (batch < 0 || rows < 0 || cols < 0 || (elem_bytes != 2 && elem_bytes != 4)) return MOE_ERR_INVALID_ARGUMENT;
     if (batch == 0 || rows == 0 || cols == 0) return MOE_OK;
     if (batch > 65535 || rows > 65535 * 64) return MOE_ERR_UNSUPPORTED;
+    if (cols > INT64_MAX / 4 / batch / rows) return MOE_ERR_UNSUPPORTED;   // the byte count must fit int64
     if (!src || !dst) return MOE_ERR_INVALID_ARGUMENT;
     const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
     const uintptr_t n = static_cast<uintptr_t>(batch * rows * cols * elem_bytes);

@@ -154,5 +154,6 @@ def test_pack_weights_argument_checks():
     assert L.moe_pack_weights(a + 16, a, 1, 4, 4, 2, None) == L.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_pack_weights(a, b, 65536, 4, 4, 2, None) == L.MOE_ERR_UNSUPPORTED
     assert L.moe_pack_weights(a, b, 1, 65535 * 64 + 1, 4, 2, None) == L.MOE_ERR_UNSUPPORTED
+    assert L.moe_pack_weights(a, b, 65535, 1 << 22, 1 << 40, 2, None) == L.MOE_ERR_UNSUPPORTED   # int64 bytes
     assert L.moe_pack_weights(None, None, 0, 4, 4, 2, None) == L.MOE_OK                   # empty: nothing to do
     assert L.moe_pack_weights(None, None, 3, 4, 0, 4, None) == L.MOE_OK
