@@ -582,7 +582,7 @@ def test_dispatch_row_copy_widths(T, d, dtype, E, k, cf):
     disp = api.dispatch(shape, x, torch.tensor(ids_np, device=DEV))
     torch.cuda.synchronize()
     plain = MoEConfig("dispatch_only", T=T, d=d, m=8, E=E, k=k, dtype="bf16" if dtype == torch.bfloat16 else "f32",
-                      gate_mode=0, cf=cf, cfg_id=0)
+                      gate_mode=0, cf=cf, cfg_id=61)
     ref = compare_dispatch(plain, ids_np, C, disp, x)
     log(f"[dispatch] T={T} d={d} {dtype} E={E} k={k} C={C}: ok  accepted {int(ref.offsets[-1])} of {T * k}, "
         f"tokens dropped {ref.tokens_dropped}")
@@ -611,7 +611,7 @@ def test_forward_on_weights_packed_from_the_pages_layout():
     moe_pack_weights give the same layer, bit for bit, as the library's own
     layout."""
     cfg = MoEConfig("packed", T=300, d=256, m=192, E=8, k=2, dtype="bf16", gate_mode=0, cf=(5, 4), m_shared=64,
-                    cfg_id=31)
+                    cfg_id=59)
     inp = make_inputs(cfg, 0, DEV)
     shape = shape_of(cfg)
     ref = api.forward(shape, inp.x, inp.w_r, inp.b_r, inp.w_gate, inp.w_up, inp.w_down, inp.s_gate, inp.s_up,
@@ -924,6 +924,9 @@ def test_gpu_balance_matches_oracle(cfg):
     # the dispatch kernel clears inside the graph on every replay
     MoEConfig("graph_multi_round", T=2048, d=2048, m=1024, E=64, k=8, dtype="bf16", gate_mode=0, cf=(5, 4),
               bias="zipf", cfg_id=54),
+    # fp32: the forward copies the grouped rows, with the placement inside the copy
+    # kernel and the token statistics from their own kernel (C < T)
+    MoEConfig("graph_fp32_copy", T=600, d=128, m=64, E=12, k=3, dtype="f32", gate_mode=0, cf=(1, 2), cfg_id=62),
 ], ids=lambda c: c.name)
 def test_forward_captures_into_a_graph(cfg):
     """moe_forward queues no host synchronisation and no memset, so it can be
