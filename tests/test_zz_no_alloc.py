@@ -46,6 +46,9 @@ CASES = [
                bias="zipf", cfg_id=72), 333),
     # fp32 layer
     (MoEConfig("noalloc_f32", T=200, d=96, m=64, E=6, k=2, dtype="f32", gate_mode=0, cf=(1, 1), cfg_id=73), 17),
+    # fp32 over several token blocks: the grouped-row copy with the placement inside it
+    (MoEConfig("noalloc_f32_copy", T=600, d=128, m=64, E=12, k=3, dtype="f32", gate_mode=0, cf=(1, 2),
+               cfg_id=74), 300),
 ]
 
 
