@@ -566,6 +566,8 @@ def test_exact_ties_lower_id_wins(case):
     (600, 64, torch.bfloat16, 1, 1, (1, 2)),     # one expert
     (777, 4160, torch.bfloat16, 16, 2, (5, 4)),  # rows longer than the chunks loaded ahead (16-byte)
     (300, 1025, torch.float32, 7, 4, (1, 2)),    # rows longer than the chunks loaded ahead (4-byte)
+    (4096, 64, torch.bfloat16, 256, 2, (1, 2)),  # the largest table the copy kernel stages (16 x 256)
+    (3000, 64, torch.bfloat16, 128, 8, (5, 4)),  # k = 8, a ragged last block
 ])
 def test_dispatch_row_copy_widths(T, d, dtype, E, k, cf):
     """The standalone dispatch over more than one 256-token block, on both row
